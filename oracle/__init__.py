@@ -1,0 +1,189 @@
+"""CPU oracle for the Q4_K batched verify step (ctypes wrapper over kq_oracle.c).
+
+TEST INFRASTRUCTURE ONLY. The product library never imports, links or runs
+anything here; only tests/, the smoke check and the bench's CPU-baseline leg
+do. It shares no code with the HIP path: its own fp16 decode, its own scale
+unpacking, its own fp64 dot products.
+
+What each function follows is stated in kq_oracle.c. Every function here is
+pinned by CPU tests against hand-built blocks, exact rational arithmetic,
+closed forms and brute-force enumeration (tests/test_oracle_*.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kq_oracle.c")
+_LIB = os.path.join(_HERE, "libkq_oracle.so")
+_lib = None
+
+REL_TOL = 1e-4  # declared logit tolerance: |G - L| <= REL_TOL * sum_k |w_k x_k|
+
+
+def build(force: bool = True) -> str:
+    """Compile kq_oracle.c with gcc (-O2 -fopenmp, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.kqo_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.kqo_half_to_double.restype = ctypes.c_double
+    lib.kqo_scales_mins.argtypes = [P, P, P]
+    lib.kqo_quant.argtypes = [P, ctypes.c_int]
+    lib.kqo_quant.restype = ctypes.c_int
+    lib.kqo_decode_block.argtypes = [P, P]
+    lib.kqo_decode_block.restype = ctypes.c_int
+    lib.kqo_decode_row.argtypes = [P, i64, P]
+    lib.kqo_decode_row.restype = ctypes.c_int
+    lib.kqo_gemv_rows.argtypes = [P, i64, i64, P, ctypes.c_int, P, i64, P, P, ctypes.c_int]
+    lib.kqo_gemv_rows.restype = ctypes.c_int
+    lib.kqo_argmax_flags.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_double, P, P]
+    lib.kqo_argmax_flags.restype = ctypes.c_int
+    lib.kqo_candidates.argtypes = [P, P, i64, ctypes.c_int32, ctypes.c_double, P, i64]
+    lib.kqo_candidates.restype = i64
+    lib.kqo_accept.argtypes = [P, ctypes.c_int, P, P, P]
+    lib.kqo_accept.restype = ctypes.c_int
+    lib.kqo_num_threads.argtypes = []
+    lib.kqo_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().kqo_num_threads())
+
+
+def half_to_double(bits: int) -> float:
+    return float(_load().kqo_half_to_double(int(bits) & 0xFFFF))
+
+
+def scales_mins(s12: bytes) -> Tuple[np.ndarray, np.ndarray]:
+    s = np.frombuffer(bytes(s12), dtype=np.uint8).copy()
+    assert s.shape == (12,)
+    sc = np.zeros(8, dtype=np.int32)
+    mn = np.zeros(8, dtype=np.int32)
+    _load().kqo_scales_mins(_p(s), _p(sc), _p(mn))
+    return sc, mn
+
+
+def decode_block(blk) -> np.ndarray:
+    b = np.ascontiguousarray(np.frombuffer(bytes(blk), dtype=np.uint8))
+    assert b.shape == (144,)
+    w = np.zeros(256, dtype=np.float64)
+    if _load().kqo_decode_block(_p(b), _p(w)):
+        raise ValueError("non-finite d or dmin")
+    return w
+
+
+def decode_matrix(w: np.ndarray, k: int) -> np.ndarray:
+    """Exact fp64 weights [N, K] of a Q4_K matrix (small matrices only)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    n = w.shape[0]
+    out = np.zeros((n, k), dtype=np.float64)
+    lib = _load()
+    for r in range(n):
+        row = np.ascontiguousarray(w[r])
+        if lib.kqo_decode_row(_p(row), k, _p(out[r])):
+            raise ValueError("non-finite d or dmin")
+    return out
+
+
+def gemv_rows(w: np.ndarray, k: int, x: np.ndarray, rows: Optional[Sequence[int]] = None,
+              threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """(L, A), each float64 [M, n_out]: L = W x^T in fp64, A = sum |w x|.
+
+    w: uint8 [N, K/256*144]; x: float32 [M, K]; rows: optional subset of the
+    N output rows (outputs then follow that order)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    n = w.shape[0]
+    m = x.shape[0]
+    if x.shape[1] != k or w.shape[1] != (k // 256) * 144:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        r_arr = None
+        nout = n
+    else:
+        r_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nout = r_arr.shape[0]
+    L = np.zeros((m, nout), dtype=np.float64)
+    A = np.zeros((m, nout), dtype=np.float64)
+    rc = _load().kqo_gemv_rows(_p(w), n, k, _p(x), m,
+                               _p(r_arr) if r_arr is not None else None, nout,
+                               _p(L), _p(A), int(threads))
+    if rc == -3:
+        raise ValueError("non-finite activation")
+    if rc == -2:
+        raise ValueError("non-finite d or dmin")
+    if rc:
+        raise ValueError("bad shape")
+    return L, A
+
+
+def argmax_flags(L: np.ndarray, A: np.ndarray, rel: float = REL_TOL) -> Tuple[np.ndarray, np.ndarray]:
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    m, n = L.shape
+    am = np.zeros(m, dtype=np.int32)
+    nc = np.zeros(m, dtype=np.int64)
+    if _load().kqo_argmax_flags(_p(L), _p(A), m, n, float(rel), _p(am), _p(nc)):
+        raise ValueError("bad shape")
+    return am, nc
+
+
+def candidates(L_row: np.ndarray, A_row: np.ndarray, best: int, rel: float = REL_TOL) -> np.ndarray:
+    L_row = np.ascontiguousarray(L_row, dtype=np.float64)
+    A_row = np.ascontiguousarray(A_row, dtype=np.float64)
+    n = L_row.shape[0]
+    lib = _load()
+    cnt = lib.kqo_candidates(_p(L_row), _p(A_row), n, int(best), float(rel), None, 0)
+    out = np.zeros(max(cnt, 1), dtype=np.int32)
+    lib.kqo_candidates(_p(L_row), _p(A_row), n, int(best), float(rel), _p(out), cnt)
+    return out[:cnt]
+
+
+def accept(draft: Sequence[int], argmax: Sequence[int]) -> Tuple[int, int]:
+    d = np.ascontiguousarray(np.asarray(draft, dtype=np.int32))
+    a = np.ascontiguousarray(np.asarray(argmax, dtype=np.int32))
+    k = d.shape[0]
+    if a.shape[0] != k + 1:
+        raise ValueError("need k+1 target rows for k draft tokens")
+    acc = ctypes.c_int32(0)
+    nxt = ctypes.c_int32(0)
+    _load().kqo_accept(_p(d) if k else None, k, _p(a), ctypes.byref(acc), ctypes.byref(nxt))
+    return int(acc.value), int(nxt.value)
+
+
+def verify(w: np.ndarray, k: int, x: np.ndarray, draft: Sequence[int], rel: float = REL_TOL,
+           threads: int = 0):
+    """The whole step on the CPU: logits, argmax with flags, greedy accept.
+    Returns dict(L, A, argmax, n_cand, accepted, next_token)."""
+    L, A = gemv_rows(w, k, x, threads=threads)
+    am, nc = argmax_flags(L, A, rel)
+    acc, nxt = accept(draft, am)
+    return dict(L=L, A=A, argmax=am, n_cand=nc, accepted=acc, next_token=nxt)

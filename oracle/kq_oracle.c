@@ -1,0 +1,221 @@
+/*
+ * kq_oracle.c -- plain, slow, obviously-correct CPU oracle for the Q4_K
+ * batched verify step. TEST INFRASTRUCTURE ONLY: the library under
+ * quant_verify_gemv_amd/ never links, loads or calls this file; only the
+ * tests, the smoke check and the bench's CPU-baseline leg do.
+ *
+ * What it computes (fp64 throughout):
+ *
+ *  1. Decode. Every Q4_K super-block is decoded to its 256 exact weights
+ *     w = d * sc_j * q - dmin * m_j (sub-block j of 32 weights). The pages
+ *     name the format (muser-book ch. 8 "The DFlash draft", section 8.2:
+ *     draft.fc is Q4_K) and say the blocks are consumed in place, never
+ *     expanded to f32 on the device (section 8.5); the byte layout is the
+ *     llama.cpp GGUF one (parity against llama.cpp itself: unpinned here).
+ *  2. Logits. L[m][n] = sum_k W[n][k] * x[m][k]: the target scores k+1 rows
+ *     per weight read (ch. 33 "Speculation...", section 33.1; ch. 8,
+ *     section 8.1). The sum runs over k in increasing order in fp64.
+ *  3. Tolerance mass. A[m][n] = sum_k |W[n][k] * x[m][k]|.
+ *  4. Argmax. The index of each row's largest score (ch. 8, section 8.6,
+ *     guarantee 3); ties go to the lowest index. The row is "flagged" when
+ *     another index j has L[i*] - L[j] <= tol[i*] + tol[j], tol = rel * A.
+ *  5. Greedy accept. The temperature-0 limit of the accept/resample rule in
+ *     ch. 33, section 33.2: with one-hot target and draft distributions the
+ *     acceptance probability is 1 on a match and 0 on a mismatch, and the
+ *     residual after a mismatch is the target's one-hot row. So accepted is
+ *     the first position whose draft differs from the target argmax (or k),
+ *     and next_token is the argmax of row `accepted` (the last row when all
+ *     k are accepted).
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no fast-math, no intrinsics).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define KQO_QK 256
+#define KQO_BLOCK 144
+
+/* IEEE-754 binary16 bit pattern to double: sign, 5-bit exponent (bias 15),
+ * 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24). Returns NaN
+ * for inf/NaN encodings so that callers can reject them. */
+double kqo_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else if (e == 31) {
+        return NAN;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* The eight 6-bit scales and eight 6-bit mins of a super-block, from its 12
+ * packed bytes. The first four of each sit in the low six bits of bytes 0-3
+ * (scales) and 4-7 (mins). The last four are split: their low four bits are
+ * the low/high nibble of bytes 8-11 (scales/mins) and their top two bits are
+ * the spare top two bits of bytes 0-3 (scales) and 4-7 (mins). */
+void kqo_scales_mins(const uint8_t *s12, int sc[8], int mn[8]) {
+    for (int j = 0; j < 4; ++j) {
+        sc[j] = s12[j] & 63;
+        mn[j] = s12[j + 4] & 63;
+    }
+    for (int j = 4; j < 8; ++j) {
+        int lo_sc = s12[j + 4] & 15;
+        int lo_mn = s12[j + 4] >> 4;
+        int hi_sc = s12[j - 4] >> 6;
+        int hi_mn = s12[j] >> 6;
+        sc[j] = lo_sc + 16 * hi_sc;
+        mn[j] = lo_mn + 16 * hi_mn;
+    }
+}
+
+/* The 4-bit quant of weight i (0..255) of a block. Weights come in four
+ * groups of 64 that each own 32 bytes: the low nibbles hold the group's
+ * first 32 weights, the high nibbles its second 32. */
+int kqo_quant(const uint8_t *q128, int i) {
+    int g = i / 64, r = i % 64;
+    uint8_t b = q128[32 * g + (r % 32)];
+    return r < 32 ? (b & 15) : (b >> 4);
+}
+
+/* Decode one 144-byte block into 256 exact weights. Returns 0, or -1 when
+ * d or dmin is not finite. */
+int kqo_decode_block(const uint8_t *blk, double *w) {
+    uint16_t dh = (uint16_t)(blk[0] | (blk[1] << 8));
+    uint16_t mh = (uint16_t)(blk[2] | (blk[3] << 8));
+    double d = kqo_half_to_double(dh);
+    double dmin = kqo_half_to_double(mh);
+    if (isnan(d) || isnan(dmin)) return -1;
+    int sc[8], mn[8];
+    kqo_scales_mins(blk + 4, sc, mn);
+    for (int i = 0; i < KQO_QK; ++i) {
+        int j = i / 32;
+        int q = kqo_quant(blk + 16, i);
+        w[i] = d * (double)sc[j] * (double)q - dmin * (double)mn[j];
+    }
+    return 0;
+}
+
+/* Decode a full row of K weights. */
+int kqo_decode_row(const uint8_t *row, int64_t k, double *w) {
+    for (int64_t b = 0; b < k / KQO_QK; ++b)
+        if (kqo_decode_block(row + b * KQO_BLOCK, w + b * KQO_QK)) return -1;
+    return 0;
+}
+
+/* L[m][n] and A[m][n] (row-major [m][n], fp64) for an N x K Q4_K matrix and
+ * M fp32 activation rows [m][k]. `rows` may be NULL (all rows 0..n-1) or a
+ * list of n_rows row indices, in which case outputs are [m][n_rows].
+ * Returns 0; -1 for bad shapes; -2 for a non-finite d/dmin; -3 for a
+ * non-finite activation. nthreads <= 0 keeps the OpenMP default. */
+int kqo_gemv_rows(const uint8_t *w, int64_t n, int64_t k, const float *x, int m,
+                  const int64_t *rows, int64_t n_rows, double *L, double *A,
+                  int nthreads) {
+    if (n <= 0 || k <= 0 || k % KQO_QK || m <= 0) return -1;
+    for (int64_t i = 0; i < (int64_t)m * k; ++i)
+        if (!isfinite(x[i])) return -3;
+    int64_t nout = rows ? n_rows : n;
+    for (int64_t r = 0; r < nout; ++r)
+        if (rows && (rows[r] < 0 || rows[r] >= n)) return -1;
+    int64_t row_bytes = (k / KQO_QK) * KQO_BLOCK;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *wr = (double *)malloc(sizeof(double) * (size_t)k);
+        double *s = (double *)malloc(sizeof(double) * (size_t)m);
+        double *a = (double *)malloc(sizeof(double) * (size_t)m);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nout; ++r) {
+            int64_t nn = rows ? rows[r] : r;
+            if (kqo_decode_row(w + nn * row_bytes, k, wr)) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            for (int mm = 0; mm < m; ++mm) { s[mm] = 0.0; a[mm] = 0.0; }
+            for (int64_t kk = 0; kk < k; ++kk) {
+                for (int mm = 0; mm < m; ++mm) {
+                    double p = wr[kk] * (double)x[(int64_t)mm * k + kk];
+                    s[mm] += p;
+                    a[mm] += fabs(p);
+                }
+            }
+            for (int mm = 0; mm < m; ++mm) {
+                L[(int64_t)mm * nout + r] = s[mm];
+                A[(int64_t)mm * nout + r] = a[mm];
+            }
+        }
+        free(wr); free(s); free(a);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Per row m: argmax[m] = lowest index attaining the maximum of L[m][:],
+ * n_cand[m] = number of other indices j with
+ * L[i*] - L[j] <= rel * (A[i*] + A[j]) (0 means the row is unflagged). */
+int kqo_argmax_flags(const double *L, const double *A, int m, int64_t n,
+                     double rel, int32_t *argmax, int64_t *n_cand) {
+    if (m <= 0 || n <= 0) return -1;
+    for (int mm = 0; mm < m; ++mm) {
+        const double *l = L + (int64_t)mm * n;
+        const double *a = A + (int64_t)mm * n;
+        int64_t best = 0;
+        for (int64_t j = 1; j < n; ++j)
+            if (l[j] > l[best]) best = j;
+        int64_t c = 0;
+        for (int64_t j = 0; j < n; ++j)
+            if (j != best && l[best] - l[j] <= rel * (a[best] + a[j])) ++c;
+        argmax[mm] = (int32_t)best;
+        n_cand[mm] = c;
+    }
+    return 0;
+}
+
+/* Candidate set of row m (the indices counted by kqo_argmax_flags), written
+ * in increasing order to out[0..cap); returns how many exist. */
+int64_t kqo_candidates(const double *L, const double *A, int64_t n, int32_t best,
+                       double rel, int32_t *out, int64_t cap) {
+    int64_t c = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        if (j == best) continue;
+        if (L[best] - L[j] <= rel * (A[best] + A[j])) {
+            if (c < cap) out[c] = (int32_t)j;
+            ++c;
+        }
+    }
+    return c;
+}
+
+/* Greedy accept over k draft tokens judged by rows 0..k of the target.
+ * Row i < k judges draft[i]; row k supplies the bonus token. */
+int kqo_accept(const int32_t *draft, int k, const int32_t *argmax,
+               int32_t *accepted, int32_t *next_token) {
+    if (k < 0) return -1;
+    int i = 0;
+    while (i < k && draft[i] == argmax[i]) ++i;
+    *accepted = i;
+    *next_token = argmax[i];
+    return 0;
+}
+
+int kqo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs for the Q4_K batched-verify path.
+
+This module is shared by the HIP path's tests/bench and by the CPU oracle's
+tests. It holds no arithmetic of the method itself: it only draws random
+bytes and random floats and writes them where the Q4_K super-block format
+puts them (two little-endian fp16 words, then 140 free bytes).
+
+Super-block format (256 weights, 144 bytes): bytes 0-1 ``d`` (fp16), bytes
+2-3 ``dmin`` (fp16), bytes 4-15 the twelve bytes that carry eight 6-bit scales
+and eight 6-bit mins, bytes 16-143 the 128 bytes of 4-bit quants. The pages
+name the format only (muser-book ch. 8, section 8.2, "It is kquant"); the
+layout is the llama.cpp GGUF one. Because every bit of bytes 4..143 belongs
+to exactly one field, uniformly random bytes there give independent uniform
+6-bit scales/mins and uniform 4-bit quants.
+
+Workloads follow the shapes the pages give for the target and its DFlash
+draft: hidden width 6,656 and the fc projection 33,280 -> 6,656 (muser-book
+ch. 8, section 8.2), 16-row verify blocks (ch. 8, section 8.2, block size 16),
+a 52-layer target (ch. 33, section 33.1). Vocabulary 131,072 and FFN width
+17,920 are the workload's own choices, not from the pages.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+QK = 256            # weights per super-block
+BLOCK_BYTES = 144   # bytes per super-block
+HIDDEN = 6656
+FFN = 17920
+VOCAB = 131072
+FC_IN = 5 * HIDDEN  # 33,280: five concatenated target hidden vectors
+LAYERS = 52
+
+# Per-position probability that the draft's token differs from the target's
+# argmax. One minus the acceptance chain 0.831, 0.786, 0.771, 0.758 reported
+# for an MTP depth sweep ("The squeeze", sanctum.run 2026-08-17 post), then
+# held flat at the last value because that chain barely decays.
+MISMATCH_CHAIN = (0.169, 0.214, 0.229, 0.242)
+
+
+def _seq(seed: int, stream: int) -> np.random.SeedSequence:
+    return np.random.SeedSequence([int(seed), int(stream)])
+
+
+def q4k_bytes_per_row(k: int) -> int:
+    if k % QK:
+        raise ValueError(f"K={k} is not a multiple of {QK}")
+    return (k // QK) * BLOCK_BYTES
+
+
+def q4k_matrix(n: int, k: int, seed: int, d_range=(0.001, 0.05)) -> np.ndarray:
+    """Random Q4_K matrix of N rows x K weights as uint8 [N, K/256*144].
+
+    d and dmin are drawn ~U(d_range) in float64 and rounded to fp16 (numpy's
+    conversion rounds to nearest even); the other 140 bytes of every block
+    are uniform random bytes.
+    """
+    nb = n * (k // QK) if k % QK == 0 else None
+    if nb is None:
+        raise ValueError(f"K={k} is not a multiple of {QK}")
+    raw = np.random.SFC64(_seq(seed, 0)).random_raw(nb * BLOCK_BYTES // 8)
+    blocks = raw.view(np.uint8).reshape(nb, BLOCK_BYTES)
+    g = np.random.Generator(np.random.PCG64(_seq(seed, 1)))
+    dd = g.uniform(d_range[0], d_range[1], size=(nb, 2)).astype(np.float16)
+    blocks[:, 0:4] = dd.view(np.uint8).reshape(nb, 4)
+    return blocks.reshape(n, (k // QK) * BLOCK_BYTES)
+
+
+def activations(m: int, k: int, seed: int) -> np.ndarray:
+    """fp32 activation rows [M, K] ~ N(0, 1)."""
+    g = np.random.Generator(np.random.PCG64(_seq(seed, 2)))
+    return g.standard_normal((m, k), dtype=np.float32)
+
+
+def fc_activations(m: int, seed: int, width: int = HIDDEN, parts: int = 5) -> np.ndarray:
+    """DFlash fc input rows [M, parts*width]: each row concatenates `parts`
+    independent N(0,1) vectors, each scaled to unit RMS (computed in float64,
+    then rounded to fp32; no epsilon, no gain)."""
+    g = np.random.Generator(np.random.PCG64(_seq(seed, 3)))
+    v = g.standard_normal((m, parts, width))
+    rms = np.sqrt(np.mean(v * v, axis=2, keepdims=True))
+    return (v / rms).astype(np.float32).reshape(m, parts * width)
+
+
+def mismatch_probs(k: int) -> np.ndarray:
+    p = np.empty(k)
+    for i in range(k):
+        p[i] = MISMATCH_CHAIN[min(i, len(MISMATCH_CHAIN) - 1)]
+    return p
+
+
+def inject_mismatches(target_tokens: Sequence[int], n_vocab: int, seed: int,
+                      probs: Sequence[float] | None = None) -> np.ndarray:
+    """Draft tokens: a copy of `target_tokens` where position i is replaced,
+    with probability probs[i], by a token drawn uniformly from the other
+    n_vocab - 1 tokens."""
+    t = np.asarray(target_tokens, dtype=np.int64)
+    k = t.shape[0]
+    p = mismatch_probs(k) if probs is None else np.asarray(probs, dtype=np.float64)
+    g = np.random.Generator(np.random.PCG64(_seq(seed, 4)))
+    u = g.random(k)
+    other = g.integers(0, n_vocab - 1, size=k)
+    out = t.copy()
+    for i in range(k):
+        if u[i] < p[i]:
+            out[i] = other[i] + (1 if other[i] >= t[i] else 0)
+    return out.astype(np.int32)
+
+
+def forced_draft(target_tokens: Sequence[int], accepted: int, n_vocab: int) -> np.ndarray:
+    """Draft that matches the target on positions < accepted and differs at
+    position `accepted` (if accepted < k); later positions are copied."""
+    t = np.asarray(target_tokens, dtype=np.int64).copy()
+    if accepted < t.shape[0]:
+        t[accepted] = (t[accepted] + 1) % n_vocab
+    return t.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Named workloads.
+
+@dataclasses.dataclass(frozen=True)
+class Gemv:
+    n: int
+    k: int
+    seed: int
+
+    @property
+    def weight_bytes(self) -> int:
+        return self.n * q4k_bytes_per_row(self.k)
+
+
+TINY = dict(n=512, k=1024, m=4, k_draft=3, seed=0)
+SQUARE = dict(n=HIDDEN, k=HIDDEN, ms=(1, 2, 4, 8, 16), seed=1)
+FC = dict(n=HIDDEN, k=FC_IN, m=16, seed=2)
+LM_HEAD = dict(n=VOCAB, k=HIDDEN, m=16, k_draft=15, seed=3)
+
+
+def stack_matrices(layers: int = LAYERS) -> List[Gemv]:
+    """The synthetic target stack: per layer four HIDDEN x HIDDEN matrices,
+    two HIDDEN -> FFN and one FFN -> HIDDEN; matrix i of layer l uses seed
+    10000 + 8 l + i. (The LM head is the LM_HEAD workload.)"""
+    out = []
+    for layer in range(layers):
+        shapes = [(HIDDEN, HIDDEN)] * 4 + [(FFN, HIDDEN)] * 2 + [(HIDDEN, FFN)]
+        for i, (n, k) in enumerate(shapes):
+            out.append(Gemv(n=n, k=k, seed=10000 + 8 * layer + i))
+    return out
+
+
+def stack_activation_seed(k: int) -> int:
+    """One activation block per distinct K, reused by every stack matrix with
+    that K (the stack matrices are independent products, not a chained model)."""
+    return 20000 + k
+
+
+def stack_weight_bytes(layers: int = LAYERS, with_head: bool = True) -> int:
+    tot = sum(g.weight_bytes for g in stack_matrices(layers))
+    if with_head:
+        tot += LM_HEAD["n"] * q4k_bytes_per_row(LM_HEAD["k"])
+    return tot
