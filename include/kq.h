@@ -1,0 +1,147 @@
+/*
+ * kq.h -- C ABI of libkq: the Q4_K batched speculative-verify step on
+ * MI355X (gfx950).
+ *
+ * The operation (muser-book ch. 33 "Speculation: the local win and the
+ * distributed verdict", section 33.1; ch. 8 "The DFlash draft", section 8.1):
+ * a draft proposes k tokens and the target scores all k+1 positions in one
+ * pass over its weights, k+1 activation rows per weight read. For a Q4_K
+ * weight matrix W with N output rows of K weights and M = k+1 fp32 rows x,
+ *
+ *     logits[m][n] = sum_k W[n][k] * x[m][k]
+ *
+ * where W is decoded on the fly from 144-byte, 256-weight super-blocks
+ * (w = d * sc_j * q - dmin * m_j; fp16 d/dmin, 6-bit sub-block scales and
+ * mins, 4-bit quants; the llama.cpp GGUF layout). The pages name the format
+ * and say kquant matrices are consumed in place, never expanded (ch. 8,
+ * sections 8.2 and 8.5); this library reads the raw block bytes.
+ *
+ * The verify call also takes each row's argmax ("the index of each row's
+ * largest score", ch. 8 section 8.6; ties -> lowest index) and applies the
+ * greedy accept rule, the temperature-0 limit of the accept/resample rule of
+ * ch. 33 section 33.2: accepted = first i < k with draft[i] != argmax[i]
+ * (k if none), next_token = argmax[accepted], emitted = accepted + 1.
+ *
+ * Conventions (all entry points):
+ *  - Shapes: 1 <= m <= 16, k > 0 and k % 256 == 0, 1 <= n < 2^31,
+ *    n * (k/256) * 144 < 2^62.
+ *  - Layouts: w is [n][k/256] blocks of 144 bytes, row-major, 16-byte aligned;
+ *    x is fp32 [m][k] row-major, 16-byte aligned; logits fp32 [m][n].
+ *  - Pointers marked "device" are HIP device memory owned by the caller; the
+ *    library allocates nothing and keeps no global mutable state.
+ *  - Every call is enqueued on `stream` (a hipStream_t; NULL = default
+ *    stream) and returns without synchronising; results are valid once the
+ *    stream reaches that point.
+ *  - Errors: every argument check runs before any HIP call; on a non-OK
+ *    return nothing has been enqueued. KQ_ERR_LAUNCH reports a HIP launch
+ *    failure (hipGetLastError after enqueue).
+ *  - Concurrency: calls on different streams need different workspaces;
+ *    calls sharing a workspace must be ordered (e.g. the same stream).
+ *  - Numerics: fp32 accumulation. |logit - exact| <= 1e-4 * sum_k |w_k x_k|
+ *    for finite inputs with |dmin| * 63 <= 65504; results are bitwise
+ *    deterministic and row i of an m-row call equals the 1-row call on x[i].
+ *    There is no CPU or alternate path.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int kq_status;
+#define KQ_OK            0
+#define KQ_ERR_NULL      1  /* a required pointer is NULL                       */
+#define KQ_ERR_SHAPE     2  /* m, n or k out of range                           */
+#define KQ_ERR_ALIGN     3  /* w, x, staged or workspace not 16/256-byte aligned */
+#define KQ_ERR_TOKEN     4  /* a draft token outside [0, n)                     */
+#define KQ_ERR_WORKSPACE 5  /* workspace / staged buffer smaller than required  */
+#define KQ_ERR_LAUNCH    6  /* HIP reported an error when enqueuing             */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kq_status_string(kq_status s);
+
+/* Bytes of device workspace kq_gemv_rows / kq_verify_argmax_accept need for
+ * an n x k matrix and m rows (0 for invalid shapes). The workspace holds the
+ * staged activations, split-K partial sums and the control words. */
+size_t kq_workspace_bytes(int64_t n, int64_t k, int m);
+
+/* Bytes of a staged activation block for k columns (any m <= 16). */
+size_t kq_staged_bytes(int64_t k);
+
+/* Bytes of device scratch the *_staged calls need for an n x k matrix. */
+size_t kq_scratch_bytes(int64_t n, int64_t k);
+
+/* Zero the control words of a workspace or scratch buffer of `bytes` bytes
+ * (device, 256-byte aligned). Scratch passed to the *_staged calls must be
+ * zeroed once before first use; every call leaves it zeroed again.
+ * kq_gemv_rows / kq_verify_argmax_accept re-zero their workspace themselves. */
+kq_status kq_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* Logits of m activation rows against one Q4_K matrix.
+ *  w_q4k      device, n * (k/256) * 144 bytes (read only)
+ *  x          device, fp32 [m][k] (read only)
+ *  logits     device, fp32 [m][n] (written)
+ *  workspace  device, >= kq_workspace_bytes(n, k, m) bytes, 256-byte aligned
+ * Passage: ch. 33 section 33.1 / ch. 8 section 8.1 (k+1 rows per weight read);
+ * the same call serves the draft's fc projection 33,280 -> 6,656 of five
+ * concatenated target hidden states (ch. 8 section 8.2). */
+kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k,
+                       const float *x, int m, float *logits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* The verify step: logits (optional), per-row argmax and greedy accept.
+ *  m               k_draft + 1 (1..16): row i < m-1 judges draft[i], row
+ *                  m-1 supplies the token after a full accept
+ *  draft_host      host, m-1 int32 tokens in [0, n) (copied before return;
+ *                  may be NULL when m == 1)
+ *  argmax          device, int32 [m] (written)
+ *  accept_out      device, int32 [2] = {accepted, next_token} (written)
+ *  logits_or_null  device fp32 [m][n], or NULL to skip writing logits
+ * Passages: ch. 33 section 33.2 (accept rule, greedy limit), ch. 8 section
+ * 8.6 (argmax of each row). */
+kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k,
+                                  const float *x, int m,
+                                  const int32_t *draft_host,
+                                  int32_t *argmax, int32_t *accept_out,
+                                  float *logits_or_null,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* Stage m fp32 activation rows once for any number of matrices with the same
+ * k (projections that share an input: q/k/v, gate/up).
+ *  x       device, fp32 [m][k]
+ *  staged  device, >= kq_staged_bytes(k) bytes, 256-byte aligned (written)
+ * A staged block is valid for the m it was staged with. */
+kq_status kq_stage_rows(const float *x, int m, int64_t k,
+                        void *staged, size_t staged_bytes, void *stream);
+
+/* kq_gemv_rows on staged activations.
+ *  scratch  device, >= kq_scratch_bytes(n, k) bytes, 256-byte aligned,
+ *           zeroed once by kq_workspace_init */
+kq_status kq_gemv_staged(const void *w_q4k, int64_t n, int64_t k,
+                         const void *staged, int m, float *logits,
+                         void *scratch, size_t scratch_bytes, void *stream);
+
+/* kq_verify_argmax_accept on staged activations (same arguments as above;
+ * scratch as for kq_gemv_staged). */
+kq_status kq_verify_staged(const void *w_q4k, int64_t n, int64_t k,
+                           const void *staged, int m,
+                           const int32_t *draft_host,
+                           int32_t *argmax, int32_t *accept_out,
+                           float *logits_or_null,
+                           void *scratch, size_t scratch_bytes, void *stream);
+
+/* Launch geometry the library uses for an n x k matrix (a function of n and
+ * k only, never of m): tiles of 16 rows per wave (*nt), workgroups along n
+ * (*n_wg) and along k (*splits). Returns KQ_ERR_SHAPE for invalid shapes. */
+kq_status kq_launch_geometry(int64_t n, int64_t k, int *nt, int *n_wg, int *splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

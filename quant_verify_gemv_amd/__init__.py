@@ -1,0 +1,13 @@
+"""quant_verify_gemv_amd: the Q4_K batched speculative-verify step on MI355X.
+
+The hot path (activation staging, Q4_K dequant + MFMA skinny GEMM, split-K
+combine, row argmax, greedy accept) runs in HIP kernels inside libkq.so,
+behind the C ABI of include/kq.h. This package is the thin Python binding.
+"""
+from .lib import (KQError, gemv_rows, gemv_staged, launch_geometry, load, new_scratch,  # noqa: F401
+                  scratch_bytes, stage_rows, staged_bytes, status_string, verify, verify_staged,
+                  workspace_bytes)
+
+QK = 256
+BLOCK_BYTES = 144
+MAX_ROWS = 16

@@ -1,0 +1,210 @@
+// kq_api.cpp -- the C ABI declared in include/kq.h: argument validation
+// (always before any HIP call), workspace layout, launch geometry.
+#include "kq.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static bool shape_ok(int64_t n, int64_t k) {
+  return n >= 1 && n < ((int64_t)1 << 31) && k > 0 && k % kQK == 0 && k <= ((int64_t)1 << 28) &&
+         (k / kQK) * kBlockBytes <= (((int64_t)1 << 62) / n);
+}
+
+Geometry geometry(int64_t n, int64_t k) {
+  Geometry g;
+  const int64_t tiles = cdiv(n, 16);
+  g.quads = (int)cdiv(k, kQuadK);
+  g.nt = 2;
+  g.n_wg = (int)cdiv(tiles, (int64_t)kWaves * g.nt);
+  const int64_t target = 1024;  // workgroups wanted to fill 256 CUs several times over
+  int64_t splits = cdiv(target, g.n_wg);
+  if (splits > g.quads) splits = g.quads;
+  if (splits < 1) splits = 1;
+  g.qps = (int)cdiv(g.quads, splits);
+  g.splits = (int)cdiv(g.quads, g.qps);
+  return g;
+}
+
+ScratchLayout scratch_layout(int64_t n, int64_t k) {
+  const Geometry g = geometry(n, k);
+  ScratchLayout s;
+  s.cnt_off = 256;
+  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * (size_t)g.n_wg);
+  s.ctrl_bytes = s.keys_off;  // words that must be zero between calls
+  s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxRows * (size_t)g.n_wg);
+  s.total = s.part_off;
+  if (g.splits > 1) s.total += align256(sizeof(float) * (size_t)g.splits * kMaxRows * (size_t)n);
+  return s;
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+extern "C" {
+
+const char *kq_status_string(kq_status s) {
+  switch (s) {
+    case KQ_OK: return "KQ_OK";
+    case KQ_ERR_NULL: return "KQ_ERR_NULL: a required pointer is NULL";
+    case KQ_ERR_SHAPE: return "KQ_ERR_SHAPE: m, n or k out of range";
+    case KQ_ERR_ALIGN: return "KQ_ERR_ALIGN: misaligned pointer";
+    case KQ_ERR_TOKEN: return "KQ_ERR_TOKEN: draft token outside [0, n)";
+    case KQ_ERR_WORKSPACE: return "KQ_ERR_WORKSPACE: workspace too small";
+    case KQ_ERR_LAUNCH: return "KQ_ERR_LAUNCH: HIP launch failed";
+    default: return "KQ_ERR_UNKNOWN";
+  }
+}
+
+size_t kq_staged_bytes(int64_t k) {
+  if (k <= 0 || k % kQK || k > ((int64_t)1 << 28)) return 0;
+  return (size_t)cdiv(k, kQuadK) * (size_t)kQuadBytes;
+}
+
+size_t kq_scratch_bytes(int64_t n, int64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  return scratch_layout(n, k).total;
+}
+
+size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
+  if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return 0;
+  return align256(kq_staged_bytes(k)) + kq_scratch_bytes(n, k);
+}
+
+kq_status kq_launch_geometry(int64_t n, int64_t k, int *nt, int *n_wg, int *splits) {
+  if (!shape_ok(n, k)) return KQ_ERR_SHAPE;
+  const Geometry g = geometry(n, k);
+  if (nt) *nt = g.nt;
+  if (n_wg) *n_wg = g.n_wg;
+  if (splits) *splits = g.splits;
+  return KQ_OK;
+}
+
+static inline bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+kq_status kq_workspace_init(void *workspace, size_t bytes, void *stream) {
+  if (!workspace) return KQ_ERR_NULL;
+  if (!al(workspace, 256)) return KQ_ERR_ALIGN;
+  if (bytes < 256) return KQ_ERR_WORKSPACE;
+  if (launch_fill((unsigned *)workspace, (int64_t)(bytes / 4), stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+kq_status kq_stage_rows(const float *x, int m, int64_t k, void *staged, size_t staged_bytes,
+                        void *stream) {
+  if (!x || !staged) return KQ_ERR_NULL;
+  if (m < 1 || m > kMaxRows || k <= 0 || k % kQK || k > ((int64_t)1 << 28)) return KQ_ERR_SHAPE;
+  if (!al(x, 16) || !al(staged, 256)) return KQ_ERR_ALIGN;
+  if (staged_bytes < kq_staged_bytes(k)) return KQ_ERR_WORKSPACE;
+  if (launch_stage(x, m, k, (uint8_t *)staged, nullptr, 0, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+// Shared validation + launch of the main kernel on staged activations.
+static kq_status run(const void *w, int64_t n, int64_t k, const void *staged, int m, float *logits,
+                     bool verify, const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
+                     void *scratch, size_t scratch_bytes, const float *x_to_stage, void *stream) {
+  if (!w || !staged || !scratch) return KQ_ERR_NULL;
+  if (!verify && !logits) return KQ_ERR_NULL;
+  if (verify && (!argmax || !accept_out)) return KQ_ERR_NULL;
+  if (verify && m > 1 && !draft_host) return KQ_ERR_NULL;
+  if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
+  if (!al(w, 16) || !al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
+  if (x_to_stage && !al(x_to_stage, 16)) return KQ_ERR_ALIGN;
+  const ScratchLayout sl = scratch_layout(n, k);
+  if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
+  GemvLaunch a;
+  memset(&a, 0, sizeof(a));
+  if (verify) {
+    for (int i = 0; i < m - 1; ++i) {
+      if (draft_host[i] < 0 || (int64_t)draft_host[i] >= n) return KQ_ERR_TOKEN;
+      a.draft[i] = draft_host[i];
+    }
+  }
+  a.w = (const uint8_t *)w;
+  a.n = n;
+  a.k = k;
+  a.row_bytes = (k / kQK) * kBlockBytes;
+  a.m = m;
+  a.staged = (const uint8_t *)staged;
+  a.logits = logits;
+  uint8_t *sc = (uint8_t *)scratch;
+  a.done = (unsigned *)sc;
+  a.tile_cnt = (unsigned *)(sc + sl.cnt_off);
+  a.wg_keys = (unsigned long long *)(sc + sl.keys_off);
+  a.partials = (float *)(sc + sl.part_off);
+  a.argmax_out = argmax;
+  a.accept_out = accept_out;
+  a.k_draft = verify ? m - 1 : 0;
+  a.verify = verify ? 1 : 0;
+  a.g = geometry(n, k);
+  if (x_to_stage) {
+    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch,
+                     (int64_t)(sl.ctrl_bytes / 4), stream))
+      return KQ_ERR_LAUNCH;
+  }
+  if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+kq_status kq_gemv_staged(const void *w_q4k, int64_t n, int64_t k, const void *staged, int m,
+                         float *logits, void *scratch, size_t scratch_bytes, void *stream) {
+  return run(w_q4k, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch,
+             scratch_bytes, nullptr, stream);
+}
+
+kq_status kq_verify_staged(const void *w_q4k, int64_t n, int64_t k, const void *staged, int m,
+                           const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
+                           float *logits_or_null, void *scratch, size_t scratch_bytes,
+                           void *stream) {
+  return run(w_q4k, n, k, staged, m, logits_or_null, true, draft_host, argmax, accept_out, scratch,
+             scratch_bytes, nullptr, stream);
+}
+
+static kq_status split_workspace(int64_t n, int64_t k, int m, void *ws, size_t ws_bytes,
+                                 void **staged, void **scratch, size_t *scratch_bytes) {
+  if (!ws) return KQ_ERR_NULL;
+  if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
+  if (!al(ws, 256)) return KQ_ERR_ALIGN;
+  const size_t need = kq_workspace_bytes(n, k, m);
+  if (ws_bytes < need) return KQ_ERR_WORKSPACE;
+  const size_t st = align256(kq_staged_bytes(k));
+  *staged = ws;
+  *scratch = (uint8_t *)ws + st;
+  *scratch_bytes = ws_bytes - st;
+  return KQ_OK;
+}
+
+kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
+                       float *logits, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!w_q4k || !x || !logits) return KQ_ERR_NULL;
+  void *staged, *scratch;
+  size_t sb;
+  kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
+  if (s != KQ_OK) return s;
+  return run(w_q4k, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch, sb, x,
+             stream);
+}
+
+kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
+                                  const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
+                                  float *logits_or_null, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  if (!w_q4k || !x || !argmax || !accept_out) return KQ_ERR_NULL;
+  if (m > 1 && !draft_host) return KQ_ERR_NULL;
+  void *staged, *scratch;
+  size_t sb;
+  kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
+  if (s != KQ_OK) return s;
+  return run(w_q4k, n, k, staged, m, logits_or_null, true, draft_host, argmax, accept_out, scratch,
+             sb, x, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+"""Thin ctypes binding over libkq.so (the C ABI in include/kq.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the verify path runs in the HIP kernels. There is no
+fallback: if libkq.so is missing or the device is not a HIP GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkq.so")
+
+KQ_OK = 0
+STATUS_NAMES = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIGN",
+                4: "KQ_ERR_TOKEN", 5: "KQ_ERR_WORKSPACE", 6: "KQ_ERR_LAUNCH"}
+
+EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scratch_bytes",
+            "kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
+            "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry")
+
+_lib = None
+
+
+class KQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libkq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m quant_verify_gemv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.kq_status_string.argtypes = [I32]
+    lib.kq_status_string.restype = ctypes.c_char_p
+    lib.kq_workspace_bytes.argtypes = [I64, I64, I32]
+    lib.kq_workspace_bytes.restype = SZ
+    lib.kq_staged_bytes.argtypes = [I64]
+    lib.kq_staged_bytes.restype = SZ
+    lib.kq_scratch_bytes.argtypes = [I64, I64]
+    lib.kq_scratch_bytes.restype = SZ
+    lib.kq_workspace_init.argtypes = [P, SZ, P]
+    lib.kq_gemv_rows.argtypes = [P, I64, I64, P, I32, P, P, SZ, P]
+    lib.kq_verify_argmax_accept.argtypes = [P, I64, I64, P, I32, P, P, P, P, P, SZ, P]
+    lib.kq_stage_rows.argtypes = [P, I32, I64, P, SZ, P]
+    lib.kq_gemv_staged.argtypes = [P, I64, I64, P, I32, P, P, SZ, P]
+    lib.kq_verify_staged.argtypes = [P, I64, I64, P, I32, P, P, P, P, P, SZ, P]
+    lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P]
+    for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
+                 "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != KQ_OK:
+        raise KQError(status, where)
+
+
+def workspace_bytes(n: int, k: int, m: int) -> int:
+    return int(load().kq_workspace_bytes(n, k, m))
+
+
+def staged_bytes(k: int) -> int:
+    return int(load().kq_staged_bytes(k))
+
+
+def scratch_bytes(n: int, k: int) -> int:
+    return int(load().kq_scratch_bytes(n, k))
+
+
+def launch_geometry(n: int, k: int) -> Tuple[int, int, int]:
+    nt, nwg, sp = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().kq_launch_geometry(n, k, ctypes.byref(nt), ctypes.byref(nwg), ctypes.byref(sp)),
+           "kq_launch_geometry")
+    return nt.value, nwg.value, sp.value
+
+
+# ----------------------------------------------------------------- torch side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dev_ptr(t, name: str, dtype=None) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return int(t.data_ptr())
+
+
+def alloc_workspace(nbytes: int, device):
+    """A zeroed, 256-byte aligned device buffer of at least nbytes bytes."""
+    torch = _torch()
+    buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+class Workspace:
+    """Device workspace cache keyed by device (grows as needed)."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, nbytes: int, device):
+        key = str(device)
+        b = self._bufs.get(key)
+        if b is None or b.numel() < nbytes:
+            b = alloc_workspace(nbytes, device)
+            self._bufs[key] = b
+        return b
+
+
+_WS = Workspace()
+
+
+def gemv_rows(w, n: int, k: int, x, logits=None, workspace=None, stream=None):
+    """logits[m][n] = sum_k W[n][k] x[m][k] for a Q4_K matrix w (uint8 device
+    tensor of n*(k/256)*144 bytes) and fp32 rows x [m, k]."""
+    torch = _torch()
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    m = int(x.shape[0])
+    if logits is None:
+        logits = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    need = workspace_bytes(n, k, m)
+    ws = workspace if workspace is not None else _WS.get(need, x.device)
+    _check(load().kq_gemv_rows(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(x, "x", torch.float32), m,
+                               _dev_ptr(logits, "logits", torch.float32), _dev_ptr(ws, "workspace"),
+                               ws.numel(), _stream_handle(stream)), "kq_gemv_rows")
+    return logits
+
+
+def verify(w, n: int, k: int, x, draft: Sequence[int], want_logits: bool = False,
+           workspace=None, stream=None, out=None):
+    """The verify step. Returns (argmax int32[m] device, accept int32[2]
+    device = {accepted, next_token}, logits or None)."""
+    torch = _torch()
+    m = int(x.shape[0])
+    dr = (ctypes.c_int32 * max(1, m - 1))(*[int(t) for t in draft])
+    if len(draft) != m - 1:
+        raise ValueError(f"need m-1 = {m - 1} draft tokens, got {len(draft)}")
+    if out is None:
+        am = torch.empty(m, dtype=torch.int32, device=x.device)
+        acc = torch.empty(2, dtype=torch.int32, device=x.device)
+        lg = torch.empty((m, n), dtype=torch.float32, device=x.device) if want_logits else None
+    else:
+        am, acc, lg = out
+    need = workspace_bytes(n, k, m)
+    ws = workspace if workspace is not None else _WS.get(need, x.device)
+    _check(load().kq_verify_argmax_accept(
+        _dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(x, "x", torch.float32), m, dr,
+        _dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
+        _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
+        _dev_ptr(ws, "workspace"), ws.numel(), _stream_handle(stream)), "kq_verify_argmax_accept")
+    return am, acc, lg
+
+
+def stage_rows(x, staged=None, stream=None):
+    torch = _torch()
+    m, k = int(x.shape[0]), int(x.shape[1])
+    if staged is None:
+        staged = alloc_workspace(staged_bytes(k), x.device)
+    _check(load().kq_stage_rows(_dev_ptr(x, "x", torch.float32), m, k, _dev_ptr(staged, "staged"),
+                                staged.numel(), _stream_handle(stream)), "kq_stage_rows")
+    return staged
+
+
+def new_scratch(n: int, k: int, device):
+    """Zeroed scratch for the *_staged calls."""
+    return alloc_workspace(scratch_bytes(n, k), device)
+
+
+def gemv_staged(w, n: int, k: int, staged, m: int, scratch, logits=None, stream=None):
+    torch = _torch()
+    if logits is None:
+        logits = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check(load().kq_gemv_staged(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(staged, "staged"), m,
+                                 _dev_ptr(logits, "logits", torch.float32), _dev_ptr(scratch, "scratch"),
+                                 scratch.numel(), _stream_handle(stream)), "kq_gemv_staged")
+    return logits
+
+
+def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scratch, want_logits=False,
+                  stream=None, out=None):
+    torch = _torch()
+    if len(draft) != m - 1:
+        raise ValueError(f"need m-1 = {m - 1} draft tokens, got {len(draft)}")
+    dr = (ctypes.c_int32 * max(1, m - 1))(*[int(t) for t in draft])
+    if out is None:
+        am = torch.empty(m, dtype=torch.int32, device=w.device)
+        acc = torch.empty(2, dtype=torch.int32, device=w.device)
+        lg = torch.empty((m, n), dtype=torch.float32, device=w.device) if want_logits else None
+    else:
+        am, acc, lg = out
+    _check(load().kq_verify_staged(
+        _dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(staged, "staged"), m, dr,
+        _dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
+        _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
+        _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_verify_staged")
+    return am, acc, lg

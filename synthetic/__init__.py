@@ -22,6 +22,8 @@ a 52-layer target (ch. 33, section 33.1). Vocabulary 131,072 and FFN width
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import List, Sequence, Tuple
 
 import numpy as np
@@ -51,21 +53,67 @@ def q4k_bytes_per_row(k: int) -> int:
     return (k // QK) * BLOCK_BYTES
 
 
+_SM_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_SM_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_SM_M2 = np.uint64(0x94D049BB133111EB)
+_THREADS = min(8, os.cpu_count() or 1)
+
+
+def _key(seed: int, stream: int) -> np.uint64:
+    return np.uint64(_seq(seed, stream).generate_state(1, np.uint64)[0])
+
+
+def _splitmix64_fill(out: np.ndarray, start: int, key: np.uint64) -> None:
+    """out[i] = SplitMix64 output number start+i+1 of the stream keyed by
+    `key` (Steele, Lea & Flood 2014: add the golden-ratio increment, then the
+    two xor-shift-multiply mixing rounds)."""
+    z = np.arange(start, start + out.shape[0], dtype=np.uint64)
+    z += np.uint64(1)
+    z *= _SM_GAMMA
+    z += key
+    z ^= z >> np.uint64(30)
+    z *= _SM_M1
+    z ^= z >> np.uint64(27)
+    z *= _SM_M2
+    z ^= z >> np.uint64(31)
+    out[:] = z
+
+
+def random_u64(count: int, seed: int, stream: int) -> np.ndarray:
+    """`count` uniformly distributed 64-bit words, deterministic in (seed,
+    stream), generated in parallel chunks."""
+    key = _key(seed, stream)
+    out = np.empty(count, dtype=np.uint64)
+    chunk = 1 << 20
+    starts = range(0, count, chunk)
+    if count <= chunk or _THREADS == 1:
+        for s0 in starts:
+            _splitmix64_fill(out[s0:s0 + chunk], s0, key)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(lambda s0: _splitmix64_fill(out[s0:s0 + chunk], s0, key), starts))
+    return out
+
+
 def q4k_matrix(n: int, k: int, seed: int, d_range=(0.001, 0.05)) -> np.ndarray:
     """Random Q4_K matrix of N rows x K weights as uint8 [N, K/256*144].
 
-    d and dmin are drawn ~U(d_range) in float64 and rounded to fp16 (numpy's
-    conversion rounds to nearest even); the other 140 bytes of every block
-    are uniform random bytes.
+    Bytes 4..143 of every block are uniform random bytes; d and dmin are
+    drawn ~U(d_range) in float64 (53-bit uniforms) and rounded to fp16
+    (numpy's conversion rounds to nearest even).
     """
-    nb = n * (k // QK) if k % QK == 0 else None
-    if nb is None:
+    if k % QK:
         raise ValueError(f"K={k} is not a multiple of {QK}")
-    raw = np.random.SFC64(_seq(seed, 0)).random_raw(nb * BLOCK_BYTES // 8)
-    blocks = raw.view(np.uint8).reshape(nb, BLOCK_BYTES)
-    g = np.random.Generator(np.random.PCG64(_seq(seed, 1)))
-    dd = g.uniform(d_range[0], d_range[1], size=(nb, 2)).astype(np.float16)
-    blocks[:, 0:4] = dd.view(np.uint8).reshape(nb, 4)
+    nb = n * (k // QK)
+    blocks = random_u64(nb * (BLOCK_BYTES // 8), seed, 0).view(np.uint8).reshape(nb, BLOCK_BYTES)
+    lo, hi = d_range
+    step = 1 << 22
+    for b0 in range(0, nb, step):
+        b1 = min(nb, b0 + step)
+        u = random_u64(2 * (b1 - b0), seed * 1000003 + b0 // step, 1)
+        uf = (u >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        dd = (lo + (hi - lo) * uf).astype(np.float16)
+        blocks[b0:b1, 0:4] = dd.view(np.uint8).reshape(b1 - b0, 4)
     return blocks.reshape(n, (k // QK) * BLOCK_BYTES)
 
 
@@ -102,8 +150,10 @@ def inject_mismatches(target_tokens: Sequence[int], n_vocab: int, seed: int,
     p = mismatch_probs(k) if probs is None else np.asarray(probs, dtype=np.float64)
     g = np.random.Generator(np.random.PCG64(_seq(seed, 4)))
     u = g.random(k)
-    other = g.integers(0, n_vocab - 1, size=k)
+    other = g.integers(0, max(1, n_vocab - 1), size=k)
     out = t.copy()
+    if n_vocab < 2:  # no other token exists
+        return out.astype(np.int32)
     for i in range(k):
         if u[i] < p[i]:
             out[i] = other[i] + (1 if other[i] >= t[i] else 0)

@@ -1,0 +1,112 @@
+"""CPU checks of the C ABI (no GPU): libkq.so loads, exports every function
+include/kq.h declares, and every argument error is reported before any HIP
+call (the fake device pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quant_verify_gemv_amd import lib as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+NULL, SHAPE, ALIGN, TOKEN, WS = 1, 2, 3, 4, 5
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = kq.load()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kq.EXPORTED)
+
+
+def test_status_strings():
+    for code, name in kq.STATUS_NAMES.items():
+        assert kq.status_string(code).startswith(name)
+    assert kq.status_string(99) == "KQ_ERR_UNKNOWN"
+
+
+def test_sizes_and_geometry():
+    assert kq.workspace_bytes(512, 1000, 4) == 0       # k not a multiple of 256
+    assert kq.workspace_bytes(512, 1024, 0) == 0
+    assert kq.workspace_bytes(512, 1024, 17) == 0
+    assert kq.workspace_bytes(0, 1024, 1) == 0
+    assert kq.staged_bytes(1024) == 67840
+    assert kq.staged_bytes(6656) == 7 * 67840
+    for n, k in [(512, 1024), (6656, 6656), (6656, 33280), (131072, 6656), (17920, 6656), (6656, 17920), (1, 256)]:
+        assert kq.workspace_bytes(n, k, 1) == kq.workspace_bytes(n, k, 16) > 0
+        nt, nwg, sp = kq.launch_geometry(n, k)
+        assert nt in (1, 2) and nwg * 64 * nt >= n and 1 <= sp <= -(-k // 1024)
+        assert kq.scratch_bytes(n, k) <= kq.workspace_bytes(n, k, 16)
+    with pytest.raises(kq.KQError):
+        kq.launch_geometry(16, 100)
+
+
+def _call_gemv(w=FAKE, n=512, k=1024, x=FAKE, m=4, out=FAKE, ws=FAKE, wsb=None):
+    lib = kq.load()
+    if wsb is None:
+        wsb = kq.workspace_bytes(n, k, m) or 1 << 30
+    return lib.kq_gemv_rows(w, n, k, x, m, out, ws, wsb, None)
+
+
+def _call_verify(w=FAKE, n=512, k=1024, x=FAKE, m=4, draft=(1, 2, 3), am=FAKE, acc=FAKE, lg=None,
+                 ws=FAKE, wsb=None):
+    lib = kq.load()
+    if wsb is None:
+        wsb = kq.workspace_bytes(n, k, m) or 1 << 30
+    d = (ctypes.c_int32 * max(1, len(draft)))(*draft) if draft is not None else None
+    return lib.kq_verify_argmax_accept(w, n, k, x, m, d, am, acc, lg, ws, wsb, None)
+
+
+def test_gemv_argument_errors():
+    assert _call_gemv(w=None) == NULL
+    assert _call_gemv(x=None) == NULL
+    assert _call_gemv(out=None) == NULL
+    assert _call_gemv(ws=None) == NULL
+    assert _call_gemv(m=0) == SHAPE
+    assert _call_gemv(m=17) == SHAPE
+    assert _call_gemv(k=1000) == SHAPE
+    assert _call_gemv(k=0) == SHAPE
+    assert _call_gemv(n=0) == SHAPE
+    assert _call_gemv(n=1 << 31) == SHAPE
+    assert _call_gemv(w=FAKE + 8) == ALIGN
+    assert _call_gemv(x=FAKE + 4) == ALIGN
+    assert _call_gemv(ws=FAKE + 16) == ALIGN
+    assert _call_gemv(wsb=kq.workspace_bytes(512, 1024, 4) - 1) == WS
+
+
+def test_verify_argument_errors():
+    assert _call_verify(am=None) == NULL
+    assert _call_verify(acc=None) == NULL
+    assert _call_verify(draft=None) == NULL
+    assert _call_verify(m=17, draft=tuple(range(16))) == SHAPE
+    assert _call_verify(draft=(1, 2, 512)) == TOKEN
+    assert _call_verify(draft=(-1, 2, 3)) == TOKEN
+    assert _call_verify(wsb=100) == WS
+
+
+def test_staged_argument_errors():
+    lib = kq.load()
+    assert lib.kq_stage_rows(None, 4, 1024, FAKE, 1 << 20, None) == NULL
+    assert lib.kq_stage_rows(FAKE, 0, 1024, FAKE, 1 << 20, None) == SHAPE
+    assert lib.kq_stage_rows(FAKE, 4, 1024, FAKE + 16, 1 << 20, None) == ALIGN
+    assert lib.kq_stage_rows(FAKE, 4, 1024, FAKE, 100, None) == WS
+    sb = kq.scratch_bytes(512, 1024)
+    assert lib.kq_gemv_staged(FAKE, 512, 1024, None, 4, FAKE, FAKE, sb, None) == NULL
+    assert lib.kq_gemv_staged(FAKE, 512, 1024, FAKE, 4, FAKE, FAKE, sb - 1, None) == WS
+    d = (ctypes.c_int32 * 3)(0, 1, 600)
+    assert lib.kq_verify_staged(FAKE, 512, 1024, FAKE, 4, d, FAKE, FAKE, None, FAKE, sb, None) == TOKEN
+    assert lib.kq_workspace_init(None, 256, None) == NULL
+    assert lib.kq_workspace_init(FAKE + 4, 256, None) == ALIGN
+    assert lib.kq_workspace_init(FAKE, 8, None) == WS

@@ -1,0 +1,228 @@
+"""GPU parity tests: the HIP path (through the C ABI) against the CPU oracle,
+element by element, on seeded inputs of every workload shape, plus edge
+shapes, planted ties, row invariance, determinism and the staged API."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.parity import check_accept, check_argmax, check_logits, log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import quant_verify_gemv_amd as kq
+    kq.load()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return kq
+
+
+DEV = "cuda:0"
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def gpu_logits(kq, w_d, n, k, x):
+    out = kq.gemv_rows(w_d, n, k, to_dev(x))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def gpu_verify(kq, w_d, n, k, x, draft, want_logits=False):
+    am, acc, lg = kq.verify(w_d, n, k, to_dev(x), list(draft), want_logits=want_logits)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), acc.cpu().numpy(), (lg.cpu().numpy() if lg is not None else None)
+
+
+def test_tiny_config_verify_all_accept_lengths(kq):
+    c = synthetic.TINY
+    n, k, m = c["n"], c["k"], c["m"]
+    log(f"tiny: n={n} k={k} m={m}")
+    w = synthetic.q4k_matrix(n, k, c["seed"])
+    x = synthetic.activations(m, k, c["seed"])
+    L, A = oracle.gemv_rows(w, k, x)
+    w_d = to_dev(w)
+    G = gpu_logits(kq, w_d, n, k, x)
+    ratio = check_logits(G, L, A, what="tiny")
+    log(f"tiny: max |d|/tol = {ratio:.3g}")
+    o_am, o_nc = oracle.argmax_flags(L, A)
+    drafts = [synthetic.forced_draft(o_am[:m - 1], a, n) for a in range(m)]
+    drafts += [synthetic.inject_mismatches(o_am[:m - 1], n, seed=1000 + t) for t in range(16)]
+    seen = set()
+    for i, d in enumerate(drafts):
+        g_am, g_acc, g_lg = gpu_verify(kq, w_d, n, k, x, d, want_logits=(i == 0))
+        check_argmax(g_am, L, A, what=f"tiny trial {i}")
+        acc_o, _ = check_accept(g_acc[0], g_acc[1], d, g_am, o_am, o_nc, what=f"tiny trial {i}")
+        seen.add(int(g_acc[0]))
+        if g_lg is not None:
+            assert np.array_equal(g_lg, G), "verify logits differ from gemv logits"
+    assert seen >= set(range(m)), f"accepted lengths seen: {sorted(seen)}"
+
+
+def test_square_m_sweep_row_invariance(kq):
+    c = synthetic.SQUARE
+    n = k = c["n"]
+    log(f"square: n=k={n}")
+    w = synthetic.q4k_matrix(n, k, c["seed"])
+    x = synthetic.activations(16, k, c["seed"])
+    L, A = oracle.gemv_rows(w, k, x)
+    w_d = to_dev(w)
+    G16 = gpu_logits(kq, w_d, n, k, x)
+    check_logits(G16, L, A, what="square m=16")
+    for mm in c["ms"]:
+        Gm = gpu_logits(kq, w_d, n, k, x[:mm])
+        check_logits(Gm, L[:mm], A[:mm], what=f"square m={mm}")
+        assert np.array_equal(Gm, G16[:mm]), f"rows of m={mm} call differ from m=16 call"
+    for i in (0, 7, 15):  # row i of the 16-row call equals the 1-row call on x[i]
+        G1 = gpu_logits(kq, w_d, n, k, x[i:i + 1])
+        assert np.array_equal(G1[0], G16[i])
+    log("square: ok")
+
+
+def test_fc_projection(kq):
+    c = synthetic.FC
+    n, k, m = c["n"], c["k"], c["m"]
+    log(f"fc: n={n} k={k} m={m}")
+    w = synthetic.q4k_matrix(n, k, c["seed"])
+    x = synthetic.fc_activations(m, c["seed"])
+    L, A = oracle.gemv_rows(w, k, x)
+    G = gpu_logits(kq, to_dev(w), n, k, x)
+    ratio = check_logits(G, L, A, what="fc")
+    log(f"fc: max |d|/tol = {ratio:.3g}")
+
+
+def test_lm_head_verify_full_size(kq):
+    c = synthetic.LM_HEAD
+    n, k, m = c["n"], c["k"], c["m"]
+    log(f"lm head: n={n} k={k} m={m} (oracle over all rows)")
+    w = synthetic.q4k_matrix(n, k, c["seed"])
+    x = synthetic.activations(m, k, c["seed"])
+    L, A = oracle.gemv_rows(w, k, x)
+    o_am, o_nc = oracle.argmax_flags(L, A)
+    log(f"lm head: oracle flagged rows {int(np.sum(o_nc > 0))}")
+    w_d = to_dev(w)
+    drafts = [synthetic.forced_draft(o_am[:m - 1], a, n) for a in (0, 1, 7, 15)]
+    drafts += [synthetic.inject_mismatches(o_am[:m - 1], n, seed=1000 + t) for t in range(8)]
+    for i, d in enumerate(drafts):
+        g_am, g_acc, g_lg = gpu_verify(kq, w_d, n, k, x, d, want_logits=(i == 0))
+        if g_lg is not None:
+            ratio = check_logits(g_lg, L, A, what="lm head")
+            log(f"lm head: max |d|/tol = {ratio:.3g}")
+        check_argmax(g_am, L, A, what=f"lm head trial {i}")
+        check_accept(g_acc[0], g_acc[1], d, g_am, o_am, o_nc, what=f"lm head trial {i}")
+    log("lm head: ok")
+
+
+@pytest.mark.parametrize("shape", [(6656, 6656), (17920, 6656), (6656, 17920)])
+def test_stack_shapes_sampled_rows(kq, shape):
+    n, k = shape
+    log(f"stack shape n={n} k={k}")
+    g = [s for s in synthetic.stack_matrices(1) if (s.n, s.k) == shape][0]
+    w = synthetic.q4k_matrix(n, k, g.seed)
+    x = synthetic.activations(16, k, synthetic.stack_activation_seed(k))
+    rng = np.random.default_rng(n + k)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, n - 17, n - 1], rng.integers(0, n, 250)]))
+    L, A = oracle.gemv_rows(w, k, x, rows=rows)
+    w_d = to_dev(w)
+    staged = kq.stage_rows(to_dev(x))
+    scratch = kq.new_scratch(n, k, DEV)
+    for mm in (1, 16):
+        st = staged if mm == 16 else kq.stage_rows(to_dev(x[:1]))
+        G = kq.gemv_staged(w_d, n, k, st, mm, scratch)
+        torch.cuda.synchronize()
+        check_logits(G.cpu().numpy()[:, rows], L[:mm], A[:mm], what=f"stack {shape} m={mm}")
+
+
+EDGE = [(1, 256), (17, 256), (16, 512), (129, 1280), (1000, 2304), (513, 3328), (2048, 9216)]
+
+
+@pytest.mark.parametrize("n,k", EDGE)
+def test_edge_shapes(kq, n, k):
+    log(f"edge n={n} k={k}")
+    w = synthetic.q4k_matrix(n, k, 7 + n + k)
+    x = synthetic.activations(16, k, 9 + n + k)
+    L, A = oracle.gemv_rows(w, k, x)
+    w_d = to_dev(w)
+    for mm in (1, 3, 16):
+        G = gpu_logits(kq, w_d, n, k, x[:mm])
+        check_logits(G, L[:mm], A[:mm], what=f"edge {n}x{k} m={mm}")
+        o_am, o_nc = oracle.argmax_flags(L[:mm], A[:mm])
+        d = synthetic.inject_mismatches(o_am[:mm - 1], n, seed=n * 31 + mm) if mm > 1 else []
+        g_am, g_acc, _ = gpu_verify(kq, w_d, n, k, x[:mm], d)
+        check_argmax(g_am, L[:mm], A[:mm], what=f"edge {n}x{k} m={mm}")
+        check_accept(g_acc[0], g_acc[1], d, g_am, o_am, o_nc, what=f"edge {n}x{k} m={mm}")
+
+
+def test_one_hot_rows_extract_weights(kq):
+    n, k = 300, 2048
+    w = synthetic.q4k_matrix(n, k, 41)
+    Wd = oracle.decode_matrix(w, k)
+    cols = [0, 31, 32, 255, 256, 1023, 1024, 2047, 100, 600, 1500, 1999, 64, 96, 128, 160]
+    x = np.zeros((16, k), dtype=np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    G = gpu_logits(kq, to_dev(w), n, k, x)
+    for i, c in enumerate(cols):
+        # d*sc*q and dmin*m are exact in fp32, so one rounding of their difference
+        assert np.all(np.abs(G[i] - Wd[:, c]) <= 2.0 ** -24 * np.abs(Wd[:, c])), c
+
+
+def test_planted_exact_ties_pick_lowest_index(kq):
+    n, k = 700, 1024
+    w = synthetic.q4k_matrix(n, k, 51)
+    x = synthetic.activations(1, k, 52)
+    L, A = oracle.gemv_rows(w, k, x)
+    o_am, _ = oracle.argmax_flags(L, A)
+    b = int(o_am[0])
+    p = 5 if b != 5 else 6
+    q = n - 3 if b != n - 3 else n - 4
+    w2 = w.copy()
+    w2[p] = w[b]  # identical weight rows: an exact three-way tie for the maximum
+    w2[q] = w[b]
+    w2_d = to_dev(w2)
+    G = gpu_logits(kq, w2_d, n, k, x)
+    assert G[0, p] == G[0, b] == G[0, q]
+    g_am, g_acc, _ = gpu_verify(kq, w2_d, n, k, x, [])
+    assert int(g_am[0]) == min(p, q, b)
+    assert int(g_acc[0]) == 0 and int(g_acc[1]) == min(p, q, b)
+
+
+def test_deterministic_and_staged_equals_all_in_one(kq):
+    n, k = 3000, 6656
+    w = synthetic.q4k_matrix(n, k, 61)
+    x = synthetic.activations(16, k, 62)
+    w_d, x_d = to_dev(w), to_dev(x)
+    a = kq.gemv_rows(w_d, n, k, x_d).cpu().numpy()
+    b = kq.gemv_rows(w_d, n, k, x_d).cpu().numpy()
+    assert np.array_equal(a, b)
+    st = kq.stage_rows(x_d)
+    sc = kq.new_scratch(n, k, DEV)
+    c = kq.gemv_staged(w_d, n, k, st, 16, sc).cpu().numpy()
+    assert np.array_equal(a, c)
+    d = list(range(15))
+    am1, acc1, _ = kq.verify(w_d, n, k, x_d, d)
+    am2, acc2, lg2 = kq.verify_staged(w_d, n, k, st, 16, d, sc, want_logits=True)
+    assert np.array_equal(am1.cpu().numpy(), am2.cpu().numpy())
+    assert np.array_equal(acc1.cpu().numpy(), acc2.cpu().numpy())
+    assert np.array_equal(lg2.cpu().numpy(), a)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        e = kq.gemv_rows(w_d, n, k, x_d)
+    s.synchronize()
+    assert np.array_equal(e.cpu().numpy(), a)
+
+
+def test_activation_range_scaling(kq):
+    n, k = 256, 2048
+    w = synthetic.q4k_matrix(n, k, 71)
+    base = synthetic.activations(16, k, 72)
+    scales = np.array([1e-30, 1e-8, 1e-4, 1.0, 1e4, 1e8, 1e20, 3e30] * 2, dtype=np.float64)
+    x = (base * scales[:, None]).astype(np.float32)
+    L, A = oracle.gemv_rows(w, k, x)
+    G = gpu_logits(kq, to_dev(w), n, k, x)
+    check_logits(G, L, A, what="activation range")
