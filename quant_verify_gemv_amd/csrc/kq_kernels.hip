@@ -43,8 +43,33 @@ __device__ __forceinline__ half8 make_h8(unsigned a, unsigned b, unsigned c, uns
   return __builtin_bit_cast(half8, v);
 }
 
-__device__ __forceinline__ u32x4 ld16_stream(const uint8_t *p) {
-  return __builtin_nontemporal_load((const u32x4 *)p);
+__device__ __forceinline__ u32x4 ld16_stream(const uint8_t *p) { return *(const u32x4 *)p; }
+
+// Cross-workgroup hand-off without device-scope fences. Values another
+// workgroup will read are written with agent-scope relaxed atomic stores
+// (write-through to the device coherence point) and read back with
+// agent-scope relaxed atomic loads (never served from a stale cache); the
+// writer waits for its stores to complete (vmcnt(0)) before the arrival
+// counter is incremented. This is the device-scope release/acquire
+// sequence minus the L2 write-back/invalidate that only ordinary cached
+// stores need, which would otherwise cost every workgroup an L2 flush.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned long long *p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this thread's global stores have completed, then barrier
+__device__ __forceinline__ void stores_done_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
 }
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4 *)p; }
 
@@ -71,7 +96,7 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
   const int64_t q = blockIdx.x;
   const int64_t k0 = q * kQuadK + 64 * c;
   const bool valid = k0 < k;
-  const bool active = m < m_rows;
+  const bool active = m < m_rows;  // rows >= m_rows are staged as zeros
 
   if (zero_words && q == 0) {
     for (int64_t i = t; i < n_zero_words; i += 256) zero_words[i] = 0u;
@@ -105,8 +130,8 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
     e = 10 - E;
     e = e > 100 ? 100 : e;
   }
-  if (!active) return;
-
+  // rows >= m_rows are staged as zeros with scale 1: the main kernel then
+  // runs every row unpredicated and simply does not store rows >= m.
   uint8_t *qbase = staged + q * kQuadBytes;
   if (c == 0) *(float *)(qbase + kXiOffset + 4 * m) = ldexpf(1.0f, -e);
 
@@ -190,7 +215,6 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
   const int kg = lane >> 4;
   const int ln = lane & 15;
   const int M = a.m;
-  const bool m_ok = ln < M;  // this lane's A-operand row exists
 
   const int64_t N = a.n;
   const int64_t KB = a.k / kQK;
@@ -207,188 +231,172 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
   const int q_begin = blockIdx.y * a.g.qps;
   const int q_end = min(a.g.quads, q_begin + a.g.qps);
   const int64_t b_begin = (int64_t)q_begin * 4;
-  const int64_t b_end = min(KB, (int64_t)q_end * 4);
+  const int64_t b_last = min(KB, (int64_t)q_end * 4) - 1;  // last block of this split
 
-  f32x4 acc[NT], G[NT];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    G[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // copy helpers for the staged block of activations (only rows < M)
-  const bool cp_ok = (tid & 15) < M;
+  // Software pipeline. The weights of a wave's NT tiles rotate through four
+  // register sets (the quad loop is unrolled four times, one step per block)
+  // so that the loads of block b+3 are in flight while block b computes; the
+  // activations of block b+1 are loaded during block b and written to the
+  // other LDS buffer at its end. Every load is unconditional (indices are
+  // clamped to the split's last block) so that outstanding loads are counted
+  // statically and waits cover only the data about to be used.
+  auto clampb = [&](int64_t b) -> int64_t { return b < b_last ? b : b_last; };
+  auto load_w = [&](WTile (&w)[NT], int64_t b) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint8_t *p = rowp[t] + b * kBlockBytes;
+      w[t].hdr = ld16_stream(p);
+      w[t].q0 = ld16_stream(p + 16 + 32 * kg);
+      w[t].q1 = ld16_stream(p + 32 + 32 * kg);
+    }
+  };
   auto x_src = [&](int64_t b) -> const uint8_t * {
     return a.staged + (b >> 2) * kQuadBytes + (b & 3) * kXaBlockBytes;
   };
-
-  WTile cur[NT], nxt[NT];
-  u32x4 xr[4];
-  // prologue: weights of block b_begin, activations of b_begin into LDS 0
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint8_t *p = rowp[t] + b_begin * kBlockBytes;
-    cur[t].hdr = ld16_stream(p);
-    cur[t].q0 = ld16_stream(p + 16 + 32 * kg);
-    cur[t].q1 = ld16_stream(p + 32 + 32 * kg);
-  }
-  if (cp_ok) {
+  WTile w0[NT], w1[NT], w2[NT], w3[NT];
+  load_w(w0, b_begin);
+  load_w(w1, clampb(b_begin + 1));
+  load_w(w2, clampb(b_begin + 2));
+  {
     const uint8_t *src = x_src(b_begin);
+    u32x4 xr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[0][(tid + 256 * j) * 16]) = ld16(src + (tid + 256 * j) * 16);
+    for (int j = 0; j < 4; ++j) xr[j] = ld16(src + (tid + 256 * j) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[0][(tid + 256 * j) * 16]) = xr[j];
   }
   __syncthreads();
 
-  u32x4 hmin[NT];   // header of block 4q + kg (min term of the quad)
-  u32x4 xs_hi, xs_lo;
-  f32x4 xinv;
+  for (int q = q_begin; q < q_end; ++q) {
+    const uint8_t *qb = a.staged + (int64_t)q * kQuadBytes;
+    const u32x4 xs_hi = ld16(qb + kXsOffset + lane * 16);
+    const u32x4 xs_lo = ld16(qb + kXsOffset + 1024 + lane * 16);
+    const f32x4 xinv = *(const f32x4 *)(qb + kXiOffset + 16 * kg);
+    const int64_t qb0 = (int64_t)q * 4;
+    const int nblk = (int)(min((int64_t)4, b_last + 1 - qb0));
+    f32x4 G[NT];
+    u32x4 hmin[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) hmin[t] = u32x4{0u, 0u, 0u, 0u};
-
-  for (int64_t b = b_begin; b < b_end; ++b) {
-    const int buf = (int)((b - b_begin) & 1);
-    const int bq = (int)(b & 3);
-    const bool more = b + 1 < b_end;
-    if (bq == 0 || b == b_begin) {
-      const uint8_t *qb = a.staged + (b >> 2) * kQuadBytes;
-      if (m_ok) {
-        xs_hi = ld16(qb + kXsOffset + lane * 16);
-        xs_lo = ld16(qb + kXsOffset + 1024 + lane * 16);
-      } else {
-        xs_hi = u32x4{0u, 0u, 0u, 0u};
-        xs_lo = u32x4{0u, 0u, 0u, 0u};
-      }
-      xinv = *(const f32x4 *)(qb + kXiOffset + 16 * kg);
+    for (int t = 0; t < NT; ++t) {
+      G[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      hmin[t] = u32x4{0u, 0u, 0u, 0u};
     }
-    if (more) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint8_t *p = rowp[t] + (b + 1) * kBlockBytes;
-        nxt[t].hdr = ld16_stream(p);
-        nxt[t].q0 = ld16_stream(p + 16 + 32 * kg);
-        nxt[t].q1 = ld16_stream(p + 32 + 32 * kg);
-      }
-      if (cp_ok) {
-        const uint8_t *src = x_src(b + 1);
+
+    // one block: prefetch block b+3 into `pf` and activations of b+1, then
+    // contract the weights in `cur` with the activations in LDS buffer bq&1.
+    auto step = [&](WTile (&cur)[NT], WTile (&pf)[NT], const int bq) {
+      const int64_t b = qb0 + bq;
+      u32x4 xr[4];
+      {
+        const uint8_t *src = x_src(clampb(b + 1));
 #pragma unroll
         for (int j = 0; j < 4; ++j) xr[j] = ld16(src + (tid + 256 * j) * 16);
       }
-    }
-
-    // per-tile scale constants for this block
-    unsigned slo[NT], nlo[NT], shi[NT], nhi[NT];
-    float dsc[NT];
+      load_w(pf, clampb(b + 3));
+      __builtin_amdgcn_sched_barrier(0);
+      if (bq < nblk) {
+        unsigned slo[NT], nlo[NT], shi[NT], nhi[NT];
+        float dsc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const u32x4 h = cur[t].hdr;
-      if (bq == kg) hmin[t] = h;
-      dsc[t] = h2f_lo(h.x);
-      const unsigned sc03 = h.y & 0x3F3F3F3Fu;
-      const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-      const unsigned sel = (kg < 2 ? sc03 : sc47) >> ((kg & 1) * 16);
-      const float s0 = (float)(sel & 0xFFu);         // sc[2kg]   (low nibbles)
-      const float s1 = (float)((sel >> 8) & 0xFFu);  // sc[2kg+1] (high nibbles)
-      half2v a0 = {(_Float16)s0, (_Float16)s0};
-      half2v a1 = {(_Float16)(-1024.0f * s0), (_Float16)(-1024.0f * s0)};
-      half2v a2 = {(_Float16)(0.0625f * s1), (_Float16)(0.0625f * s1)};
-      half2v a3 = {(_Float16)(-64.0f * s1), (_Float16)(-64.0f * s1)};
-      slo[t] = as_u(a0); nlo[t] = as_u(a1); shi[t] = as_u(a2); nhi[t] = as_u(a3);
-    }
-
-    f32x4 chi[NT], clo[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      chi[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      clo[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const uint8_t *xb = s_x[buf];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8 ahi, alo;
-      if (m_ok) {
-        ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
-        alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
-      } else {
-        ahi = half8{0, 0, 0, 0, 0, 0, 0, 0};
-        alo = ahi;
-      }
-      const int sp = s & 3;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 q0 = cur[t].q0, q1 = cur[t].q1;
-        const unsigned da = sp == 0 ? q0.x : sp == 1 ? q0.z : sp == 2 ? q1.x : q1.z;
-        const unsigned db = sp == 0 ? q0.y : sp == 1 ? q0.w : sp == 2 ? q1.y : q1.w;
-        const unsigned mask = s < 4 ? 0x000F000Fu : 0x00F000F0u;
-        const half2v sc = as_h2(s < 4 ? slo[t] : shi[t]);
-        const half2v nb = as_h2(s < 4 ? nlo[t] : nhi[t]);
-        const unsigned u0 = (da & mask) | 0x64006400u;
-        const unsigned u1 = ((da >> 8) & mask) | 0x64006400u;
-        const unsigned u2 = (db & mask) | 0x64006400u;
-        const unsigned u3 = ((db >> 8) & mask) | 0x64006400u;
-        const half2v w0 = __builtin_elementwise_fma(as_h2(u0), sc, nb);
-        const half2v w1 = __builtin_elementwise_fma(as_h2(u1), sc, nb);
-        const half2v w2 = __builtin_elementwise_fma(as_h2(u2), sc, nb);
-        const half2v w3 = __builtin_elementwise_fma(as_h2(u3), sc, nb);
-        const half8 bw = make_h8(as_u(w0), as_u(w1), as_u(w2), as_u(w3));
-        chi[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw, chi[t], 0, 0, 0);
-        clo[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw, clo[t], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) G[t][r] += dsc[t] * (chi[t][r] + clo[t][r]);
-    }
-
-    // end of a quad: min term and the row scale
-    if (bq == 3 || b + 1 == b_end) {
-      const int nblk = bq + 1;  // blocks of this quad that exist
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 h = hmin[t];
-        const bool ok = kg < nblk;
-        const float dmin = h2f_hi(h.x);
-        const unsigned m03 = h.z & 0x3F3F3F3Fu;
-        const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-        unsigned bh[4], bl[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const unsigned src = p < 2 ? m03 : m47;
-          const int sh = (p & 1) * 16;
-          const float v0 = ok ? dmin * (float)((src >> sh) & 0xFFu) : 0.0f;
-          const float v1 = ok ? dmin * (float)((src >> (sh + 8)) & 0xFFu) : 0.0f;
-          const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-          const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-          half2v hh = {h0, h1}, ll = {l0, l1};
-          bh[p] = as_u(hh);
-          bl[p] = as_u(ll);
+        for (int t = 0; t < NT; ++t) {
+          const u32x4 h = cur[t].hdr;
+          hmin[t] = bq == kg ? h : hmin[t];
+          dsc[t] = h2f_lo(h.x);
+          const unsigned sc03 = h.y & 0x3F3F3F3Fu;
+          const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+          const unsigned sel = (kg < 2 ? sc03 : sc47) >> ((kg & 1) * 16);
+          const float s0 = (float)(sel & 0xFFu);         // sc[2kg]   (low nibbles)
+          const float s1 = (float)((sel >> 8) & 0xFFu);  // sc[2kg+1] (high nibbles)
+          half2v a0 = {(_Float16)s0, (_Float16)s0};
+          half2v a1 = {(_Float16)(-1024.0f * s0), (_Float16)(-1024.0f * s0)};
+          half2v a2 = {(_Float16)(0.0625f * s1), (_Float16)(0.0625f * s1)};
+          half2v a3 = {(_Float16)(-64.0f * s1), (_Float16)(-64.0f * s1)};
+          slo[t] = as_u(a0); nlo[t] = as_u(a1); shi[t] = as_u(a2); nhi[t] = as_u(a3);
         }
-        const half8 b2h = make_h8(bh[0], bh[1], bh[2], bh[3]);
-        const half8 b2l = make_h8(bl[0], bl[1], bl[2], bl[3]);
-        const half8 a2h = __builtin_bit_cast(half8, xs_hi);
-        const half8 a2l = __builtin_bit_cast(half8, xs_lo);
-        f32x4 c2 = {0.f, 0.f, 0.f, 0.f};
-        c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2h, c2, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2l, b2h, c2, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2l, c2, 0, 0, 0);
+        f32x4 chi[NT], clo[NT];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[t][r] += xinv[r] * (G[t][r] - c2[r]);
-          G[t][r] = 0.0f;
+        for (int t = 0; t < NT; ++t) {
+          chi[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          clo[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        hmin[t] = u32x4{0u, 0u, 0u, 0u};
+        const uint8_t *xb = s_x[bq & 1];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
+          const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+          const int sp = s & 3;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const u32x4 q0 = cur[t].q0, q1 = cur[t].q1;
+            const unsigned da = sp == 0 ? q0.x : sp == 1 ? q0.z : sp == 2 ? q1.x : q1.z;
+            const unsigned db = sp == 0 ? q0.y : sp == 1 ? q0.w : sp == 2 ? q1.y : q1.w;
+            const unsigned mask = s < 4 ? 0x000F000Fu : 0x00F000F0u;
+            const half2v sc = as_h2(s < 4 ? slo[t] : shi[t]);
+            const half2v nb = as_h2(s < 4 ? nlo[t] : nhi[t]);
+            const unsigned u0 = (da & mask) | 0x64006400u;
+            const unsigned u1 = ((da >> 8) & mask) | 0x64006400u;
+            const unsigned u2 = (db & mask) | 0x64006400u;
+            const unsigned u3 = ((db >> 8) & mask) | 0x64006400u;
+            const half2v v0 = __builtin_elementwise_fma(as_h2(u0), sc, nb);
+            const half2v v1 = __builtin_elementwise_fma(as_h2(u1), sc, nb);
+            const half2v v2 = __builtin_elementwise_fma(as_h2(u2), sc, nb);
+            const half2v v3 = __builtin_elementwise_fma(as_h2(u3), sc, nb);
+            const half8 bw = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
+            chi[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw, chi[t], 0, 0, 0);
+            clo[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw, clo[t], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) G[t][r] += dsc[t] * (chi[t][r] + clo[t][r]);
+        }
       }
-    }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[(bq & 1) ^ 1][(tid + 256 * j) * 16]) = xr[j];
+      __syncthreads();
+    };
+    step(w0, w3, 0);
+    step(w1, w0, 1);
+    step(w2, w1, 2);
+    step(w3, w2, 3);
 
-    if (more) {
-      if (cp_ok) {
+    // end of the quad: min term (three MFMAs) and the row scale 2^-e
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[buf ^ 1][(tid + 256 * j) * 16]) = xr[j];
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 h = hmin[t];
+      const bool ok = kg < nblk;
+      const float dmin = h2f_hi(h.x);
+      const unsigned m03 = h.z & 0x3F3F3F3Fu;
+      const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+      unsigned bh[4], bl[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const unsigned src = p < 2 ? m03 : m47;
+        const int sh = (p & 1) * 16;
+        const float v0 = ok ? dmin * (float)((src >> sh) & 0xFFu) : 0.0f;
+        const float v1 = ok ? dmin * (float)((src >> (sh + 8)) & 0xFFu) : 0.0f;
+        const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+        const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+        half2v hh = {h0, h1}, ll = {l0, l1};
+        bh[p] = as_u(hh);
+        bl[p] = as_u(ll);
       }
+      const half8 b2h = make_h8(bh[0], bh[1], bh[2], bh[3]);
+      const half8 b2l = make_h8(bl[0], bl[1], bl[2], bl[3]);
+      const half8 a2h = __builtin_bit_cast(half8, xs_hi);
+      const half8 a2l = __builtin_bit_cast(half8, xs_lo);
+      f32x4 c2 = {0.f, 0.f, 0.f, 0.f};
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2h, c2, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2l, b2h, c2, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2l, c2, 0, 0, 0);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) cur[t] = nxt[t];
+      for (int r = 0; r < 4; ++r) acc[t][r] += xinv[r] * (G[t][r] - c2[r]);
     }
-    __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -436,28 +444,26 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = 4 * kg + r;
-          if (m < M) a.partials[((int64_t)blockIdx.y * kMaxRows + m) * N + rows[t]] = acc[t][r];
+          if (m < M) st_dev(&a.partials[((int64_t)blockIdx.y * kMaxRows + m) * N + rows[t]], acc[t][r]);
         }
       }
     }
-    __threadfence();
-    __syncthreads();
+    stores_done_barrier();
     if (tid == 0) {
-      const unsigned old = atomicAdd(&a.tile_cnt[wg], 1u);
+      const unsigned old = __hip_atomic_fetch_add(&a.tile_cnt[wg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = old == (unsigned)(splits - 1);
-      if (last) a.tile_cnt[wg] = 0u;
+      if (last) __hip_atomic_store(&a.tile_cnt[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag = last;
     }
     __syncthreads();
     if (!s_flag) return;
-    __threadfence();
     const int64_t nrows = min((int64_t)rows_wg, N - row0);
     for (int64_t e = tid; e < (int64_t)M * nrows; e += kThreads) {
       const int m = (int)(e / nrows);
       const int64_t n = row0 + e % nrows;
       float v = 0.0f;
       for (int sp = 0; sp < splits; ++sp) {
-        const float pv = __builtin_nontemporal_load(&a.partials[((int64_t)sp * kMaxRows + m) * N + n]);
+        const float pv = ld_dev(&a.partials[((int64_t)sp * kMaxRows + m) * N + n]);
         v = sp == 0 ? pv : v + pv;
       }
       if (a.logits) a.logits[(int64_t)m * N + n] = v;
@@ -467,16 +473,14 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
 
   if (!a.verify) return;
   __syncthreads();
-  if (tid < kMaxRows) a.wg_keys[(int64_t)wg * kMaxRows + tid] = s_keys[tid];
-  __threadfence();
-  __syncthreads();
+  if (tid < kMaxRows) st_dev(&a.wg_keys[(int64_t)wg * kMaxRows + tid], s_keys[tid]);
+  stores_done_barrier();
   if (tid == 0) {
-    const unsigned old = atomicAdd(a.done, 1u);
+    const unsigned old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_flag = old == (unsigned)(a.g.n_wg - 1);
   }
   __syncthreads();
   if (!s_flag) return;
-  __threadfence();
   if (tid < kMaxRows) s_keys[tid] = 0ull;
   __syncthreads();
   {
@@ -484,8 +488,7 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     if (m < M) {
       unsigned long long best = 0ull;
       for (int w = tid >> 4; w < a.g.n_wg; w += kThreads / 16) {
-        const unsigned long long key = __hip_atomic_load(&a.wg_keys[(int64_t)w * kMaxRows + m],
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long key = ld_dev(&a.wg_keys[(int64_t)w * kMaxRows + m]);
         best = key > best ? key : best;
       }
       atomicMax(&s_keys[m], best);
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     while (i < a.k_draft && a.draft[i] == am[i]) ++i;
     a.accept_out[0] = i;
     a.accept_out[1] = am[i];
-    *a.done = 0u;
+    __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
