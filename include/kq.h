@@ -135,8 +135,25 @@ kq_status kq_verify_staged(const void *w_q4k, int64_t n, int64_t k,
                            float *logits_or_null,
                            void *scratch, size_t scratch_bytes, void *stream);
 
-/* Launch geometry the library uses for an n x k matrix (a function of n and
- * k only, never of m): tiles of 16 rows per wave (*nt), workgroups along n
+/* Bytes of device scratch kq_gemv_staged_group needs for `count` matrices
+ * of n x k (0 for invalid arguments). */
+size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count);
+
+/* kq_gemv_staged for 1 <= count <= 8 matrices of the same shape that share
+ * the staged activations (projections of one input, e.g. q/k/v or gate/up),
+ * in one launch.
+ *  w_q4k   host array of `count` device pointers (each 16-byte aligned)
+ *  logits  host array of `count` device pointers, fp32 [m][n] each
+ *  scratch device, >= kq_group_scratch_bytes(n, k, count) bytes, zeroed once
+ * Each matrix's logits are deterministic and within the kq.h tolerance; they
+ * may differ in the last bits from a separate kq_gemv_staged call because the
+ * launch can split k differently (the split depends on n, k and count). */
+kq_status kq_gemv_staged_group(const void *const *w_q4k, int count, int64_t n, int64_t k,
+                               const void *staged, int m, float *const *logits,
+                               void *scratch, size_t scratch_bytes, void *stream);
+
+/* Launch geometry the library uses for one n x k matrix (a function of n and
+ * k only, never of m): 16-row tiles per wave (*nt), workgroups along n
  * (*n_wg) and along k (*splits). Returns KQ_ERR_SHAPE for invalid shapes. */
 kq_status kq_launch_geometry(int64_t n, int64_t k, int *nt, int *n_wg, int *splits);
 

@@ -4,9 +4,9 @@ The hot path (activation staging, Q4_K dequant + MFMA skinny GEMM, split-K
 combine, row argmax, greedy accept) runs in HIP kernels inside libkq.so,
 behind the C ABI of include/kq.h. This package is the thin Python binding.
 """
-from .lib import (KQError, gemv_rows, gemv_staged, launch_geometry, load, new_scratch,  # noqa: F401
-                  scratch_bytes, stage_rows, staged_bytes, status_string, verify, verify_staged,
-                  workspace_bytes)
+from .lib import (KQError, gemv_rows, gemv_staged, gemv_staged_group, group_scratch_bytes,  # noqa: F401
+                  launch_geometry, load, new_group_scratch, new_scratch, scratch_bytes, stage_rows,
+                  staged_bytes, status_string, verify, verify_staged, workspace_bytes)
 
 QK = 256
 BLOCK_BYTES = 144

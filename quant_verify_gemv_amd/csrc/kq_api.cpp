@@ -17,13 +17,16 @@ static bool shape_ok(int64_t n, int64_t k) {
          (k / kQK) * kBlockBytes <= (((int64_t)1 << 62) / n);
 }
 
-Geometry geometry(int64_t n, int64_t k) {
+Geometry geometry(int64_t n, int64_t k, int count) {
   Geometry g;
   const int64_t tiles = cdiv(n, 16);
+  g.count = count;
   g.quads = (int)cdiv(k, kQuadK);
-  g.nt = 2;
-  g.n_wg = (int)cdiv(tiles, (int64_t)kWaves * g.nt);
-  const int64_t target = 1024;  // workgroups wanted to fill 256 CUs several times over
+  g.n_wg_per = (int)cdiv(tiles, kWaves);
+  g.n_wg = g.count * g.n_wg_per;
+  // Enough workgroups to give every CU several (256 CUs); split k only when
+  // the rows alone do not provide them.
+  const int64_t target = 768;
   int64_t splits = cdiv(target, g.n_wg);
   if (splits > g.quads) splits = g.quads;
   if (splits < 1) splits = 1;
@@ -32,15 +35,16 @@ Geometry geometry(int64_t n, int64_t k) {
   return g;
 }
 
-ScratchLayout scratch_layout(int64_t n, int64_t k) {
-  const Geometry g = geometry(n, k);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count) {
+  const Geometry g = geometry(n, k, count);
   ScratchLayout s;
   s.cnt_off = 256;
   s.keys_off = align256(s.cnt_off + sizeof(unsigned) * (size_t)g.n_wg);
   s.ctrl_bytes = s.keys_off;  // words that must be zero between calls
   s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxRows * (size_t)g.n_wg);
   s.total = s.part_off;
-  if (g.splits > 1) s.total += align256(sizeof(float) * (size_t)g.splits * kMaxRows * (size_t)n);
+  if (g.splits > 1)
+    s.total += align256(sizeof(float) * (size_t)g.splits * (size_t)count * kMaxRows * (size_t)n);
   return s;
 }
 
@@ -70,7 +74,12 @@ size_t kq_staged_bytes(int64_t k) {
 
 size_t kq_scratch_bytes(int64_t n, int64_t k) {
   if (!shape_ok(n, k)) return 0;
-  return scratch_layout(n, k).total;
+  return scratch_layout(n, k, 1).total;
+}
+
+size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count) {
+  if (!shape_ok(n, k) || count < 1 || count > kMaxGroup) return 0;
+  return scratch_layout(n, k, count).total;
 }
 
 size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
@@ -80,8 +89,8 @@ size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
 
 kq_status kq_launch_geometry(int64_t n, int64_t k, int *nt, int *n_wg, int *splits) {
   if (!shape_ok(n, k)) return KQ_ERR_SHAPE;
-  const Geometry g = geometry(n, k);
-  if (nt) *nt = g.nt;
+  const Geometry g = geometry(n, k, 1);
+  if (nt) *nt = 1;
   if (n_wg) *n_wg = g.n_wg;
   if (splits) *splits = g.splits;
   return KQ_OK;
@@ -107,18 +116,26 @@ kq_status kq_stage_rows(const float *x, int m, int64_t k, void *staged, size_t s
   return KQ_OK;
 }
 
-// Shared validation + launch of the main kernel on staged activations.
-static kq_status run(const void *w, int64_t n, int64_t k, const void *staged, int m, float *logits,
-                     bool verify, const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
-                     void *scratch, size_t scratch_bytes, const float *x_to_stage, void *stream) {
+// Shared validation + launch of the main kernel on staged activations for
+// `count` matrices of the same shape (verify: count == 1).
+static kq_status run(const void *const *w, int count, int64_t n, int64_t k, const void *staged,
+                     int m, float *const *logits, bool verify, const int32_t *draft_host,
+                     int32_t *argmax, int32_t *accept_out, void *scratch, size_t scratch_bytes,
+                     const float *x_to_stage, void *stream) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
-  if (!verify && !logits) return KQ_ERR_NULL;
+  if (count < 1 || count > kMaxGroup || (verify && count != 1)) return KQ_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    if (!w[i]) return KQ_ERR_NULL;
+    if (!verify && (!logits || !logits[i])) return KQ_ERR_NULL;
+  }
   if (verify && (!argmax || !accept_out)) return KQ_ERR_NULL;
   if (verify && m > 1 && !draft_host) return KQ_ERR_NULL;
   if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
-  if (!al(w, 16) || !al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i)
+    if (!al(w[i], 16)) return KQ_ERR_ALIGN;
+  if (!al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
   if (x_to_stage && !al(x_to_stage, 16)) return KQ_ERR_ALIGN;
-  const ScratchLayout sl = scratch_layout(n, k);
+  const ScratchLayout sl = scratch_layout(n, k, count);
   if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
@@ -128,13 +145,15 @@ static kq_status run(const void *w, int64_t n, int64_t k, const void *staged, in
       a.draft[i] = draft_host[i];
     }
   }
-  a.w = (const uint8_t *)w;
+  for (int i = 0; i < count; ++i) {
+    a.w[i] = (const uint8_t *)w[i];
+    a.logits[i] = logits ? logits[i] : nullptr;
+  }
   a.n = n;
   a.k = k;
   a.row_bytes = (k / kQK) * kBlockBytes;
   a.m = m;
   a.staged = (const uint8_t *)staged;
-  a.logits = logits;
   uint8_t *sc = (uint8_t *)scratch;
   a.done = (unsigned *)sc;
   a.tile_cnt = (unsigned *)(sc + sl.cnt_off);
@@ -144,7 +163,7 @@ static kq_status run(const void *w, int64_t n, int64_t k, const void *staged, in
   a.accept_out = accept_out;
   a.k_draft = verify ? m - 1 : 0;
   a.verify = verify ? 1 : 0;
-  a.g = geometry(n, k);
+  a.g = geometry(n, k, count);
   if (x_to_stage) {
     if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch,
                      (int64_t)(sl.ctrl_bytes / 4), stream))
@@ -156,7 +175,15 @@ static kq_status run(const void *w, int64_t n, int64_t k, const void *staged, in
 
 kq_status kq_gemv_staged(const void *w_q4k, int64_t n, int64_t k, const void *staged, int m,
                          float *logits, void *scratch, size_t scratch_bytes, void *stream) {
-  return run(w_q4k, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch,
+  return run(&w_q4k, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, scratch,
+             scratch_bytes, nullptr, stream);
+}
+
+kq_status kq_gemv_staged_group(const void *const *w_q4k, int count, int64_t n, int64_t k,
+                               const void *staged, int m, float *const *logits, void *scratch,
+                               size_t scratch_bytes, void *stream) {
+  if (!w_q4k || !logits) return KQ_ERR_NULL;
+  return run(w_q4k, count, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch,
              scratch_bytes, nullptr, stream);
 }
 
@@ -164,8 +191,8 @@ kq_status kq_verify_staged(const void *w_q4k, int64_t n, int64_t k, const void *
                            const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
                            float *logits_or_null, void *scratch, size_t scratch_bytes,
                            void *stream) {
-  return run(w_q4k, n, k, staged, m, logits_or_null, true, draft_host, argmax, accept_out, scratch,
-             scratch_bytes, nullptr, stream);
+  return run(&w_q4k, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out,
+             scratch, scratch_bytes, nullptr, stream);
 }
 
 static kq_status split_workspace(int64_t n, int64_t k, int m, void *ws, size_t ws_bytes,
@@ -189,7 +216,7 @@ kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k, const float *x, 
   size_t sb;
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
-  return run(w_q4k, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch, sb, x,
+  return run(&w_q4k, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, scratch, sb, x,
              stream);
 }
 
@@ -203,8 +230,8 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const
   size_t sb;
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
-  return run(w_q4k, n, k, staged, m, logits_or_null, true, draft_host, argmax, accept_out, scratch,
-             sb, x, stream);
+  return run(&w_q4k, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out,
+             scratch, sb, x, stream);
 }
 
 }  // extern "C"

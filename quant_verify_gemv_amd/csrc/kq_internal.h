@@ -9,8 +9,9 @@ namespace kq {
 constexpr int64_t kQK = 256;          // weights per Q4_K super-block
 constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // verify rows per call (block size of the draft)
-constexpr int kWaves = 4;             // waves per workgroup
+constexpr int kWaves = 4;             // waves per workgroup, one 16-row tile each
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxGroup = 8;          // matrices per grouped launch
 
 // Activations are staged in "quads" of 4 super-blocks (1,024 columns) that
 // share one power-of-two scale per row. Per quad:
@@ -23,18 +24,19 @@ constexpr int64_t kXsOffset = 65536;
 constexpr int64_t kXiOffset = 65536 + 2048;
 constexpr int64_t kQuadBytes = 67840;  // 67,648 rounded up to 256
 
-// Control words at the start of a scratch area (all zero between calls).
-//   [0, 256)      done counter (u32) at 0
-//   [256, ...)    per-workgroup-column split-K arrival counters (u32)
-//   then          per-workgroup-column argmax keys [n_wg][16] (u64)
-//   then          split-K partial sums [splits][16][n] fp32 (not control)
+// Scratch area of the main kernel:
+//   [0, 256)      done counter (u32) at 0                    -- zero between calls
+//   cnt_off       per-workgroup-column split-K arrivals (u32) -- zero between calls
+//   keys_off      per-workgroup-column argmax keys [n_wg][16] (u64)
+//   part_off      split-K partial sums [splits][count][16][n] fp32
 
 struct Geometry {
-  int nt;       // 16-row tiles per wave
-  int n_wg;     // workgroups along n
-  int splits;   // workgroups along k
-  int qps;      // quads per split
-  int quads;    // total quads
+  int count;     // matrices in the launch (same n, k, activations)
+  int n_wg_per;  // workgroup columns per matrix (4 tiles of 16 rows each)
+  int n_wg;      // workgroup columns in total = count * n_wg_per
+  int splits;    // workgroups along k
+  int qps;       // quads per split
+  int quads;     // total quads
 };
 
 struct ScratchLayout {
@@ -42,15 +44,15 @@ struct ScratchLayout {
 };
 
 struct GemvLaunch {
-  const uint8_t *w;
+  const uint8_t *w[kMaxGroup];
+  float *logits[kMaxGroup];  // entries may be null in verify mode
   int64_t n, k, row_bytes;
   int m;
   const uint8_t *staged;
-  float *logits;        // may be null in verify mode
-  float *partials;      // [splits][16][n]
+  float *partials;
   unsigned *done;
-  unsigned *tile_cnt;   // [n_wg]
-  unsigned long long *wg_keys;  // [n_wg][16]
+  unsigned *tile_cnt;
+  unsigned long long *wg_keys;
   int32_t *argmax_out;  // verify only
   int32_t *accept_out;  // verify only
   int32_t draft[kMaxRows];
@@ -59,8 +61,8 @@ struct GemvLaunch {
   Geometry g;
 };
 
-Geometry geometry(int64_t n, int64_t k);
-ScratchLayout scratch_layout(int64_t n, int64_t k);
+Geometry geometry(int64_t n, int64_t k, int count);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
 
 // Kernel launches (return a hipError_t as int).
 int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *zero_words,

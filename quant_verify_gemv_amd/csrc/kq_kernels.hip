@@ -1,21 +1,21 @@
 // kq_kernels.hip -- HIP kernels for the Q4_K batched verify step on gfx950.
 //
-// Three kernels:
 //  * kq_stage_kernel: fp32 activation rows -> the MFMA operand format: per
 //    row and 1,024-column quad a power-of-two scale, then each scaled value
 //    split into an fp16 pair hi + lo (|x - hi - lo| <= 2^-22 |x| in range),
 //    laid out in the lane order the weight unpack produces, plus the scaled
 //    32-column sub-block sums the min term needs.
-//  * kq_gemv_kernel<NT>: streams each 144-byte super-block once for all rows,
-//    unpacks 4-bit quants times their 6-bit sub-block scale into exact fp16
-//    (q * sc <= 945), and contracts them with the staged rows on
-//    v_mfma_f32_16x16x32_f16 (16 rows x 16 outputs x 32 columns). The block
-//    scale d and the 1/2^e row scale are applied in fp32; the min term
-//    -dmin * m_j * sum(x over sub-block j) runs as three more MFMAs per quad.
-//    Split-K partials are combined in fixed split order by the last
-//    workgroup to arrive; in verify mode each workgroup column also takes the
-//    row argmax (ties -> lowest index) and the last column to finish applies
-//    the greedy accept rule.
+//  * kq_gemv_kernel: each wave owns 16 output rows; it streams their 144-byte
+//    super-blocks once for all activation rows, unpacks the 4-bit quants
+//    times their 6-bit sub-block scale into exact fp16 (q * sc <= 945) and
+//    contracts them with the staged rows on v_mfma_f32_16x16x32_f16 (16
+//    activation rows x 16 outputs x 32 columns). The block scale d and the
+//    row scale 2^-e are applied in fp32; the min term -dmin * m_j * (sum of
+//    x over sub-block j) runs as three more MFMAs per quad. A launch may
+//    cover several matrices that share the activations. Split-K partials are
+//    combined in fixed split order by the last workgroup to arrive; in verify
+//    mode every workgroup column also takes the row argmax (ties -> lowest
+//    index) and the last column to finish applies the greedy accept rule.
 //  * kq_fill_kernel: zeroes control words.
 //
 // The format (muser-book ch. 8 "The DFlash draft", section 8.2) and the
@@ -43,7 +43,15 @@ __device__ __forceinline__ half8 make_h8(unsigned a, unsigned b, unsigned c, uns
   return __builtin_bit_cast(half8, v);
 }
 
-__device__ __forceinline__ u32x4 ld16_stream(const uint8_t *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4 *)p; }
+
+// A value the compiler must keep in a VGPR: lets (x & mask) | magic become
+// one v_and_or_b32 (a VOP3 instruction may read one scalar operand only).
+__device__ __forceinline__ unsigned in_vgpr(unsigned c) {
+  unsigned v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(c));
+  return v;
+}
 
 // Cross-workgroup hand-off without device-scope fences. Values another
 // workgroup will read are written with agent-scope relaxed atomic stores
@@ -71,7 +79,6 @@ __device__ __forceinline__ void stores_done_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
 }
-__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4 *)p; }
 
 // Ordered 64-bit argmax key: larger value wins, equal values -> lower index.
 __device__ __forceinline__ unsigned long long argmax_key(float v, unsigned n) {
@@ -82,9 +89,26 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, unsigned n) {
 }
 
 // ---------------------------------------------------------------------------
-// Staging. One workgroup per quad, thread t handles row m = t/16 and the 64
-// columns c = t%16 of the quad (block bq = c/4 within the quad, 64-weight
-// group grp = c%4 of that block).
+// Lane order of the weights. Lane l of a wave: ln = l%16 is the output row
+// within the 16-row tile (B operand / C column) and also the activation row
+// m of the A operand; kg = l/16 selects the bytes the lane unpacks from each
+// super-block: q0 = quant bytes [16kg, 16kg+16) and q1 = quant bytes
+// [64+16kg, 80+16kg) (so the four lanes of a row read 64 contiguous bytes per
+// load). In k-step s (0..7) the lane contributes the 8 nibbles of dwords
+// 2(s&1), 2(s&1)+1 of q0 (s < 4) or q1 (s >= 4), low nibbles if (s&2) == 0,
+// in the byte order {0,2,1,3,4,6,5,7} that the unpack produces. The staging
+// kernel writes the activations in exactly this order.
+__device__ __forceinline__ constexpr int lane_weight_index(int kg, int s, int i) {
+  // byte order {0,2,1,3,4,6,5,7} within the 8 bytes of a k-step
+  const int byte = (s < 4 ? 16 * kg : 64 + 16 * kg) + 8 * (s & 1) + (i & 4) + ((i & 1) << 1) + ((i >> 1) & 1);
+  const int g = byte >> 5, l = byte & 31;
+  return 64 * g + ((s & 2) ? 32 : 0) + l;
+}
+
+// ---------------------------------------------------------------------------
+// Staging. One workgroup per quad; thread t handles row m = t/16 and the 64
+// columns c = t%16 of the quad: block bq = c/4 of the quad, weight group
+// grp = c%4 of that block (weights 64 grp .. 64 grp + 63).
 __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__ x, int m_rows,
                                                        int64_t k, uint8_t *__restrict__ staged,
                                                        unsigned *__restrict__ zero_words,
@@ -122,7 +146,8 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
   for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
 
   // scale 2^e puts the quad's largest magnitude in [2^9, 2^10): scaled values
-  // and their 32-term sums stay inside fp16 range.
+  // and their 32-term sums stay inside fp16 range. Rows >= m_rows are staged
+  // as zeros with scale 1, so the main kernel runs every row unpredicated.
   int e = 0;
   if (amax > 0.0f) {
     int E;
@@ -130,13 +155,10 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
     e = 10 - E;
     e = e > 100 ? 100 : e;
   }
-  // rows >= m_rows are staged as zeros with scale 1: the main kernel then
-  // runs every row unpredicated and simply does not store rows >= m.
   uint8_t *qbase = staged + q * kQuadBytes;
   if (c == 0) *(float *)(qbase + kXiOffset + 4 * m) = ldexpf(1.0f, -e);
 
-  const int lane_l = m + 16 * grp;   // lane index of this row/group in XA
-  const int lane_s = m + 16 * bq;    // lane index of this row/block in XS
+  const int lane_s = m + 16 * bq;  // lane index of this row/block in XS
   if (!valid) {
     *(unsigned *)(qbase + kXsOffset + 0 * 1024 + lane_s * 16 + grp * 4) = 0u;
     *(unsigned *)(qbase + kXsOffset + 1 * 1024 + lane_s * 16 + grp * 4) = 0u;
@@ -159,27 +181,33 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
     *(unsigned *)(qbase + kXsOffset + 1 * 1024 + lane_s * 16 + grp * 4) = as_u(ll);
   }
 
-  // XA: k-step s takes 8 columns of the group in the order the weight unpack
-  // produces them: bytes {0,2,1,3} of two consecutive quant dwords.
-  const int perm[4] = {0, 2, 1, 3};
+  // XA: group grp is read by lanes kg = 2(grp%2), 2(grp%2)+1, in k-steps
+  // 0..3 (q0, grp < 2) or 4..7 (q1, grp >= 2).
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int sp = s & 3, half = s >> 2;
-    unsigned hw[4], lw[4];
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kg = 2 * (grp & 1) + kk;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int i0 = 2 * p, i1 = 2 * p + 1;
-      const float x0 = v[32 * half + 8 * sp + 4 * (i0 >> 2) + perm[i0 & 3]];
-      const float x1 = v[32 * half + 8 * sp + 4 * (i1 >> 2) + perm[i1 & 3]];
-      _Float16 a0 = (_Float16)x0, a1 = (_Float16)x1;
-      _Float16 b0 = (_Float16)(x0 - (float)a0), b1 = (_Float16)(x1 - (float)a1);
-      half2v ha = {a0, a1}, hb = {b0, b1};
-      hw[p] = as_u(ha);
-      lw[p] = as_u(hb);
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int s = (grp < 2 ? 0 : 4) + s4;
+      unsigned hw[4], lw[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // lane_weight_index(kg, s, i) - 64 grp: the same offset for every
+        // group, which keeps the index into v[] a compile-time constant
+        const int i0 = 2 * p, i1 = 2 * p + 1;
+        const int base = ((s4 & 2) ? 32 : 0) + 16 * kk + 8 * (s4 & 1);
+        const float x0 = v[base + (i0 & 4) + ((i0 & 1) << 1) + ((i0 >> 1) & 1)];
+        const float x1 = v[base + (i1 & 4) + ((i1 & 1) << 1) + ((i1 >> 1) & 1)];
+        _Float16 a0 = (_Float16)x0, a1 = (_Float16)x1;
+        _Float16 b0 = (_Float16)(x0 - (float)a0), b1 = (_Float16)(x1 - (float)a1);
+        half2v ha = {a0, a1}, hb = {b0, b1};
+        hw[p] = as_u(ha);
+        lw[p] = as_u(hb);
+      }
+      uint8_t *dst = qbase + (int64_t)bq * kXaBlockBytes + (int64_t)(s * 2) * 1024 + (m + 16 * kg) * 16;
+      *(u32x4 *)dst = u32x4{hw[0], hw[1], hw[2], hw[3]};
+      *(u32x4 *)(dst + 1024) = u32x4{lw[0], lw[1], lw[2], lw[3]};
     }
-    uint8_t *dst = qbase + (int64_t)bq * kXaBlockBytes + (int64_t)(s * 2) * 1024 + lane_l * 16;
-    *(u32x4 *)dst = u32x4{hw[0], hw[1], hw[2], hw[3]};
-    *(u32x4 *)(dst + 1024) = u32x4{lw[0], lw[1], lw[2], lw[3]};
   }
 }
 
@@ -192,18 +220,15 @@ __global__ void kq_fill_kernel(unsigned *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel. Workgroup (blockIdx.x, blockIdx.y) covers rows
-// [64*NT*blockIdx.x, +64*NT) -- wave w owns tiles 4*NT*blockIdx.x... -- and
-// quads [qps*blockIdx.y, +qps). Lane l of a wave: ln = l%16 is both the
-// output row within a tile (B operand / C column) and the activation row m
-// of the A operand; kg = l/16 selects the 64-weight group of each block the
-// lane unpacks (sub-blocks 2kg, 2kg+1) and the C rows 4kg..4kg+3.
+// Main kernel. Workgroup (blockIdx.x, blockIdx.y): matrix mat =
+// blockIdx.x / n_wg_per, rows [64 (blockIdx.x % n_wg_per), +64) of it (wave w
+// owns the 16-row tile 4 (blockIdx.x % n_wg_per) + w), quads
+// [qps blockIdx.y, +qps) of k.
 
 struct WTile {
   u32x4 hdr, q0, q1;
 };
 
-template <int NT>
 __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXaBlockBytes];
   __shared__ unsigned long long s_keys[kMaxRows];
@@ -218,56 +243,52 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
 
   const int64_t N = a.n;
   const int64_t KB = a.k / kQK;
-  const int tile0 = (blockIdx.x * kWaves + wave) * NT;
-  int64_t rows[NT];
-  const uint8_t *rowp[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    rows[t] = (int64_t)(tile0 + t) * 16 + ln;
-    const int64_t r = rows[t] < N ? rows[t] : N - 1;
-    rowp[t] = a.w + r * a.row_bytes;
-  }
+  const int wg = blockIdx.x;
+  const int mat = wg / a.g.n_wg_per;
+  const int wgl = wg - mat * a.g.n_wg_per;
+  const int64_t row = (int64_t)(wgl * kWaves + wave) * 16 + ln;
+  const uint8_t *rowp = a.w[mat] + (row < N ? row : N - 1) * a.row_bytes;
 
   const int q_begin = blockIdx.y * a.g.qps;
   const int q_end = min(a.g.quads, q_begin + a.g.qps);
   const int64_t b_begin = (int64_t)q_begin * 4;
   const int64_t b_last = min(KB, (int64_t)q_end * 4) - 1;  // last block of this split
 
-  f32x4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const unsigned mask_lo = in_vgpr(0x000F000Fu);
+  const unsigned mask_hi = in_vgpr(0x00F000F0u);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  // Software pipeline. The weights of a wave's NT tiles rotate through four
-  // register sets (the quad loop is unrolled four times, one step per block)
-  // so that the loads of block b+3 are in flight while block b computes; the
-  // activations of block b+1 are loaded during block b and written to the
-  // other LDS buffer at its end. Every load is unconditional (indices are
-  // clamped to the split's last block) so that outstanding loads are counted
-  // statically and waits cover only the data about to be used.
+  // Software pipeline. The weights rotate through four register sets (the
+  // quad loop is unrolled four times, one step per block) so that the loads
+  // of block b+3 are in flight while block b computes; the activations of
+  // block b+2 are loaded during block b and written to LDS at the end of
+  // block b+1. Every load is unconditional (indices are clamped to the
+  // split's last block) so that outstanding loads are counted statically and
+  // each wait covers only the data about to be used.
   auto clampb = [&](int64_t b) -> int64_t { return b < b_last ? b : b_last; };
-  auto load_w = [&](WTile (&w)[NT], int64_t b) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint8_t *p = rowp[t] + b * kBlockBytes;
-      w[t].hdr = ld16_stream(p);
-      w[t].q0 = ld16_stream(p + 16 + 32 * kg);
-      w[t].q1 = ld16_stream(p + 32 + 32 * kg);
-    }
+  auto load_w = [&](WTile &w, int64_t b) {
+    const uint8_t *p = rowp + b * kBlockBytes;
+    w.hdr = ld16(p);
+    w.q0 = ld16(p + 16 + 16 * kg);
+    w.q1 = ld16(p + 80 + 16 * kg);
   };
   auto x_src = [&](int64_t b) -> const uint8_t * {
     return a.staged + (b >> 2) * kQuadBytes + (b & 3) * kXaBlockBytes;
   };
-  WTile w0[NT], w1[NT], w2[NT], w3[NT];
+  WTile w0, w1, w2, w3;
   load_w(w0, b_begin);
   load_w(w1, clampb(b_begin + 1));
   load_w(w2, clampb(b_begin + 2));
+  u32x4 xr0[4], xr1[4];
   {
     const uint8_t *src = x_src(b_begin);
-    u32x4 xr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr[j] = ld16(src + (tid + 256 * j) * 16);
+    for (int j = 0; j < 4; ++j) xr0[j] = ld16(src + (tid + 256 * j) * 16);
+    const uint8_t *src1 = x_src(clampb(b_begin + 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[0][(tid + 256 * j) * 16]) = xr[j];
+    for (int j = 0; j < 4; ++j) xr1[j] = ld16(src1 + (tid + 256 * j) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[0][(tid + 256 * j) * 16]) = xr0[j];
   }
   __syncthreads();
 
@@ -278,97 +299,86 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     const f32x4 xinv = *(const f32x4 *)(qb + kXiOffset + 16 * kg);
     const int64_t qb0 = (int64_t)q * 4;
     const int nblk = (int)(min((int64_t)4, b_last + 1 - qb0));
-    f32x4 G[NT];
-    u32x4 hmin[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      G[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      hmin[t] = u32x4{0u, 0u, 0u, 0u};
-    }
+    f32x4 G = {0.f, 0.f, 0.f, 0.f};
+    u32x4 hmin = {0u, 0u, 0u, 0u};
 
-    // one block: prefetch block b+3 into `pf` and activations of b+1, then
-    // contract the weights in `cur` with the activations in LDS buffer bq&1.
-    auto step = [&](WTile (&cur)[NT], WTile (&pf)[NT], const int bq) {
+    // One block: prefetch the activations of block b+2 (into xl) and the
+    // weights of block b+3 (into pf), contract the weights in `cur` with the
+    // activations in LDS buffer bq&1, then move the activations of block b+1
+    // (loaded one step earlier, in xw) into the other LDS buffer.
+    auto step = [&](WTile &cur, WTile &pf, u32x4 (&xl)[4], u32x4 (&xw)[4], const int bq) {
       const int64_t b = qb0 + bq;
-      u32x4 xr[4];
       {
-        const uint8_t *src = x_src(clampb(b + 1));
+        const uint8_t *src = x_src(clampb(b + 2));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xr[j] = ld16(src + (tid + 256 * j) * 16);
+        for (int j = 0; j < 4; ++j) xl[j] = ld16(src + (tid + 256 * j) * 16);
       }
       load_w(pf, clampb(b + 3));
       __builtin_amdgcn_sched_barrier(0);
       if (bq < nblk) {
-        unsigned slo[NT], nlo[NT], shi[NT], nhi[NT];
-        float dsc[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const u32x4 h = cur[t].hdr;
-          hmin[t] = bq == kg ? h : hmin[t];
-          dsc[t] = h2f_lo(h.x);
-          const unsigned sc03 = h.y & 0x3F3F3F3Fu;
-          const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-          const unsigned sel = (kg < 2 ? sc03 : sc47) >> ((kg & 1) * 16);
-          const float s0 = (float)(sel & 0xFFu);         // sc[2kg]   (low nibbles)
-          const float s1 = (float)((sel >> 8) & 0xFFu);  // sc[2kg+1] (high nibbles)
-          half2v a0 = {(_Float16)s0, (_Float16)s0};
-          half2v a1 = {(_Float16)(-1024.0f * s0), (_Float16)(-1024.0f * s0)};
-          half2v a2 = {(_Float16)(0.0625f * s1), (_Float16)(0.0625f * s1)};
-          half2v a3 = {(_Float16)(-64.0f * s1), (_Float16)(-64.0f * s1)};
-          slo[t] = as_u(a0); nlo[t] = as_u(a1); shi[t] = as_u(a2); nhi[t] = as_u(a3);
-        }
-        f32x4 chi[NT], clo[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          chi[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          clo[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        const u32x4 h = cur.hdr;
+        hmin = bq == kg ? h : hmin;
+        const float d = h2f_lo(h.x);
+        const unsigned sc03 = h.y & 0x3F3F3F3Fu;
+        const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+        const int sh = (kg >> 1) * 16;
+        // q0: sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
+        // q1: sub-blocks 4+2(kg>>1) and 5+2(kg>>1).
+        const float s00 = (float)((sc03 >> sh) & 0xFFu);
+        const float s01 = (float)((sc03 >> (sh + 8)) & 0xFFu);
+        const float s10 = (float)((sc47 >> sh) & 0xFFu);
+        const float s11 = (float)((sc47 >> (sh + 8)) & 0xFFu);
+        // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
+        const half2v m00 = {(_Float16)s00, (_Float16)s00};
+        const half2v c00 = {(_Float16)(-1024.0f * s00), (_Float16)(-1024.0f * s00)};
+        const half2v m01 = {(_Float16)(0.0625f * s01), (_Float16)(0.0625f * s01)};
+        const half2v c01 = {(_Float16)(-64.0f * s01), (_Float16)(-64.0f * s01)};
+        const half2v m10 = {(_Float16)s10, (_Float16)s10};
+        const half2v c10 = {(_Float16)(-1024.0f * s10), (_Float16)(-1024.0f * s10)};
+        const half2v m11 = {(_Float16)(0.0625f * s11), (_Float16)(0.0625f * s11)};
+        const half2v c11 = {(_Float16)(-64.0f * s11), (_Float16)(-64.0f * s11)};
+        f32x4 chi = {0.f, 0.f, 0.f, 0.f}, clo = {0.f, 0.f, 0.f, 0.f};
         const uint8_t *xb = s_x[bq & 1];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
           const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
-          const int sp = s & 3;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const u32x4 q0 = cur[t].q0, q1 = cur[t].q1;
-            const unsigned da = sp == 0 ? q0.x : sp == 1 ? q0.z : sp == 2 ? q1.x : q1.z;
-            const unsigned db = sp == 0 ? q0.y : sp == 1 ? q0.w : sp == 2 ? q1.y : q1.w;
-            const unsigned mask = s < 4 ? 0x000F000Fu : 0x00F000F0u;
-            const half2v sc = as_h2(s < 4 ? slo[t] : shi[t]);
-            const half2v nb = as_h2(s < 4 ? nlo[t] : nhi[t]);
-            const unsigned u0 = (da & mask) | 0x64006400u;
-            const unsigned u1 = ((da >> 8) & mask) | 0x64006400u;
-            const unsigned u2 = (db & mask) | 0x64006400u;
-            const unsigned u3 = ((db >> 8) & mask) | 0x64006400u;
-            const half2v v0 = __builtin_elementwise_fma(as_h2(u0), sc, nb);
-            const half2v v1 = __builtin_elementwise_fma(as_h2(u1), sc, nb);
-            const half2v v2 = __builtin_elementwise_fma(as_h2(u2), sc, nb);
-            const half2v v3 = __builtin_elementwise_fma(as_h2(u3), sc, nb);
-            const half8 bw = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
-            chi[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw, chi[t], 0, 0, 0);
-            clo[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw, clo[t], 0, 0, 0);
-          }
+          const u32x4 qq = s < 4 ? cur.q0 : cur.q1;
+          const unsigned da = (s & 1) ? qq.z : qq.x;
+          const unsigned db = (s & 1) ? qq.w : qq.y;
+          const bool hi = (s & 2) != 0;
+          const unsigned mask = hi ? mask_hi : mask_lo;
+          const half2v sc = s < 4 ? (hi ? m01 : m00) : (hi ? m11 : m10);
+          const half2v nb = s < 4 ? (hi ? c01 : c00) : (hi ? c11 : c10);
+          const unsigned u0 = (da & mask) | 0x64006400u;
+          const unsigned u1 = ((da >> 8) & mask) | 0x64006400u;
+          const unsigned u2 = (db & mask) | 0x64006400u;
+          const unsigned u3 = ((db >> 8) & mask) | 0x64006400u;
+          const half2v v0 = __builtin_elementwise_fma(as_h2(u0), sc, nb);
+          const half2v v1 = __builtin_elementwise_fma(as_h2(u1), sc, nb);
+          const half2v v2 = __builtin_elementwise_fma(as_h2(u2), sc, nb);
+          const half2v v3 = __builtin_elementwise_fma(as_h2(u3), sc, nb);
+          const half8 bw = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
+          chi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw, chi, 0, 0, 0);
+          clo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw, clo, 0, 0, 0);
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) G[t][r] += dsc[t] * (chi[t][r] + clo[t][r]);
-        }
+        for (int r = 0; r < 4; ++r) G[r] += d * (chi[r] + clo[r]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[(bq & 1) ^ 1][(tid + 256 * j) * 16]) = xr[j];
+      for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[(bq & 1) ^ 1][(tid + 256 * j) * 16]) = xw[j];
       __syncthreads();
     };
-    step(w0, w3, 0);
-    step(w1, w0, 1);
-    step(w2, w1, 2);
-    step(w3, w2, 3);
+    step(w0, w3, xr0, xr1, 0);
+    step(w1, w0, xr1, xr0, 1);
+    step(w2, w1, xr0, xr1, 2);
+    step(w3, w2, xr1, xr0, 3);
 
-    // end of the quad: min term (three MFMAs) and the row scale 2^-e
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const u32x4 h = hmin[t];
+    // end of the quad: min term (three MFMAs) and the row scale 2^-e. Lane
+    // kg supplies dmin * m_j of block kg of the quad in k-slots 8kg..8kg+7;
+    // the A operand holds the matching scaled sub-block sums.
+    {
+      const u32x4 h = hmin;
       const bool ok = kg < nblk;
       const float dmin = h2f_hi(h.x);
       const unsigned m03 = h.z & 0x3F3F3F3Fu;
@@ -395,78 +405,69 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
       c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2l, b2h, c2, 0, 0, 0);
       c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2l, c2, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] += xinv[r] * (G[t][r] - c2[r]);
+      for (int r = 0; r < 4; ++r) acc[r] += xinv[r] * (G[r] - c2[r]);
     }
   }
 
   // ---------------------------------------------------------------- epilogue
+  // the lane holds acc[r] = logit of activation row 4kg+r, output row `row`
   const int splits = a.g.splits;
-  const int wg = blockIdx.x;
-  const int rows_wg = 64 * NT;
-  const int64_t row0 = (int64_t)wg * rows_wg;
+  const int64_t row0 = (int64_t)wgl * 64;
+  float *logits = a.logits[mat];
 
   if (tid < kMaxRows) s_keys[tid] = 0ull;
 
   if (splits == 1) {
+    if (row < N && logits) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (rows[t] < N) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 4 * kg + r;
-          if (m < M && a.logits) a.logits[(int64_t)m * N + rows[t]] = acc[t][r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        if (m < M) logits[(int64_t)m * N + row] = acc[r];
       }
     }
     if (a.verify) {
       __syncthreads();
+      if (row < N) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (m < M) {
-          unsigned long long best = 0ull;
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            if (rows[t] < N) {
-              const unsigned long long key = argmax_key(acc[t][r], (unsigned)rows[t]);
-              best = key > best ? key : best;
-            }
-          if (best) atomicMax(&s_keys[m], best);
+        for (int r = 0; r < 4; ++r) {
+          const int m = 4 * kg + r;
+          if (m < M) atomicMax(&s_keys[m], argmax_key(acc[r], (unsigned)row));
         }
       }
     }
   } else {
     // write this split's partial sums, then the last arriving split sums all
     // splits in split order.
+    float *part = a.partials + ((int64_t)blockIdx.y * a.g.count + mat) * kMaxRows * N;
+    if (row < N) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (rows[t] < N) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 4 * kg + r;
-          if (m < M) st_dev(&a.partials[((int64_t)blockIdx.y * kMaxRows + m) * N + rows[t]], acc[t][r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        if (m < M) st_dev(&part[(int64_t)m * N + row], acc[r]);
       }
     }
     stores_done_barrier();
     if (tid == 0) {
-      const unsigned old = __hip_atomic_fetch_add(&a.tile_cnt[wg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned old =
+          __hip_atomic_fetch_add(&a.tile_cnt[wg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = old == (unsigned)(splits - 1);
       if (last) __hip_atomic_store(&a.tile_cnt[wg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag = last;
     }
     __syncthreads();
     if (!s_flag) return;
-    const int64_t nrows = min((int64_t)rows_wg, N - row0);
+    const int64_t nrows = min((int64_t)64, N - row0);
+    const int64_t split_stride = (int64_t)a.g.count * kMaxRows * N;
+    const float *p0 = a.partials + (int64_t)mat * kMaxRows * N;
     for (int64_t e = tid; e < (int64_t)M * nrows; e += kThreads) {
       const int m = (int)(e / nrows);
       const int64_t n = row0 + e % nrows;
       float v = 0.0f;
       for (int sp = 0; sp < splits; ++sp) {
-        const float pv = ld_dev(&a.partials[((int64_t)sp * kMaxRows + m) * N + n]);
+        const float pv = ld_dev(&p0[sp * split_stride + (int64_t)m * N + n]);
         v = sp == 0 ? pv : v + pv;
       }
-      if (a.logits) a.logits[(int64_t)m * N + n] = v;
+      if (logits) logits[(int64_t)m * N + n] = v;
       if (a.verify) atomicMax(&s_keys[m], argmax_key(v, (unsigned)n));
     }
   }
@@ -530,16 +531,7 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream) {
 
 int launch_gemv(const GemvLaunch &a, void *stream) {
   dim3 grid((unsigned)a.g.n_wg, (unsigned)a.g.splits);
-  switch (a.g.nt) {
-    case 1:
-      hipLaunchKernelGGL(kq_gemv_kernel<1>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
-      break;
-    case 2:
-      hipLaunchKernelGGL(kq_gemv_kernel<2>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
-      break;
-    default:
-      return (int)hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(kq_gemv_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

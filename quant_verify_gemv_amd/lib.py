@@ -19,7 +19,8 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIG
 
 EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scratch_bytes",
             "kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
-            "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry")
+            "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
+            "kq_gemv_staged_group")
 
 _lib = None
 
@@ -54,8 +55,11 @@ def load() -> ctypes.CDLL:
     lib.kq_gemv_staged.argtypes = [P, I64, I64, P, I32, P, P, SZ, P]
     lib.kq_verify_staged.argtypes = [P, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P]
+    lib.kq_group_scratch_bytes.argtypes = [I64, I64, I32]
+    lib.kq_group_scratch_bytes.restype = SZ
+    lib.kq_gemv_staged_group.argtypes = [P, I32, I64, I64, P, I32, P, P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
-                 "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry"):
+                 "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -80,6 +84,10 @@ def staged_bytes(k: int) -> int:
 
 def scratch_bytes(n: int, k: int) -> int:
     return int(load().kq_scratch_bytes(n, k))
+
+
+def group_scratch_bytes(n: int, k: int, count: int) -> int:
+    return int(load().kq_group_scratch_bytes(n, k, count))
 
 
 def launch_geometry(n: int, k: int) -> Tuple[int, int, int]:
@@ -205,6 +213,25 @@ def gemv_staged(w, n: int, k: int, staged, m: int, scratch, logits=None, stream=
     _check(load().kq_gemv_staged(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(staged, "staged"), m,
                                  _dev_ptr(logits, "logits", torch.float32), _dev_ptr(scratch, "scratch"),
                                  scratch.numel(), _stream_handle(stream)), "kq_gemv_staged")
+    return logits
+
+
+def new_group_scratch(n: int, k: int, count: int, device):
+    """Zeroed scratch for kq_gemv_staged_group."""
+    return alloc_workspace(group_scratch_bytes(n, k, count), device)
+
+
+def gemv_staged_group(ws, n: int, k: int, staged, m: int, scratch, logits=None, stream=None):
+    """One launch for several same-shape matrices sharing staged rows."""
+    torch = _torch()
+    count = len(ws)
+    if logits is None:
+        logits = [torch.empty((m, n), dtype=torch.float32, device=ws[0].device) for _ in range(count)]
+    wp = (ctypes.c_void_p * count)(*[_dev_ptr(w, "w", torch.uint8) for w in ws])
+    lp = (ctypes.c_void_p * count)(*[_dev_ptr(l, "logits", torch.float32) for l in logits])
+    _check(load().kq_gemv_staged_group(wp, count, n, k, _dev_ptr(staged, "staged"), m, lp,
+                                       _dev_ptr(scratch, "scratch"), scratch.numel(),
+                                       _stream_handle(stream)), "kq_gemv_staged_group")
     return logits
 
 

@@ -31,6 +31,16 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(kq.EXPORTED)
 
 
+def test_every_export_has_a_prototype():
+    lib = kq.load()
+    for n in kq.EXPORTED:
+        fn = getattr(lib, n)
+        if n != "kq_status_string":
+            assert fn.argtypes is not None, f"{n} has no argtypes"
+    assert lib.kq_group_scratch_bytes.restype is ctypes.c_size_t
+    assert lib.kq_workspace_bytes.restype is ctypes.c_size_t
+
+
 def test_status_strings():
     for code, name in kq.STATUS_NAMES.items():
         assert kq.status_string(code).startswith(name)
@@ -110,3 +120,23 @@ def test_staged_argument_errors():
     assert lib.kq_workspace_init(None, 256, None) == NULL
     assert lib.kq_workspace_init(FAKE + 4, 256, None) == ALIGN
     assert lib.kq_workspace_init(FAKE, 8, None) == WS
+
+
+def test_grouped_argument_errors():
+    lib = kq.load()
+    n, k, m = 2000, 6656, 16
+    sb = kq.group_scratch_bytes(n, k, 3)
+    assert sb > kq.scratch_bytes(n, k) > 0
+    assert kq.group_scratch_bytes(n, k, 0) == 0 and kq.group_scratch_bytes(n, k, 9) == 0
+    wp = (ctypes.c_void_p * 3)(FAKE, FAKE + 0x100000, FAKE + 0x200000)
+    lp = (ctypes.c_void_p * 3)(FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000)
+    call = lib.kq_gemv_staged_group
+    assert call(wp, 0, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
+    assert call(wp, 9, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
+    assert call(wp, 3, n, 100, FAKE, m, lp, FAKE, sb, None) == SHAPE
+    assert call(wp, 3, n, k, FAKE, m, lp, FAKE, sb - 1, None) == WS
+    assert call(None, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
+    bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert call(bad, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
+    mis = (ctypes.c_void_p * 3)(FAKE, FAKE + 8, FAKE)
+    assert call(mis, 3, n, k, FAKE, m, lp, FAKE, sb, None) == ALIGN

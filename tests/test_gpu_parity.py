@@ -226,3 +226,24 @@ def test_activation_range_scaling(kq):
     L, A = oracle.gemv_rows(w, k, x)
     G = gpu_logits(kq, to_dev(w), n, k, x)
     check_logits(G, L, A, what="activation range")
+
+
+def test_grouped_launch(kq):
+    n, k, count = 2000, 6656, 3
+    log(f"grouped launch: {count} x n={n} k={k}")
+    ws = [synthetic.q4k_matrix(n, k, 80 + i) for i in range(count)]
+    x = synthetic.activations(16, k, 85)
+    rows = np.array([0, 1, 15, 16, 777, n - 17, n - 1])
+    ws_d = [to_dev(w) for w in ws]
+    st = kq.stage_rows(to_dev(x))
+    gs = kq.new_group_scratch(n, k, count, DEV)
+    for mm in (16, 5):
+        st_m = st if mm == 16 else kq.stage_rows(to_dev(x[:mm]))
+        outs = kq.gemv_staged_group(ws_d, n, k, st_m, mm, gs)
+        again = kq.gemv_staged_group(ws_d, n, k, st_m, mm, gs)
+        torch.cuda.synchronize()
+        for i in range(count):
+            G = outs[i].cpu().numpy()
+            assert np.array_equal(G, again[i].cpu().numpy())
+            L, A = oracle.gemv_rows(ws[i], k, x[:mm], rows=rows)
+            check_logits(G[:, rows], L, A, what=f"group member {i} m={mm}")
