@@ -153,9 +153,12 @@ kq_status kq_gemv_staged_group(const void *const *w_q4k, int count, int64_t n, i
                                void *scratch, size_t scratch_bytes, void *stream);
 
 /* Launch geometry the library uses for one n x k matrix (a function of n and
- * k only, never of m): 16-row tiles per wave (*nt), workgroups along n
- * (*n_wg) and along k (*splits). Returns KQ_ERR_SHAPE for invalid shapes. */
-kq_status kq_launch_geometry(int64_t n, int64_t k, int *nt, int *n_wg, int *splits);
+ * k only, never of m): waves per workgroup (*waves), 16-row tiles per wave
+ * (*tiles_per_wave; a workgroup covers 16 * waves * tiles_per_wave rows),
+ * workgroups along n (*n_wg) and along k (*splits). Any output pointer may be
+ * NULL. Returns KQ_ERR_SHAPE for invalid shapes. */
+kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave, int *n_wg,
+                             int *splits);
 
 #ifdef __cplusplus
 }

@@ -17,16 +17,39 @@ static bool shape_ok(int64_t n, int64_t k) {
          (k / kQK) * kBlockBytes <= (((int64_t)1 << 62) / n);
 }
 
+// Launch geometry. Workgroup shapes (waves per workgroup x 16-row tiles per
+// wave) and how many of them one CU holds at once (set by their register
+// use): 4x1 -> 3, 8x1 -> 1, 8x2 -> 1. Tall workgroups share each staged
+// activation block among more rows; short ones give small matrices more
+// workgroups. Measured on MI355X: the 131,072-row LM head is fastest with
+// 8x2, a launch of two or three 6,656-wide matrices (q/k/v, gate/up) with
+// 4x1, and a single 6,656-row matrix with 8x1.
+static constexpr int64_t kCUs = 256;
+
+struct Shape {
+  int waves, tpw, per_cu;
+};
+
+static Shape pick_shape(int64_t n, int count) {
+  const int64_t rows = n * count;
+  if (rows >= 131072) return {8, 2, 1};
+  if (count == 1 && n <= 8192) return {8, 1, 1};
+  return {4, 1, 3};
+}
+
 Geometry geometry(int64_t n, int64_t k, int count) {
   Geometry g;
+  const Shape sh = pick_shape(n, count);
   const int64_t tiles = cdiv(n, 16);
   g.count = count;
+  g.waves = sh.waves;
+  g.tpw = sh.tpw;
   g.quads = (int)cdiv(k, kQuadK);
-  g.n_wg_per = (int)cdiv(tiles, kWaves);
+  g.n_wg_per = (int)cdiv(tiles, (int64_t)g.waves * g.tpw);
   g.n_wg = g.count * g.n_wg_per;
-  // Enough workgroups to give every CU several (256 CUs); split k only when
-  // the rows alone do not provide them.
-  const int64_t target = 768;
+  // Enough workgroups to fill every CU; split k only when the rows alone do
+  // not provide them (splits are whole 1,024-column quads).
+  const int64_t target = kCUs * sh.per_cu;
   int64_t splits = cdiv(target, g.n_wg);
   if (splits > g.quads) splits = g.quads;
   if (splits < 1) splits = 1;
@@ -87,10 +110,12 @@ size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
   return align256(kq_staged_bytes(k)) + kq_scratch_bytes(n, k);
 }
 
-kq_status kq_launch_geometry(int64_t n, int64_t k, int *nt, int *n_wg, int *splits) {
+kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave, int *n_wg,
+                             int *splits) {
   if (!shape_ok(n, k)) return KQ_ERR_SHAPE;
   const Geometry g = geometry(n, k, 1);
-  if (nt) *nt = 1;
+  if (waves) *waves = g.waves;
+  if (tiles_per_wave) *tiles_per_wave = g.tpw;
   if (n_wg) *n_wg = g.n_wg;
   if (splits) *splits = g.splits;
   return KQ_OK;

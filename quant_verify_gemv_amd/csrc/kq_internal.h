@@ -9,8 +9,6 @@ namespace kq {
 constexpr int64_t kQK = 256;          // weights per Q4_K super-block
 constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // verify rows per call (block size of the draft)
-constexpr int kWaves = 4;             // waves per workgroup, one 16-row tile each
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
 
 // Activations are staged in "quads" of 4 super-blocks (1,024 columns) that
@@ -32,7 +30,9 @@ constexpr int64_t kQuadBytes = 67840;  // 67,648 rounded up to 256
 
 struct Geometry {
   int count;     // matrices in the launch (same n, k, activations)
-  int n_wg_per;  // workgroup columns per matrix (4 tiles of 16 rows each)
+  int waves;     // waves per workgroup (4 or 8)
+  int tpw;       // 16-row tiles per wave (1, 2 or 4)
+  int n_wg_per;  // workgroup columns per matrix (16 * tpw * waves rows each)
   int n_wg;      // workgroup columns in total = count * n_wg_per
   int splits;    // workgroups along k
   int qps;       // quads per split

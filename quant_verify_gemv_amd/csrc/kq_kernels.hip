@@ -220,16 +220,25 @@ __global__ void kq_fill_kernel(unsigned *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel. Workgroup (blockIdx.x, blockIdx.y): matrix mat =
-// blockIdx.x / n_wg_per, rows [64 (blockIdx.x % n_wg_per), +64) of it (wave w
-// owns the 16-row tile 4 (blockIdx.x % n_wg_per) + w), quads
-// [qps blockIdx.y, +qps) of k.
+// Main kernel. A workgroup of W waves owns R = 16 T W consecutive output rows
+// of one matrix (blockIdx.x = matrix * n_wg_per + row group) and the quads
+// [qps blockIdx.y, +qps) of k. Wave w processes the T 16-row tiles t W + w
+// (t < T); the activations of each block are staged once in LDS per
+// workgroup and every A-operand read from LDS feeds all T tiles of the wave,
+// so both the activation traffic and the LDS reads per weight byte fall as
+// 1/T (and the staging as 1/W). Every tile runs exactly the arithmetic of a
+// one-tile wave, so results do not depend on W or T.
 
 struct WTile {
   u32x4 hdr, q0, q1;
 };
 
-__global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
+template <int W, int T>
+__global__ __launch_bounds__(64 * W) void kq_gemv_kernel(GemvLaunch a) {
+  constexpr int kNth = 64 * W;
+  constexpr int kRows = 16 * T * W;
+  constexpr int kXj = (int)(kXaBlockBytes / 16) / kNth;  // 16-B activation chunks per thread per block
+  static_assert(kXj * 16 * kNth == kXaBlockBytes, "activation block must split evenly");
   __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXaBlockBytes];
   __shared__ unsigned long long s_keys[kMaxRows];
   __shared__ int s_flag;
@@ -246,8 +255,14 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
   const int wg = blockIdx.x;
   const int mat = wg / a.g.n_wg_per;
   const int wgl = wg - mat * a.g.n_wg_per;
-  const int64_t row = (int64_t)(wgl * kWaves + wave) * 16 + ln;
-  const uint8_t *rowp = a.w[mat] + (row < N ? row : N - 1) * a.row_bytes;
+  const int64_t row0 = (int64_t)wgl * kRows;
+  int64_t row[T];
+  const uint8_t *rowp[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    row[t] = row0 + (int64_t)(t * W + wave) * 16 + ln;
+    rowp[t] = a.w[mat] + (row[t] < N ? row[t] : N - 1) * a.row_bytes;
+  }
 
   const int q_begin = blockIdx.y * a.g.qps;
   const int q_end = min(a.g.quads, q_begin + a.g.qps);
@@ -256,7 +271,9 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
 
   const unsigned mask_lo = in_vgpr(0x000F000Fu);
   const unsigned mask_hi = in_vgpr(0x00F000F0u);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Software pipeline. The weights rotate through four register sets (the
   // quad loop is unrolled four times, one step per block) so that the loads
@@ -266,30 +283,32 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
   // split's last block) so that outstanding loads are counted statically and
   // each wait covers only the data about to be used.
   auto clampb = [&](int64_t b) -> int64_t { return b < b_last ? b : b_last; };
-  auto load_w = [&](WTile &w, int64_t b) {
-    const uint8_t *p = rowp + b * kBlockBytes;
-    w.hdr = ld16(p);
-    w.q0 = ld16(p + 16 + 16 * kg);
-    w.q1 = ld16(p + 80 + 16 * kg);
+  auto load_w = [&](WTile(&w)[T], int64_t b) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint8_t *p = rowp[t] + b * kBlockBytes;
+      w[t].hdr = ld16(p);
+      w[t].q0 = ld16(p + 16 + 16 * kg);
+      w[t].q1 = ld16(p + 80 + 16 * kg);
+    }
   };
   auto x_src = [&](int64_t b) -> const uint8_t * {
     return a.staged + (b >> 2) * kQuadBytes + (b & 3) * kXaBlockBytes;
   };
-  WTile w0, w1, w2, w3;
+  auto load_x = [&](u32x4(&xr)[kXj], int64_t b) {
+    const uint8_t *src = x_src(b);
+#pragma unroll
+    for (int j = 0; j < kXj; ++j) xr[j] = ld16(src + (tid + kNth * j) * 16);
+  };
+  WTile w0[T], w1[T], w2[T], w3[T];
   load_w(w0, b_begin);
   load_w(w1, clampb(b_begin + 1));
   load_w(w2, clampb(b_begin + 2));
-  u32x4 xr0[4], xr1[4];
-  {
-    const uint8_t *src = x_src(b_begin);
+  u32x4 xr0[kXj], xr1[kXj];
+  load_x(xr0, b_begin);
+  load_x(xr1, clampb(b_begin + 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr0[j] = ld16(src + (tid + 256 * j) * 16);
-    const uint8_t *src1 = x_src(clampb(b_begin + 1));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xr1[j] = ld16(src1 + (tid + 256 * j) * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[0][(tid + 256 * j) * 16]) = xr0[j];
-  }
+  for (int j = 0; j < kXj; ++j) *(u32x4 *)(&s_x[0][(tid + kNth * j) * 16]) = xr0[j];
   __syncthreads();
 
   for (int q = q_begin; q < q_end; ++q) {
@@ -299,74 +318,91 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     const f32x4 xinv = *(const f32x4 *)(qb + kXiOffset + 16 * kg);
     const int64_t qb0 = (int64_t)q * 4;
     const int nblk = (int)(min((int64_t)4, b_last + 1 - qb0));
-    f32x4 G = {0.f, 0.f, 0.f, 0.f};
-    u32x4 hmin = {0u, 0u, 0u, 0u};
+    f32x4 G[T];
+    u32x4 hmin[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      G[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      hmin[t] = u32x4{0u, 0u, 0u, 0u};
+    }
 
     // One block: prefetch the activations of block b+2 (into xl) and the
     // weights of block b+3 (into pf), contract the weights in `cur` with the
     // activations in LDS buffer bq&1, then move the activations of block b+1
     // (loaded one step earlier, in xw) into the other LDS buffer.
-    auto step = [&](WTile &cur, WTile &pf, u32x4 (&xl)[4], u32x4 (&xw)[4], const int bq) {
+    auto step = [&](WTile(&cur)[T], WTile(&pf)[T], u32x4(&xl)[kXj], u32x4(&xw)[kXj], const int bq) {
       const int64_t b = qb0 + bq;
-      {
-        const uint8_t *src = x_src(clampb(b + 2));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xl[j] = ld16(src + (tid + 256 * j) * 16);
-      }
+      load_x(xl, clampb(b + 2));
       load_w(pf, clampb(b + 3));
       __builtin_amdgcn_sched_barrier(0);
       if (bq < nblk) {
-        const u32x4 h = cur.hdr;
-        hmin = bq == kg ? h : hmin;
-        const float d = h2f_lo(h.x);
-        const unsigned sc03 = h.y & 0x3F3F3F3Fu;
-        const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+        // per tile: block scale d and the four sub-block scales this lane
+        // applies. q0 holds sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1
+        // (high); q1 holds 4+2(kg>>1) and 5+2(kg>>1).
+        float d[T];
+        half2v m00[T], c00[T], m01[T], c01[T], m10[T], c10[T], m11[T], c11[T];
         const int sh = (kg >> 1) * 16;
-        // q0: sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
-        // q1: sub-blocks 4+2(kg>>1) and 5+2(kg>>1).
-        const float s00 = (float)((sc03 >> sh) & 0xFFu);
-        const float s01 = (float)((sc03 >> (sh + 8)) & 0xFFu);
-        const float s10 = (float)((sc47 >> sh) & 0xFFu);
-        const float s11 = (float)((sc47 >> (sh + 8)) & 0xFFu);
-        // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
-        const half2v m00 = {(_Float16)s00, (_Float16)s00};
-        const half2v c00 = {(_Float16)(-1024.0f * s00), (_Float16)(-1024.0f * s00)};
-        const half2v m01 = {(_Float16)(0.0625f * s01), (_Float16)(0.0625f * s01)};
-        const half2v c01 = {(_Float16)(-64.0f * s01), (_Float16)(-64.0f * s01)};
-        const half2v m10 = {(_Float16)s10, (_Float16)s10};
-        const half2v c10 = {(_Float16)(-1024.0f * s10), (_Float16)(-1024.0f * s10)};
-        const half2v m11 = {(_Float16)(0.0625f * s11), (_Float16)(0.0625f * s11)};
-        const half2v c11 = {(_Float16)(-64.0f * s11), (_Float16)(-64.0f * s11)};
-        f32x4 chi = {0.f, 0.f, 0.f, 0.f}, clo = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const u32x4 h = cur[t].hdr;
+          hmin[t] = bq == kg ? h : hmin[t];
+          d[t] = h2f_lo(h.x);
+          const unsigned sc03 = h.y & 0x3F3F3F3Fu;
+          const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+          const float s00 = (float)((sc03 >> sh) & 0xFFu);
+          const float s01 = (float)((sc03 >> (sh + 8)) & 0xFFu);
+          const float s10 = (float)((sc47 >> sh) & 0xFFu);
+          const float s11 = (float)((sc47 >> (sh + 8)) & 0xFFu);
+          // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
+          m00[t] = half2v{(_Float16)s00, (_Float16)s00};
+          c00[t] = half2v{(_Float16)(-1024.0f * s00), (_Float16)(-1024.0f * s00)};
+          m01[t] = half2v{(_Float16)(0.0625f * s01), (_Float16)(0.0625f * s01)};
+          c01[t] = half2v{(_Float16)(-64.0f * s01), (_Float16)(-64.0f * s01)};
+          m10[t] = half2v{(_Float16)s10, (_Float16)s10};
+          c10[t] = half2v{(_Float16)(-1024.0f * s10), (_Float16)(-1024.0f * s10)};
+          m11[t] = half2v{(_Float16)(0.0625f * s11), (_Float16)(0.0625f * s11)};
+          c11[t] = half2v{(_Float16)(-64.0f * s11), (_Float16)(-64.0f * s11)};
+        }
+        f32x4 chi[T], clo[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          chi[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          clo[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         const uint8_t *xb = s_x[bq & 1];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
           const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
-          const u32x4 qq = s < 4 ? cur.q0 : cur.q1;
-          const unsigned da = (s & 1) ? qq.z : qq.x;
-          const unsigned db = (s & 1) ? qq.w : qq.y;
           const bool hi = (s & 2) != 0;
           const unsigned mask = hi ? mask_hi : mask_lo;
-          const half2v sc = s < 4 ? (hi ? m01 : m00) : (hi ? m11 : m10);
-          const half2v nb = s < 4 ? (hi ? c01 : c00) : (hi ? c11 : c10);
-          const unsigned u0 = (da & mask) | 0x64006400u;
-          const unsigned u1 = ((da >> 8) & mask) | 0x64006400u;
-          const unsigned u2 = (db & mask) | 0x64006400u;
-          const unsigned u3 = ((db >> 8) & mask) | 0x64006400u;
-          const half2v v0 = __builtin_elementwise_fma(as_h2(u0), sc, nb);
-          const half2v v1 = __builtin_elementwise_fma(as_h2(u1), sc, nb);
-          const half2v v2 = __builtin_elementwise_fma(as_h2(u2), sc, nb);
-          const half2v v3 = __builtin_elementwise_fma(as_h2(u3), sc, nb);
-          const half8 bw = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
-          chi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw, chi, 0, 0, 0);
-          clo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw, clo, 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
+            const unsigned da = (s & 1) ? qq.z : qq.x;
+            const unsigned db = (s & 1) ? qq.w : qq.y;
+            const half2v sc = s < 4 ? (hi ? m01[t] : m00[t]) : (hi ? m11[t] : m10[t]);
+            const half2v nb = s < 4 ? (hi ? c01[t] : c00[t]) : (hi ? c11[t] : c10[t]);
+            const unsigned u0 = (da & mask) | 0x64006400u;
+            const unsigned u1 = ((da >> 8) & mask) | 0x64006400u;
+            const unsigned u2 = (db & mask) | 0x64006400u;
+            const unsigned u3 = ((db >> 8) & mask) | 0x64006400u;
+            const half2v v0 = __builtin_elementwise_fma(as_h2(u0), sc, nb);
+            const half2v v1 = __builtin_elementwise_fma(as_h2(u1), sc, nb);
+            const half2v v2 = __builtin_elementwise_fma(as_h2(u2), sc, nb);
+            const half2v v3 = __builtin_elementwise_fma(as_h2(u3), sc, nb);
+            const half8 bw = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
+            chi[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw, chi[t], 0, 0, 0);
+            clo[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw, clo[t], 0, 0, 0);
+          }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) G[r] += d * (chi[r] + clo[r]);
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) G[t][r] += d[t] * (chi[t][r] + clo[t][r]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4 *)(&s_x[(bq & 1) ^ 1][(tid + 256 * j) * 16]) = xw[j];
+      for (int j = 0; j < kXj; ++j) *(u32x4 *)(&s_x[(bq & 1) ^ 1][(tid + kNth * j) * 16]) = xw[j];
       __syncthreads();
     };
     step(w0, w3, xr0, xr1, 0);
@@ -374,12 +410,15 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     step(w2, w1, xr0, xr1, 2);
     step(w3, w2, xr1, xr0, 3);
 
-    // end of the quad: min term (three MFMAs) and the row scale 2^-e. Lane
-    // kg supplies dmin * m_j of block kg of the quad in k-slots 8kg..8kg+7;
-    // the A operand holds the matching scaled sub-block sums.
-    {
-      const u32x4 h = hmin;
-      const bool ok = kg < nblk;
+    // end of the quad: min term (three MFMAs per tile) and the row scale
+    // 2^-e. Lane kg supplies dmin * m_j of block kg of the quad in k-slots
+    // 8kg..8kg+7; the A operand holds the matching scaled sub-block sums.
+    const half8 a2h = __builtin_bit_cast(half8, xs_hi);
+    const half8 a2l = __builtin_bit_cast(half8, xs_lo);
+    const bool ok = kg < nblk;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const u32x4 h = hmin[t];
       const float dmin = h2f_hi(h.x);
       const unsigned m03 = h.z & 0x3F3F3F3Fu;
       const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
@@ -387,9 +426,9 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const unsigned src = p < 2 ? m03 : m47;
-        const int sh = (p & 1) * 16;
-        const float v0 = ok ? dmin * (float)((src >> sh) & 0xFFu) : 0.0f;
-        const float v1 = ok ? dmin * (float)((src >> (sh + 8)) & 0xFFu) : 0.0f;
+        const int shp = (p & 1) * 16;
+        const float v0 = ok ? dmin * (float)((src >> shp) & 0xFFu) : 0.0f;
+        const float v1 = ok ? dmin * (float)((src >> (shp + 8)) & 0xFFu) : 0.0f;
         const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
         const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
         half2v hh = {h0, h1}, ll = {l0, l1};
@@ -398,40 +437,45 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
       }
       const half8 b2h = make_h8(bh[0], bh[1], bh[2], bh[3]);
       const half8 b2l = make_h8(bl[0], bl[1], bl[2], bl[3]);
-      const half8 a2h = __builtin_bit_cast(half8, xs_hi);
-      const half8 a2l = __builtin_bit_cast(half8, xs_lo);
       f32x4 c2 = {0.f, 0.f, 0.f, 0.f};
       c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2h, c2, 0, 0, 0);
       c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2l, b2h, c2, 0, 0, 0);
       c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2h, b2l, c2, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] += xinv[r] * (G[r] - c2[r]);
+      for (int r = 0; r < 4; ++r) acc[t][r] += xinv[r] * (G[t][r] - c2[r]);
     }
   }
 
   // ---------------------------------------------------------------- epilogue
-  // the lane holds acc[r] = logit of activation row 4kg+r, output row `row`
+  // lane holds acc[t][r] = logit of activation row 4kg+r, output row row[t]
   const int splits = a.g.splits;
-  const int64_t row0 = (int64_t)wgl * 64;
   float *logits = a.logits[mat];
 
   if (tid < kMaxRows) s_keys[tid] = 0ull;
 
   if (splits == 1) {
-    if (row < N && logits) {
+    if (logits) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (m < M) logits[(int64_t)m * N + row] = acc[r];
+      for (int t = 0; t < T; ++t) {
+        if (row[t] < N) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kg + r;
+            if (m < M) logits[(int64_t)m * N + row[t]] = acc[t][r];
+          }
+        }
       }
     }
     if (a.verify) {
       __syncthreads();
-      if (row < N) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 4 * kg + r;
-          if (m < M) atomicMax(&s_keys[m], argmax_key(acc[r], (unsigned)row));
+      for (int t = 0; t < T; ++t) {
+        if (row[t] < N) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kg + r;
+            if (m < M) atomicMax(&s_keys[m], argmax_key(acc[t][r], (unsigned)row[t]));
+          }
         }
       }
     }
@@ -439,11 +483,14 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     // write this split's partial sums, then the last arriving split sums all
     // splits in split order.
     float *part = a.partials + ((int64_t)blockIdx.y * a.g.count + mat) * kMaxRows * N;
-    if (row < N) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (m < M) st_dev(&part[(int64_t)m * N + row], acc[r]);
+    for (int t = 0; t < T; ++t) {
+      if (row[t] < N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 4 * kg + r;
+          if (m < M) st_dev(&part[(int64_t)m * N + row[t]], acc[t][r]);
+        }
       }
     }
     stores_done_barrier();
@@ -456,16 +503,28 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     }
     __syncthreads();
     if (!s_flag) return;
-    const int64_t nrows = min((int64_t)64, N - row0);
+    // Sum the splits in split order. Thread i handles row i % kRows of the
+    // group for activation rows i / kRows, +kNth / kRows, ...; all loads of
+    // a chunk of splits are issued before the first is used.
+    const int nrows = (int)min((int64_t)kRows, N - row0);
     const int64_t split_stride = (int64_t)a.g.count * kMaxRows * N;
     const float *p0 = a.partials + (int64_t)mat * kMaxRows * N;
-    for (int64_t e = tid; e < (int64_t)M * nrows; e += kThreads) {
-      const int m = (int)(e / nrows);
-      const int64_t n = row0 + e % nrows;
+    constexpr int kChunk = 8;
+    for (int i = tid; i < kRows * kMaxRows; i += kNth) {
+      const int m = i / kRows;
+      const int r = i % kRows;
+      if (m >= M || r >= nrows) continue;
+      const int64_t n = row0 + r;
+      const float *src = p0 + (int64_t)m * N + n;
       float v = 0.0f;
-      for (int sp = 0; sp < splits; ++sp) {
-        const float pv = ld_dev(&p0[sp * split_stride + (int64_t)m * N + n]);
-        v = sp == 0 ? pv : v + pv;
+      for (int sp0 = 0; sp0 < splits; sp0 += kChunk) {
+        float pv[kChunk];
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c)
+          pv[c] = sp0 + c < splits ? ld_dev(src + (int64_t)(sp0 + c) * split_stride) : 0.0f;
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c)
+          if (sp0 + c < splits) v = sp0 + c == 0 ? pv[c] : v + pv[c];
       }
       if (logits) logits[(int64_t)m * N + n] = v;
       if (a.verify) atomicMax(&s_keys[m], argmax_key(v, (unsigned)n));
@@ -488,7 +547,7 @@ __global__ __launch_bounds__(256) void kq_gemv_kernel(GemvLaunch a) {
     const int m = tid & 15;
     if (m < M) {
       unsigned long long best = 0ull;
-      for (int w = tid >> 4; w < a.g.n_wg; w += kThreads / 16) {
+      for (int w = tid >> 4; w < a.g.n_wg; w += kNth / 16) {
         const unsigned long long key = ld_dev(&a.wg_keys[(int64_t)w * kMaxRows + m]);
         best = key > best ? key : best;
       }
@@ -530,8 +589,16 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream) {
 }
 
 int launch_gemv(const GemvLaunch &a, void *stream) {
-  dim3 grid((unsigned)a.g.n_wg, (unsigned)a.g.splits);
-  hipLaunchKernelGGL(kq_gemv_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+  const dim3 grid((unsigned)a.g.n_wg, (unsigned)a.g.splits);
+  hipStream_t st = (hipStream_t)stream;
+  switch (a.g.waves * 16 + a.g.tpw) {
+    case 4 * 16 + 1: hipLaunchKernelGGL((kq_gemv_kernel<4, 1>), grid, dim3(256), 0, st, a); break;
+    case 4 * 16 + 2: hipLaunchKernelGGL((kq_gemv_kernel<4, 2>), grid, dim3(256), 0, st, a); break;
+    case 4 * 16 + 4: hipLaunchKernelGGL((kq_gemv_kernel<4, 4>), grid, dim3(256), 0, st, a); break;
+    case 8 * 16 + 1: hipLaunchKernelGGL((kq_gemv_kernel<8, 1>), grid, dim3(512), 0, st, a); break;
+    case 8 * 16 + 2: hipLaunchKernelGGL((kq_gemv_kernel<8, 2>), grid, dim3(512), 0, st, a); break;
+    default: return (int)hipErrorInvalidConfiguration;
+  }
   return (int)hipGetLastError();
 }
 

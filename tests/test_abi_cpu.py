@@ -56,8 +56,10 @@ def test_sizes_and_geometry():
     assert kq.staged_bytes(6656) == 7 * 67840
     for n, k in [(512, 1024), (6656, 6656), (6656, 33280), (131072, 6656), (17920, 6656), (6656, 17920), (1, 256)]:
         assert kq.workspace_bytes(n, k, 1) == kq.workspace_bytes(n, k, 16) > 0
-        nt, nwg, sp = kq.launch_geometry(n, k)
-        assert nt in (1, 2) and nwg * 64 * nt >= n and 1 <= sp <= -(-k // 1024)
+        waves, tpw, nwg, sp = kq.launch_geometry(n, k)
+        assert waves in (4, 8) and tpw in (1, 2, 4)
+        assert nwg * 16 * waves * tpw >= n > (nwg - 1) * 16 * waves * tpw
+        assert 1 <= sp <= -(-k // 1024)
         assert kq.scratch_bytes(n, k) <= kq.workspace_bytes(n, k, 16)
     with pytest.raises(kq.KQError):
         kq.launch_geometry(16, 100)
