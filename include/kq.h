@@ -147,18 +147,22 @@ size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count);
  *  scratch device, >= kq_group_scratch_bytes(n, k, count) bytes, zeroed once
  * Each matrix's logits are deterministic and within the kq.h tolerance; they
  * may differ in the last bits from a separate kq_gemv_staged call because the
- * launch can split k differently (the split depends on n, k and count). */
+ * launch can divide k differently among workgroups (the division depends on
+ * n, k and count). */
 kq_status kq_gemv_staged_group(const void *const *w_q4k, int count, int64_t n, int64_t k,
                                const void *staged, int m, float *const *logits,
                                void *scratch, size_t scratch_bytes, void *stream);
 
 /* Launch geometry the library uses for one n x k matrix (a function of n and
- * k only, never of m): waves per workgroup (*waves), 16-row tiles per wave
- * (*tiles_per_wave; a workgroup covers 16 * waves * tiles_per_wave rows),
- * workgroups along n (*n_wg) and along k (*splits). Any output pointer may be
- * NULL. Returns KQ_ERR_SHAPE for invalid shapes. */
-kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave, int *n_wg,
-                             int *splits);
+ * k only, never of m). The work is cut into units of one row group (16 *
+ * waves * tiles_per_wave consecutive rows) by one 256-column block; a fixed
+ * number of persistent workgroups (*workgroups) each take an equal,
+ * contiguous run of the *units units in row-group-major order. Also returns
+ * the waves per workgroup (*waves) and 16-row tiles per wave
+ * (*tiles_per_wave). Any output pointer may be NULL. Returns KQ_ERR_SHAPE for
+ * invalid shapes. */
+kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave,
+                             int *workgroups, int64_t *units);
 
 #ifdef __cplusplus
 }

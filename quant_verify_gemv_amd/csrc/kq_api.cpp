@@ -17,44 +17,52 @@ static bool shape_ok(int64_t n, int64_t k) {
          (k / kQK) * kBlockBytes <= (((int64_t)1 << 62) / n);
 }
 
-// Launch geometry. Workgroup shapes (waves per workgroup x 16-row tiles per
-// wave) and how many of them one CU holds at once (set by their register
-// use): 4x1 -> 3, 8x1 -> 1, 8x2 -> 1. Tall workgroups share each staged
-// activation block among more rows; short ones give small matrices more
-// workgroups. Measured on MI355X: the 131,072-row LM head is fastest with
-// 8x2, a launch of two or three 6,656-wide matrices (q/k/v, gate/up) with
-// 4x1, and a single 6,656-row matrix with 8x1.
+// Launch geometry: persistent workgroups of 8 waves, one per CU (their LDS
+// activation ring of 8 blocks fills most of a CU's 160 KB), each taking an
+// equal, contiguous run of (row group, block) units. Row groups are 256 rows
+// (two 16-row tiles per wave) for the 131,072-row LM head and 128 rows (one
+// tile per wave) for the 6,656- and 17,920-row matrices, where a taller group
+// would leave too few groups to share among 256 workgroups. Barriers every 4
+// units. Measured on MI355X with the shapes of the 52-layer stack, the
+// DFlash fc projection and the LM head.
 static constexpr int64_t kCUs = 256;
 
 struct Shape {
-  int waves, tpw, per_cu;
+  int waves, tpw, per_cu, bi;
 };
 
 static Shape pick_shape(int64_t n, int count) {
+#ifdef KQ_GEOM_WAVES  // build-time override for tuning sweeps
+#ifndef KQ_GEOM_BI
+#define KQ_GEOM_BI 1
+#endif
+  (void)n;
+  (void)count;
+  return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI};
+#endif
   const int64_t rows = n * count;
-  if (rows >= 131072) return {8, 2, 1};
-  if (count == 1 && n <= 8192) return {8, 1, 1};
-  return {4, 1, 3};
+  if (rows >= 131072) return {8, 2, 1, 4};
+  return {8, 1, 1, 4};
 }
 
 Geometry geometry(int64_t n, int64_t k, int count) {
   Geometry g;
   const Shape sh = pick_shape(n, count);
-  const int64_t tiles = cdiv(n, 16);
   g.count = count;
   g.waves = sh.waves;
   g.tpw = sh.tpw;
-  g.quads = (int)cdiv(k, kQuadK);
-  g.n_wg_per = (int)cdiv(tiles, (int64_t)g.waves * g.tpw);
-  g.n_wg = g.count * g.n_wg_per;
-  // Enough workgroups to fill every CU; split k only when the rows alone do
-  // not provide them (splits are whole 1,024-column quads).
-  const int64_t target = kCUs * sh.per_cu;
-  int64_t splits = cdiv(target, g.n_wg);
-  if (splits > g.quads) splits = g.quads;
-  if (splits < 1) splits = 1;
-  g.qps = (int)cdiv(g.quads, splits);
-  g.splits = (int)cdiv(g.quads, g.qps);
+  g.bi = sh.bi;
+  g.rows = 16 * sh.waves * sh.tpw;
+  g.n_wg_per = (int)cdiv(n, g.rows);
+  g.n_groups = g.count * g.n_wg_per;
+  g.kb = (int)(k / kQK);
+  g.units = (int64_t)g.n_groups * g.kb;
+  // persistent workgroups: as many as the CUs hold at once
+  int64_t slots = kCUs * sh.per_cu;
+#ifdef KQ_GEOM_SPLIT  // build-time override for tuning sweeps: row groups x splits workgroups
+  slots = (int64_t)g.n_groups * KQ_GEOM_SPLIT;
+#endif
+  g.n_wg = (int)(g.units < slots ? g.units : slots);
   return g;
 }
 
@@ -62,12 +70,10 @@ ScratchLayout scratch_layout(int64_t n, int64_t k, int count) {
   const Geometry g = geometry(n, k, count);
   ScratchLayout s;
   s.cnt_off = 256;
-  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * (size_t)g.n_wg);
+  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * (size_t)g.n_groups);
   s.ctrl_bytes = s.keys_off;  // words that must be zero between calls
   s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxRows * (size_t)g.n_wg);
-  s.total = s.part_off;
-  if (g.splits > 1)
-    s.total += align256(sizeof(float) * (size_t)g.splits * (size_t)count * kMaxRows * (size_t)n);
+  s.total = s.part_off + align256(sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * (size_t)g.rows);
   return s;
 }
 
@@ -92,7 +98,7 @@ const char *kq_status_string(kq_status s) {
 
 size_t kq_staged_bytes(int64_t k) {
   if (k <= 0 || k % kQK || k > ((int64_t)1 << 28)) return 0;
-  return (size_t)cdiv(k, kQuadK) * (size_t)kQuadBytes;
+  return (size_t)(k / kQK) * (size_t)kStageBytes;
 }
 
 size_t kq_scratch_bytes(int64_t n, int64_t k) {
@@ -110,14 +116,14 @@ size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
   return align256(kq_staged_bytes(k)) + kq_scratch_bytes(n, k);
 }
 
-kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave, int *n_wg,
-                             int *splits) {
+kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave,
+                             int *workgroups, int64_t *units) {
   if (!shape_ok(n, k)) return KQ_ERR_SHAPE;
   const Geometry g = geometry(n, k, 1);
   if (waves) *waves = g.waves;
   if (tiles_per_wave) *tiles_per_wave = g.tpw;
-  if (n_wg) *n_wg = g.n_wg;
-  if (splits) *splits = g.splits;
+  if (workgroups) *workgroups = g.n_wg;
+  if (units) *units = g.units;
   return KQ_OK;
 }
 
@@ -181,7 +187,7 @@ static kq_status run(const void *const *w, int count, int64_t n, int64_t k, cons
   a.staged = (const uint8_t *)staged;
   uint8_t *sc = (uint8_t *)scratch;
   a.done = (unsigned *)sc;
-  a.tile_cnt = (unsigned *)(sc + sl.cnt_off);
+  a.group_cnt = (unsigned *)(sc + sl.cnt_off);
   a.wg_keys = (unsigned long long *)(sc + sl.keys_off);
   a.partials = (float *)(sc + sl.part_off);
   a.argmax_out = argmax;

@@ -11,32 +11,39 @@ constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // verify rows per call (block size of the draft)
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
 
-// Activations are staged in "quads" of 4 super-blocks (1,024 columns) that
-// share one power-of-two scale per row. Per quad:
-//   XA [4 blocks][8 k-steps][hi,lo][64 lanes][8 x fp16]   65,536 B
-//   XS [hi,lo][64 lanes][8 x fp16]  (sub-block sums)         2,048 B
-//   XI [16] fp32 (per-row 2^-e)                                 64 B
-constexpr int64_t kQuadK = 1024;
-constexpr int64_t kXaBlockBytes = 16384;
-constexpr int64_t kXsOffset = 65536;
-constexpr int64_t kXiOffset = 65536 + 2048;
-constexpr int64_t kQuadBytes = 67840;  // 67,648 rounded up to 256
+// Staged activations, one record per 256-column block (each row scaled by a
+// power of two 2^e chosen from that row's largest magnitude in the block):
+//   XA  [8 k-steps][hi,lo][64 lanes][8 x fp16]  16,384 B  MFMA A operand
+//   XSB [64 lanes][4 x fp16]                       512 B  sub-block sums (min-term A operand)
+//   XI  [16] fp32                                    64 B  per-row 2^-e
+constexpr int64_t kXaBytes = 16384;
+constexpr int64_t kXsbOffset = 16384;
+constexpr int64_t kXiOffset = 16384 + 512;
+constexpr int64_t kStageBytes = 16384 + 512 + 64;  // 16,960 B per block (16-B aligned)
 
-// Scratch area of the main kernel:
-//   [0, 256)      done counter (u32) at 0                    -- zero between calls
-//   cnt_off       per-workgroup-column split-K arrivals (u32) -- zero between calls
-//   keys_off      per-workgroup-column argmax keys [n_wg][16] (u64)
-//   part_off      split-K partial sums [splits][count][16][n] fp32
+// Scratch area of the main kernel (control words zero between calls; every
+// launch leaves them zero again):
+//   [0, 256)   done counter (u32)
+//   cnt_off    per-row-group arrival counters [n_groups] (u32)
+//   keys_off   per-workgroup argmax keys [n_wg][16] (u64)
+//   part_off   partial sums [n_wg][2][16][rows per group] fp32
 
+// Work decomposition. A row group is 16 * waves * tpw consecutive output rows
+// of one matrix; a unit is one row group times one 256-column block. The
+// launch has n_wg persistent workgroups; workgroup p processes the units
+// [p * base + min(p, rem), +base + (p < rem)) of the row-group-major unit
+// order, base = units / n_wg, rem = units % n_wg.
 struct Geometry {
-  int count;     // matrices in the launch (same n, k, activations)
-  int waves;     // waves per workgroup (4 or 8)
-  int tpw;       // 16-row tiles per wave (1, 2 or 4)
-  int n_wg_per;  // workgroup columns per matrix (16 * tpw * waves rows each)
-  int n_wg;      // workgroup columns in total = count * n_wg_per
-  int splits;    // workgroups along k
-  int qps;       // quads per split
-  int quads;     // total quads
+  int count;      // matrices in the launch (same n, k, activations)
+  int waves;      // waves per workgroup (4 or 8)
+  int tpw;        // 16-row tiles per wave (1 or 2)
+  int bi;         // units between workgroup barriers (1, 2 or 4; LDS ring of 2 bi blocks)
+  int rows;       // rows per row group = 16 * waves * tpw
+  int n_wg_per;   // row groups per matrix
+  int n_groups;   // row groups in total = count * n_wg_per
+  int kb;         // 256-column blocks per row
+  int64_t units;  // n_groups * kb
+  int n_wg;       // persistent workgroups (<= units)
 };
 
 struct ScratchLayout {
@@ -51,7 +58,7 @@ struct GemvLaunch {
   const uint8_t *staged;
   float *partials;
   unsigned *done;
-  unsigned *tile_cnt;
+  unsigned *group_cnt;
   unsigned long long *wg_keys;
   int32_t *argmax_out;  // verify only
   int32_t *accept_out;  // verify only

@@ -54,7 +54,7 @@ def load() -> ctypes.CDLL:
     lib.kq_stage_rows.argtypes = [P, I32, I64, P, SZ, P]
     lib.kq_gemv_staged.argtypes = [P, I64, I64, P, I32, P, P, SZ, P]
     lib.kq_verify_staged.argtypes = [P, I64, I64, P, I32, P, P, P, P, P, SZ, P]
-    lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P, P]
+    lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P, P]  # int*, int*, int*, int64_t*
     lib.kq_group_scratch_bytes.argtypes = [I64, I64, I32]
     lib.kq_group_scratch_bytes.restype = SZ
     lib.kq_gemv_staged_group.argtypes = [P, I32, I64, I64, P, I32, P, P, SZ, P]
@@ -91,9 +91,10 @@ def group_scratch_bytes(n: int, k: int, count: int) -> int:
 
 
 def launch_geometry(n: int, k: int) -> Tuple[int, int, int, int]:
-    """(waves per workgroup, 16-row tiles per wave, workgroups along n,
-    splits along k) the library uses for an n x k matrix."""
-    v = [ctypes.c_int(0) for _ in range(4)]
+    """(waves per workgroup, 16-row tiles per wave, persistent workgroups,
+    units) the library uses for an n x k matrix; a unit is one row group of
+    16 * waves * tiles rows times one 256-column block."""
+    v = [ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int64(0)]
     _check(load().kq_launch_geometry(n, k, *[ctypes.byref(x) for x in v]), "kq_launch_geometry")
     return tuple(x.value for x in v)
 
