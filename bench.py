@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--m", choices=("both", "16", "1"), default="both", help="row counts to time")
+    p.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
+                   help="weight layout: the tiled copy (default) or llama.cpp's row-major blocks")
     p.add_argument("--copy-probe", action="store_true",
                    help="first run plain 1 GiB device copies (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
@@ -62,18 +64,20 @@ def log(*a):
 class Stack:
     """Device-resident weights, staged activations, outputs and scratch."""
 
-    def __init__(self, kq, torch, dev, layers):
+    def __init__(self, kq, torch, dev, layers, layout):
         self.kq, self.torch, self.dev = kq, torch, dev
+        self.layout = layout
         self.mats = synthetic.stack_matrices(layers)
         head = synthetic.LM_HEAD
         self.head = synthetic.Gemv(n=head["n"], k=head["k"], seed=head["seed"])
         t0 = time.time()
         self.w = []
         for i, g in enumerate(self.mats):
-            self.w.append(torch.from_numpy(synthetic.q4k_matrix(g.n, g.k, g.seed)).to(dev))
+            self.w.append(self.resident(synthetic.q4k_matrix(g.n, g.k, g.seed), g.n, g.k))
             if i % 50 == 0:
                 log(f"bench: generated {i + 1}/{len(self.mats)} matrices ({time.time() - t0:.1f} s)")
-        self.w_head = torch.from_numpy(synthetic.q4k_matrix(self.head.n, self.head.k, self.head.seed)).to(dev)
+        self.w_head = self.resident(synthetic.q4k_matrix(self.head.n, self.head.k, self.head.seed),
+                                    self.head.n, self.head.k)
         torch.cuda.synchronize()
         log(f"bench: weights resident ({time.time() - t0:.1f} s)")
         self.ks = sorted({g.k for g in self.mats} | {self.head.k})
@@ -99,6 +103,17 @@ class Stack:
         self.draft = [int(t) for t in g.integers(0, self.head.n, 15)]
         self.weight_bytes = sum(g.weight_bytes for g in self.mats) + self.head.weight_bytes
 
+    def resident(self, w_host, n, k):
+        """Device copy of a Q4_K matrix in the benchmark's weight layout (the
+        tiled copy is made once, outside the timed region, as an engine would
+        when it loads weights)."""
+        w = self.torch.from_numpy(w_host).to(self.dev)
+        if self.layout == self.kq.LAYOUT_TILED16:
+            t = self.kq.tile_weights(w, n, k)
+            del w
+            return t
+        return w
+
     @property
     def launches(self):
         return len(self.groups) + 1
@@ -111,10 +126,10 @@ class Stack:
             g = self.mats[grp[0]]
             key = (g.n, g.k, len(grp))
             kq.gemv_staged_group([self.w[j] for j in grp], g.n, g.k, self.staged[g.k], m, self.scratch[key],
-                                 logits=[o[:m] for o in self.out[key]])
+                                 logits=[o[:m] for o in self.out[key]], layout=self.layout)
         h = self.head
         kq.verify_staged(self.w_head, h.n, h.k, self.staged[h.k], m, self.draft[:m - 1],
-                         self.head_scratch, out=(self.am[:m], self.acc, None))
+                         self.head_scratch, out=(self.am[:m], self.acc, None), layout=self.layout)
 
     def algorithmic_bytes(self, m):
         """Per main-kernel launch: every matrix's weights once, the M
@@ -199,7 +214,7 @@ def source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload, m):
+def stored_traffic(workload, m, layout_name):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), or None
     when there is none for this workload and M or the kernel source changed
@@ -212,13 +227,13 @@ def stored_traffic(workload, m):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("source_sha256") != source_digest():
+    if vals.get("source_sha256") != source_digest() or vals.get("weight_layout") != layout_name:
         return None
     v = vals.get(f"traffic_bytes_per_launch_m{m}")
     return float(v) if v else None
 
 
-def kernel_roofline(stack, m, ev_step, workload):
+def kernel_roofline(stack, m, ev_step, workload, layout_name):
     """The main kernel's roofline point. Its average launch duration is the
     timed region's HIP-event time per step divided by its launches per step
     (the kernels run back to back in the graph; the two small staging
@@ -229,7 +244,7 @@ def kernel_roofline(stack, m, ev_step, workload):
     avg_b = float(np.mean(stack.algorithmic_bytes(m)))
     ach = avg_b / avg_s / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": stored_traffic(workload, m),
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": stored_traffic(workload, m, layout_name),
             "kernel": "kq_gemv_kernel", "launches_per_step": n, "avg_launch_us": round(avg_s * 1e6, 3),
             "avg_algorithmic_bytes": int(avg_b)}
 
@@ -293,13 +308,14 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_probe:
         copy_probe(torch, dev)
-    stack = Stack(kq, torch, dev, args.layers)
+    layout = kq.LAYOUT_TILED16 if args.layout == "tiled" else kq.LAYOUT_ROWS
+    stack = Stack(kq, torch, dev, args.layers, layout)
     use_graph = not args.no_graph
     workload = f"stack{args.layers}_q4k+lmhead_verify"
     res = {}
     for m in ((16, 1) if args.m == "both" else (int(args.m),)):
         wall, ev = run_m(stack, torch, m, args.steps, args.warmup, use_graph)
-        roof = kernel_roofline(stack, m, ev, workload)
+        roof = kernel_roofline(stack, m, ev, workload, "tiled16" if layout == kq.LAYOUT_TILED16 else "rows")
         gbs = stack.weight_bytes / wall / 1e9
         res[m] = {"ms_per_step": round(wall * 1e3, 4), "rows_per_s": round(m / wall, 2),
                   "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -330,7 +346,8 @@ def main():
         "config": {"workload": workload,
                    "matrices": len(stack.mats) + 1, "launches_per_step": stack.launches + len(stack.ks),
                    "weight_bytes": stack.weight_bytes,
-                   "m": head_m, "k_draft": head_m - 1, "launch": "hipgraph" if use_graph else "eager"},
+                   "m": head_m, "k_draft": head_m - 1, "launch": "hipgraph" if use_graph else "eager",
+                   "weight_layout": "tiled16" if layout == kq.LAYOUT_TILED16 else "llama.cpp rows"},
         "m16": res.get(16),
         "m1": res.get(1),
         "m16_over_m1": round(res[16]["ms_per_step"] / res[1]["ms_per_step"], 4) if len(res) == 2 else None,

@@ -61,6 +61,10 @@ typedef int kq_status;
 #define KQ_ERR_WORKSPACE 5  /* workspace / staged buffer smaller than required  */
 #define KQ_ERR_LAUNCH    6  /* HIP reported an error when enqueuing             */
 
+/* Weight layouts accepted by the staged calls. */
+#define KQ_LAYOUT_ROWS    0  /* llama.cpp: row n is k/256 consecutive 144-byte blocks */
+#define KQ_LAYOUT_TILED16 1  /* kq_tile_weights output (same bytes, reordered) */
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *kq_status_string(kq_status s);
 
@@ -119,16 +123,36 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k,
 kq_status kq_stage_rows(const float *x, int m, int64_t k,
                         void *staged, size_t staged_bytes, void *stream);
 
+/* Bytes of the tiled copy of an n x k Q4_K matrix (0 for invalid shapes):
+ * ceil(n/16) * (k/256) * 2,304. */
+size_t kq_tiled_bytes(int64_t n, int64_t k);
+
+/* Reorder the bytes of an n x k Q4_K matrix (llama.cpp layout, device) into
+ * KQ_LAYOUT_TILED16 (device, >= kq_tiled_bytes(n, k) bytes, 16-byte aligned,
+ * not overlapping the input). Every byte of every 144-byte block is kept;
+ * only their order changes: record (b, t) = block b of the 16-row tile t
+ * (rows 16t .. 16t+15) is 2,304 bytes at (b * ceil(n/16) + t) * 2,304 and
+ * holds the 16 block headers (row order), then quant bytes [16g, 16g+16) of
+ * row r at 256 + 16 (16 g + r) and quant bytes [64+16g, 80+16g) of row r at
+ * 1,280 + 16 (16 g + r), g = 0..3. Rows past n are zero. All blocks of one
+ * 256-column block index for consecutive rows are contiguous, so each wave
+ * reads whole cache lines. One-time preparation of resident weights; the
+ * staged calls accept either layout and give bitwise identical results.
+ * Overlapping input and output buffers are refused with KQ_ERR_SHAPE. */
+kq_status kq_tile_weights(const void *w_q4k, int64_t n, int64_t k,
+                          void *w_tiled, size_t tiled_bytes, void *stream);
+
 /* kq_gemv_rows on staged activations.
+ *  layout   KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16 (the layout of w_q4k)
  *  scratch  device, >= kq_scratch_bytes(n, k) bytes, 256-byte aligned,
  *           zeroed once by kq_workspace_init */
-kq_status kq_gemv_staged(const void *w_q4k, int64_t n, int64_t k,
+kq_status kq_gemv_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
                          const void *staged, int m, float *logits,
                          void *scratch, size_t scratch_bytes, void *stream);
 
 /* kq_verify_argmax_accept on staged activations (same arguments as above;
- * scratch as for kq_gemv_staged). */
-kq_status kq_verify_staged(const void *w_q4k, int64_t n, int64_t k,
+ * layout and scratch as for kq_gemv_staged). */
+kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
                            const void *staged, int m,
                            const int32_t *draft_host,
                            int32_t *argmax, int32_t *accept_out,
@@ -142,14 +166,15 @@ size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count);
 /* kq_gemv_staged for 1 <= count <= 8 matrices of the same shape that share
  * the staged activations (projections of one input, e.g. q/k/v or gate/up),
  * in one launch.
- *  w_q4k   host array of `count` device pointers (each 16-byte aligned)
+ *  w_q4k   host array of `count` device pointers (each 16-byte aligned), all
+ *          in `layout` (KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16)
  *  logits  host array of `count` device pointers, fp32 [m][n] each
  *  scratch device, >= kq_group_scratch_bytes(n, k, count) bytes, zeroed once
  * Each matrix's logits are deterministic and within the kq.h tolerance; they
  * may differ in the last bits from a separate kq_gemv_staged call because the
  * launch can divide k differently among workgroups (the division depends on
  * n, k and count). */
-kq_status kq_gemv_staged_group(const void *const *w_q4k, int count, int64_t n, int64_t k,
+kq_status kq_gemv_staged_group(const void *const *w_q4k, int layout, int count, int64_t n, int64_t k,
                                const void *staged, int m, float *const *logits,
                                void *scratch, size_t scratch_bytes, void *stream);
 

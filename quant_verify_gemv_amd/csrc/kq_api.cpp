@@ -129,6 +129,25 @@ kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wa
 
 static inline bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+size_t kq_tiled_bytes(int64_t n, int64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  return (size_t)cdiv(n, 16) * (size_t)(k / kQK) * (size_t)kTileBlockBytes;
+}
+
+kq_status kq_tile_weights(const void *w_q4k, int64_t n, int64_t k, void *w_tiled, size_t tiled_bytes,
+                          void *stream) {
+  if (!w_q4k || !w_tiled) return KQ_ERR_NULL;
+  if (!shape_ok(n, k)) return KQ_ERR_SHAPE;
+  if (!al(w_q4k, 16) || !al(w_tiled, 16)) return KQ_ERR_ALIGN;
+  const size_t need = kq_tiled_bytes(n, k);
+  if (tiled_bytes < need) return KQ_ERR_WORKSPACE;
+  const uintptr_t a0 = (uintptr_t)w_q4k, a1 = a0 + (uintptr_t)(n * (k / kQK) * kBlockBytes);
+  const uintptr_t b0 = (uintptr_t)w_tiled, b1 = b0 + (uintptr_t)need;
+  if (a0 < b1 && b0 < a1) return KQ_ERR_SHAPE;  // buffers overlap
+  if (launch_tile((const uint8_t *)w_q4k, n, k, (uint8_t *)w_tiled, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
 kq_status kq_workspace_init(void *workspace, size_t bytes, void *stream) {
   if (!workspace) return KQ_ERR_NULL;
   if (!al(workspace, 256)) return KQ_ERR_ALIGN;
@@ -149,11 +168,12 @@ kq_status kq_stage_rows(const float *x, int m, int64_t k, void *staged, size_t s
 
 // Shared validation + launch of the main kernel on staged activations for
 // `count` matrices of the same shape (verify: count == 1).
-static kq_status run(const void *const *w, int count, int64_t n, int64_t k, const void *staged,
-                     int m, float *const *logits, bool verify, const int32_t *draft_host,
-                     int32_t *argmax, int32_t *accept_out, void *scratch, size_t scratch_bytes,
-                     const float *x_to_stage, void *stream) {
+static kq_status run(const void *const *w, int layout, int count, int64_t n, int64_t k,
+                     const void *staged, int m, float *const *logits, bool verify,
+                     const int32_t *draft_host, int32_t *argmax, int32_t *accept_out, void *scratch,
+                     size_t scratch_bytes, const float *x_to_stage, void *stream) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
+  if (layout != KQ_LAYOUT_ROWS && layout != KQ_LAYOUT_TILED16) return KQ_ERR_SHAPE;
   if (count < 1 || count > kMaxGroup || (verify && count != 1)) return KQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i) {
     if (!w[i]) return KQ_ERR_NULL;
@@ -183,6 +203,8 @@ static kq_status run(const void *const *w, int count, int64_t n, int64_t k, cons
   a.n = n;
   a.k = k;
   a.row_bytes = (k / kQK) * kBlockBytes;
+  a.layout = layout;
+  a.n_tiles = cdiv(n, 16);
   a.m = m;
   a.staged = (const uint8_t *)staged;
   uint8_t *sc = (uint8_t *)scratch;
@@ -204,25 +226,25 @@ static kq_status run(const void *const *w, int count, int64_t n, int64_t k, cons
   return KQ_OK;
 }
 
-kq_status kq_gemv_staged(const void *w_q4k, int64_t n, int64_t k, const void *staged, int m,
+kq_status kq_gemv_staged(const void *w_q4k, int layout, int64_t n, int64_t k, const void *staged, int m,
                          float *logits, void *scratch, size_t scratch_bytes, void *stream) {
-  return run(&w_q4k, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, scratch,
+  return run(&w_q4k, layout, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, scratch,
              scratch_bytes, nullptr, stream);
 }
 
-kq_status kq_gemv_staged_group(const void *const *w_q4k, int count, int64_t n, int64_t k,
+kq_status kq_gemv_staged_group(const void *const *w_q4k, int layout, int count, int64_t n, int64_t k,
                                const void *staged, int m, float *const *logits, void *scratch,
                                size_t scratch_bytes, void *stream) {
   if (!w_q4k || !logits) return KQ_ERR_NULL;
-  return run(w_q4k, count, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch,
+  return run(w_q4k, layout, count, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch,
              scratch_bytes, nullptr, stream);
 }
 
-kq_status kq_verify_staged(const void *w_q4k, int64_t n, int64_t k, const void *staged, int m,
+kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k, const void *staged, int m,
                            const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
                            float *logits_or_null, void *scratch, size_t scratch_bytes,
                            void *stream) {
-  return run(&w_q4k, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out,
+  return run(&w_q4k, layout, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out,
              scratch, scratch_bytes, nullptr, stream);
 }
 
@@ -247,8 +269,8 @@ kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k, const float *x, 
   size_t sb;
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
-  return run(&w_q4k, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, scratch, sb, x,
-             stream);
+  return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr,
+             scratch, sb, x, stream);
 }
 
 kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
@@ -261,8 +283,8 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const
   size_t sb;
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
-  return run(&w_q4k, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out,
-             scratch, sb, x, stream);
+  return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax,
+             accept_out, scratch, sb, x, stream);
 }
 
 }  // extern "C"

@@ -4,12 +4,21 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include "kq.h"
+
 namespace kq {
 
 constexpr int64_t kQK = 256;          // weights per Q4_K super-block
 constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // verify rows per call (block size of the draft)
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
+
+// Tiled weight layout (see kq_tile_weights in kq.h): 2,304-byte records of
+// one block of one 16-row tile: headers, then the two quant halves in lane
+// order.
+constexpr int64_t kTileBlockBytes = 16 * kBlockBytes;  // 2,304
+constexpr int64_t kTileQ0 = 256;
+constexpr int64_t kTileQ1 = 1280;
 
 // Staged activations, one record per 256-column block (each row scaled by a
 // power of two 2^e chosen from that row's largest magnitude in the block):
@@ -55,6 +64,8 @@ struct GemvLaunch {
   float *logits[kMaxGroup];  // entries may be null in verify mode
   int64_t n, k, row_bytes;
   int m;
+  int layout;       // KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16
+  int64_t n_tiles;  // ceil(n / 16)
   const uint8_t *staged;
   float *partials;
   unsigned *done;
@@ -76,5 +87,6 @@ int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ze
                  int64_t n_zero_words, void *stream);
 int launch_gemv(const GemvLaunch &a, void *stream);
 int launch_fill(unsigned *p, int64_t n_words, void *stream);
+int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
 
 }  // namespace kq

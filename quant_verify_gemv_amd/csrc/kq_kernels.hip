@@ -304,23 +304,40 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
   int64_t uw = u0;
   int gw = (int)(u0 / KB), bw = (int)(u0 % KB);
   const uint8_t *rowp[T];
+  // Weight addressing, one code path for both layouts: the lane's bytes of
+  // block b of tile t sit at rowp[t] + b * block_stride + {off_h, off_0,
+  // off_1}. Row-major (llama.cpp): rowp = the lane's row (clamped to the
+  // last row), stride 144, offsets {0, 16 + 16kg, 80 + 16kg}. Tiled: rowp =
+  // the 16-row tile's record, stride = tiles * 2,304, offsets {16 ln,
+  // 256 + 16 lane, 1,280 + 16 lane}.
+  const bool tiled = a.layout == KQ_LAYOUT_TILED16;
+  const int off_h = tiled ? 16 * ln : 0;
+  const int off_0 = tiled ? (int)kTileQ0 + 16 * lane : 16 + 16 * kg;
+  const int off_1 = tiled ? (int)kTileQ1 + 16 * lane : 80 + 16 * kg;
+  const int64_t block_stride = tiled ? a.n_tiles * kTileBlockBytes : kBlockBytes;
   auto set_rowp = [&]() {
     int mat;
     const int64_t r0 = group_row0(gw, mat);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int64_t row = r0 + tile_row(t);
-      rowp[t] = a.w[mat] + (row < N ? row : N - 1) * a.row_bytes;
+      if (tiled) {
+        int64_t ti = (r0 + (t * W + wave) * 16) / 16;
+        ti = ti < a.n_tiles ? ti : a.n_tiles - 1;
+        rowp[t] = a.w[mat] + ti * kTileBlockBytes;
+      } else {
+        const int64_t row = r0 + tile_row(t);
+        rowp[t] = a.w[mat] + (row < N ? row : N - 1) * a.row_bytes;
+      }
     }
   };
   set_rowp();
   auto load_w = [&](WTile(&w)[T]) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const uint8_t *q = rowp[t] + (int64_t)bw * kBlockBytes;
-      w[t].hdr = ld16(q);
-      w[t].q0 = ld16(q + 16 + 16 * kg);
-      w[t].q1 = ld16(q + 80 + 16 * kg);
+      const uint8_t *q = rowp[t] + (int64_t)bw * block_stride;
+      w[t].hdr = ld16(q + off_h);
+      w[t].q0 = ld16(q + off_0);
+      w[t].q1 = ld16(q + off_1);
     }
     if (uw < u_last) {
       ++uw;
@@ -678,6 +695,49 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
 }
 
 // ---------------------------------------------------------------------------
+// Tiled layout. Record (b, t) = block b of 16-row tile t is 2,304 bytes at
+// (b * tiles + t) * 2,304: the 16 headers (row order), then bytes [16kg,
+// 16kg + 16) of the quants of row ln at 256 + 16 (16 kg + ln), then bytes
+// [64 + 16kg, 80 + 16kg) at 1,280 + 16 (16 kg + ln). Rows past n are zero.
+// One thread per 16-byte output chunk.
+__global__ __launch_bounds__(256) void kq_tile_kernel(const uint8_t *__restrict__ w, int64_t n,
+                                                      int64_t kb, int64_t n_tiles,
+                                                      uint8_t *__restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = kb * n_tiles * 144;
+  if (idx >= total) return;
+  const int c = (int)(idx % 144);
+  const int64_t tb = idx / 144;
+  const int64_t ti = tb % n_tiles;
+  const int64_t b = tb / n_tiles;
+  int ln, chunk;
+  if (c < 16) {
+    ln = c;
+    chunk = 0;
+  } else if (c < 80) {
+    ln = (c - 16) & 15;
+    chunk = 1 + ((c - 16) >> 4);
+  } else {
+    ln = (c - 80) & 15;
+    chunk = 5 + ((c - 80) >> 4);
+  }
+  const int64_t row = ti * 16 + ln;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < n) v = ld16(w + (row * kb + b) * kBlockBytes + chunk * 16);
+  *(u32x4 *)(out + idx * 16) = v;
+}
+
+// ---------------------------------------------------------------------------
+
+int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream) {
+  const int64_t kb = k / kQK;
+  const int64_t n_tiles = (n + 15) / 16;
+  const int64_t total = kb * n_tiles * 144;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(kq_tile_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, n, kb,
+                     n_tiles, out);
+  return (int)hipGetLastError();
+}
 
 int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *zero_words,
                  int64_t n_zero_words, void *stream) {

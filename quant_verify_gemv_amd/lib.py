@@ -20,7 +20,10 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIG
 EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scratch_bytes",
             "kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
             "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
-            "kq_gemv_staged_group")
+            "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights")
+
+LAYOUT_ROWS = 0      # llama.cpp row-major blocks
+LAYOUT_TILED16 = 1   # kq_tile_weights output
 
 _lib = None
 
@@ -52,14 +55,18 @@ def load() -> ctypes.CDLL:
     lib.kq_gemv_rows.argtypes = [P, I64, I64, P, I32, P, P, SZ, P]
     lib.kq_verify_argmax_accept.argtypes = [P, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_stage_rows.argtypes = [P, I32, I64, P, SZ, P]
-    lib.kq_gemv_staged.argtypes = [P, I64, I64, P, I32, P, P, SZ, P]
-    lib.kq_verify_staged.argtypes = [P, I64, I64, P, I32, P, P, P, P, P, SZ, P]
+    lib.kq_gemv_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, SZ, P]
+    lib.kq_verify_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P, P]  # int*, int*, int*, int64_t*
     lib.kq_group_scratch_bytes.argtypes = [I64, I64, I32]
     lib.kq_group_scratch_bytes.restype = SZ
-    lib.kq_gemv_staged_group.argtypes = [P, I32, I64, I64, P, I32, P, P, SZ, P]
+    lib.kq_gemv_staged_group.argtypes = [P, I32, I32, I64, I64, P, I32, P, P, SZ, P]
+    lib.kq_tiled_bytes.argtypes = [I64, I64]
+    lib.kq_tiled_bytes.restype = SZ
+    lib.kq_tile_weights.argtypes = [P, I64, I64, P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
-                 "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group"):
+                 "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
+                 "kq_tile_weights"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -88,6 +95,10 @@ def scratch_bytes(n: int, k: int) -> int:
 
 def group_scratch_bytes(n: int, k: int, count: int) -> int:
     return int(load().kq_group_scratch_bytes(n, k, count))
+
+
+def tiled_bytes(n: int, k: int) -> int:
+    return int(load().kq_tiled_bytes(n, k))
 
 
 def launch_geometry(n: int, k: int) -> Tuple[int, int, int, int]:
@@ -208,11 +219,22 @@ def new_scratch(n: int, k: int, device):
     return alloc_workspace(scratch_bytes(n, k), device)
 
 
-def gemv_staged(w, n: int, k: int, staged, m: int, scratch, logits=None, stream=None):
+def tile_weights(w, n: int, k: int, out=None, stream=None):
+    """The KQ_LAYOUT_TILED16 copy of a Q4_K matrix (uint8 device tensor)."""
+    torch = _torch()
+    nb = tiled_bytes(n, k)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    _check(load().kq_tile_weights(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(out, "out", torch.uint8),
+                                  out.numel(), _stream_handle(stream)), "kq_tile_weights")
+    return out
+
+
+def gemv_staged(w, n: int, k: int, staged, m: int, scratch, logits=None, stream=None, layout=LAYOUT_ROWS):
     torch = _torch()
     if logits is None:
         logits = torch.empty((m, n), dtype=torch.float32, device=w.device)
-    _check(load().kq_gemv_staged(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(staged, "staged"), m,
+    _check(load().kq_gemv_staged(_dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"), m,
                                  _dev_ptr(logits, "logits", torch.float32), _dev_ptr(scratch, "scratch"),
                                  scratch.numel(), _stream_handle(stream)), "kq_gemv_staged")
     return logits
@@ -223,7 +245,8 @@ def new_group_scratch(n: int, k: int, count: int, device):
     return alloc_workspace(group_scratch_bytes(n, k, count), device)
 
 
-def gemv_staged_group(ws, n: int, k: int, staged, m: int, scratch, logits=None, stream=None):
+def gemv_staged_group(ws, n: int, k: int, staged, m: int, scratch, logits=None, stream=None,
+                      layout=LAYOUT_ROWS):
     """One launch for several same-shape matrices sharing staged rows."""
     torch = _torch()
     count = len(ws)
@@ -231,14 +254,14 @@ def gemv_staged_group(ws, n: int, k: int, staged, m: int, scratch, logits=None, 
         logits = [torch.empty((m, n), dtype=torch.float32, device=ws[0].device) for _ in range(count)]
     wp = (ctypes.c_void_p * count)(*[_dev_ptr(w, "w", torch.uint8) for w in ws])
     lp = (ctypes.c_void_p * count)(*[_dev_ptr(l, "logits", torch.float32) for l in logits])
-    _check(load().kq_gemv_staged_group(wp, count, n, k, _dev_ptr(staged, "staged"), m, lp,
+    _check(load().kq_gemv_staged_group(wp, layout, count, n, k, _dev_ptr(staged, "staged"), m, lp,
                                        _dev_ptr(scratch, "scratch"), scratch.numel(),
                                        _stream_handle(stream)), "kq_gemv_staged_group")
     return logits
 
 
 def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scratch, want_logits=False,
-                  stream=None, out=None):
+                  stream=None, out=None, layout=LAYOUT_ROWS):
     torch = _torch()
     if len(draft) != m - 1:
         raise ValueError(f"need m-1 = {m - 1} draft tokens, got {len(draft)}")
@@ -250,7 +273,7 @@ def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scrat
     else:
         am, acc, lg = out
     _check(load().kq_verify_staged(
-        _dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(staged, "staged"), m, dr,
+        _dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"), m, dr,
         _dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
         _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
         _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_verify_staged")

@@ -115,10 +115,13 @@ def test_staged_argument_errors():
     assert lib.kq_stage_rows(FAKE, 4, 1024, FAKE + 16, 1 << 20, None) == ALIGN
     assert lib.kq_stage_rows(FAKE, 4, 1024, FAKE, 100, None) == WS
     sb = kq.scratch_bytes(512, 1024)
-    assert lib.kq_gemv_staged(FAKE, 512, 1024, None, 4, FAKE, FAKE, sb, None) == NULL
-    assert lib.kq_gemv_staged(FAKE, 512, 1024, FAKE, 4, FAKE, FAKE, sb - 1, None) == WS
+    assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, None, 4, FAKE, FAKE, sb, None) == NULL
+    assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, FAKE, 4, FAKE, FAKE, sb - 1, None) == WS
+    assert lib.kq_gemv_staged(FAKE, 2, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
+    assert lib.kq_gemv_staged(FAKE, -1, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
     d = (ctypes.c_int32 * 3)(0, 1, 600)
-    assert lib.kq_verify_staged(FAKE, 512, 1024, FAKE, 4, d, FAKE, FAKE, None, FAKE, sb, None) == TOKEN
+    assert lib.kq_verify_staged(FAKE, 0, 512, 1024, FAKE, 4, d, FAKE, FAKE, None, FAKE, sb, None) == TOKEN
+    assert lib.kq_verify_staged(FAKE, 1, 512, 1024, FAKE, 4, d, FAKE, FAKE, None, FAKE, sb, None) == TOKEN
     assert lib.kq_workspace_init(None, 256, None) == NULL
     assert lib.kq_workspace_init(FAKE + 4, 256, None) == ALIGN
     assert lib.kq_workspace_init(FAKE, 8, None) == WS
@@ -133,12 +136,34 @@ def test_grouped_argument_errors():
     wp = (ctypes.c_void_p * 3)(FAKE, FAKE + 0x100000, FAKE + 0x200000)
     lp = (ctypes.c_void_p * 3)(FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000)
     call = lib.kq_gemv_staged_group
-    assert call(wp, 0, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
-    assert call(wp, 9, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
-    assert call(wp, 3, n, 100, FAKE, m, lp, FAKE, sb, None) == SHAPE
-    assert call(wp, 3, n, k, FAKE, m, lp, FAKE, sb - 1, None) == WS
-    assert call(None, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
-    bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
-    assert call(bad, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
-    mis = (ctypes.c_void_p * 3)(FAKE, FAKE + 8, FAKE)
-    assert call(mis, 3, n, k, FAKE, m, lp, FAKE, sb, None) == ALIGN
+    for layout in (0, 1):
+        assert call(wp, layout, 0, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
+        assert call(wp, layout, 9, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
+        assert call(wp, layout, 3, n, 100, FAKE, m, lp, FAKE, sb, None) == SHAPE
+        assert call(wp, layout, 3, n, k, FAKE, m, lp, FAKE, sb - 1, None) == WS
+        assert call(None, layout, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
+        bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+        assert call(bad, layout, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
+        mis = (ctypes.c_void_p * 3)(FAKE, FAKE + 8, FAKE)
+        assert call(mis, layout, 3, n, k, FAKE, m, lp, FAKE, sb, None) == ALIGN
+    assert call(wp, 7, 3, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
+
+
+def test_tiling_sizes_and_argument_errors():
+    lib = kq.load()
+    assert kq.tiled_bytes(512, 1024) == 32 * 4 * 2304
+    assert kq.tiled_bytes(17, 256) == 2 * 1 * 2304       # rows padded to 16
+    assert kq.tiled_bytes(16, 100) == 0
+    n, k = 1000, 2048
+    nb = kq.tiled_bytes(n, k)
+    rowmajor = n * (k // 256) * 144
+    assert nb == 63 * 8 * 2304 and nb >= rowmajor
+    out = FAKE + 0x40000000
+    tw = lib.kq_tile_weights
+    assert tw(None, n, k, out, nb, None) == NULL
+    assert tw(FAKE, n, k, None, nb, None) == NULL
+    assert tw(FAKE, n, 100, out, nb, None) == SHAPE
+    assert tw(FAKE + 8, n, k, out, nb, None) == ALIGN
+    assert tw(FAKE, n, k, out + 4, nb, None) == ALIGN
+    assert tw(FAKE, n, k, out, nb - 1, None) == WS
+    assert tw(FAKE, n, k, FAKE + 4096, nb, None) == SHAPE    # overlapping buffers

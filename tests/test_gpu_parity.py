@@ -247,3 +247,73 @@ def test_grouped_launch(kq):
             assert np.array_equal(G, again[i].cpu().numpy())
             L, A = oracle.gemv_rows(ws[i], k, x[:mm], rows=rows)
             check_logits(G[:, rows], L, A, what=f"group member {i} m={mm}")
+
+
+def tile_reference(w_bytes, n, k):
+    """The tiled layout written out from its definition in kq.h, in numpy:
+    record (b, t) of 2,304 bytes at (b * tiles + t) * 2,304 holds the 16
+    headers of tile t's rows, then quant bytes [16g, 16g+16) of row r at
+    256 + 16 (16g + r), then quant bytes [64+16g, 80+16g) at 1,280 + ..."""
+    kb, nt = k // 256, -(-n // 16)
+    pad = np.zeros((nt * 16, kb, 144), np.uint8)
+    pad[:n] = w_bytes.reshape(n, kb, 144)
+    t = pad.reshape(nt, 16, kb, 144).transpose(2, 0, 1, 3)  # [b][tile][row][144]
+    out = np.zeros((kb, nt, 2304), np.uint8)
+    out[:, :, :256] = t[:, :, :, :16].reshape(kb, nt, 256)
+    for half, base in ((0, 256), (1, 1280)):
+        q = t[:, :, :, 16 + 64 * half:80 + 64 * half].reshape(kb, nt, 16, 4, 16)  # [b][tile][row][g][16]
+        out[:, :, base:base + 1024] = q.transpose(0, 1, 3, 2, 4).reshape(kb, nt, 1024)
+    return out.reshape(-1)
+
+
+def test_tile_weights_matches_layout_definition(kq):
+    for n, k in [(37, 512), (16, 256), (1000, 2304)]:
+        w = synthetic.q4k_matrix(n, k, 90 + n)
+        got = kq.tile_weights(to_dev(w), n, k).cpu().numpy()
+        assert got.size == kq.tiled_bytes(n, k)
+        assert np.array_equal(got, tile_reference(w, n, k)), (n, k)
+
+
+@pytest.mark.parametrize("n,k,m", [(512, 1024, 4), (17, 256, 16), (129, 1280, 16), (1000, 2304, 7),
+                                   (6656, 6656, 16), (2048, 9216, 16), (6656, 17920, 1)])
+def test_tiled_layout_bitwise_equal_to_rows(kq, n, k, m):
+    log(f"tiled vs rows: n={n} k={k} m={m}")
+    w = synthetic.q4k_matrix(n, k, 100 + n + k)
+    x = synthetic.activations(m, k, 101)
+    w_d = to_dev(w)
+    wt = kq.tile_weights(w_d, n, k)
+    st = kq.stage_rows(to_dev(x))
+    sc = kq.new_scratch(n, k, DEV)
+    a = kq.gemv_staged(w_d, n, k, st, m, sc).cpu().numpy()
+    b = kq.gemv_staged(wt, n, k, st, m, sc, layout=kq.LAYOUT_TILED16).cpu().numpy()
+    assert np.array_equal(a, b)
+    rows = np.unique(np.array([0, 1, 15, 16, n // 2, n - 1]))
+    L, A = oracle.gemv_rows(w, k, x, rows=rows)
+    check_logits(b[:, rows], L, A, what=f"tiled n={n} k={k}")
+
+
+def test_tiled_lm_head_verify_and_group(kq):
+    h = synthetic.LM_HEAD
+    n, k = h["n"], h["k"]
+    w = synthetic.q4k_matrix(n, k, h["seed"])
+    x = synthetic.activations(16, k, 7)
+    w_d = to_dev(w)
+    wt = kq.tile_weights(w_d, n, k)
+    st = kq.stage_rows(to_dev(x))
+    sc = kq.new_scratch(n, k, DEV)
+    d = [int(t) for t in np.random.default_rng(3).integers(0, n, 15)]
+    r = kq.verify_staged(w_d, n, k, st, 16, d, sc, want_logits=True)
+    t = kq.verify_staged(wt, n, k, st, 16, d, sc, want_logits=True, layout=kq.LAYOUT_TILED16)
+    for u, v in zip(r, t):
+        assert np.array_equal(u.cpu().numpy(), v.cpu().numpy())
+    del w_d, wt
+    n2, k2, count = 2000, 6656, 3
+    ws = [synthetic.q4k_matrix(n2, k2, 80 + i) for i in range(count)]
+    ws_d = [to_dev(v) for v in ws]
+    wts = [kq.tile_weights(v, n2, k2) for v in ws_d]
+    st2 = kq.stage_rows(to_dev(synthetic.activations(16, k2, 85)))
+    gs = kq.new_group_scratch(n2, k2, count, DEV)
+    a = kq.gemv_staged_group(ws_d, n2, k2, st2, 16, gs)
+    b = kq.gemv_staged_group(wts, n2, k2, st2, 16, gs, layout=kq.LAYOUT_TILED16)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.cpu().numpy(), v.cpu().numpy())
