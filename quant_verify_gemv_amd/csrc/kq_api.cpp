@@ -28,7 +28,7 @@ static bool shape_ok(int64_t n, int64_t k) {
 static constexpr int64_t kCUs = 256;
 
 struct Shape {
-  int waves, tpw, per_cu, bi;
+  int waves, tpw, per_cu, bi, depth;
 };
 
 static Shape pick_shape(int64_t n, int count) {
@@ -36,13 +36,16 @@ static Shape pick_shape(int64_t n, int count) {
 #ifndef KQ_GEOM_BI
 #define KQ_GEOM_BI 1
 #endif
+#ifndef KQ_GEOM_DEPTH
+#define KQ_GEOM_DEPTH 4
+#endif
   (void)n;
   (void)count;
-  return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI};
+  return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI, KQ_GEOM_DEPTH};
 #endif
   const int64_t rows = n * count;
-  if (rows >= 131072) return {8, 2, 1, 4};
-  return {8, 1, 1, 4};
+  if (rows >= 131072) return {8, 2, 1, 4, 4};
+  return {8, 1, 1, 4, 4};
 }
 
 Geometry geometry(int64_t n, int64_t k, int count) {
@@ -52,6 +55,7 @@ Geometry geometry(int64_t n, int64_t k, int count) {
   g.waves = sh.waves;
   g.tpw = sh.tpw;
   g.bi = sh.bi;
+  g.depth = sh.depth;
   g.rows = 16 * sh.waves * sh.tpw;
   g.n_wg_per = (int)cdiv(n, g.rows);
   g.n_groups = g.count * g.n_wg_per;
@@ -69,9 +73,8 @@ Geometry geometry(int64_t n, int64_t k, int count) {
 ScratchLayout scratch_layout(int64_t n, int64_t k, int count) {
   const Geometry g = geometry(n, k, count);
   ScratchLayout s;
-  s.cnt_off = 256;
-  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * (size_t)g.n_groups);
-  s.ctrl_bytes = s.keys_off;  // words that must be zero between calls
+  s.cnt_off = kCntOff;
+  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * kCntStride * (size_t)g.n_groups);
   s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxRows * (size_t)g.n_wg);
   s.total = s.part_off + align256(sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * (size_t)g.rows);
   return s;
@@ -218,8 +221,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   a.verify = verify ? 1 : 0;
   a.g = geometry(n, k, count);
   if (x_to_stage) {
-    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch,
-                     (int64_t)(sl.ctrl_bytes / 4), stream))
+    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, a.g.n_groups, stream))
       return KQ_ERR_LAUNCH;
   }
   if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;

@@ -33,9 +33,13 @@ constexpr int64_t kStageBytes = 16384 + 512 + 64;  // 16,960 B per block (16-B a
 // Scratch area of the main kernel (control words zero between calls; every
 // launch leaves them zero again):
 //   [0, 256)   done counter (u32)
-//   cnt_off    per-row-group arrival counters [n_groups] (u32)
+//   cnt_off    per-row-group arrival counters [n_groups], one u32 per
+//              128-byte line (kCntStride words apart) so that the atomics of
+//              different groups do not queue on one line
 //   keys_off   per-workgroup argmax keys [n_wg][16] (u64)
 //   part_off   partial sums [n_wg][2][16][rows per group] fp32
+constexpr int64_t kCntOff = 256;
+constexpr int kCntStride = 32;
 
 // Work decomposition. A row group is 16 * waves * tpw consecutive output rows
 // of one matrix; a unit is one row group times one 256-column block. The
@@ -47,6 +51,7 @@ struct Geometry {
   int waves;      // waves per workgroup (4 or 8)
   int tpw;        // 16-row tiles per wave (1 or 2)
   int bi;         // units between workgroup barriers (1, 2 or 4; LDS ring of 2 bi blocks)
+  int depth;      // weight register sets (prefetch depth + 1: 4 or 8)
   int rows;       // rows per row group = 16 * waves * tpw
   int n_wg_per;   // row groups per matrix
   int n_groups;   // row groups in total = count * n_wg_per
@@ -56,7 +61,7 @@ struct Geometry {
 };
 
 struct ScratchLayout {
-  size_t cnt_off, keys_off, part_off, ctrl_bytes, total;
+  size_t cnt_off, keys_off, part_off, total;
 };
 
 struct GemvLaunch {
@@ -83,8 +88,10 @@ Geometry geometry(int64_t n, int64_t k, int count);
 ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
 
 // Kernel launches (return a hipError_t as int).
-int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *zero_words,
-                 int64_t n_zero_words, void *stream);
+// kq_stage_kernel also zeroes the control words of `ctrl` (a scratch area
+// laid out as above for n_groups row groups) when ctrl is not null.
+int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ctrl, int64_t n_groups,
+                 void *stream);
 int launch_gemv(const GemvLaunch &a, void *stream);
 int launch_fill(unsigned *p, int64_t n_words, void *stream);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);

@@ -86,6 +86,18 @@ __device__ __forceinline__ float ld_dev(const float *p) {
 __device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte versions for the partial sums: buffer instructions with the same
+// cache policy (sc1) as the agent-scope atomic accesses above
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ void st_dev16(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ f32x4 ld_dev16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
+}
 // wait until this thread's global stores have completed, then barrier
 __device__ __forceinline__ void stores_done_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -93,9 +105,10 @@ __device__ __forceinline__ void stores_done_barrier() {
   __syncthreads();
 }
 
-// Max of a 64-bit key over the lanes l ^ 1, ..., l ^ (width - 1).
-__device__ __forceinline__ unsigned long long lanes_max(unsigned long long v, int width) {
-  for (int off = 1; off < width; off <<= 1) {
+// Max of a 64-bit key over the lanes l ^ off for off = first, 2 first, ...
+// below width (first = 1: the aligned group of `width` lanes).
+__device__ __forceinline__ unsigned long long lanes_max(unsigned long long v, int width, int first = 1) {
+  for (int off = first; off < width; off <<= 1) {
     const unsigned long long o = __shfl_xor(v, off, 64);
     v = o > v ? o : v;
   }
@@ -137,16 +150,17 @@ __device__ __forceinline__ constexpr int perm8(int i) { return (i & 4) | ((i & 1
 // and the 16 columns [16c, 16c+16) of the block, c = t%16.
 __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__ x, int m_rows,
                                                        int64_t k, uint8_t *__restrict__ staged,
-                                                       unsigned *__restrict__ zero_words,
-                                                       int64_t n_zero_words) {
+                                                       unsigned *__restrict__ ctrl,
+                                                       int64_t n_groups) {
   const int t = threadIdx.x;
   const int m = t >> 4;
   const int c = t & 15;
   const int64_t b = blockIdx.x;
   const bool active = m < m_rows;  // rows >= m_rows are staged as zeros
 
-  if (zero_words && b == 0) {
-    for (int64_t i = t; i < n_zero_words; i += 256) zero_words[i] = 0u;
+  if (ctrl && b == 0) {
+    if (t == 0) ctrl[0] = 0u;
+    for (int64_t i = t; i < n_groups; i += 256) ctrl[kCntOff / 4 + i * kCntStride] = 0u;
   }
 
   float v[16];
@@ -241,8 +255,28 @@ struct WTile {
   u32x4 hdr, q0, q1;
 };
 
-template <int W, int T, int BI>
-__global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_kernel(GemvLaunch a) {
+constexpr int lcm_int(int a, int b) {
+  int x = a, y = b;
+  while (y) {
+    const int r = x % y;
+    x = y;
+    y = r;
+  }
+  return a / x * b;
+}
+
+template <int W, int T, int BI, int D>
+__global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv_kernel(GemvLaunch a) {
+  // D weight register sets: the weights of unit i + D - 1 are loaded while
+  // unit i computes. The activations of unit i + BI are stored to LDS in
+  // step i from registers loaded kXL steps earlier: loads complete in issue
+  // order, so waiting for them waits only for weights issued before step
+  // i - kXL, which step i needs anyway when kXL >= D - 2. Four-wave
+  // workgroups stage twice the activation chunks per thread and keep one
+  // set in flight. The unit loop is unrolled kU = lcm(D, BI, kXL + 1) times
+  // so that every register set index and every interval position is static.
+  constexpr int kXL = (W == 8 && T == 1) ? 3 : 1;
+  constexpr int kU = lcm_int(lcm_int(D, BI), kXL + 1);
   constexpr int kNth = 64 * W;
   constexpr int kRows = 16 * T * W;
   constexpr int kXj = (int)(kXaBytes / 16) / kNth;                 // XA chunks per thread
@@ -253,7 +287,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
   // once every BI units: between two barriers the waves read BI buffers and
   // fill the other BI.
   constexpr int kNB = 2 * BI;
-  static_assert(BI == 1 || BI == 2 || BI == 4, "barrier interval divides the 4-unit unroll");
+  static_assert(BI == 1 || BI == 2 || BI == 4, "barrier interval");
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kNB][kStageBytes];
   __shared__ unsigned long long s_keys[kMaxRows];
   __shared__ int s_flag;
@@ -351,25 +385,30 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
   int64_t ux = u0;
   int bx = (int)(u0 % KB);
   const int xe_idx = tid < kXe ? tid : kXe - 1;
-  auto load_x = [&](u32x4(&xr)[kXj], u32x4 &xe) {
+  struct XRegs {
+    u32x4 a[kXj], e;
+  };
+  auto load_x = [&](XRegs &x) {
     const uint8_t *src = a.staged + (int64_t)bx * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < kXj; ++j) xr[j] = ld16(src + (tid + kNth * j) * 16);
-    xe = ld16(src + kXaBytes + xe_idx * 16);
+    for (int j = 0; j < kXj; ++j) x.a[j] = ld16(src + (tid + kNth * j) * 16);
+    x.e = ld16(src + kXaBytes + xe_idx * 16);
     if (ux < u_last) {
       ++ux;
       if (++bx == KB) bx = 0;
     }
   };
-  auto store_x = [&](int buf, const u32x4(&xr)[kXj], const u32x4 &xe) {
+  auto store_x = [&](int buf, const XRegs &x) {
 #pragma unroll
-    for (int j = 0; j < kXj; ++j) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = xr[j];
-    if (tid < kXe) *(u32x4 *)(&s_x[buf][kXaBytes + tid * 16]) = xe;
+    for (int j = 0; j < kXj; ++j) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
+    if (tid < kXe) *(u32x4 *)(&s_x[buf][kXaBytes + tid * 16]) = x.e;
   };
 
   // finished rows of a whole row group: logits and/or the argmax keys. The
   // keys are reduced over the wave's tiles and its 16 rows per lane group
-  // first, so each wave posts one LDS atomic per activation row.
+  // into a running maximum per activation row 4kg + r (wave_key[r], held
+  // by every lane of the group) that goes to LDS after the loop.
+  unsigned long long wave_key[4] = {0ull, 0ull, 0ull, 0ull};
   auto write_rows = [&](int g, const f32x4(&v)[T]) {
     int mat;
     const int64_t r0 = group_row0(g, mat);
@@ -398,28 +437,27 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
           best = key > best ? key : best;
         }
         best = lanes_max(best, 16);
-        const int m = 4 * kg + r;
-        if (ln == 0 && m < M) atomicMax(&s_keys[m], best);
+        wave_key[r] = best > wave_key[r] ? best : wave_key[r];
       }
     }
   };
 
-  // Activations first: loads complete in issue order, so the first LDS
-  // stores then wait for the first BI activation blocks only, not for the
-  // three blocks of weights behind them. After the prologue, buffers
-  // 0..BI-1 hold units 0..BI-1 and xr1 holds unit BI.
-  u32x4 xr0[kXj], xr1[kXj], xe0, xe1;
-  WTile w0[T], w1[T], w2[T], w3[T];
+  // Prologue. Activations first (loads complete in issue order, so the
+  // first LDS stores wait for the first BI activation blocks only): units
+  // 0..BI-1 go to buffers 0..BI-1, units BI..BI+kXL-1 stay in registers
+  // (set u % (kXL + 1)); then the first D - 1 weight sets.
+  XRegs xr[kXL + 1];
+  WTile wr[D][T];
   {
-    u32x4 xp[BI][kXj], xpe[BI];
+    XRegs xp[BI];
 #pragma unroll
-    for (int j = 0; j < BI; ++j) load_x(xp[j], xpe[j]);
-    load_x(xr1, xe1);
-    load_w(w0);
-    load_w(w1);
-    load_w(w2);
+    for (int j = 0; j < BI; ++j) load_x(xp[j]);
 #pragma unroll
-    for (int j = 0; j < BI; ++j) store_x(j, xp[j], xpe[j]);
+    for (int q = 0; q < kXL; ++q) load_x(xr[(BI + q) % (kXL + 1)]);
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) load_w(wr[d]);
+#pragma unroll
+    for (int j = 0; j < BI; ++j) store_x(j, xp[j]);
   }
   __syncthreads();
 
@@ -427,14 +465,14 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
   int gc = g_first, bc = (int)(u0 % KB), seg0 = bc;
   int have_first = 0;
 
-  // One unit: prefetch the activations of unit i+BI+1 (into xl) and the
-  // weights of unit i+3 (into pf), contract the weights in `cur` with the
+  // One unit: prefetch the activations of unit i+BI+kXL (into xl) and the
+  // weights of unit i+D-1 (into pf), contract the weights in `cur` with the
   // activations in LDS buffer i % kNB, then move the activations of unit
-  // i+BI (loaded one step earlier, in xw) into their buffer; barrier after
-  // every BI-th unit (pos = i % 4).
-  auto step = [&](WTile(&cur)[T], WTile(&pf)[T], u32x4(&xl)[kXj], u32x4 &xel, u32x4(&xw)[kXj],
-                  u32x4 &xew, const int64_t i, const int pos) {
-    load_x(xl, xel);
+  // i+BI (in xs) into their buffer; barrier after every BI-th unit (pos is
+  // the static position within the unrolled iteration).
+  auto step = [&](WTile(&cur)[T], WTile(&pf)[T], XRegs &xl, const XRegs &xs, const int64_t i,
+                  const int pos) {
+    load_x(xl);
     load_w(pf);
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t *xb = s_x[i % kNB];
@@ -534,17 +572,16 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
       bc = 0;
       ++gc;
     }
-    store_x((int)((i + BI) % kNB), xw, xew);
+    store_x((int)((i + BI) % kNB), xs);
     if (pos % BI == BI - 1) __syncthreads();
   };
 
-  // Four units per iteration so the register sets rotate statically; steps
+  // kU units per iteration so the register sets rotate statically; steps
   // past the last unit only keep the loads and barriers in step.
-  for (int64_t i = 0; i < nu; i += 4) {
-    step(w0, w3, xr0, xe0, xr1, xe1, i, 0);
-    step(w1, w0, xr1, xe1, xr0, xe0, i + 1, 1);
-    step(w2, w1, xr0, xe0, xr1, xe1, i + 2, 2);
-    step(w3, w2, xr1, xe1, xr0, xe0, i + 3, 3);
+  for (int64_t i = 0; i < nu; i += kU) {
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      step(wr[j % D], wr[(j + D - 1) % D], xr[(j + BI + kXL) % (kXL + 1)], xr[(j + BI) % (kXL + 1)], i + j, j);
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -554,106 +591,150 @@ __global__ __launch_bounds__(64 * W, (W == 4 && T == 1) ? 3 : 1) void kq_gemv_ke
   // goes to slot 0 (first group) or 1 (last group) of this workgroup; the
   // last contributor of a group to arrive sums all contributors' partials in
   // workgroup order.
+  if (a.verify) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * kg + r;
+      if (ln == 0 && m < M && wave_key[r]) atomicMax(&s_keys[m], wave_key[r]);
+    }
+  }
   const int g_last = (int)(u_last / KB);
   const int last_partial = (g_last != g_first) && (u_last % KB != KB - 1);
-  float *my_part = a.partials + p * 2 * kMaxRows * kRows;
+  // A partial is [row of the group][16 activation rows] fp32: the lane's
+  // four sums (activation rows 4kg..4kg+3 of its output row) are one
+  // 16-byte store.
+  const __amdgpu_buffer_rsrc_t part_rsrc = dev_rsrc(a.partials);
   auto write_partial = [&](int slot, const f32x4(&v)[T]) {
-    float *dst = my_part + slot * kMaxRows * kRows;
+    const unsigned base_off = (unsigned)((p * 2 + slot) * kMaxRows * kRows) * 4u;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (m < M) st_dev(&dst[m * kRows + tile_row(t)], v[t][r]);
-      }
-    }
+    for (int t = 0; t < T; ++t)
+      st_dev16(part_rsrc, base_off + (unsigned)(tile_row(t) * kMaxRows + 4 * kg) * 4u, v[t]);
   };
-  // Sum a row group's partials over its contributors in workgroup order.
-  // Thread tid handles elements tid + j kNth (activation row e / kRows, row
-  // e % kRows of the group; a whole wave shares the activation row), and
-  // issues the loads of eight contributors for all its elements before it
-  // adds any of them.
-  auto reduce_group = [&](int g) {
+  // Sum the partials of one or two row groups over their contributors in
+  // workgroup order, the loads of both groups in flight together. Thread
+  // tid handles the 16-byte chunks c = tid + j kNth of each group (row c / 4
+  // of the group, activation rows 4 (c % 4) .. +3) and issues the loads of
+  // eight contributors per group before it adds any of them.
+  constexpr int kE = kRows * kMaxRows / (4 * kNth);  // chunks per thread
+  constexpr int kC = 8;
+  static_assert(kE * 4 * kNth == kRows * kMaxRows, "chunks must split evenly");
+  struct Contributors {
+    int64_t pf, pl;  // first and last contributing workgroup
+    int pf_slot;     // the first one's slot (the others use slot 0)
+  };
+  auto contributors = [&](int g) {
     const int64_t ufirst = (int64_t)g * KB;
-    const int64_t pf = owner(ufirst), pl = owner(ufirst + KB - 1);
+    Contributors c;
+    c.pf = owner(ufirst);
+    c.pl = owner(ufirst + KB - 1);
     // every contributor after the first starts inside g (slot 0); the first
     // used slot 1 unless its run also starts at the group's first block
-    const int64_t pf_u0 = pf * base + (pf < rem ? pf : rem);
-    const int pf_slot = pf_u0 < ufirst ? 1 : 0;
+    const int64_t pf_u0 = c.pf * base + (c.pf < rem ? c.pf : rem);
+    c.pf_slot = pf_u0 < ufirst ? 1 : 0;
+    return c;
+  };
+  auto load_partials = [&](const Contributors &cb, int64_t c0, f32x4 (&pv)[kE][kC]) {
+    // unconditional loads: contributors past the last one re-read it and
+    // are dropped when summed
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      const int64_t q = cb.pf + c0 + c <= cb.pl ? cb.pf + c0 + c : cb.pl;
+      const int slot = q == cb.pf ? cb.pf_slot : 0;
+      const unsigned src = (unsigned)((q * 2 + slot) * kMaxRows * kRows) * 4u;
+#pragma unroll
+      for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
+    }
+  };
+  auto sum_partials = [&](const Contributors &cb, int64_t c0, const f32x4 (&pv)[kE][kC], f32x4 (&v)[kE]) {
+#pragma unroll
+    for (int c = 0; c < kC; ++c)
+#pragma unroll
+      for (int j = 0; j < kE; ++j)
+        if (cb.pf + c0 + c <= cb.pl) v[j] = c0 + c == 0 ? pv[j][c] : v[j] + pv[j][c];
+  };
+  // logits and argmax keys of a reduced group (elements past M or the
+  // matrix end are dropped)
+  auto finish_group = [&](int g, const f32x4 (&v)[kE]) {
     int mat;
     const int64_t r0 = group_row0(g, mat);
     float *logits = a.logits[mat];
     const int nrows = (int)((N - r0) < kRows ? (N - r0) : kRows);
-    constexpr int kE = kRows * kMaxRows / kNth;
-    constexpr int kC = 8;
-    static_assert(kE * kNth == kRows * kMaxRows, "elements must split evenly");
-    float v[kE];
-#pragma unroll
-    for (int j = 0; j < kE; ++j) v[j] = 0.0f;
-    for (int64_t q0 = pf; q0 <= pl; q0 += kC) {
-      // unconditional loads (contributors past the last one re-read it and
-      // are dropped below; elements past M or the matrix end are dropped
-      // when stored)
-      float pv[kE][kC];
-#pragma unroll
-      for (int c = 0; c < kC; ++c) {
-        const int64_t q = q0 + c <= pl ? q0 + c : pl;
-        const int slot = q == pf ? pf_slot : 0;
-        const float *src = a.partials + (q * 2 + slot) * kMaxRows * kRows;
-#pragma unroll
-        for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev(src + tid + j * kNth);
-      }
-#pragma unroll
-      for (int c = 0; c < kC; ++c)
-#pragma unroll
-        for (int j = 0; j < kE; ++j)
-          if (q0 + c <= pl) v[j] = q0 + c == pf ? pv[j][c] : v[j] + pv[j][c];
-    }
 #pragma unroll
     for (int j = 0; j < kE; ++j) {
-      const int e = tid + j * kNth;
-      const int m = e / kRows, r = e % kRows;
-      const int64_t n = r0 + r;
-      const bool ok = m < M && r < nrows;
-      if (ok && logits) logits[(int64_t)m * N + n] = v[j];
-      if (a.verify) {
-        unsigned long long best = ok ? argmax_key(v[j], (unsigned)n) : 0ull;
-        best = lanes_max(best, 64);
-        if (lane == 0 && m < M) atomicMax(&s_keys[m], best);
+      const int c = tid + j * kNth;
+      const int row = c >> 2, m0 = 4 * (c & 3);
+      const int64_t n = r0 + row;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + r;
+        const bool ok = m < M && row < nrows;
+        if (ok && logits) logits[(int64_t)m * N + n] = v[j][r];
+        if (a.verify) {
+          // max over the wave's 16 rows: the lanes with the same c % 4
+          unsigned long long best = ok ? argmax_key(v[j][r], (unsigned)n) : 0ull;
+          best = lanes_max(best, 64, 4);
+          if (lane < 4 && m < M) atomicMax(&s_keys[m], best);
+        }
       }
     }
+  };
+  auto reduce_groups = [&](int ga, int gb, bool both) {
+    const Contributors ca = contributors(ga);
+    const Contributors cbb = contributors(both ? gb : ga);
+    const int64_t na = ca.pl - ca.pf + 1;
+    const int64_t nb = both ? cbb.pl - cbb.pf + 1 : 0;
+    const int64_t nmax = na > nb ? na : nb;
+    f32x4 va[kE], vb[kE];
+#pragma unroll
+    for (int j = 0; j < kE; ++j) va[j] = vb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t c0 = 0; c0 < nmax; c0 += kC) {
+      f32x4 pa[kE][kC], pb[kE][kC];
+      load_partials(ca, c0, pa);
+      if (both) load_partials(cbb, c0, pb);
+      sum_partials(ca, c0, pa, va);
+      if (both) sum_partials(cbb, c0, pb, vb);
+    }
+    finish_group(ga, va);
+    if (both) finish_group(gb, vb);
   };
 
   if (have_first || last_partial) {
     if (have_first) write_partial(0, acc_first);
     if (last_partial) write_partial(1, acc);
+    // contributor counts of both groups (computed while the stores drain)
+    int64_t c_first = 0, c_last = 0;
+    if (tid == 0) {
+      c_first = owner((int64_t)g_first * KB + KB - 1) - owner((int64_t)g_first * KB) + 1;
+      c_last = owner((int64_t)g_last * KB + KB - 1) - owner((int64_t)g_last * KB) + 1;
+    }
     stores_done_barrier();
     if (tid == 0) {
+      // both arrivals in flight at once; a group this workgroup has no
+      // partial for gets an increment of 0
+      unsigned *cnt_f = a.group_cnt + (int64_t)g_first * kCntStride;
+      unsigned *cnt_l = a.group_cnt + (int64_t)g_last * kCntStride;
+      const unsigned old_f = __hip_atomic_fetch_add(cnt_f, have_first ? 1u : 0u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned old_l = __hip_atomic_fetch_add(cnt_l, last_partial ? 1u : 0u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
       int flags = 0;
-      if (have_first) {
-        const int64_t c = owner((int64_t)g_first * KB + KB - 1) - owner((int64_t)g_first * KB) + 1;
-        const unsigned old =
-            __hip_atomic_fetch_add(&a.group_cnt[g_first], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (unsigned)(c - 1)) {
-          __hip_atomic_store(&a.group_cnt[g_first], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          flags |= 1;
-        }
+      if (have_first && old_f == (unsigned)(c_first - 1)) {
+        __hip_atomic_store(cnt_f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flags |= 1;
       }
-      if (last_partial) {
-        const int64_t c = owner((int64_t)g_last * KB + KB - 1) - owner((int64_t)g_last * KB) + 1;
-        const unsigned old =
-            __hip_atomic_fetch_add(&a.group_cnt[g_last], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (unsigned)(c - 1)) {
-          __hip_atomic_store(&a.group_cnt[g_last], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          flags |= 2;
-        }
+      if (last_partial && old_l == (unsigned)(c_last - 1)) {
+        __hip_atomic_store(cnt_l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flags |= 2;
       }
       s_flag = flags;
     }
     __syncthreads();
     const int flags = s_flag;
-    if (flags & 1) reduce_group(g_first);
-    if (flags & 2) reduce_group(g_last);
+    if (flags == 3) {
+      reduce_groups(g_first, g_last, true);
+    } else if (flags) {
+      reduce_groups(flags == 1 ? g_first : g_last, 0, false);
+    }
   }
 
   if (!a.verify) return;
@@ -739,11 +820,11 @@ int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stre
   return (int)hipGetLastError();
 }
 
-int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *zero_words,
-                 int64_t n_zero_words, void *stream) {
+int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ctrl, int64_t n_groups,
+                 void *stream) {
   const int64_t blocks = k / kQK;
   hipLaunchKernelGGL(kq_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, m,
-                     k, staged, zero_words, n_zero_words);
+                     k, staged, ctrl, n_groups);
   return (int)hipGetLastError();
 }
 
@@ -759,15 +840,19 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream) {
 int launch_gemv(const GemvLaunch &a, void *stream) {
   const dim3 grid((unsigned)a.g.n_wg);
   hipStream_t st = (hipStream_t)stream;
-  switch (a.g.waves * 256 + a.g.tpw * 16 + a.g.bi) {
-    case 4 * 256 + 1 * 16 + 1: hipLaunchKernelGGL((kq_gemv_kernel<4, 1, 1>), grid, dim3(256), 0, st, a); break;
-    case 4 * 256 + 2 * 16 + 1: hipLaunchKernelGGL((kq_gemv_kernel<4, 2, 1>), grid, dim3(256), 0, st, a); break;
-    case 8 * 256 + 1 * 16 + 4: hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4>), grid, dim3(512), 0, st, a); break;
-    case 8 * 256 + 2 * 16 + 4: hipLaunchKernelGGL((kq_gemv_kernel<8, 2, 4>), grid, dim3(512), 0, st, a); break;
-    case 8 * 256 + 1 * 16 + 2: hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 2>), grid, dim3(512), 0, st, a); break;
-    case 8 * 256 + 2 * 16 + 2: hipLaunchKernelGGL((kq_gemv_kernel<8, 2, 2>), grid, dim3(512), 0, st, a); break;
-    case 8 * 256 + 1 * 16 + 1: hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 1>), grid, dim3(512), 0, st, a); break;
-    case 8 * 256 + 2 * 16 + 1: hipLaunchKernelGGL((kq_gemv_kernel<8, 2, 1>), grid, dim3(512), 0, st, a); break;
+  switch (a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
+#define KQ_CASE(W_, T_, BI_, D_)                                                                   \
+  case W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                                                       \
+    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_>), grid, dim3(64 * W_), 0, st, a);          \
+    break;
+    KQ_CASE(8, 2, 4, 4)
+    KQ_CASE(8, 1, 4, 4)
+    KQ_CASE(8, 1, 2, 4)
+    KQ_CASE(8, 2, 2, 4)
+    KQ_CASE(4, 1, 1, 4)
+    KQ_CASE(4, 2, 2, 3)
+    KQ_CASE(4, 2, 1, 3)
+#undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;
   }
   return (int)hipGetLastError();
