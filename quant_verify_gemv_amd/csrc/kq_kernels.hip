@@ -472,6 +472,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // the static position within the unrolled iteration).
   auto step = [&](WTile(&cur)[T], WTile(&pf)[T], XRegs &xl, const XRegs &xs, const int64_t i,
                   const int pos) {
+    // Waves w and w + 4 share a SIMD, and the older one would otherwise
+    // win issue every cycle and reach the barrier first; alternating the
+    // priority each unit keeps the pair in step.
+    if ((wave >> 2) == (pos & 1))
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
     load_x(xl);
     load_w(pf);
     __builtin_amdgcn_sched_barrier(0);
@@ -583,6 +590,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     for (int j = 0; j < kU; ++j)
       step(wr[j % D], wr[(j + D - 1) % D], xr[(j + BI + kXL) % (kXL + 1)], xr[(j + BI) % (kXL + 1)], i + j, j);
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // ---------------------------------------------------------------- epilogue
   // Row groups this workgroup finished only in part: its first (acc_first)
