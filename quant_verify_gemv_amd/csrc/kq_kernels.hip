@@ -324,6 +324,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   if (tid < kMaxRows) s_keys[tid] = 0ull;
 
   const unsigned mask_lo = in_vgpr(0x000F000Fu);
+  // byte-permute selector that puts this lane's two scale bytes 2(kg>>1),
+  // 2(kg>>1)+1 of a packed word into the low bytes of an fp16 pair
+  const unsigned sel_sc = (kg >> 1) ? 0x00070006u : 0x00050004u;
   const unsigned mask_hi = in_vgpr(0x00F000F0u);
   f32x4 acc[T], acc_first[T];
 #pragma unroll
@@ -488,40 +491,39 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       // per sub-block {scale, offset} pairs; the fma broadcasts each half
       half2v k00[T], k01[T], k10[T], k11[T];
       half4 bm[T];
-      const int sh = (kg >> 1) * 16;
+      const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+      const half2v lo_pair = {(_Float16)1.0f, (_Float16)-1024.0f};
+      const half2v hi_pair = {(_Float16)0.0625f, (_Float16)-64.0f};
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const u32x4 h = cur[t].hdr;
         d[t] = h2f_lo(h.x);
         dmin[t] = h2f_hi(h.x);
         // q0 holds sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
-        // q1 holds 4+2(kg>>1) and 5+2(kg>>1).
+        // q1 holds 4+2(kg>>1) and 5+2(kg>>1). Their 6-bit scales are bytes
+        // 2(kg>>1), 2(kg>>1)+1 of sc03 and sc47; one byte permute sets each
+        // below an fp16 exponent byte 0x64 (1024 + s), so {s, s'} is exact.
         const unsigned sc03 = h.y & 0x3F3F3F3Fu;
         const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-        const float s00 = (float)((sc03 >> sh) & 0xFFu);
-        const float s01 = (float)((sc03 >> (sh + 8)) & 0xFFu);
-        const float s10 = (float)((sc47 >> sh) & 0xFFu);
-        const float s11 = (float)((sc47 >> (sh + 8)) & 0xFFu);
+        const half2v s0 = as_h2(__builtin_amdgcn_perm(sc03, 0x64646464u, sel_sc)) + neg1024;
+        const half2v s1 = as_h2(__builtin_amdgcn_perm(sc47, 0x64646464u, sel_sc)) + neg1024;
         // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
-        k00[t] = half2v{(_Float16)s00, (_Float16)(-1024.0f * s00)};
-        k01[t] = half2v{(_Float16)(0.0625f * s01), (_Float16)(-64.0f * s01)};
-        k10[t] = half2v{(_Float16)s10, (_Float16)(-1024.0f * s10)};
-        k11[t] = half2v{(_Float16)(0.0625f * s11), (_Float16)(-64.0f * s11)};
+        k00[t] = half2v{s0[0], s0[0]} * lo_pair;
+        k01[t] = half2v{s0[1], s0[1]} * hi_pair;
+        k10[t] = half2v{s1[0], s1[0]} * lo_pair;
+        k11[t] = half2v{s1[1], s1[1]} * hi_pair;
         // min-term B operand: the 6-bit m of sub-blocks 4(kg&1) + {0,2,1,3}
         const unsigned m03 = h.z & 0x3F3F3F3Fu;
         const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
         const unsigned msrc = (kg & 1) ? m47 : m03;
-        const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-        const half2v p0 = as_h2((msrc & 0x00FF00FFu) | 0x64006400u) + neg1024;
-        const half2v p1 = as_h2(((msrc >> 8) & 0x00FF00FFu) | 0x64006400u) + neg1024;
+        const half2v p0 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00060004u)) + neg1024;
+        const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
         bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
       }
-      f32x4 chi[T], clo[T];
+      // x hi and x lo products accumulate in one fp32 sum per tile
+      f32x4 cq[T];
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        chi[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        clo[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
@@ -543,8 +545,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
           const half2v v2 = fma_bcast(as_h2(u2_), kk);
           const half2v v3 = fma_bcast(as_h2(u3_), kk);
           const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
-          chi[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, chi[t], 0, 0, 0);
-          clo[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, clo[t], 0, 0, 0);
+          cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
+          cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
         }
       }
       // min term and the block's contribution in the row's scaled units
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
             __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          acc[t][r] += xinv[r] * (d[t] * (chi[t][r] + clo[t][r]) - dmin[t] * c2[r]);
+          acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
       }
     }
     // end of a row group's segment
