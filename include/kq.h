@@ -23,8 +23,11 @@
  * (k if none), next_token = argmax[accepted], emitted = accepted + 1.
  *
  * Conventions (all entry points):
- *  - Shapes: 1 <= m <= 16, k > 0 and k % 256 == 0, 1 <= n < 2^31,
- *    n * (k/256) * 144 < 2^62.
+ *  - Shapes: 1 <= m <= 16, k > 0 and k % 256 == 0, k <= 2^28, 1 <= n < 2^31,
+ *    and the weight matrix (n rounded up to a multiple of 16) and the staged
+ *    activations each smaller than 4 GiB: ceil(n/16) * 16 * (k/256) * 144 <
+ *    2^32 and (k/256) * 16,960 < 2^32 (the kernels address them with 32-bit
+ *    offsets). Other shapes give KQ_ERR_SHAPE (size queries return 0).
  *  - Layouts: w is [n][k/256] blocks of 144 bytes, row-major, 16-byte aligned;
  *    x is fp32 [m][k] row-major, 16-byte aligned; logits fp32 [m][n].
  *  - Pointers marked "device" are HIP device memory owned by the caller; the

@@ -12,9 +12,14 @@ namespace kq {
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The kernels address a weight matrix (either layout, rows rounded up to a
+// 16-row tile) and a staged activation block with 32-bit offsets, so both
+// must be smaller than 4 GiB.
 static bool shape_ok(int64_t n, int64_t k) {
-  return n >= 1 && n < ((int64_t)1 << 31) && k > 0 && k % kQK == 0 && k <= ((int64_t)1 << 28) &&
-         (k / kQK) * kBlockBytes <= (((int64_t)1 << 62) / n);
+  if (!(n >= 1 && n < ((int64_t)1 << 31) && k > 0 && k % kQK == 0 && k <= ((int64_t)1 << 28))) return false;
+  const int64_t kb = k / kQK;
+  const int64_t limit = (int64_t)1 << 32;
+  return cdiv(n, 16) * 16 * kb * kBlockBytes < limit && kb * kStageBytes < limit;
 }
 
 // Launch geometry: persistent workgroups of 8 waves, one per CU (their LDS

@@ -86,11 +86,17 @@ __device__ __forceinline__ float ld_dev(const float *p) {
 __device__ __forceinline__ unsigned long long ld_dev(const unsigned long long *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Raw buffer resource over [base, base + 4 GiB): loads and stores through
+// it take a 32-bit lane offset and a 32-bit uniform offset, so no 64-bit
+// address arithmetic per access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)0xFFFFFFFFu, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
 // 16-byte versions for the partial sums: buffer instructions with the same
 // cache policy (sc1) as the agent-scope atomic accesses above
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
-}
 constexpr int kCpolSc1 = 16;
 __device__ __forceinline__ void st_dev16(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSc1);
@@ -340,30 +346,39 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // unconditional and outstanding loads are counted statically).
   int64_t uw = u0;
   int gw = (int)(u0 / KB), bw = (int)(u0 % KB);
-  const uint8_t *rowp[T];
-  // Weight addressing, one code path for both layouts: the lane's bytes of
-  // block b of tile t sit at rowp[t] + b * block_stride + {off_h, off_0,
-  // off_1}. Row-major (llama.cpp): rowp = the lane's row (clamped to the
-  // last row), stride 144, offsets {0, 16 + 16kg, 80 + 16kg}. Tiled: rowp =
-  // the 16-row tile's record, stride = tiles * 2,304, offsets {16 ln,
-  // 256 + 16 lane, 1,280 + 16 lane}.
+  // Weight addressing, one code path for both layouts, through buffer loads
+  // from the current matrix (every matrix is smaller than 4 GiB): the lane's
+  // bytes of block b of tile t sit at voff[t][0..2] + soff[t] + b *
+  // block_stride. Row-major (llama.cpp): voff = the lane's row (clamped to
+  // the last row) times the row bytes + {0, 16 + 16kg, 80 + 16kg}, soff = 0,
+  // stride 144. Tiled: voff = {16 ln, 256 + 16 lane, 1,280 + 16 lane}, soff
+  // = the 16-row tile's record, stride = tiles * 2,304.
   const bool tiled = a.layout == KQ_LAYOUT_TILED16;
-  const int off_h = tiled ? 16 * ln : 0;
-  const int off_0 = tiled ? (int)kTileQ0 + 16 * lane : 16 + 16 * kg;
-  const int off_1 = tiled ? (int)kTileQ1 + 16 * lane : 80 + 16 * kg;
-  const int64_t block_stride = tiled ? a.n_tiles * kTileBlockBytes : kBlockBytes;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned block_stride = tiled ? (unsigned)(a.n_tiles * kTileBlockBytes) : (unsigned)kBlockBytes;
+  __amdgpu_buffer_rsrc_t w_rsrc;
+  unsigned voff[T][3], soff[T];
+  unsigned boff = (unsigned)bw * block_stride;  // block bw within the row
   auto set_rowp = [&]() {
     int mat;
     const int64_t r0 = group_row0(gw, mat);
+    w_rsrc = dev_rsrc(a.w[mat]);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (tiled) {
-        int64_t ti = (r0 + (t * W + wave) * 16) / 16;
+        int64_t ti = (r0 + (t * W + wave_u) * 16) / 16;
         ti = ti < a.n_tiles ? ti : a.n_tiles - 1;
-        rowp[t] = a.w[mat] + ti * kTileBlockBytes;
+        soff[t] = (unsigned)(ti * kTileBlockBytes);
+        voff[t][0] = 16u * ln;
+        voff[t][1] = (unsigned)kTileQ0 + 16u * lane;
+        voff[t][2] = (unsigned)kTileQ1 + 16u * lane;
       } else {
         const int64_t row = r0 + tile_row(t);
-        rowp[t] = a.w[mat] + (row < N ? row : N - 1) * a.row_bytes;
+        const unsigned rb = (unsigned)((row < N ? row : N - 1) * a.row_bytes);
+        soff[t] = 0u;
+        voff[t][0] = rb;
+        voff[t][1] = rb + 16u + 16u * kg;
+        voff[t][2] = rb + 80u + 16u * kg;
       }
     }
   };
@@ -371,15 +386,16 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   auto load_w = [&](WTile(&w)[T]) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const uint8_t *q = rowp[t] + (int64_t)bw * block_stride;
-      w[t].hdr = ld16(q + off_h);
-      w[t].q0 = ld16(q + off_0);
-      w[t].q1 = ld16(q + off_1);
+      w[t].hdr = buf_ld16(w_rsrc, voff[t][0], soff[t] + boff);
+      w[t].q0 = buf_ld16(w_rsrc, voff[t][1], soff[t] + boff);
+      w[t].q1 = buf_ld16(w_rsrc, voff[t][2], soff[t] + boff);
     }
     if (uw < u_last) {
       ++uw;
+      boff += block_stride;
       if (++bw == KB) {
         bw = 0;
+        boff = 0u;
         ++gw;
         set_rowp();
       }
@@ -388,14 +404,15 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   int64_t ux = u0;
   int bx = (int)(u0 % KB);
   const int xe_idx = tid < kXe ? tid : kXe - 1;
+  const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(a.staged);
   struct XRegs {
     u32x4 a[kXj], e;
   };
   auto load_x = [&](XRegs &x) {
-    const uint8_t *src = a.staged + (int64_t)bx * kStageBytes;
+    const unsigned src = (unsigned)bx * (unsigned)kStageBytes;
 #pragma unroll
-    for (int j = 0; j < kXj; ++j) x.a[j] = ld16(src + (tid + kNth * j) * 16);
-    x.e = ld16(src + kXaBytes + xe_idx * 16);
+    for (int j = 0; j < kXj; ++j) x.a[j] = buf_ld16(x_rsrc, (unsigned)(tid + kNth * j) * 16u, src);
+    x.e = buf_ld16(x_rsrc, (unsigned)kXaBytes + (unsigned)xe_idx * 16u, src);
     if (ux < u_last) {
       ++ux;
       if (++bx == KB) bx = 0;

@@ -98,6 +98,24 @@ def test_gemv_argument_errors():
     assert _call_gemv(wsb=kq.workspace_bytes(512, 1024, 4) - 1) == WS
 
 
+def test_four_gib_limits():
+    # the weight matrix (rows rounded up to 16) must be smaller than 4 GiB
+    assert 131072 * 227 * 144 < 1 << 32 <= 131072 * 228 * 144
+    assert kq.workspace_bytes(131072, 227 * 256, 16) > 0
+    assert kq.workspace_bytes(131072, 228 * 256, 16) == 0
+    assert _call_gemv(n=131072, k=228 * 256, wsb=1 << 40) == SHAPE
+    # n is rounded up to a whole 16-row tile
+    q = 1864135
+    assert 16 * q * 144 < 1 << 32 <= 16 * (q + 1) * 144
+    assert kq.scratch_bytes(16 * q, 256) > 0
+    assert kq.scratch_bytes(16 * q + 1, 256) == 0
+    # the staged activations must be smaller than 4 GiB
+    kb = (1 << 32) // 16960
+    assert kb * 16960 < 1 << 32 <= (kb + 1) * 16960
+    assert kq.scratch_bytes(1, kb * 256) > 0
+    assert kq.scratch_bytes(1, (kb + 1) * 256) == 0
+
+
 def test_verify_argument_errors():
     assert _call_verify(am=None) == NULL
     assert _call_verify(acc=None) == NULL
