@@ -22,14 +22,15 @@ static bool shape_ok(int64_t n, int64_t k) {
   return cdiv(n, 16) * 16 * kb * kBlockBytes < limit && kb * kStageBytes < limit;
 }
 
-// Launch geometry: persistent workgroups of 8 waves, one per CU (their LDS
-// activation ring of 8 blocks fills most of a CU's 160 KB), each taking an
-// equal, contiguous run of (row group, block) units. Row groups are 256 rows
-// (two 16-row tiles per wave) for the 131,072-row LM head and 128 rows (one
-// tile per wave) for the 6,656- and 17,920-row matrices, where a taller group
-// would leave too few groups to share among 256 workgroups. Barriers every 4
-// units. Measured on MI355X with the shapes of the 52-layer stack, the
-// DFlash fc projection and the LM head.
+// Launch geometry: persistent workgroups, one per CU (their LDS activation
+// ring of 8 blocks fills most of a CU's 160 KB), each taking an equal,
+// contiguous run of (row group, block) units. Row groups are 256 rows (8
+// waves of two 16-row tiles) for 131,072 rows or more (the LM head), 192
+// rows (12 waves, three per SIMD, one tile each) from 32,768 rows (gate and
+// up together), and 128 rows (8 waves, one tile each) below that, where a
+// taller group would leave too few groups to share among 256 workgroups.
+// Barriers every 4 units. Measured on MI355X with the shapes of the 52-layer
+// stack, the DFlash fc projection and the LM head.
 static constexpr int64_t kCUs = 256;
 
 struct Shape {
@@ -50,6 +51,7 @@ static Shape pick_shape(int64_t n, int count) {
 #endif
   const int64_t rows = n * count;
   if (rows >= 131072) return {8, 2, 1, 4, 4};
+  if (rows >= 32768) return {12, 1, 1, 4, 4};
   return {8, 1, 1, 4, 4};
 }
 

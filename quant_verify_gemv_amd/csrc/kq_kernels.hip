@@ -273,6 +273,7 @@ constexpr int lcm_int(int a, int b) {
 
 template <int W, int T, int BI, int D>
 __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv_kernel(GemvLaunch a) {
+  static_assert(W % 4 == 0, "waves spread evenly over the 4 SIMDs");
   // D weight register sets: the weights of unit i + D - 1 are loaded while
   // unit i computes. The activations of unit i + BI are stored to LDS in
   // step i from registers loaded kXL steps earlier: loads complete in issue
@@ -281,14 +282,14 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // workgroups stage twice the activation chunks per thread and keep one
   // set in flight. The unit loop is unrolled kU = lcm(D, BI, kXL + 1) times
   // so that every register set index and every interval position is static.
-  constexpr int kXL = (W == 8 && T == 1) ? 3 : 1;
+  constexpr int kXL = (W >= 8 && T == 1) ? 3 : 1;
   constexpr int kU = lcm_int(lcm_int(D, BI), kXL + 1);
   constexpr int kNth = 64 * W;
   constexpr int kRows = 16 * T * W;
-  constexpr int kXj = (int)(kXaBytes / 16) / kNth;                 // XA chunks per thread
-  constexpr int kXe = (int)((kStageBytes - kXaBytes) / 16);        // XSB + XI chunks (36)
-  static_assert(kXj * 16 * kNth == kXaBytes, "activation block must split evenly");
-  static_assert(kXe <= kNth, "one extra chunk per thread at most");
+  // The staged record is kXc 16-byte chunks, copied linearly; thread tid
+  // moves chunks tid + j kNth (the last round only partly).
+  constexpr int kXc = (int)(kStageBytes / 16);  // 1,060
+  constexpr int kXj = (kXc + kNth - 1) / kNth;   // chunks per thread
   // Activation ring: unit i sits in buffer i % kNB. Workgroups synchronise
   // once every BI units: between two barriers the waves read BI buffers and
   // fill the other BI.
@@ -403,16 +404,17 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   };
   int64_t ux = u0;
   int bx = (int)(u0 % KB);
-  const int xe_idx = tid < kXe ? tid : kXe - 1;
+  // last round: threads past the record re-load its last chunk and skip the store
+  const int xlast = tid + kNth * (kXj - 1) < kXc ? tid + kNth * (kXj - 1) : kXc - 1;
   const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(a.staged);
   struct XRegs {
-    u32x4 a[kXj], e;
+    u32x4 a[kXj];
   };
   auto load_x = [&](XRegs &x) {
     const unsigned src = (unsigned)bx * (unsigned)kStageBytes;
 #pragma unroll
-    for (int j = 0; j < kXj; ++j) x.a[j] = buf_ld16(x_rsrc, (unsigned)(tid + kNth * j) * 16u, src);
-    x.e = buf_ld16(x_rsrc, (unsigned)kXaBytes + (unsigned)xe_idx * 16u, src);
+    for (int j = 0; j < kXj; ++j)
+      x.a[j] = buf_ld16(x_rsrc, (unsigned)(j < kXj - 1 ? tid + kNth * j : xlast) * 16u, src);
     if (ux < u_last) {
       ++ux;
       if (++bx == KB) bx = 0;
@@ -420,8 +422,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   };
   auto store_x = [&](int buf, const XRegs &x) {
 #pragma unroll
-    for (int j = 0; j < kXj; ++j) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
-    if (tid < kXe) *(u32x4 *)(&s_x[buf][kXaBytes + tid * 16]) = x.e;
+    for (int j = 0; j < kXj; ++j)
+      if (j < kXj - 1 || tid + kNth * j < kXc) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
   };
 
   // finished rows of a whole row group: logits and/or the argmax keys. The
@@ -492,10 +494,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // the static position within the unrolled iteration).
   auto step = [&](WTile(&cur)[T], WTile(&pf)[T], XRegs &xl, const XRegs &xs, const int64_t i,
                   const int pos) {
-    // Waves w and w + 4 share a SIMD, and the older one would otherwise
-    // win issue every cycle and reach the barrier first; alternating the
-    // priority each unit keeps the pair in step.
-    if ((wave >> 2) == (pos & 1))
+    // Waves w, w + 4, ... share a SIMD, and the oldest would otherwise win
+    // issue every cycle and reach the barrier first; rotating the priority
+    // each unit keeps them in step.
+    if ((wave >> 2) == pos % (W / 4))
       __builtin_amdgcn_s_setprio(1);
     else
       __builtin_amdgcn_s_setprio(0);
@@ -877,6 +879,7 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(8, 1, 2, 4)
     KQ_CASE(8, 2, 2, 4)
     KQ_CASE(4, 1, 1, 4)
+    KQ_CASE(12, 1, 4, 4)
     KQ_CASE(4, 2, 2, 3)
     KQ_CASE(4, 2, 1, 3)
 #undef KQ_CASE

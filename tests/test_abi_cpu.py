@@ -54,10 +54,11 @@ def test_sizes_and_geometry():
     assert kq.workspace_bytes(0, 1024, 1) == 0
     assert kq.staged_bytes(1024) == 4 * 16960
     assert kq.staged_bytes(6656) == 26 * 16960
-    for n, k in [(512, 1024), (6656, 6656), (6656, 33280), (131072, 6656), (17920, 6656), (6656, 17920), (1, 256)]:
+    for n, k in [(512, 1024), (6656, 6656), (6656, 33280), (131072, 6656), (17920, 6656), (6656, 17920), (1, 256),
+                 (35840, 6656)]:
         assert kq.workspace_bytes(n, k, 1) == kq.workspace_bytes(n, k, 16) > 0
         waves, tpw, nwg, units = kq.launch_geometry(n, k)
-        assert waves in (4, 8) and tpw in (1, 2)
+        assert waves in (4, 8, 12) and tpw in (1, 2)
         assert units == -(-n // (16 * waves * tpw)) * (k // 256)
         assert 1 <= nwg <= min(units, 768)
         assert kq.scratch_bytes(n, k) <= kq.workspace_bytes(n, k, 16)

@@ -138,6 +138,28 @@ def test_stack_shapes_sampled_rows(kq, shape):
         check_logits(G.cpu().numpy()[:, rows], L[:mm], A[:mm], what=f"stack {shape} m={mm}")
 
 
+@pytest.mark.parametrize("n,k,count", [(6656, 6656, 3), (17920, 6656, 2)])
+def test_stack_grouped_launches_sampled_rows(kq, n, k, count):
+    """The stack's grouped launches (q,k,v and gate,up) at full size, in the
+    launch configuration bench.py times: tiled weights, one launch per group."""
+    log(f"stack group {count} x n={n} k={k}")
+    mats = [s for s in synthetic.stack_matrices(1) if (s.n, s.k) == (n, k)][:count]
+    assert len(mats) == count
+    ws = [synthetic.q4k_matrix(n, k, g.seed) for g in mats]
+    x = synthetic.activations(16, k, synthetic.stack_activation_seed(k))
+    rng = np.random.default_rng(n + 7 * k + count)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, 191, 192, n - 17, n - 1], rng.integers(0, n, 100)]))
+    wts = [kq.tile_weights(to_dev(w), n, k) for w in ws]
+    gs = kq.new_group_scratch(n, k, count, DEV)
+    for mm in (16, 1):
+        st = kq.stage_rows(to_dev(x[:mm]))
+        outs = kq.gemv_staged_group(wts, n, k, st, mm, gs, layout=kq.LAYOUT_TILED16)
+        torch.cuda.synchronize()
+        for i in range(count):
+            L, A = oracle.gemv_rows(ws[i], k, x[:mm], rows=rows)
+            check_logits(outs[i].cpu().numpy()[:, rows], L, A, what=f"group {n}x{k} member {i} m={mm}")
+
+
 EDGE = [(1, 256), (17, 256), (16, 512), (129, 1280), (1000, 2304), (513, 3328), (2048, 9216)]
 
 
