@@ -203,6 +203,42 @@ def run_m(stack, torch, m, steps, warmup, use_graph):
     return wall, ev
 
 
+def draft_block_timing(stack, torch, calls=50):
+    """The draft block's proposals (argmax of rows 1..15 of a 16-row block
+    against the LM head, no accept), timed on the resident LM-head weights
+    and checked bitwise against the verify step's argmax of the same rows."""
+    kq = stack.kq
+    h = stack.head
+    st = stack.staged[h.k]
+    kq.stage_rows(stack.x[h.k][:16], staged=st)
+    props = torch.empty(15, dtype=torch.int32, device=stack.dev)
+    head = torch.empty(1, dtype=torch.int32, device=stack.dev)
+
+    def call():
+        kq.draft_block_argmax_staged(stack.w_head, h.n, h.k, st, 15, stack.head_scratch, want_head=True,
+                                     out=(props, head), layout=stack.layout)
+    for _ in range(5):
+        call()
+    kq.verify_staged(stack.w_head, h.n, h.k, st, 16, stack.draft[:15], stack.head_scratch,
+                     out=(stack.am, stack.acc, None), layout=stack.layout)
+    torch.cuda.synchronize()
+    same_rows = bool(torch.equal(props, stack.am[1:16]) and torch.equal(head, stack.am[:1]))
+    if not same_rows:
+        raise RuntimeError("draft block proposals differ from the verify step's argmax of the same rows")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    gbs = h.weight_bytes / (us * 1e-6) / 1e9
+    return {"verify_length": 15, "us_per_call": round(us, 2), "weight_gb_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "calls": calls, "launch": "eager",
+            "matches_verify_argmax": same_rows}
+
+
 def source_digest():
     """sha256 over the kernel sources and the launch-geometry code: a stored
     traffic figure is only valid for the code it was measured on."""
@@ -322,6 +358,8 @@ def main():
                   "event_ms_per_step": round(ev * 1e3, 4), "roofline": roof}
         log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s, "
             f"kernel {roof['avg_launch_us']} us/launch, {roof['achieved']} GB/s")
+    draft = draft_block_timing(stack, torch)
+    log(f"bench: draft block proposals {draft['us_per_call']} us/call, {draft['weight_gb_s']} GB/s")
     cpu = None
     if not args.no_cpu:
         try:
@@ -352,6 +390,7 @@ def main():
         "m1": res.get(1),
         "m16_over_m1": round(res[16]["ms_per_step"] / res[1]["ms_per_step"], 4) if len(res) == 2 else None,
         "roofline": top["roofline"],
+        "draft_block_argmax": draft,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

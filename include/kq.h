@@ -153,6 +153,38 @@ kq_status kq_gemv_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
                          const void *staged, int m, float *logits,
                          void *scratch, size_t scratch_bytes, void *stream);
 
+/* Draft block proposals (ch. 8 section 8.6, guarantee 3; the 16-row block of
+ * section 8.2). The draft forwards one 16-row block (a seed row followed by 15
+ * mask rows), scores the block's output rows with the target's LM head and
+ * proposes the argmax (ties -> lowest index) of rows 1..verify_length; the
+ * verify length is exactly 3, 7 or 15, and any other value is an error
+ * before any GPU work. Only rows 0..verify_length are scored (the weight
+ * stream, and so the cost, does not depend on how many).
+ *  w_q4k          device, the LM head, n * (k/256) * 144 bytes (read only)
+ *  x              device, fp32 [>= verify_length + 1][k]: the block's output
+ *                 rows; rows past verify_length are not read
+ *  verify_length  3, 7 or 15 (else KQ_ERR_SHAPE)
+ *  proposals      device, int32 [verify_length] (written): argmax of rows
+ *                 1..verify_length, in row order
+ *  head_or_null   device int32 [1] (written: argmax of row 0, the block head
+ *                 the pages check against the seed token) or NULL
+ *  workspace      >= kq_workspace_bytes(n, k, verify_length + 1) bytes, as for
+ *                 kq_verify_argmax_accept
+ * Argmax rows whose top-2 gap lies inside the logit tolerance may resolve to
+ * any of the tied candidates (as in the verify step). */
+kq_status kq_draft_block_argmax(const void *w_q4k, int64_t n, int64_t k,
+                                const float *x, int verify_length,
+                                int32_t *proposals, int32_t *head_or_null,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* kq_draft_block_argmax on staged activations (staged holds at least rows
+ * 0..verify_length of the block, kq_stage_rows); layout and scratch as for
+ * kq_gemv_staged. */
+kq_status kq_draft_block_argmax_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
+                                       const void *staged, int verify_length,
+                                       int32_t *proposals, int32_t *head_or_null,
+                                       void *scratch, size_t scratch_bytes, void *stream);
+
 /* kq_verify_argmax_accept on staged activations (same arguments as above;
  * layout and scratch as for kq_gemv_staged). */
 kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k,

@@ -178,10 +178,15 @@ kq_status kq_stage_rows(const float *x, int m, int64_t k, void *staged, size_t s
 
 // Shared validation + launch of the main kernel on staged activations for
 // `count` matrices of the same shape (verify: count == 1).
+// verify: per-row argmax, written from row argmax_from on (0 for the verify
+// step, 1 for a draft block's proposals), row 0's also to head_out when not
+// null, and the accept decision against draft_host when accept_out is not
+// null.
 static kq_status run(const void *const *w, int layout, int count, int64_t n, int64_t k,
                      const void *staged, int m, float *const *logits, bool verify,
-                     const int32_t *draft_host, int32_t *argmax, int32_t *accept_out, void *scratch,
-                     size_t scratch_bytes, const float *x_to_stage, void *stream) {
+                     const int32_t *draft_host, int32_t *argmax, int32_t *accept_out, int argmax_from,
+                     int32_t *head_out, void *scratch, size_t scratch_bytes, const float *x_to_stage,
+                     void *stream) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
   if (layout != KQ_LAYOUT_ROWS && layout != KQ_LAYOUT_TILED16) return KQ_ERR_SHAPE;
   if (count < 1 || count > kMaxGroup || (verify && count != 1)) return KQ_ERR_SHAPE;
@@ -189,8 +194,8 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
     if (!w[i]) return KQ_ERR_NULL;
     if (!verify && (!logits || !logits[i])) return KQ_ERR_NULL;
   }
-  if (verify && (!argmax || !accept_out)) return KQ_ERR_NULL;
-  if (verify && m > 1 && !draft_host) return KQ_ERR_NULL;
+  if (verify && (!argmax || (!accept_out && argmax_from == 0))) return KQ_ERR_NULL;
+  if (verify && accept_out && m > 1 && !draft_host) return KQ_ERR_NULL;
   if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i)
     if (!al(w[i], 16)) return KQ_ERR_ALIGN;
@@ -200,7 +205,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
-  if (verify) {
+  if (verify && accept_out) {
     for (int i = 0; i < m - 1; ++i) {
       if (draft_host[i] < 0 || (int64_t)draft_host[i] >= n) return KQ_ERR_TOKEN;
       a.draft[i] = draft_host[i];
@@ -223,8 +228,10 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   a.wg_keys = (unsigned long long *)(sc + sl.keys_off);
   a.partials = (float *)(sc + sl.part_off);
   a.argmax_out = argmax;
+  a.argmax_from = argmax_from;
+  a.head_out = head_out;
   a.accept_out = accept_out;
-  a.k_draft = verify ? m - 1 : 0;
+  a.k_draft = verify && accept_out ? m - 1 : 0;
   a.verify = verify ? 1 : 0;
   a.g = geometry(n, k, count);
   if (x_to_stage) {
@@ -237,7 +244,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
 
 kq_status kq_gemv_staged(const void *w_q4k, int layout, int64_t n, int64_t k, const void *staged, int m,
                          float *logits, void *scratch, size_t scratch_bytes, void *stream) {
-  return run(&w_q4k, layout, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, scratch,
+  return run(&w_q4k, layout, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, 0, nullptr, scratch,
              scratch_bytes, nullptr, stream);
 }
 
@@ -245,7 +252,7 @@ kq_status kq_gemv_staged_group(const void *const *w_q4k, int layout, int count, 
                                const void *staged, int m, float *const *logits, void *scratch,
                                size_t scratch_bytes, void *stream) {
   if (!w_q4k || !logits) return KQ_ERR_NULL;
-  return run(w_q4k, layout, count, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, scratch,
+  return run(w_q4k, layout, count, n, k, staged, m, logits, false, nullptr, nullptr, nullptr, 0, nullptr, scratch,
              scratch_bytes, nullptr, stream);
 }
 
@@ -253,8 +260,8 @@ kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k, 
                            const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
                            float *logits_or_null, void *scratch, size_t scratch_bytes,
                            void *stream) {
-  return run(&w_q4k, layout, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out,
-             scratch, scratch_bytes, nullptr, stream);
+  return run(&w_q4k, layout, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out, 0,
+             nullptr, scratch, scratch_bytes, nullptr, stream);
 }
 
 static kq_status split_workspace(int64_t n, int64_t k, int m, void *ws, size_t ws_bytes,
@@ -278,8 +285,8 @@ kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k, const float *x, 
   size_t sb;
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
-  return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr,
-             scratch, sb, x, stream);
+  return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &logits, false, nullptr, nullptr, nullptr, 0,
+             nullptr, scratch, sb, x, stream);
 }
 
 kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
@@ -293,7 +300,34 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
   return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax,
-             accept_out, scratch, sb, x, stream);
+             accept_out, 0, nullptr, scratch, sb, x, stream);
+}
+
+static bool verify_length_ok(int length) { return length == 3 || length == 7 || length == 15; }
+
+kq_status kq_draft_block_argmax(const void *w_q4k, int64_t n, int64_t k, const float *x, int verify_length,
+                                int32_t *proposals, int32_t *head_or_null, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (!w_q4k || !x || !proposals) return KQ_ERR_NULL;
+  if (!verify_length_ok(verify_length)) return KQ_ERR_SHAPE;
+  const int m = verify_length + 1;
+  void *staged, *scratch;
+  size_t sb;
+  kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
+  if (s != KQ_OK) return s;
+  float *no_logits = nullptr;
+  return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &no_logits, true, nullptr, proposals, nullptr, 1,
+             head_or_null, scratch, sb, x, stream);
+}
+
+kq_status kq_draft_block_argmax_staged(const void *w_q4k, int layout, int64_t n, int64_t k, const void *staged,
+                                       int verify_length, int32_t *proposals, int32_t *head_or_null,
+                                       void *scratch, size_t scratch_bytes, void *stream) {
+  if (!w_q4k || !staged || !proposals) return KQ_ERR_NULL;
+  if (!verify_length_ok(verify_length)) return KQ_ERR_SHAPE;
+  float *no_logits = nullptr;
+  return run(&w_q4k, layout, 1, n, k, staged, verify_length + 1, &no_logits, true, nullptr, proposals, nullptr,
+             1, head_or_null, scratch, scratch_bytes, nullptr, stream);
 }
 
 }  // extern "C"

@@ -76,8 +76,10 @@ struct GemvLaunch {
   unsigned *done;
   unsigned *group_cnt;
   unsigned long long *wg_keys;
-  int32_t *argmax_out;  // verify only
-  int32_t *accept_out;  // verify only
+  int32_t *argmax_out;  // verify only: row m's argmax at argmax_out[m - argmax_from], m >= argmax_from
+  int argmax_from;
+  int32_t *head_out;    // verify only, may be null: row 0's argmax
+  int32_t *accept_out;  // verify only, may be null (then no accept decision)
   int32_t draft[kMaxRows];
   int k_draft;
   int verify;

@@ -794,12 +794,15 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     int am[kMaxRows];
     for (int m = 0; m < M; ++m) {
       am[m] = (int)(0xFFFFFFFFu - (unsigned)(s_keys[m] & 0xFFFFFFFFull));
-      a.argmax_out[m] = am[m];
+      if (m >= a.argmax_from) a.argmax_out[m - a.argmax_from] = am[m];
     }
-    int i = 0;
-    while (i < a.k_draft && a.draft[i] == am[i]) ++i;
-    a.accept_out[0] = i;
-    a.accept_out[1] = am[i];
+    if (a.head_out) a.head_out[0] = am[0];
+    if (a.accept_out) {
+      int i = 0;
+      while (i < a.k_draft && a.draft[i] == am[i]) ++i;
+      a.accept_out[0] = i;
+      a.accept_out[1] = am[i];
+    }
     __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

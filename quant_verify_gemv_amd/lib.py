@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "KQ_OK", 1: "KQ_ERR_NULL", 2: "KQ_ERR_SHAPE", 3: "KQ_ERR_ALIG
 EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scratch_bytes",
             "kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
             "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
-            "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights")
+            "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights", "kq_draft_block_argmax",
+            "kq_draft_block_argmax_staged")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -58,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.kq_gemv_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, SZ, P]
     lib.kq_verify_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P, P]  # int*, int*, int*, int64_t*
+    lib.kq_draft_block_argmax.argtypes = [P, I64, I64, P, I32, P, P, P, SZ, P]
+    lib.kq_draft_block_argmax_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, SZ, P]
     lib.kq_group_scratch_bytes.argtypes = [I64, I64, I32]
     lib.kq_group_scratch_bytes.restype = SZ
     lib.kq_gemv_staged_group.argtypes = [P, I32, I32, I64, I64, P, I32, P, P, SZ, P]
@@ -66,7 +69,7 @@ def load() -> ctypes.CDLL:
     lib.kq_tile_weights.argtypes = [P, I64, I64, P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
-                 "kq_tile_weights"):
+                 "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -204,6 +207,33 @@ def verify(w, n: int, k: int, x, draft: Sequence[int], want_logits: bool = False
     return am, acc, lg
 
 
+DRAFT_VERIFY_LENGTHS = (3, 7, 15)
+
+
+def draft_block_argmax(w, n: int, k: int, x, verify_length: int, want_head: bool = False,
+                       workspace=None, stream=None, out=None):
+    """The draft block's proposals: argmax of rows 1..verify_length of x
+    (fp32 [>= verify_length + 1][k]) against the LM head w. Returns
+    (proposals int32[verify_length] device, head int32[1] device or None)."""
+    torch = _torch()
+    if verify_length not in DRAFT_VERIFY_LENGTHS:
+        raise ValueError(f"verify_length must be 3, 7 or 15, got {verify_length}")
+    if int(x.shape[0]) < verify_length + 1:
+        raise ValueError(f"x needs {verify_length + 1} rows, has {int(x.shape[0])}")
+    if out is None:
+        props = torch.empty(verify_length, dtype=torch.int32, device=x.device)
+        head = torch.empty(1, dtype=torch.int32, device=x.device) if want_head else None
+    else:
+        props, head = out
+    need = workspace_bytes(n, k, verify_length + 1)
+    ws = workspace if workspace is not None else _WS.get(need, x.device)
+    _check(load().kq_draft_block_argmax(
+        _dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(x, "x", torch.float32), verify_length,
+        _dev_ptr(props, "proposals", torch.int32), _dev_ptr(head, "head", torch.int32) if head is not None else None,
+        _dev_ptr(ws, "workspace"), ws.numel(), _stream_handle(stream)), "kq_draft_block_argmax")
+    return props, head
+
+
 def stage_rows(x, staged=None, stream=None):
     torch = _torch()
     m, k = int(x.shape[0]), int(x.shape[1])
@@ -258,6 +288,24 @@ def gemv_staged_group(ws, n: int, k: int, staged, m: int, scratch, logits=None, 
                                        _dev_ptr(scratch, "scratch"), scratch.numel(),
                                        _stream_handle(stream)), "kq_gemv_staged_group")
     return logits
+
+
+def draft_block_argmax_staged(w, n: int, k: int, staged, verify_length: int, scratch, want_head=False,
+                              stream=None, out=None, layout=LAYOUT_ROWS):
+    torch = _torch()
+    if verify_length not in DRAFT_VERIFY_LENGTHS:
+        raise ValueError(f"verify_length must be 3, 7 or 15, got {verify_length}")
+    dev = staged.device
+    if out is None:
+        props = torch.empty(verify_length, dtype=torch.int32, device=dev)
+        head = torch.empty(1, dtype=torch.int32, device=dev) if want_head else None
+    else:
+        props, head = out
+    _check(load().kq_draft_block_argmax_staged(
+        _dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"), verify_length,
+        _dev_ptr(props, "proposals", torch.int32), _dev_ptr(head, "head", torch.int32) if head is not None else None,
+        _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_draft_block_argmax_staged")
+    return props, head
 
 
 def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scratch, want_logits=False,

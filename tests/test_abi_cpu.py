@@ -127,6 +127,36 @@ def test_verify_argument_errors():
     assert _call_verify(wsb=100) == WS
 
 
+def test_draft_block_argument_errors():
+    lib = kq.load()
+    n, k = 512, 1024
+
+    def call(w=FAKE, x=FAKE, vl=7, props=FAKE, head=None, ws=FAKE, wsb=None):
+        if wsb is None:
+            wsb = kq.workspace_bytes(n, k, 16)
+        return lib.kq_draft_block_argmax(w, n, k, x, vl, props, head, ws, wsb, None)
+
+    # verify lengths other than 3, 7 and 15 are refused before any GPU work
+    for vl in (-1, 0, 1, 2, 4, 5, 6, 8, 14, 16, 31):
+        assert call(vl=vl) == SHAPE, vl
+    assert call(w=None) == NULL
+    assert call(x=None) == NULL
+    assert call(props=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(x=FAKE + 4) == ALIGN
+    assert call(wsb=kq.workspace_bytes(n, k, 8) - 1) == WS
+    sb = kq.scratch_bytes(n, k)
+    st = lib.kq_draft_block_argmax_staged
+    assert st(FAKE, 0, n, k, FAKE, 4, FAKE, None, FAKE, sb, None) == SHAPE
+    assert st(FAKE, 2, n, k, FAKE, 3, FAKE, None, FAKE, sb, None) == SHAPE
+    assert st(FAKE, 0, n, k, None, 3, FAKE, None, FAKE, sb, None) == NULL
+    assert st(FAKE, 0, n, k, FAKE, 3, None, None, FAKE, sb, None) == NULL
+    assert st(FAKE, 0, n, k, FAKE, 15, FAKE, None, FAKE, sb - 1, None) == WS
+    with pytest.raises(ValueError):
+        kq.draft_block_argmax(None, n, k, None, 5)
+    assert kq.DRAFT_VERIFY_LENGTHS == (3, 7, 15)
+
+
 def test_staged_argument_errors():
     lib = kq.load()
     assert lib.kq_stage_rows(None, 4, 1024, FAKE, 1 << 20, None) == NULL

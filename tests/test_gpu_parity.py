@@ -116,6 +116,26 @@ def test_lm_head_verify_full_size(kq):
         check_argmax(g_am, L, A, what=f"lm head trial {i}")
         check_accept(g_acc[0], g_acc[1], d, g_am, o_am, o_nc, what=f"lm head trial {i}")
     log("lm head: ok")
+    # The same 16-row block as a draft block: proposals are the argmax of rows
+    # 1..verify_length, the head is row 0's (row-major and tiled weights, the
+    # full block and exactly verify_length + 1 rows).
+    x_d = to_dev(x)
+    wt = kq.tile_weights(w_d, n, k)
+    scratch = kq.new_scratch(n, k, DEV)
+    for vl in kq.DRAFT_VERIFY_LENGTHS:
+        props, head = kq.draft_block_argmax(w_d, n, k, x_d, vl, want_head=True)
+        props_short, _ = kq.draft_block_argmax(w_d, n, k, x_d[:vl + 1].contiguous(), vl)
+        st = kq.stage_rows(x_d[:vl + 1].contiguous())
+        props_t, head_t = kq.draft_block_argmax_staged(wt, n, k, st, vl, scratch, want_head=True,
+                                                       layout=kq.LAYOUT_TILED16)
+        torch.cuda.synchronize()
+        p, h = props.cpu().numpy(), head.cpu().numpy()
+        assert p.shape == (vl,)
+        check_argmax(p, L[1:vl + 1], A[1:vl + 1], what=f"draft block proposals vl={vl}")
+        check_argmax(h, L[:1], A[:1], what=f"draft block head vl={vl}")
+        assert np.array_equal(p, props_short.cpu().numpy())
+        assert np.array_equal(p, props_t.cpu().numpy()) and np.array_equal(h, head_t.cpu().numpy())
+    log("draft block proposals: ok")
 
 
 @pytest.mark.parametrize("shape", [(6656, 6656), (17920, 6656), (6656, 17920)])
@@ -178,6 +198,24 @@ def test_edge_shapes(kq, n, k):
         g_am, g_acc, _ = gpu_verify(kq, w_d, n, k, x[:mm], d)
         check_argmax(g_am, L[:mm], A[:mm], what=f"edge {n}x{k} m={mm}")
         check_accept(g_acc[0], g_acc[1], d, g_am, o_am, o_nc, what=f"edge {n}x{k} m={mm}")
+
+
+@pytest.mark.parametrize("n,k", [(2000, 1024), (513, 3328)])
+def test_draft_block_small(kq, n, k):
+    log(f"draft block n={n} k={k}")
+    w = synthetic.q4k_matrix(n, k, 61 + n)
+    # duplicate row 7 at row 700 (or the last row): an exact tie, the lowest
+    # index must win wherever it is the maximum
+    w = w.copy()
+    w[min(700, n - 1)] = w[7]
+    x = synthetic.activations(16, k, 62 + n)
+    L, A = oracle.gemv_rows(w, k, x)
+    w_d, x_d = to_dev(w), to_dev(x)
+    for vl in kq.DRAFT_VERIFY_LENGTHS:
+        props, head = kq.draft_block_argmax(w_d, n, k, x_d, vl, want_head=True)
+        torch.cuda.synchronize()
+        check_argmax(props.cpu().numpy(), L[1:vl + 1], A[1:vl + 1], what=f"draft {n}x{k} vl={vl}")
+        check_argmax(head.cpu().numpy(), L[:1], A[:1], what=f"draft head {n}x{k} vl={vl}")
 
 
 def test_one_hot_rows_extract_weights(kq):
