@@ -68,6 +68,17 @@ typedef int kq_status;
 #define KQ_LAYOUT_ROWS    0  /* llama.cpp: row n is k/256 consecutive 144-byte blocks */
 #define KQ_LAYOUT_TILED16 1  /* kq_tile_weights output (same bytes, reordered) */
 
+/* Measurement helper, not part of the verify step: reads every byte of a
+ * device buffer once (16-byte loads over the whole GPU) and writes one
+ * XOR-fold word per workgroup to `sink`, so a caller can time the HBM read
+ * rate the weight stream could reach on this device (bench.py reports it
+ * next to the roofline).
+ *  buf   device, `bytes` bytes, 16-byte aligned, bytes % 16 == 0 (else KQ_ERR_SHAPE)
+ *  sink  device, >= kq_stream_probe_sink_bytes() bytes (written; contents
+ *        are a checksum, not a result) */
+size_t kq_stream_probe_sink_bytes(void);
+kq_status kq_stream_probe(const void *buf, size_t bytes, uint32_t *sink, size_t sink_bytes, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *kq_status_string(kq_status s);
 

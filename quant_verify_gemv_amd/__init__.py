@@ -6,7 +6,7 @@ behind the C ABI of include/kq.h. This package is the thin Python binding.
 """
 from .lib import (DRAFT_VERIFY_LENGTHS, LAYOUT_ROWS, LAYOUT_TILED16, KQError,  # noqa: F401
                   draft_block_argmax, draft_block_argmax_staged, gemv_rows, gemv_staged, gemv_staged_group, group_scratch_bytes, launch_geometry, load, new_group_scratch,
-                  new_scratch, scratch_bytes, stage_rows, staged_bytes, status_string, tile_weights,
+                  new_scratch, scratch_bytes, stage_rows, staged_bytes, status_string, stream_probe, tile_weights,
                   tiled_bytes, verify, verify_staged, workspace_bytes)
 
 QK = 256

@@ -303,6 +303,18 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const
              accept_out, 0, nullptr, scratch, sb, x, stream);
 }
 
+size_t kq_stream_probe_sink_bytes(void) { return 4 * 8192; }
+
+kq_status kq_stream_probe(const void *buf, size_t bytes, uint32_t *sink, size_t sink_bytes, void *stream) {
+  if (!buf || !sink) return KQ_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return KQ_ERR_SHAPE;
+  if (!al(buf, 16) || !al(sink, 4)) return KQ_ERR_ALIGN;
+  const int blocks = 8192;  // 32 contiguous slabs per CU
+  if (sink_bytes < (size_t)4 * blocks) return KQ_ERR_WORKSPACE;
+  if (launch_stream_probe((const uint8_t *)buf, (int64_t)(bytes / 16), sink, blocks, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
 static bool verify_length_ok(int length) { return length == 3 || length == 7 || length == 15; }
 
 kq_status kq_draft_block_argmax(const void *w_q4k, int64_t n, int64_t k, const float *x, int verify_length,

@@ -97,5 +97,6 @@ int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ct
 int launch_gemv(const GemvLaunch &a, void *stream);
 int launch_fill(unsigned *p, int64_t n_words, void *stream);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
+int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);
 
 }  // namespace kq

@@ -95,6 +95,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void *base) {
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
+// Weight loads: every byte is read once per call, so they carry the
+// nontemporal (streaming) cache policy; the activations, which every
+// workgroup re-reads, keep the default.
+constexpr int kCpolNt = 2;
+__device__ __forceinline__ u32x4 buf_ld16_w(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCpolNt));
+}
 // 16-byte versions for the partial sums: buffer instructions with the same
 // cache policy (sc1) as the agent-scope atomic accesses above
 constexpr int kCpolSc1 = 16;
@@ -387,9 +394,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   auto load_w = [&](WTile(&w)[T]) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      w[t].hdr = buf_ld16(w_rsrc, voff[t][0], soff[t] + boff);
-      w[t].q0 = buf_ld16(w_rsrc, voff[t][1], soff[t] + boff);
-      w[t].q1 = buf_ld16(w_rsrc, voff[t][2], soff[t] + boff);
+      w[t].hdr = buf_ld16_w(w_rsrc, voff[t][0], soff[t] + boff);
+      w[t].q0 = buf_ld16_w(w_rsrc, voff[t][1], soff[t] + boff);
+      w[t].q1 = buf_ld16_w(w_rsrc, voff[t][2], soff[t] + boff);
     }
     if (uw < u_last) {
       ++uw;
@@ -841,6 +848,35 @@ __global__ __launch_bounds__(256) void kq_tile_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Read probe: every 16-byte chunk of a buffer is loaded once, workgroup b
+// streaming its own contiguous slab (four 1 KB wave loads in flight per
+// wave), XOR-folded, and one word per workgroup is written so the loads are
+// not dead. Measures the HBM read rate the weight stream can reach.
+__global__ __launch_bounds__(256) void kq_stream_probe_kernel(const u32x4 *__restrict__ p, int64_t chunks,
+                                                              unsigned *__restrict__ sink) {
+  const int64_t per = (chunks + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < chunks ? b0 + per : chunks;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t i = b0 + threadIdx.x;
+  for (; i + 3 * 256 < b1; i += 4 * 256) {
+    const u32x4 a0 = p[i], a1 = p[i + 256], a2 = p[i + 512], a3 = p[i + 768];
+    acc ^= a0 ^ a1 ^ a2 ^ a3;
+  }
+  for (; i < b1; i += 256) acc ^= p[i];
+  unsigned v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int off = 32; off >= 1; off >>= 1) v ^= __shfl_xor(v, off, 64);
+  __shared__ unsigned s[4];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = s[0] ^ s[1] ^ s[2] ^ s[3];
+}
+
+int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream) {
+  hipLaunchKernelGGL(kq_stream_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4 *)p, chunks, sink);
+  return (int)hipGetLastError();
+}
 
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream) {
   const int64_t kb = k / kQK;

@@ -21,7 +21,7 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
             "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
             "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights", "kq_draft_block_argmax",
-            "kq_draft_block_argmax_staged")
+            "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -60,6 +60,9 @@ def load() -> ctypes.CDLL:
     lib.kq_verify_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_launch_geometry.argtypes = [I64, I64, P, P, P, P]  # int*, int*, int*, int64_t*
     lib.kq_draft_block_argmax.argtypes = [P, I64, I64, P, I32, P, P, P, SZ, P]
+    lib.kq_stream_probe.argtypes = [P, SZ, P, SZ, P]
+    lib.kq_stream_probe_sink_bytes.argtypes = []
+    lib.kq_stream_probe_sink_bytes.restype = SZ
     lib.kq_draft_block_argmax_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, SZ, P]
     lib.kq_group_scratch_bytes.argtypes = [I64, I64, I32]
     lib.kq_group_scratch_bytes.restype = SZ
@@ -69,7 +72,8 @@ def load() -> ctypes.CDLL:
     lib.kq_tile_weights.argtypes = [P, I64, I64, P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
-                 "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged"):
+                 "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
+                 "kq_stream_probe"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -205,6 +209,19 @@ def verify(w, n: int, k: int, x, draft: Sequence[int], want_logits: bool = False
         _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
         _dev_ptr(ws, "workspace"), ws.numel(), _stream_handle(stream)), "kq_verify_argmax_accept")
     return am, acc, lg
+
+
+def stream_probe(buf, sink=None, stream=None):
+    """Read every byte of the device tensor `buf` once (measurement helper).
+    Returns the sink tensor (a checksum per workgroup)."""
+    torch = _torch()
+    lib = load()
+    if sink is None:
+        sink = torch.empty(lib.kq_stream_probe_sink_bytes() // 4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.kq_stream_probe(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink", torch.int32),
+                               sink.numel() * 4, _stream_handle(stream)), "kq_stream_probe")
+    return sink
 
 
 DRAFT_VERIFY_LENGTHS = (3, 7, 15)

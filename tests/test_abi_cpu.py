@@ -157,6 +157,18 @@ def test_draft_block_argument_errors():
     assert kq.DRAFT_VERIFY_LENGTHS == (3, 7, 15)
 
 
+def test_stream_probe_argument_errors():
+    lib = kq.load()
+    sb = lib.kq_stream_probe_sink_bytes()
+    assert sb > 0
+    assert lib.kq_stream_probe(None, 1024, FAKE, sb, None) == NULL
+    assert lib.kq_stream_probe(FAKE, 1024, None, sb, None) == NULL
+    assert lib.kq_stream_probe(FAKE, 0, FAKE, sb, None) == SHAPE
+    assert lib.kq_stream_probe(FAKE, 1000, FAKE, sb, None) == SHAPE
+    assert lib.kq_stream_probe(FAKE + 8, 1024, FAKE, sb, None) == ALIGN
+    assert lib.kq_stream_probe(FAKE, 1024, FAKE, sb - 4, None) == WS
+
+
 def test_staged_argument_errors():
     lib = kq.load()
     assert lib.kq_stage_rows(None, 4, 1024, FAKE, 1 << 20, None) == NULL

@@ -218,6 +218,17 @@ def test_draft_block_small(kq, n, k):
         check_argmax(head.cpu().numpy(), L[:1], A[:1], what=f"draft head {n}x{k} vl={vl}")
 
 
+def test_stream_probe_reads_every_byte(kq):
+    # the XOR of the per-workgroup words is the XOR of every 32-bit word
+    rng = np.random.default_rng(5)
+    for nbytes in (16, 3 * (1 << 20) + 16, 8192 * 1024 * 16 + 48):
+        a = rng.integers(0, 1 << 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+        sink = kq.stream_probe(to_dev(a.view(np.uint8)))
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert int(got) == int(np.bitwise_xor.reduce(a)), nbytes
+
+
 def test_one_hot_rows_extract_weights(kq):
     n, k = 300, 2048
     w = synthetic.q4k_matrix(n, k, 41)
