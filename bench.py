@@ -200,7 +200,18 @@ def run_m(stack, torch, m, steps, warmup, use_graph):
     wall, ev = timed(torch, fn, steps)
     if not same(stack.snapshot(m), eager):
         raise RuntimeError(f"timed steps at M={m} changed the results")
-    return wall, ev
+    # spread over steps: each of `steps` further steps between its own events
+    # (outside the timed region above)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    spread = {"median_ms": round(float(np.median(per)), 4), "p95_ms": round(float(np.percentile(per, 95)), 4),
+              "cv": round(float(per.std() / per.mean()), 4) if len(per) > 1 else 0.0}
+    return wall, ev, spread
 
 
 def draft_block_timing(stack, torch, calls=50):
@@ -237,6 +248,30 @@ def draft_block_timing(stack, torch, calls=50):
     return {"verify_length": 15, "us_per_call": round(us, 2), "weight_gb_s": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "calls": calls, "launch": "eager",
             "matches_verify_argmax": same_rows}
+
+
+def read_ceiling(stack, torch, calls=20):
+    """Pure-read rate of this device on the resident LM-head weights (the
+    library's read probe: every byte loaded once): the achievable ceiling
+    the weight stream is compared with, reported next to the roofline."""
+    kq = stack.kq
+    buf = stack.w_head
+    sink = kq.stream_probe(buf)
+    for _ in range(3):
+        kq.stream_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        kq.stream_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / calls
+    nbytes = buf.numel() * buf.element_size()
+    gbs = nbytes / s / 1e9
+    return {"gb_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes,
+            "buffer": "LM-head weights as streamed", "calls": calls}
 
 
 def source_digest():
@@ -350,15 +385,17 @@ def main():
     workload = f"stack{args.layers}_q4k+lmhead_verify"
     res = {}
     for m in ((16, 1) if args.m == "both" else (int(args.m),)):
-        wall, ev = run_m(stack, torch, m, args.steps, args.warmup, use_graph)
+        wall, ev, spread = run_m(stack, torch, m, args.steps, args.warmup, use_graph)
         roof = kernel_roofline(stack, m, ev, workload, "tiled16" if layout == kq.LAYOUT_TILED16 else "rows")
         gbs = stack.weight_bytes / wall / 1e9
         res[m] = {"ms_per_step": round(wall * 1e3, 4), "rows_per_s": round(m / wall, 2),
                   "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                  "event_ms_per_step": round(ev * 1e3, 4), "roofline": roof}
+                  "event_ms_per_step": round(ev * 1e3, 4), "step_spread": spread, "roofline": roof}
         log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s, "
             f"kernel {roof['avg_launch_us']} us/launch, {roof['achieved']} GB/s")
     draft = draft_block_timing(stack, torch)
+    ceiling = read_ceiling(stack, torch)
+    log(f"bench: read ceiling {ceiling['gb_s']} GB/s ({ceiling['frac']:.3f} of peak)")
     log(f"bench: draft block proposals {draft['us_per_call']} us/call, {draft['weight_gb_s']} GB/s")
     cpu = None
     if not args.no_cpu:
@@ -390,6 +427,7 @@ def main():
         "m1": res.get(1),
         "m16_over_m1": round(res[16]["ms_per_step"] / res[1]["ms_per_step"], 4) if len(res) == 2 else None,
         "roofline": top["roofline"],
+        "read_ceiling": ceiling,
         "draft_block_argmax": draft,
         "cpu_baseline": cpu,
     }
