@@ -471,20 +471,22 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     }
   };
 
-  // Prologue. Activations first (loads complete in issue order, so the
-  // first LDS stores wait for the first BI activation blocks only): units
-  // 0..BI-1 go to buffers 0..BI-1, units BI..BI+kXL-1 stay in registers
-  // (set u % (kXL + 1)); then the first D - 1 weight sets.
+  // Prologue, in issue order (loads complete in issue order): the weights
+  // of unit 0 (from HBM, the longest wait, needed first), the activations
+  // of units 0..BI-1 (to buffers 0..BI-1 before the first barrier), the
+  // weights of units 1..D-2, then the activations of units BI..BI+kXL-1,
+  // which stay in registers (set u % (kXL + 1)).
   XRegs xr[kXL + 1];
   WTile wr[D][T];
   {
     XRegs xp[BI];
+    load_w(wr[0]);
 #pragma unroll
     for (int j = 0; j < BI; ++j) load_x(xp[j]);
 #pragma unroll
-    for (int q = 0; q < kXL; ++q) load_x(xr[(BI + q) % (kXL + 1)]);
+    for (int d = 1; d < D - 1; ++d) load_w(wr[d]);
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d) load_w(wr[d]);
+    for (int q = 0; q < kXL; ++q) load_x(xr[(BI + q) % (kXL + 1)]);
 #pragma unroll
     for (int j = 0; j < BI; ++j) store_x(j, xp[j]);
   }
