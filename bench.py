@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--layers", type=int, default=synthetic.LAYERS)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a hipGraph")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the timed steps (no per-step spread, draft-block or read-probe timing): "
+                        "the dispatch sequence the counter passes expect")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--m", choices=("both", "16", "1"), default="both", help="row counts to time")
     p.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
@@ -170,7 +173,7 @@ def timed(torch, fn, steps):
     return wall, e0.elapsed_time(e1) * 1e-3 / steps
 
 
-def run_m(stack, torch, m, steps, warmup, use_graph):
+def run_m(stack, torch, m, steps, warmup, use_graph, extras=True):
     for _ in range(max(1, warmup // 2)):
         stack.step(m)
     eager = stack.snapshot(m)
@@ -200,6 +203,8 @@ def run_m(stack, torch, m, steps, warmup, use_graph):
     wall, ev = timed(torch, fn, steps)
     if not same(stack.snapshot(m), eager):
         raise RuntimeError(f"timed steps at M={m} changed the results")
+    if not extras:
+        return wall, ev, None
     # spread over steps: each of `steps` further steps between its own events
     # (outside the timed region above)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -385,7 +390,7 @@ def main():
     workload = f"stack{args.layers}_q4k+lmhead_verify"
     res = {}
     for m in ((16, 1) if args.m == "both" else (int(args.m),)):
-        wall, ev, spread = run_m(stack, torch, m, args.steps, args.warmup, use_graph)
+        wall, ev, spread = run_m(stack, torch, m, args.steps, args.warmup, use_graph, not args.no_extras)
         roof = kernel_roofline(stack, m, ev, workload, "tiled16" if layout == kq.LAYOUT_TILED16 else "rows")
         gbs = stack.weight_bytes / wall / 1e9
         res[m] = {"ms_per_step": round(wall * 1e3, 4), "rows_per_s": round(m / wall, 2),
@@ -393,10 +398,12 @@ def main():
                   "event_ms_per_step": round(ev * 1e3, 4), "step_spread": spread, "roofline": roof}
         log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s, "
             f"kernel {roof['avg_launch_us']} us/launch, {roof['achieved']} GB/s")
-    draft = draft_block_timing(stack, torch)
-    ceiling = read_ceiling(stack, torch)
-    log(f"bench: read ceiling {ceiling['gb_s']} GB/s ({ceiling['frac']:.3f} of peak)")
-    log(f"bench: draft block proposals {draft['us_per_call']} us/call, {draft['weight_gb_s']} GB/s")
+    draft = ceiling = None
+    if not args.no_extras:
+        draft = draft_block_timing(stack, torch)
+        ceiling = read_ceiling(stack, torch)
+        log(f"bench: read ceiling {ceiling['gb_s']} GB/s ({ceiling['frac']:.3f} of peak)")
+        log(f"bench: draft block proposals {draft['us_per_call']} us/call, {draft['weight_gb_s']} GB/s")
     cpu = None
     if not args.no_cpu:
         try:
