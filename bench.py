@@ -8,10 +8,14 @@ tokens). One step = stage the activation rows (one block per distinct K, the
 stack matrices being independent products of a shared input), 364 GEMVs in
 208 launches, one LM-head verify. It runs at M = 16 rows (the headline) and M = 1 (the ratio).
 
-Launch grouping follows a transformer layer's data dependencies: the three
-projections that read the same hidden state (q, k, v) go in one launch, the
-output projection in its own, gate and up in one, down in its own -- four
-launches per layer, 208 for the stack, plus the LM-head verify.
+The stack follows a transformer layer's data dependencies: the three
+projections that read the same hidden state (q, k, v) form one phase, the
+output projection the next, gate and up the next, down the last -- four
+phases per layer, 208 for the stack. By default the whole stack is one chain
+launch (kq_gemv_chain: a grid barrier between consecutive phases, so each
+phase reads its activations only after the previous phase's outputs are
+complete); --launch grouped issues one launch per phase instead. Then the
+LM-head verify.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -55,6 +59,8 @@ def parse():
     p.add_argument("--m", choices=("both", "16", "1"), default="both", help="row counts to time")
     p.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                    help="weight layout: the tiled copy (default) or llama.cpp's row-major blocks")
+    p.add_argument("--launch", choices=("chain", "grouped"), default="chain",
+                   help="stack as one chain launch (default) or one launch per phase")
     p.add_argument("--copy-probe", action="store_true",
                    help="first run plain 1 GiB device copies (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
@@ -67,9 +73,10 @@ def log(*a):
 class Stack:
     """Device-resident weights, staged activations, outputs and scratch."""
 
-    def __init__(self, kq, torch, dev, layers, layout):
+    def __init__(self, kq, torch, dev, layers, layout, launch="chain"):
         self.kq, self.torch, self.dev = kq, torch, dev
         self.layout = layout
+        self.launch = launch
         self.mats = synthetic.stack_matrices(layers)
         head = synthetic.LM_HEAD
         self.head = synthetic.Gemv(n=head["n"], k=head["k"], seed=head["seed"])
@@ -97,6 +104,7 @@ class Stack:
         self.out = {kk: [torch.empty((16, kk[0]), dtype=torch.float32, device=dev) for _ in range(kk[2])]
                     for kk in keys}
         self.scratch = {kk: kq.new_group_scratch(kk[0], kk[1], kk[2], dev) for kk in keys}
+        self.chains = {}
         self.head_scratch = kq.new_scratch(self.head.n, self.head.k, dev)
         self.am = torch.empty(16, dtype=torch.int32, device=dev)
         self.acc = torch.empty(2, dtype=torch.int32, device=dev)
@@ -119,17 +127,33 @@ class Stack:
 
     @property
     def launches(self):
-        return len(self.groups) + 1
+        """Launches of the main kernel per step."""
+        return (1 if self.launch == "chain" else len(self.groups)) + 1
+
+    def chain(self, m):
+        """The stack as one chain (encoded once per m)."""
+        if m not in self.chains:
+            phases = []
+            for grp in self.groups:
+                g = self.mats[grp[0]]
+                key = (g.n, g.k, len(grp))
+                phases.append(([self.w[j] for j in grp], g.n, g.k, self.staged[g.k],
+                               [o[:m] for o in self.out[key]]))
+            self.chains[m] = self.kq.chain_encode(phases, m, layout=self.layout)
+        return self.chains[m]
 
     def step(self, m):
         kq = self.kq
         for k in self.ks:
             kq.stage_rows(self.x[k][:m], staged=self.staged[k])
-        for grp in self.groups:
-            g = self.mats[grp[0]]
-            key = (g.n, g.k, len(grp))
-            kq.gemv_staged_group([self.w[j] for j in grp], g.n, g.k, self.staged[g.k], m, self.scratch[key],
-                                 logits=[o[:m] for o in self.out[key]], layout=self.layout)
+        if self.launch == "chain":
+            kq.gemv_chain(self.chain(m))
+        else:
+            for grp in self.groups:
+                g = self.mats[grp[0]]
+                key = (g.n, g.k, len(grp))
+                kq.gemv_staged_group([self.w[j] for j in grp], g.n, g.k, self.staged[g.k], m, self.scratch[key],
+                                     logits=[o[:m] for o in self.out[key]], layout=self.layout)
         h = self.head
         kq.verify_staged(self.w_head, h.n, h.k, self.staged[h.k], m, self.draft[:m - 1],
                          self.head_scratch, out=(self.am[:m], self.acc, None), layout=self.layout)
@@ -142,6 +166,8 @@ class Stack:
         for grp in self.groups:
             g = self.mats[grp[0]]
             out.append(len(grp) * (0.5625 * g.n * g.k + 4 * m * g.n) + 4 * m * g.k)
+        if self.launch == "chain":
+            out = [sum(out)]
         out.append(0.5625 * self.head.n * self.head.k + 4 * m * self.head.k + 4 * (m + 2))
         return out
 
@@ -203,6 +229,8 @@ def run_m(stack, torch, m, steps, warmup, use_graph, extras=True):
     wall, ev = timed(torch, fn, steps)
     if not same(stack.snapshot(m), eager):
         raise RuntimeError(f"timed steps at M={m} changed the results")
+    if stack.launch == "chain" and stack.chain(m).error_word() != 0:
+        raise RuntimeError(f"a chain barrier timed out at M={m}")
     if not extras:
         return wall, ev, None
     # spread over steps: each of `steps` further steps between its own events
@@ -385,7 +413,7 @@ def main():
     if args.copy_probe:
         copy_probe(torch, dev)
     layout = kq.LAYOUT_TILED16 if args.layout == "tiled" else kq.LAYOUT_ROWS
-    stack = Stack(kq, torch, dev, args.layers, layout)
+    stack = Stack(kq, torch, dev, args.layers, layout, args.launch)
     use_graph = not args.no_graph
     workload = f"stack{args.layers}_q4k+lmhead_verify"
     res = {}
@@ -429,6 +457,7 @@ def main():
                    "matrices": len(stack.mats) + 1, "launches_per_step": stack.launches + len(stack.ks),
                    "weight_bytes": stack.weight_bytes,
                    "m": head_m, "k_draft": head_m - 1, "launch": "hipgraph" if use_graph else "eager",
+                   "stack_launch": args.launch,
                    "weight_layout": "tiled16" if layout == kq.LAYOUT_TILED16 else "llama.cpp rows"},
         "m16": res.get(16),
         "m1": res.get(1),

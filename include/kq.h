@@ -235,6 +235,83 @@ kq_status kq_gemv_staged_group(const void *const *w_q4k, int layout, int count, 
 kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave,
                              int *workgroups, int64_t *units);
 
+/* ---------------------------------------------------------------- chains
+ * A chain launch runs a sequence of grouped products in ONE grid, each
+ * phase depending on the one before it: phase i + 1 starts reading its
+ * activations only after every logit of phase i is complete and visible
+ * device-wide (a grid-wide barrier between phases), which is the order a
+ * transformer layer imposes (q/k/v, then o, then gate/up, then down; the
+ * target forward of ch. 33 section 33.1 and ch. 8 section 8.1 scores the
+ * k+1 rows through all of them). Weights do not depend on earlier phases,
+ * so each workgroup loads the first weights of the next phase while it
+ * waits. Every phase streams its weights once for all m rows, exactly as
+ * kq_gemv_staged_group does; results are within the kq.h tolerance and
+ * bitwise deterministic (and bitwise equal to kq_gemv_staged_group when
+ * that call uses the same geometry: 8 waves of one 16-row tile and the
+ * same number of workgroups).
+ *
+ * The kernel keeps all of its workgroups resident at once (one per CU);
+ * kq_chain_encode sizes the grid from the current device's capacity. Each
+ * barrier wait is bounded: a wait longer than one second gives up, sets the
+ * 32-bit word at byte KQ_CHAIN_ERROR_OFFSET of the scratch to nonzero and
+ * ends the launch early (its logits are then incomplete). That word is
+ * sticky: kq_workspace_init clears it, together with the barrier count the
+ * failed launch left behind. */
+
+#define KQ_MAX_GROUP 8
+#define KQ_CHAIN_ERROR_OFFSET 256
+#define KQ_MAX_CHAIN_PHASES 65536
+
+/* One phase: 1 <= count <= KQ_MAX_GROUP matrices of n x k (all in the
+ * chain's layout, each 16-byte aligned, device) that read the same staged
+ * activations (device, kq_stage_rows for this k, 256-byte aligned, staged
+ * with at least the chain's m rows), each writing fp32 [m][n] logits
+ * (device). */
+typedef struct kq_chain_phase {
+  int count;
+  int64_t n, k;
+  const void *w_q4k[KQ_MAX_GROUP];
+  float *logits[KQ_MAX_GROUP];
+  const void *staged;
+} kq_chain_phase;
+
+/* Written by kq_chain_encode, read by kq_gemv_chain (host struct). */
+typedef struct kq_chain_plan {
+  int32_t n_phases;
+  int32_t m;
+  int32_t layout;
+  int32_t workgroups;     /* grid size: min(device capacity, fewest units of any phase) */
+  int32_t max_groups;     /* largest number of row groups of any phase */
+  int32_t tiles_per_wave; /* 16-row tiles per wave (row groups of 128 x this) */
+  uint64_t table_bytes;   /* bytes of the encoded phase table */
+  uint64_t scratch_bytes; /* device scratch the launch needs */
+} kq_chain_plan;
+
+/* Bytes of the encoded table of n_phases phases (0 if n_phases is out of
+ * [1, KQ_MAX_CHAIN_PHASES]). */
+size_t kq_chain_table_bytes(int n_phases);
+
+/* Validate a chain and encode its phase table into table_host (host memory,
+ * >= kq_chain_table_bytes(n_phases) bytes); the caller copies those bytes to
+ * a device buffer (16-byte aligned) once and passes it to every
+ * kq_gemv_chain call of this chain. Checks every phase as the staged calls
+ * do (KQ_ERR_NULL / SHAPE / ALIGN), then queries the current device (HIP
+ * calls, nothing enqueued) for how many chain workgroups it holds at once;
+ * KQ_ERR_LAUNCH if that query fails. Fills *plan. The plan and table are
+ * valid on the device that was current during this call. */
+kq_status kq_chain_encode(const kq_chain_phase *phases, int n_phases, int m, int layout,
+                          void *table_host, size_t table_bytes, kq_chain_plan *plan);
+
+/* Run an encoded chain.
+ *  table_dev  device copy of the encoded table (read only)
+ *  plan       the plan kq_chain_encode wrote for it (host)
+ *  scratch    device, >= plan->scratch_bytes, 256-byte aligned, zeroed once
+ *             by kq_workspace_init; every successful launch leaves it as it
+ *             found it (a timed-out one sets the error word, see above)
+ * Calls sharing a scratch must be ordered (e.g. the same stream). */
+kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan,
+                        void *scratch, size_t scratch_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

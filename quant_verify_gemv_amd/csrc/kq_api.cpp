@@ -9,6 +9,10 @@
 
 namespace kq {
 
+#ifndef KQ_CHAIN_TPW
+#define KQ_CHAIN_TPW 1
+#endif
+
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -176,6 +180,26 @@ kq_status kq_stage_rows(const float *x, int m, int64_t k, void *staged, size_t s
   return KQ_OK;
 }
 
+// The kernel's description of one phase: count matrices of n x k on one
+// staged activation block, cut into units by geometry g.
+static void fill_phase(Phase &ph, const Geometry &g, const void *const *w, float *const *logits, int count,
+                       int64_t n, int64_t k, const void *staged) {
+  memset(&ph, 0, sizeof(ph));
+  for (int i = 0; i < count; ++i) {
+    ph.w[i] = (const uint8_t *)w[i];
+    ph.logits[i] = logits ? logits[i] : nullptr;
+  }
+  ph.staged = (const uint8_t *)staged;
+  ph.n = (int)n;
+  ph.row_bytes = (int)((k / kQK) * kBlockBytes);
+  ph.n_tiles = (int)cdiv(n, 16);
+  ph.units = (int)g.units;
+  ph.count = count;
+  ph.kb = g.kb;
+  ph.n_wg_per = g.n_wg_per;
+  ph.n_groups = g.n_groups;
+}
+
 // Shared validation + launch of the main kernel on staged activations for
 // `count` matrices of the same shape (verify: count == 1).
 // verify: per-row argmax, written from row argmax_from on (0 for the verify
@@ -211,17 +235,10 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
       a.draft[i] = draft_host[i];
     }
   }
-  for (int i = 0; i < count; ++i) {
-    a.w[i] = (const uint8_t *)w[i];
-    a.logits[i] = logits ? logits[i] : nullptr;
-  }
-  a.n = n;
-  a.k = k;
-  a.row_bytes = (k / kQK) * kBlockBytes;
+  a.g = geometry(n, k, count);
+  fill_phase(a.ph, a.g, w, logits, count, n, k, staged);
   a.layout = layout;
-  a.n_tiles = cdiv(n, 16);
   a.m = m;
-  a.staged = (const uint8_t *)staged;
   uint8_t *sc = (uint8_t *)scratch;
   a.done = (unsigned *)sc;
   a.group_cnt = (unsigned *)(sc + sl.cnt_off);
@@ -233,7 +250,6 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   a.accept_out = accept_out;
   a.k_draft = verify && accept_out ? m - 1 : 0;
   a.verify = verify ? 1 : 0;
-  a.g = geometry(n, k, count);
   if (x_to_stage) {
     if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, a.g.n_groups, stream))
       return KQ_ERR_LAUNCH;
@@ -312,6 +328,116 @@ kq_status kq_stream_probe(const void *buf, size_t bytes, uint32_t *sink, size_t 
   const int blocks = 8192;  // 32 contiguous slabs per CU
   if (sink_bytes < (size_t)4 * blocks) return KQ_ERR_WORKSPACE;
   if (launch_stream_probe((const uint8_t *)buf, (int64_t)(bytes / 16), sink, blocks, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+size_t kq_chain_table_bytes(int n_phases) {
+  if (n_phases < 1 || n_phases > KQ_MAX_CHAIN_PHASES) return 0;
+  return (size_t)n_phases * sizeof(Phase);
+}
+
+// Chain geometry: 8 waves of `tpw` 16-row tiles (row groups of 128 tpw
+// rows), barriers every 4 units, 4 weight register sets.
+static Geometry chain_geometry(int64_t n, int64_t k, int count, int tpw) {
+  Geometry g;
+  g.count = count;
+  g.waves = 8;
+  g.tpw = tpw;
+  g.bi = 4;
+  g.depth = 4;
+  g.rows = 128 * tpw;
+  g.n_wg_per = (int)cdiv(n, g.rows);
+  g.n_groups = count * g.n_wg_per;
+  g.kb = (int)(k / kQK);
+  g.units = (int64_t)g.n_groups * g.kb;
+  g.n_wg = 0;
+  return g;
+}
+
+// Tiles per wave of a chain's phases.
+static int chain_tpw() { return KQ_CHAIN_TPW; }
+
+// Chain scratch: control words, group counters, partials, then one
+// 256-byte line per workgroup for its barrier release flag.
+static size_t chain_part_off(int max_groups) {
+  return align256((size_t)kCntOff + sizeof(unsigned) * kCntStride * (size_t)max_groups);
+}
+static size_t chain_flag_off(int max_groups, int64_t wg, int tpw) {
+  return chain_part_off(max_groups) + align256(sizeof(float) * (size_t)wg * 2 * kMaxRows * 128 * (size_t)tpw);
+}
+static size_t chain_flag_bytes(int64_t wg) { return (size_t)wg * 256; }
+
+kq_status kq_chain_encode(const kq_chain_phase *phases, int n_phases, int m, int layout, void *table_host,
+                          size_t table_bytes, kq_chain_plan *plan) {
+  if (!phases || !table_host || !plan) return KQ_ERR_NULL;
+  if (n_phases < 1 || n_phases > KQ_MAX_CHAIN_PHASES || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
+  if (layout != KQ_LAYOUT_ROWS && layout != KQ_LAYOUT_TILED16) return KQ_ERR_SHAPE;
+  int64_t min_units = -1;
+  int max_groups = 0;
+  const int tpw = chain_tpw();
+  for (int i = 0; i < n_phases; ++i) {
+    const kq_chain_phase &q = phases[i];
+    if (q.count < 1 || q.count > kMaxGroup || !shape_ok(q.n, q.k)) return KQ_ERR_SHAPE;
+    if (!q.staged) return KQ_ERR_NULL;
+    for (int j = 0; j < q.count; ++j)
+      if (!q.w_q4k[j] || !q.logits[j]) return KQ_ERR_NULL;
+    for (int j = 0; j < q.count; ++j)
+      if (!al(q.w_q4k[j], 16) || !al(q.logits[j], 4)) return KQ_ERR_ALIGN;
+    if (!al(q.staged, 256)) return KQ_ERR_ALIGN;
+    const Geometry g = chain_geometry(q.n, q.k, q.count, tpw);
+    if (min_units < 0 || g.units < min_units) min_units = g.units;
+    if (g.n_groups > max_groups) max_groups = g.n_groups;
+  }
+  if (table_bytes < kq_chain_table_bytes(n_phases)) return KQ_ERR_WORKSPACE;
+  const int cap = chain_capacity(tpw);
+  if (cap <= 0) return KQ_ERR_LAUNCH;
+  const int64_t wg = min_units < cap ? min_units : cap;
+  Phase *tab = (Phase *)table_host;
+  for (int i = 0; i < n_phases; ++i) {
+    const kq_chain_phase &q = phases[i];
+    fill_phase(tab[i], chain_geometry(q.n, q.k, q.count, tpw), q.w_q4k, q.logits, q.count, q.n, q.k, q.staged);
+  }
+  memset(plan, 0, sizeof(*plan));
+  plan->n_phases = n_phases;
+  plan->m = m;
+  plan->layout = layout;
+  plan->workgroups = (int32_t)wg;
+  plan->max_groups = max_groups;
+  plan->tiles_per_wave = tpw;
+  plan->table_bytes = kq_chain_table_bytes(n_phases);
+  plan->scratch_bytes = chain_flag_off(max_groups, wg, tpw) + chain_flag_bytes(wg);
+  return KQ_OK;
+}
+
+kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan, void *scratch, size_t scratch_bytes,
+                        void *stream) {
+  if (!table_dev || !plan || !scratch) return KQ_ERR_NULL;
+  if (plan->n_phases < 1 || plan->n_phases > KQ_MAX_CHAIN_PHASES || plan->m < 1 || plan->m > kMaxRows ||
+      plan->workgroups < 1 || plan->max_groups < 1 || (plan->tiles_per_wave != 1 && plan->tiles_per_wave != 2) ||
+      (plan->layout != KQ_LAYOUT_ROWS && plan->layout != KQ_LAYOUT_TILED16))
+    return KQ_ERR_SHAPE;
+  if (!al(table_dev, 16) || !al(scratch, 256)) return KQ_ERR_ALIGN;
+  const size_t need = chain_flag_off(plan->max_groups, plan->workgroups, plan->tiles_per_wave) +
+                      chain_flag_bytes(plan->workgroups);
+  if (plan->scratch_bytes != need) return KQ_ERR_SHAPE;  // not a plan kq_chain_encode wrote
+  if (scratch_bytes < need) return KQ_ERR_WORKSPACE;
+  GemvLaunch a;
+  memset(&a, 0, sizeof(a));
+  uint8_t *sc = (uint8_t *)scratch;
+  a.chain = (const Phase *)table_dev;
+  a.n_phases = plan->n_phases;
+  a.bar = (unsigned *)(sc + kBarOff);
+  a.err = (unsigned *)(sc + kErrOff);
+  a.m = plan->m;
+  a.layout = plan->layout;
+  a.done = (unsigned *)sc;
+  a.group_cnt = (unsigned *)(sc + kCntOff);
+  a.partials = (float *)(sc + chain_part_off(plan->max_groups));
+  a.epoch = (unsigned *)(sc + kEpochOff);
+  a.flags = (unsigned long long *)(sc + chain_flag_off(plan->max_groups, plan->workgroups, plan->tiles_per_wave));
+  a.g = chain_geometry(128, kQK, 1, plan->tiles_per_wave);
+  a.g.n_wg = plan->workgroups;
+  if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;
   return KQ_OK;
 }
 

@@ -32,13 +32,20 @@ constexpr int64_t kStageBytes = 16384 + 512 + 64;  // 16,960 B per block (16-B a
 
 // Scratch area of the main kernel (control words zero between calls; every
 // launch leaves them zero again):
-//   [0, 256)   done counter (u32)
+//   0          done counter (u32, verify)
+//   128        grid-barrier arrival count (u32, chain launches)
+//   256        barrier time-out flag (u32, chain launches; sticky: set only
+//              when a barrier wait gave up, cleared by kq_workspace_init)
+//   384        launch epoch (u32, chain launches; +1 per completed launch)
 //   cnt_off    per-row-group arrival counters [n_groups], one u32 per
 //              128-byte line (kCntStride words apart) so that the atomics of
 //              different groups do not queue on one line
 //   keys_off   per-workgroup argmax keys [n_wg][16] (u64)
 //   part_off   partial sums [n_wg][2][16][rows per group] fp32
-constexpr int64_t kCntOff = 256;
+constexpr int64_t kBarOff = 128;
+constexpr int64_t kErrOff = 256;
+constexpr int64_t kEpochOff = 384;
+constexpr int64_t kCntOff = 512;
 constexpr int kCntStride = 32;
 
 // Work decomposition. A row group is 16 * waves * tpw consecutive output rows
@@ -64,14 +71,30 @@ struct ScratchLayout {
   size_t cnt_off, keys_off, part_off, total;
 };
 
-struct GemvLaunch {
+// One phase: `count` matrices of n x k that read the same staged
+// activations (units and groups as in Geometry).
+struct Phase {
   const uint8_t *w[kMaxGroup];
   float *logits[kMaxGroup];  // entries may be null in verify mode
-  int64_t n, k, row_bytes;
+  const uint8_t *staged;
+  // 32-bit: a matrix is smaller than 4 GiB, so n, its row bytes, its tiles
+  // and its units (fewer than 2^31) all fit
+  int n, row_bytes;
+  int n_tiles;  // ceil(n / 16)
+  int units;
+  int count, kb, n_wg_per, n_groups;
+};
+
+struct GemvLaunch {
+  Phase ph;            // single launches: the launch's phase
+  const Phase *chain;  // chain launches: device table of n_phases phases (else null)
+  int n_phases;
+  unsigned *bar;       // chain: barrier count (scratch + kBarOff)
+  unsigned *err;       // chain: time-out flag (scratch + kErrOff)
+  unsigned *epoch;     // chain: launch epoch (scratch + kEpochOff)
+  unsigned long long *flags;  // chain: per-workgroup release flags, 256 bytes apart
   int m;
   int layout;       // KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16
-  int64_t n_tiles;  // ceil(n / 16)
-  const uint8_t *staged;
   float *partials;
   unsigned *done;
   unsigned *group_cnt;
@@ -95,6 +118,9 @@ ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
 int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ctrl, int64_t n_groups,
                  void *stream);
 int launch_gemv(const GemvLaunch &a, void *stream);
+// Workgroups of the chain kernel (8 waves of tpw 16-row tiles) the current
+// device holds at once, or a negative HIP error code.
+int chain_capacity(int tpw);
 int launch_fill(unsigned *p, int64_t n_words, void *stream);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
 int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);

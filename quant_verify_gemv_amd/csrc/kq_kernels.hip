@@ -263,6 +263,15 @@ __global__ void kq_fill_kernel(unsigned *p, int64_t n) {
 // u % kb). Wave w owns the T 16-row tiles t W + w of the current row group;
 // the activations of each block are staged once in LDS per workgroup and
 // every A-operand read from LDS feeds all T tiles of the wave.
+//
+// A chain launch (CHAIN) runs a sequence of such phases in one grid: each
+// phase is split among all workgroups as above, and a grid-wide barrier
+// separates consecutive phases, so a phase starts reading its activations
+// only after every output of the previous one is complete and visible
+// device-wide, as when one projection's input is computed from the
+// previous one's output. Weights do not depend on earlier phases: each
+// workgroup issues the first weight loads of the next phase before it
+// waits at the barrier.
 
 struct WTile {
   u32x4 hdr, q0, q1;
@@ -278,7 +287,40 @@ constexpr int lcm_int(int a, int b) {
   return a / x * b;
 }
 
-template <int W, int T, int BI, int D>
+// Grid barrier between chain phases. Every workgroup adds one arrival to a
+// device-wide count (agent-scope atomic); the phase is complete when the
+// count reaches (phase + 1) times the workgroups. The workgroup whose
+// arrival completes the count releases the others: its threads write every
+// workgroup's own release flag, one 256-byte line per workgroup, and each
+// waiting workgroup polls only its own flag. (Polling the count itself from
+// every workgroup, one hot line, was measured to slow the last workgroups'
+// own coherent stores and atomics, the split-group reductions, severalfold.)
+// A flag holds (launch epoch << 32) | (barrier + 1), so a flag left by the
+// previous launch never matches; the epoch is a device word the final
+// arrival of each launch increments, read by every workgroup before its
+// first arrival. Every wait gives up after kSpinTicks of the 100 MHz
+// real-time counter (or when another workgroup has raised *err) and raises
+// *err, so every wait ends.
+constexpr unsigned long long kSpinTicks = 100000000ull;  // 1 s
+constexpr int kFlagStride = 32;                        // u64 words between release flags (256 bytes)
+
+__device__ __forceinline__ int spin_flag(const unsigned long long *flag, unsigned long long want, unsigned *err) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    if (ld_dev(flag) == want) return 1;
+    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return 0;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return 0;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Field f of phase ph: the launch's own phase, or entry ph of a chain's table.
+#define KQ_PH(I_, f) (CHAIN ? ((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f : a.ph.f)
+
+template <int W, int T, int BI, int D, bool CHAIN>
 __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv_kernel(GemvLaunch a) {
   static_assert(W % 4 == 0, "waves spread evenly over the 4 SIMDs");
   // D weight register sets: the weights of unit i + D - 1 are loaded while
@@ -312,27 +354,18 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   const int kg = lane >> 4;
   const int ln = lane & 15;
   const int M = a.m;
-  const int64_t N = a.n;
-  const int KB = a.g.kb;
-  const int n_wg_per = a.g.n_wg_per;
+  // unit indices fit in 32 bits: every matrix is smaller than 4 GiB, so a
+  // phase has fewer than 2^31 units
+  const int P = gridDim.x;
+  const int p = blockIdx.x;
+  const int n_ph = CHAIN ? a.n_phases : 1;
 
-  // this workgroup's units
-  const int64_t U = a.g.units;
-  const int64_t P = gridDim.x;
-  const int64_t p = blockIdx.x;
-  const int64_t base = U / P, rem = U % P;
-  const int64_t u0 = p * base + (p < rem ? p : rem);
-  const int64_t nu = base + (p < rem ? 1 : 0);
-  const int64_t u_last = u0 + nu - 1;
-  auto owner = [&](int64_t u) -> int64_t {
-    const int64_t big = rem * (base + 1);
-    return u < big ? u / (base + 1) : rem + (u - big) / base;
+  // this workgroup's run of the U units of a phase
+  auto run_start = [&](int U) -> int {
+    const int b = U / P, r = U % P;
+    return p * b + (p < r ? p : r);
   };
-
-  auto group_row0 = [&](int g, int &mat) -> int64_t {
-    mat = g / n_wg_per;
-    return (int64_t)(g - mat * n_wg_per) * kRows;
-  };
+  auto run_len = [&](int U) -> int { return U / P + (p < U % P ? 1 : 0); };
   auto tile_row = [&](int t) -> int { return (t * W + wave) * 16 + ln; };  // row within the group
 
   if (tid < kMaxRows) s_keys[tid] = 0ull;
@@ -342,20 +375,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // 2(kg>>1)+1 of a packed word into the low bytes of an fp16 pair
   const unsigned sel_sc = (kg >> 1) ? 0x00070006u : 0x00050004u;
   const unsigned mask_hi = in_vgpr(0x00F000F0u);
-  f32x4 acc[T], acc_first[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_first[t] = acc[t];
-  }
 
-  // Prefetch trackers: the weights run three units ahead of the compute,
-  // the activations two (both clamped to the last unit, so every load is
-  // unconditional and outstanding loads are counted statically).
-  int64_t uw = u0;
-  int gw = (int)(u0 / KB), bw = (int)(u0 % KB);
-  // Weight addressing, one code path for both layouts, through buffer loads
-  // from the current matrix (every matrix is smaller than 4 GiB): the lane's
+  // Weight stream: the weights run D - 1 units ahead of the compute (in a
+  // chain, across the end of a phase into the next one), clamped to the
+  // phase's last unit, so every load is unconditional and outstanding loads
+  // are counted statically. It keeps its own copy of its phase's geometry.
+  // Addressing, one code path for both layouts, through buffer loads from
+  // the current matrix (every matrix is smaller than 4 GiB): the lane's
   // bytes of block b of tile t sit at voff[t][0..2] + soff[t] + b *
   // block_stride. Row-major (llama.cpp): voff = the lane's row (clamped to
   // the last row) times the row bytes + {0, 16 + 16kg, 80 + 16kg}, soff = 0,
@@ -363,26 +389,38 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // = the 16-row tile's record, stride = tiles * 2,304.
   const bool tiled = a.layout == KQ_LAYOUT_TILED16;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const unsigned block_stride = tiled ? (unsigned)(a.n_tiles * kTileBlockBytes) : (unsigned)kBlockBytes;
+  // The phase fields the stream needs: a single launch reads them from its
+  // arguments; a chain keeps the current phase's in registers.
+  int wp = 0;  // the weight stream's phase
+  int uw = 0, uw_last = 0, gw = 0, bw = 0;
+  int cw_n = 1, cw_rb = 0, cw_nt = 1, cw_kb = 1, cw_nwg = 1;
+  auto w_n = [&]() -> int { return CHAIN ? cw_n : a.ph.n; };
+  auto w_rb = [&]() -> int { return CHAIN ? cw_rb : a.ph.row_bytes; };
+  auto w_nt = [&]() -> int { return CHAIN ? cw_nt : a.ph.n_tiles; };
+  auto w_kb = [&]() -> int { return CHAIN ? cw_kb : a.ph.kb; };
+  auto w_nwg = [&]() -> int { return CHAIN ? cw_nwg : a.ph.n_wg_per; };
+  auto block_stride = [&]() -> unsigned {
+    return tiled ? (unsigned)w_nt() * (unsigned)kTileBlockBytes : (unsigned)kBlockBytes;
+  };
+  unsigned boff = 0;
   __amdgpu_buffer_rsrc_t w_rsrc;
   unsigned voff[T][3], soff[T];
-  unsigned boff = (unsigned)bw * block_stride;  // block bw within the row
   auto set_rowp = [&]() {
-    int mat;
-    const int64_t r0 = group_row0(gw, mat);
-    w_rsrc = dev_rsrc(a.w[mat]);
+    const int mat = gw / w_nwg();
+    const int r0 = (gw - mat * w_nwg()) * kRows;
+    w_rsrc = dev_rsrc(KQ_PH(wp, w[mat]));
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (tiled) {
-        int64_t ti = (r0 + (t * W + wave_u) * 16) / 16;
-        ti = ti < a.n_tiles ? ti : a.n_tiles - 1;
-        soff[t] = (unsigned)(ti * kTileBlockBytes);
+        int ti = (r0 + (t * W + wave_u) * 16) / 16;
+        ti = ti < w_nt() ? ti : w_nt() - 1;
+        soff[t] = (unsigned)ti * (unsigned)kTileBlockBytes;
         voff[t][0] = 16u * ln;
         voff[t][1] = (unsigned)kTileQ0 + 16u * lane;
         voff[t][2] = (unsigned)kTileQ1 + 16u * lane;
       } else {
-        const int64_t row = r0 + tile_row(t);
-        const unsigned rb = (unsigned)((row < N ? row : N - 1) * a.row_bytes);
+        const int row = r0 + tile_row(t);
+        const unsigned rb = (unsigned)(row < w_n() ? row : w_n() - 1) * (unsigned)w_rb();
         soff[t] = 0u;
         voff[t][0] = rb;
         voff[t][1] = rb + 16u + 16u * kg;
@@ -390,7 +428,23 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       }
     }
   };
-  set_rowp();
+  auto begin_w = [&](int ph) {
+    wp = ph;
+    const int U = KQ_PH(ph, units);
+    if (CHAIN) {
+      cw_n = KQ_PH(ph, n);
+      cw_rb = KQ_PH(ph, row_bytes);
+      cw_nt = KQ_PH(ph, n_tiles);
+      cw_kb = KQ_PH(ph, kb);
+      cw_nwg = KQ_PH(ph, n_wg_per);
+    }
+    uw = run_start(U);
+    uw_last = uw + run_len(U) - 1;
+    gw = uw / w_kb();
+    bw = uw % w_kb();
+    boff = (unsigned)bw * block_stride();
+    set_rowp();
+  };
   auto load_w = [&](WTile(&w)[T]) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -398,10 +452,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       w[t].q0 = buf_ld16_w(w_rsrc, voff[t][1], soff[t] + boff);
       w[t].q1 = buf_ld16_w(w_rsrc, voff[t][2], soff[t] + boff);
     }
-    if (uw < u_last) {
+    if (uw < uw_last) {
       ++uw;
-      boff += block_stride;
-      if (++bw == KB) {
+      boff += block_stride();
+      if (++bw == w_kb()) {
         bw = 0;
         boff = 0u;
         ++gw;
@@ -409,412 +463,510 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       }
     }
   };
-  int64_t ux = u0;
-  int bx = (int)(u0 % KB);
+
   // last round: threads past the record re-load its last chunk and skip the store
   const int xlast = tid + kNth * (kXj - 1) < kXc ? tid + kNth * (kXj - 1) : kXc - 1;
-  const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(a.staged);
   struct XRegs {
     u32x4 a[kXj];
   };
-  auto load_x = [&](XRegs &x) {
-    const unsigned src = (unsigned)bx * (unsigned)kStageBytes;
-#pragma unroll
-    for (int j = 0; j < kXj; ++j)
-      x.a[j] = buf_ld16(x_rsrc, (unsigned)(j < kXj - 1 ? tid + kNth * j : xlast) * 16u, src);
-    if (ux < u_last) {
-      ++ux;
-      if (++bx == KB) bx = 0;
-    }
-  };
-  auto store_x = [&](int buf, const XRegs &x) {
-#pragma unroll
-    for (int j = 0; j < kXj; ++j)
-      if (j < kXj - 1 || tid + kNth * j < kXc) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
+  XRegs xr[kXL + 1];
+  WTile wr[D][T];
+  f32x4 acc[T], acc_first[T];
+  // finished rows of whole row groups: the argmax keys are reduced over the
+  // wave's tiles and its 16 rows per lane group into a running maximum per
+  // activation row 4kg + r (wave_key[r], held by every lane of the group)
+  // that goes to LDS after the loop.
+  unsigned long long wave_key[4] = {0ull, 0ull, 0ull, 0ull};
+  const __amdgpu_buffer_rsrc_t part_rsrc = dev_rsrc(a.partials);
+  // Logits of a chain phase are written through to the device coherence
+  // point (agent-scope stores), so they are visible to every workgroup once
+  // the writer's stores have completed, before it arrives at the barrier.
+  auto put = [&](float *q, float v) {
+    if (CHAIN)
+      st_dev(q, v);
+    else
+      *q = v;
   };
 
-  // finished rows of a whole row group: logits and/or the argmax keys. The
-  // keys are reduced over the wave's tiles and its 16 rows per lane group
-  // into a running maximum per activation row 4kg + r (wave_key[r], held
-  // by every lane of the group) that goes to LDS after the loop.
-  unsigned long long wave_key[4] = {0ull, 0ull, 0ull, 0ull};
-  auto write_rows = [&](int g, const f32x4(&v)[T]) {
-    int mat;
-    const int64_t r0 = group_row0(g, mat);
-    float *logits = a.logits[mat];
-    if (logits) {
+  // chain launches: the launch epoch, read by thread 0 before this
+  // workgroup's first arrival (the final arrival of the launch increments
+  // it) and shared through LDS (the prologue's barrier publishes it)
+  __shared__ unsigned long long s_epoch;
+  if (CHAIN && tid == 0) {
+    s_epoch = (unsigned long long)__hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 32;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): read before any arrival
+  }
+
+  begin_w(0);
+  if (CHAIN) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int64_t row = r0 + tile_row(t);
-        if (row < N) {
+    for (int d = 0; d < D - 1; ++d) load_w(wr[d]);
+  }
+
+  for (int ph = 0; ph < n_ph; ++ph) {
+    const int N = KQ_PH(ph, n);
+    const int KB = KQ_PH(ph, kb);
+    const int n_wg_per = KQ_PH(ph, n_wg_per);
+    const int U = KQ_PH(ph, units);
+    const int base = U / P, rem = U % P;
+    const int u0 = p * base + (p < rem ? p : rem);
+    const int nu = base + (p < rem ? 1 : 0);
+    const int u_last = u0 + nu - 1;
+    auto owner = [&](int u) -> int {
+      const int big = rem * (base + 1);
+      return u < big ? u / (base + 1) : rem + (u - big) / base;
+    };
+    auto group_row0 = [&](int g, int &mat) -> int {
+      mat = g / n_wg_per;
+      return (g - mat * n_wg_per) * kRows;
+    };
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = 4 * kg + r;
-            if (m < M) logits[(int64_t)m * N + row] = v[t][r];
+    for (int t = 0; t < T; ++t) {
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_first[t] = acc[t];
+    }
+
+    // Activation stream, two units behind the weights and never past the
+    // phase's last unit (in a chain, a phase's activations are read only
+    // after the barrier that ends the previous phase).
+    int ux = u0;
+    int bx = u0 % KB;
+    const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_PH(ph, staged));
+    auto load_x = [&](XRegs &x) {
+      const unsigned src = (unsigned)bx * (unsigned)kStageBytes;
+#pragma unroll
+      for (int j = 0; j < kXj; ++j)
+        x.a[j] = buf_ld16(x_rsrc, (unsigned)(j < kXj - 1 ? tid + kNth * j : xlast) * 16u, src);
+      if (ux < u_last) {
+        ++ux;
+        if (++bx == KB) bx = 0;
+      }
+    };
+    auto store_x = [&](int buf, const XRegs &x) {
+#pragma unroll
+      for (int j = 0; j < kXj; ++j)
+        if (j < kXj - 1 || tid + kNth * j < kXc) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
+    };
+
+    auto write_rows = [&](int g, const f32x4(&v)[T]) {
+      int mat;
+      const int r0 = group_row0(g, mat);
+      float *logits = KQ_PH(ph, logits[mat]);
+      if (logits) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int row = r0 + tile_row(t);
+          if (row < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = 4 * kg + r;
+              if (m < M) put(&logits[(int64_t)m * N + row], v[t][r]);
+            }
           }
         }
       }
-    }
-    if (a.verify) {
+      if (!CHAIN && a.verify) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        unsigned long long best = 0ull;
+        for (int r = 0; r < 4; ++r) {
+          unsigned long long best = 0ull;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const int64_t row = r0 + tile_row(t);
-          const unsigned long long key = row < N ? argmax_key(v[t][r], (unsigned)row) : 0ull;
-          best = key > best ? key : best;
-        }
-        best = lanes_max(best, 16);
-        wave_key[r] = best > wave_key[r] ? best : wave_key[r];
-      }
-    }
-  };
-
-  // Prologue, in issue order (loads complete in issue order): the weights
-  // of unit 0 (from HBM, the longest wait, needed first), the activations
-  // of units 0..BI-1 (to buffers 0..BI-1 before the first barrier), the
-  // weights of units 1..D-2, then the activations of units BI..BI+kXL-1,
-  // which stay in registers (set u % (kXL + 1)).
-  XRegs xr[kXL + 1];
-  WTile wr[D][T];
-  {
-    XRegs xp[BI];
-    load_w(wr[0]);
-#pragma unroll
-    for (int j = 0; j < BI; ++j) load_x(xp[j]);
-#pragma unroll
-    for (int d = 1; d < D - 1; ++d) load_w(wr[d]);
-#pragma unroll
-    for (int q = 0; q < kXL; ++q) load_x(xr[(BI + q) % (kXL + 1)]);
-#pragma unroll
-    for (int j = 0; j < BI; ++j) store_x(j, xp[j]);
-  }
-  __syncthreads();
-
-  const int g_first = (int)(u0 / KB);
-  int gc = g_first, bc = (int)(u0 % KB), seg0 = bc;
-  int have_first = 0;
-
-  // One unit: prefetch the activations of unit i+BI+kXL (into xl) and the
-  // weights of unit i+D-1 (into pf), contract the weights in `cur` with the
-  // activations in LDS buffer i % kNB, then move the activations of unit
-  // i+BI (in xs) into their buffer; barrier after every BI-th unit (pos is
-  // the static position within the unrolled iteration).
-  auto step = [&](WTile(&cur)[T], WTile(&pf)[T], XRegs &xl, const XRegs &xs, const int64_t i,
-                  const int pos) {
-    // Waves w, w + 4, ... share a SIMD, and the oldest would otherwise win
-    // issue every cycle and reach the barrier first; rotating the priority
-    // each unit keeps them in step.
-    if ((wave >> 2) == pos % (W / 4))
-      __builtin_amdgcn_s_setprio(1);
-    else
-      __builtin_amdgcn_s_setprio(0);
-    load_x(xl);
-    load_w(pf);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint8_t *xb = s_x[i % kNB];
-    if (i < nu) {
-      float d[T], dmin[T];
-      // per sub-block {scale, offset} pairs; the fma broadcasts each half
-      half2v k00[T], k01[T], k10[T], k11[T];
-      half4 bm[T];
-      const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-      const half2v lo_pair = {(_Float16)1.0f, (_Float16)-1024.0f};
-      const half2v hi_pair = {(_Float16)0.0625f, (_Float16)-64.0f};
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const u32x4 h = cur[t].hdr;
-        d[t] = h2f_lo(h.x);
-        dmin[t] = h2f_hi(h.x);
-        // q0 holds sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
-        // q1 holds 4+2(kg>>1) and 5+2(kg>>1). Their 6-bit scales are bytes
-        // 2(kg>>1), 2(kg>>1)+1 of sc03 and sc47; one byte permute sets each
-        // below an fp16 exponent byte 0x64 (1024 + s), so {s, s'} is exact.
-        const unsigned sc03 = h.y & 0x3F3F3F3Fu;
-        const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-        const half2v s0 = as_h2(__builtin_amdgcn_perm(sc03, 0x64646464u, sel_sc)) + neg1024;
-        const half2v s1 = as_h2(__builtin_amdgcn_perm(sc47, 0x64646464u, sel_sc)) + neg1024;
-        // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
-        k00[t] = half2v{s0[0], s0[0]} * lo_pair;
-        k01[t] = half2v{s0[1], s0[1]} * hi_pair;
-        k10[t] = half2v{s1[0], s1[0]} * lo_pair;
-        k11[t] = half2v{s1[1], s1[1]} * hi_pair;
-        // min-term B operand: the 6-bit m of sub-blocks 4(kg&1) + {0,2,1,3}
-        const unsigned m03 = h.z & 0x3F3F3F3Fu;
-        const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-        const unsigned msrc = (kg & 1) ? m47 : m03;
-        const half2v p0 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00060004u)) + neg1024;
-        const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
-        bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
-      }
-      // x hi and x lo products accumulate in one fp32 sum per tile
-      f32x4 cq[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
-        const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
-        const bool hi = (s & 2) != 0;
-        const unsigned mask = hi ? mask_hi : mask_lo;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
-          const unsigned da = (s & 1) ? qq.z : qq.x;
-          const unsigned db = (s & 1) ? qq.w : qq.y;
-          const half2v kk = s < 4 ? (hi ? k01[t] : k00[t]) : (hi ? k11[t] : k10[t]);
-          const unsigned u0_ = (da & mask) | 0x64006400u;
-          const unsigned u1_ = ((da >> 8) & mask) | 0x64006400u;
-          const unsigned u2_ = (db & mask) | 0x64006400u;
-          const unsigned u3_ = ((db >> 8) & mask) | 0x64006400u;
-          const half2v v0 = fma_bcast(as_h2(u0_), kk);
-          const half2v v1 = fma_bcast(as_h2(u1_), kk);
-          const half2v v2 = fma_bcast(as_h2(u2_), kk);
-          const half2v v3 = fma_bcast(as_h2(u3_), kk);
-          const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
-          cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
-          cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
+          for (int t = 0; t < T; ++t) {
+            const int row = r0 + tile_row(t);
+            const unsigned long long key = row < N ? argmax_key(v[t][r], (unsigned)row) : 0ull;
+            best = key > best ? key : best;
+          }
+          best = lanes_max(best, 16);
+          wave_key[r] = best > wave_key[r] ? best : wave_key[r];
         }
       }
-      // min term and the block's contribution in the row's scaled units
-      const half4 as4 = *(const half4 *)(xb + kXsbOffset + lane * 8);
-      const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const f32x4 c2 =
-            __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
-      }
-    }
-    // end of a row group's segment
-    const int64_t u = u0 + i;
-    if (i < nu && (bc == KB - 1 || u == u_last)) {
-      if (seg0 == 0 && bc == KB - 1) {
-        write_rows(gc, acc);
-      } else if (gc == g_first) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc_first[t] = acc[t];
-        have_first = 1;
-      }
-      if (u != u_last) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        seg0 = 0;
-      }
-    }
-    if (i < nu && ++bc == KB) {
-      bc = 0;
-      ++gc;
-    }
-    store_x((int)((i + BI) % kNB), xs);
-    if (pos % BI == BI - 1) __syncthreads();
-  };
+    };
 
-  // kU units per iteration so the register sets rotate statically; steps
-  // past the last unit only keep the loads and barriers in step.
-  for (int64_t i = 0; i < nu; i += kU) {
+    // Prologue, in issue order (loads complete in issue order): the weights
+    // of unit 0 (from HBM, the longest wait, needed first), the activations
+    // of units 0..BI-1 (to buffers 0..BI-1 before the first barrier), the
+    // weights of units 1..D-2, then the activations of units BI..BI+kXL-1,
+    // which stay in registers (set u % (kXL + 1)). A chain issued the
+    // weights of units 0..D-2 already (before its first phase, or before
+    // the barrier that ended the previous phase).
+    {
+      XRegs xp[BI];
+      if (!CHAIN) load_w(wr[0]);
 #pragma unroll
-    for (int j = 0; j < kU; ++j)
-      step(wr[j % D], wr[(j + D - 1) % D], xr[(j + BI + kXL) % (kXL + 1)], xr[(j + BI) % (kXL + 1)], i + j, j);
-  }
-  __builtin_amdgcn_s_setprio(0);
-
-  // ---------------------------------------------------------------- epilogue
-  // Row groups this workgroup finished only in part: its first (acc_first)
-  // and its last (acc, when the last segment neither starts at block 0 nor
-  // ends at the last block of a group other than the first). Each partial
-  // goes to slot 0 (first group) or 1 (last group) of this workgroup; the
-  // last contributor of a group to arrive sums all contributors' partials in
-  // workgroup order.
-  if (a.verify) {
+      for (int j = 0; j < BI; ++j) load_x(xp[j]);
+      if (!CHAIN) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * kg + r;
-      if (ln == 0 && m < M && wave_key[r]) atomicMax(&s_keys[m], wave_key[r]);
-    }
-  }
-  const int g_last = (int)(u_last / KB);
-  const int last_partial = (g_last != g_first) && (u_last % KB != KB - 1);
-  // A partial is [row of the group][16 activation rows] fp32: the lane's
-  // four sums (activation rows 4kg..4kg+3 of its output row) are one
-  // 16-byte store.
-  const __amdgpu_buffer_rsrc_t part_rsrc = dev_rsrc(a.partials);
-  auto write_partial = [&](int slot, const f32x4(&v)[T]) {
-    const unsigned base_off = (unsigned)((p * 2 + slot) * kMaxRows * kRows) * 4u;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-      st_dev16(part_rsrc, base_off + (unsigned)(tile_row(t) * kMaxRows + 4 * kg) * 4u, v[t]);
-  };
-  // Sum the partials of one or two row groups over their contributors in
-  // workgroup order, the loads of both groups in flight together. Thread
-  // tid handles the 16-byte chunks c = tid + j kNth of each group (row c / 4
-  // of the group, activation rows 4 (c % 4) .. +3) and issues the loads of
-  // eight contributors per group before it adds any of them.
-  constexpr int kE = kRows * kMaxRows / (4 * kNth);  // chunks per thread
-  constexpr int kC = 8;
-  static_assert(kE * 4 * kNth == kRows * kMaxRows, "chunks must split evenly");
-  struct Contributors {
-    int64_t pf, pl;  // first and last contributing workgroup
-    int pf_slot;     // the first one's slot (the others use slot 0)
-  };
-  auto contributors = [&](int g) {
-    const int64_t ufirst = (int64_t)g * KB;
-    Contributors c;
-    c.pf = owner(ufirst);
-    c.pl = owner(ufirst + KB - 1);
-    // every contributor after the first starts inside g (slot 0); the first
-    // used slot 1 unless its run also starts at the group's first block
-    const int64_t pf_u0 = c.pf * base + (c.pf < rem ? c.pf : rem);
-    c.pf_slot = pf_u0 < ufirst ? 1 : 0;
-    return c;
-  };
-  auto load_partials = [&](const Contributors &cb, int64_t c0, f32x4 (&pv)[kE][kC]) {
-    // unconditional loads: contributors past the last one re-read it and
-    // are dropped when summed
-#pragma unroll
-    for (int c = 0; c < kC; ++c) {
-      const int64_t q = cb.pf + c0 + c <= cb.pl ? cb.pf + c0 + c : cb.pl;
-      const int slot = q == cb.pf ? cb.pf_slot : 0;
-      const unsigned src = (unsigned)((q * 2 + slot) * kMaxRows * kRows) * 4u;
-#pragma unroll
-      for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
-    }
-  };
-  auto sum_partials = [&](const Contributors &cb, int64_t c0, const f32x4 (&pv)[kE][kC], f32x4 (&v)[kE]) {
-#pragma unroll
-    for (int c = 0; c < kC; ++c)
-#pragma unroll
-      for (int j = 0; j < kE; ++j)
-        if (cb.pf + c0 + c <= cb.pl) v[j] = c0 + c == 0 ? pv[j][c] : v[j] + pv[j][c];
-  };
-  // logits and argmax keys of a reduced group (elements past M or the
-  // matrix end are dropped)
-  auto finish_group = [&](int g, const f32x4 (&v)[kE]) {
-    int mat;
-    const int64_t r0 = group_row0(g, mat);
-    float *logits = a.logits[mat];
-    const int nrows = (int)((N - r0) < kRows ? (N - r0) : kRows);
-#pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      const int c = tid + j * kNth;
-      const int row = c >> 2, m0 = 4 * (c & 3);
-      const int64_t n = r0 + row;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + r;
-        const bool ok = m < M && row < nrows;
-        if (ok && logits) logits[(int64_t)m * N + n] = v[j][r];
-        if (a.verify) {
-          // max over the wave's 16 rows: the lanes with the same c % 4
-          unsigned long long best = ok ? argmax_key(v[j][r], (unsigned)n) : 0ull;
-          best = lanes_max(best, 64, 4);
-          if (lane < 4 && m < M) atomicMax(&s_keys[m], best);
-        }
+        for (int d = 1; d < D - 1; ++d) load_w(wr[d]);
       }
-    }
-  };
-  auto reduce_groups = [&](int ga, int gb, bool both) {
-    const Contributors ca = contributors(ga);
-    const Contributors cbb = contributors(both ? gb : ga);
-    const int64_t na = ca.pl - ca.pf + 1;
-    const int64_t nb = both ? cbb.pl - cbb.pf + 1 : 0;
-    const int64_t nmax = na > nb ? na : nb;
-    f32x4 va[kE], vb[kE];
 #pragma unroll
-    for (int j = 0; j < kE; ++j) va[j] = vb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t c0 = 0; c0 < nmax; c0 += kC) {
-      f32x4 pa[kE][kC], pb[kE][kC];
-      load_partials(ca, c0, pa);
-      if (both) load_partials(cbb, c0, pb);
-      sum_partials(ca, c0, pa, va);
-      if (both) sum_partials(cbb, c0, pb, vb);
-    }
-    finish_group(ga, va);
-    if (both) finish_group(gb, vb);
-  };
-
-  if (have_first || last_partial) {
-    if (have_first) write_partial(0, acc_first);
-    if (last_partial) write_partial(1, acc);
-    // contributor counts of both groups (computed while the stores drain)
-    int64_t c_first = 0, c_last = 0;
-    if (tid == 0) {
-      c_first = owner((int64_t)g_first * KB + KB - 1) - owner((int64_t)g_first * KB) + 1;
-      c_last = owner((int64_t)g_last * KB + KB - 1) - owner((int64_t)g_last * KB) + 1;
-    }
-    stores_done_barrier();
-    if (tid == 0) {
-      // both arrivals in flight at once; a group this workgroup has no
-      // partial for gets an increment of 0
-      unsigned *cnt_f = a.group_cnt + (int64_t)g_first * kCntStride;
-      unsigned *cnt_l = a.group_cnt + (int64_t)g_last * kCntStride;
-      const unsigned old_f = __hip_atomic_fetch_add(cnt_f, have_first ? 1u : 0u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned old_l = __hip_atomic_fetch_add(cnt_l, last_partial ? 1u : 0u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-      int flags = 0;
-      if (have_first && old_f == (unsigned)(c_first - 1)) {
-        __hip_atomic_store(cnt_f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        flags |= 1;
-      }
-      if (last_partial && old_l == (unsigned)(c_last - 1)) {
-        __hip_atomic_store(cnt_l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        flags |= 2;
-      }
-      s_flag = flags;
+      for (int q = 0; q < kXL; ++q) load_x(xr[(BI + q) % (kXL + 1)]);
+#pragma unroll
+      for (int j = 0; j < BI; ++j) store_x(j, xp[j]);
     }
     __syncthreads();
-    const int flags = s_flag;
-    if (flags == 3) {
-      reduce_groups(g_first, g_last, true);
-    } else if (flags) {
-      reduce_groups(flags == 1 ? g_first : g_last, 0, false);
-    }
-  }
 
-  if (!a.verify) return;
-  __syncthreads();
-  if (tid < kMaxRows) st_dev(&a.wg_keys[p * kMaxRows + tid], s_keys[tid]);
-  stores_done_barrier();
-  if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag = old == (unsigned)(P - 1);
-  }
-  __syncthreads();
-  if (!s_flag) return;
-  if (tid < kMaxRows) s_keys[tid] = 0ull;
-  __syncthreads();
-  {
-    const int m = tid & 15;
-    if (m < M) {
-      unsigned long long best = 0ull;
-      for (int64_t q = tid >> 4; q < P; q += kNth / 16) {
-        const unsigned long long key = ld_dev(&a.wg_keys[q * kMaxRows + m]);
-        best = key > best ? key : best;
+    const int g_first = u0 / KB;
+    int gc = g_first, bc = u0 % KB, seg0 = bc;
+    int have_first = 0;
+
+    // One unit: prefetch the activations of unit i+BI+kXL (into xl) and the
+    // weights of unit i+D-1 (into pf), contract the weights in `cur` with the
+    // activations in LDS buffer i % kNB, then move the activations of unit
+    // i+BI (in xs) into their buffer; barrier after every BI-th unit (pos is
+    // the static position within the unrolled iteration).
+    auto step = [&](WTile(&cur)[T], WTile(&pf)[T], XRegs &xl, const XRegs &xs, const int i,
+                    const int pos) {
+      // Waves w, w + 4, ... share a SIMD, and the oldest would otherwise win
+      // issue every cycle and reach the barrier first; rotating the priority
+      // each unit keeps them in step.
+      if ((wave >> 2) == pos % (W / 4))
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+      load_x(xl);
+      load_w(pf);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t *xb = s_x[i % kNB];
+      if (i < nu) {
+        float d[T], dmin[T];
+        // per sub-block {scale, offset} pairs; the fma broadcasts each half
+        half2v k00[T], k01[T], k10[T], k11[T];
+        half4 bm[T];
+        const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+        const half2v lo_pair = {(_Float16)1.0f, (_Float16)-1024.0f};
+        const half2v hi_pair = {(_Float16)0.0625f, (_Float16)-64.0f};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const u32x4 h = cur[t].hdr;
+          d[t] = h2f_lo(h.x);
+          dmin[t] = h2f_hi(h.x);
+          // q0 holds sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
+          // q1 holds 4+2(kg>>1) and 5+2(kg>>1). Their 6-bit scales are bytes
+          // 2(kg>>1), 2(kg>>1)+1 of sc03 and sc47; one byte permute sets each
+          // below an fp16 exponent byte 0x64 (1024 + s), so {s, s'} is exact.
+          const unsigned sc03 = h.y & 0x3F3F3F3Fu;
+          const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+          const half2v s0 = as_h2(__builtin_amdgcn_perm(sc03, 0x64646464u, sel_sc)) + neg1024;
+          const half2v s1 = as_h2(__builtin_amdgcn_perm(sc47, 0x64646464u, sel_sc)) + neg1024;
+          // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
+          k00[t] = half2v{s0[0], s0[0]} * lo_pair;
+          k01[t] = half2v{s0[1], s0[1]} * hi_pair;
+          k10[t] = half2v{s1[0], s1[0]} * lo_pair;
+          k11[t] = half2v{s1[1], s1[1]} * hi_pair;
+          // min-term B operand: the 6-bit m of sub-blocks 4(kg&1) + {0,2,1,3}
+          const unsigned m03 = h.z & 0x3F3F3F3Fu;
+          const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+          const unsigned msrc = (kg & 1) ? m47 : m03;
+          const half2v p0 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00060004u)) + neg1024;
+          const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
+          bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
+        }
+        // x hi and x lo products accumulate in one fp32 sum per tile
+        f32x4 cq[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
+          const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+          const bool hi = (s & 2) != 0;
+          const unsigned mask = hi ? mask_hi : mask_lo;
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
+            const unsigned da = (s & 1) ? qq.z : qq.x;
+            const unsigned db = (s & 1) ? qq.w : qq.y;
+            const half2v kk = s < 4 ? (hi ? k01[t] : k00[t]) : (hi ? k11[t] : k10[t]);
+            const unsigned u0_ = (da & mask) | 0x64006400u;
+            const unsigned u1_ = ((da >> 8) & mask) | 0x64006400u;
+            const unsigned u2_ = (db & mask) | 0x64006400u;
+            const unsigned u3_ = ((db >> 8) & mask) | 0x64006400u;
+            const half2v v0 = fma_bcast(as_h2(u0_), kk);
+            const half2v v1 = fma_bcast(as_h2(u1_), kk);
+            const half2v v2 = fma_bcast(as_h2(u2_), kk);
+            const half2v v3 = fma_bcast(as_h2(u3_), kk);
+            const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
+            cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
+            cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
+          }
+        }
+        // min term and the block's contribution in the row's scaled units
+        const half4 as4 = *(const half4 *)(xb + kXsbOffset + lane * 8);
+        const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const f32x4 c2 =
+              __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
+        }
       }
-      atomicMax(&s_keys[m], best);
+      // end of a row group's segment
+      const int u = u0 + i;
+      if (i < nu && (bc == KB - 1 || u == u_last)) {
+        if (seg0 == 0 && bc == KB - 1) {
+          write_rows(gc, acc);
+        } else if (gc == g_first) {
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc_first[t] = acc[t];
+          have_first = 1;
+        }
+        if (u != u_last) {
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          seg0 = 0;
+        }
+      }
+      if (i < nu && ++bc == KB) {
+        bc = 0;
+        ++gc;
+      }
+      store_x((int)((i + BI) % kNB), xs);
+      if (pos % BI == BI - 1) __syncthreads();
+    };
+
+    // kU units per iteration so the register sets rotate statically; steps
+    // past the last unit only keep the loads and barriers in step.
+    for (int i = 0; i < nu; i += kU) {
+#pragma unroll
+      for (int j = 0; j < kU; ++j)
+        step(wr[j % D], wr[(j + D - 1) % D], xr[(j + BI + kXL) % (kXL + 1)], xr[(j + BI) % (kXL + 1)], i + j,
+             j);
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int am[kMaxRows];
-    for (int m = 0; m < M; ++m) {
-      am[m] = (int)(0xFFFFFFFFu - (unsigned)(s_keys[m] & 0xFFFFFFFFull));
-      if (m >= a.argmax_from) a.argmax_out[m - a.argmax_from] = am[m];
+    __builtin_amdgcn_s_setprio(0);
+
+    // -------------------------------------------------------------- epilogue
+    // Row groups this workgroup finished only in part: its first (acc_first)
+    // and its last (acc, when the last segment neither starts at block 0 nor
+    // ends at the last block of a group other than the first). Each partial
+    // goes to slot 0 (first group) or 1 (last group) of this workgroup; the
+    // last contributor of a group to arrive sums all contributors' partials in
+    // workgroup order.
+    if (!CHAIN && a.verify) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        if (ln == 0 && m < M && wave_key[r]) atomicMax(&s_keys[m], wave_key[r]);
+      }
     }
-    if (a.head_out) a.head_out[0] = am[0];
-    if (a.accept_out) {
-      int i = 0;
-      while (i < a.k_draft && a.draft[i] == am[i]) ++i;
-      a.accept_out[0] = i;
-      a.accept_out[1] = am[i];
+    const int g_last = u_last / KB;
+    const int last_partial = (g_last != g_first) && (u_last % KB != KB - 1);
+    // A partial is [row of the group][16 activation rows] fp32: the lane's
+    // four sums (activation rows 4kg..4kg+3 of its output row) are one
+    // 16-byte store.
+    auto write_partial = [&](int slot, const f32x4(&v)[T]) {
+      const unsigned base_off = (unsigned)((p * 2 + slot) * kMaxRows * kRows) * 4u;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        st_dev16(part_rsrc, base_off + (unsigned)(tile_row(t) * kMaxRows + 4 * kg) * 4u, v[t]);
+    };
+    // Sum the partials of one or two row groups over their contributors in
+    // workgroup order, the loads of both groups in flight together. Thread
+    // tid handles the 16-byte chunks c = tid + j kNth of each group (row c / 4
+    // of the group, activation rows 4 (c % 4) .. +3) and issues the loads of
+    // eight contributors per group before it adds any of them.
+    constexpr int kE = kRows * kMaxRows / (4 * kNth);  // chunks per thread
+    constexpr int kC = 8;
+    static_assert(kE * 4 * kNth == kRows * kMaxRows, "chunks must split evenly");
+    struct Contributors {
+      int pf, pl;  // first and last contributing workgroup
+      int pf_slot;     // the first one's slot (the others use slot 0)
+    };
+    auto contributors = [&](int g) {
+      const int ufirst = g * KB;
+      Contributors c;
+      c.pf = owner(ufirst);
+      c.pl = owner(ufirst + KB - 1);
+      // every contributor after the first starts inside g (slot 0); the first
+      // used slot 1 unless its run also starts at the group's first block
+      const int pf_u0 = c.pf * base + (c.pf < rem ? c.pf : rem);
+      c.pf_slot = pf_u0 < ufirst ? 1 : 0;
+      return c;
+    };
+    auto load_partials = [&](const Contributors &cb, int c0, f32x4(&pv)[kE][kC]) {
+      // unconditional loads: contributors past the last one re-read it and
+      // are dropped when summed
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        const int q = cb.pf + c0 + c <= cb.pl ? cb.pf + c0 + c : cb.pl;
+        const int slot = q == cb.pf ? cb.pf_slot : 0;
+        const unsigned src = (unsigned)((q * 2 + slot) * kMaxRows * kRows) * 4u;
+#pragma unroll
+        for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
+      }
+    };
+    auto sum_partials = [&](const Contributors &cb, int c0, const f32x4(&pv)[kE][kC], f32x4(&v)[kE]) {
+#pragma unroll
+      for (int c = 0; c < kC; ++c)
+#pragma unroll
+        for (int j = 0; j < kE; ++j)
+          if (cb.pf + c0 + c <= cb.pl) v[j] = c0 + c == 0 ? pv[j][c] : v[j] + pv[j][c];
+    };
+    // logits and argmax keys of a reduced group (elements past M or the
+    // matrix end are dropped)
+    auto finish_group = [&](int g, const f32x4(&v)[kE]) {
+      int mat;
+      const int r0 = group_row0(g, mat);
+      float *logits = KQ_PH(ph, logits[mat]);
+      const int nrows = (N - r0) < kRows ? (N - r0) : kRows;
+#pragma unroll
+      for (int j = 0; j < kE; ++j) {
+        const int c = tid + j * kNth;
+        const int row = c >> 2, m0 = 4 * (c & 3);
+        const int n = r0 + row;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + r;
+          const bool ok = m < M && row < nrows;
+          if (ok && logits) put(&logits[(int64_t)m * N + n], v[j][r]);
+          if (!CHAIN && a.verify) {
+            // max over the wave's 16 rows: the lanes with the same c % 4
+            unsigned long long best = ok ? argmax_key(v[j][r], (unsigned)n) : 0ull;
+            best = lanes_max(best, 64, 4);
+            if (lane < 4 && m < M) atomicMax(&s_keys[m], best);
+          }
+        }
+      }
+    };
+    auto reduce_groups = [&](int ga, int gb, bool both) {
+      const Contributors ca = contributors(ga);
+      const Contributors cbb = contributors(both ? gb : ga);
+      const int na = ca.pl - ca.pf + 1;
+      const int nb = both ? cbb.pl - cbb.pf + 1 : 0;
+      const int nmax = na > nb ? na : nb;
+      f32x4 va[kE], vb[kE];
+#pragma unroll
+      for (int j = 0; j < kE; ++j) va[j] = vb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < nmax; c0 += kC) {
+        f32x4 pa[kE][kC], pb[kE][kC];
+        load_partials(ca, c0, pa);
+        if (both) load_partials(cbb, c0, pb);
+        sum_partials(ca, c0, pa, va);
+        if (both) sum_partials(cbb, c0, pb, vb);
+      }
+      finish_group(ga, va);
+      if (both) finish_group(gb, vb);
+    };
+
+    if (have_first || last_partial) {
+      if (have_first) write_partial(0, acc_first);
+      if (last_partial) write_partial(1, acc);
+      // contributor counts of both groups (computed while the stores drain)
+      int c_first = 0, c_last = 0;
+      if (tid == 0) {
+        c_first = owner(g_first * KB + KB - 1) - owner(g_first * KB) + 1;
+        c_last = owner(g_last * KB + KB - 1) - owner(g_last * KB) + 1;
+      }
+      stores_done_barrier();
+      if (tid == 0) {
+        // both arrivals in flight at once; a group this workgroup has no
+        // partial for gets an increment of 0
+        unsigned *cnt_f = a.group_cnt + (int64_t)g_first * kCntStride;
+        unsigned *cnt_l = a.group_cnt + (int64_t)g_last * kCntStride;
+        const unsigned old_f = __hip_atomic_fetch_add(cnt_f, have_first ? 1u : 0u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned old_l = __hip_atomic_fetch_add(cnt_l, last_partial ? 1u : 0u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        int flags = 0;
+        if (have_first && old_f == (unsigned)(c_first - 1)) {
+          __hip_atomic_store(cnt_f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          flags |= 1;
+        }
+        if (last_partial && old_l == (unsigned)(c_last - 1)) {
+          __hip_atomic_store(cnt_l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          flags |= 2;
+        }
+        s_flag = flags;
+      }
+      __syncthreads();
+      const int flags = s_flag;
+      if (flags == 3) {
+        reduce_groups(g_first, g_last, true);
+      } else if (flags) {
+        reduce_groups(flags == 1 ? g_first : g_last, 0, false);
+      }
     }
-    __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    if (CHAIN) {
+      // Grid barrier: this workgroup's stores of phase ph have completed
+      // (logits and the group-counter resets written through to the device
+      // coherence point); arrive, issue the first weights of the next
+      // phase, then wait for the release flag (or release everyone when
+      // this arrival completed the count). The final arrival of the last
+      // phase resets the count and advances the epoch for the next launch
+      // (every workgroup has then passed every barrier).
+      stores_done_barrier();
+      const unsigned target = (unsigned)(ph + 1) * (unsigned)P;
+      unsigned old = 0;
+      if (tid == 0) old = __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ph + 1 < n_ph) {
+        begin_w(ph + 1);
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) load_w(wr[d]);
+        if (tid == 0) s_flag = old + 1 == target;
+        __syncthreads();
+        const unsigned long long want = s_epoch | (unsigned long long)(ph + 1);
+        if (s_flag) {
+          // last to arrive: release every other workgroup
+          for (int q = tid; q < P; q += kNth)
+            if (q != p) st_dev(a.flags + (int64_t)q * kFlagStride, want);
+        }
+        int ok = 1;
+        if (tid == 0 && !s_flag) ok = spin_flag(a.flags + (int64_t)p * kFlagStride, want, a.err);
+        __syncthreads();
+        if (tid == 0) s_flag = ok;
+        __syncthreads();
+        if (!s_flag) return;  // a barrier timed out: *a.err is set, every workgroup leaves
+      } else if (tid == 0 && old + 1 == target) {
+        __hip_atomic_store(a.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      continue;
+    }
+
+    if (!a.verify) return;
+    __syncthreads();
+    if (tid < kMaxRows) st_dev(&a.wg_keys[(int64_t)p * kMaxRows + tid], s_keys[tid]);
+    stores_done_barrier();
+    if (tid == 0) {
+      const unsigned old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = old == (unsigned)(P - 1);
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    if (tid < kMaxRows) s_keys[tid] = 0ull;
+    __syncthreads();
+    {
+      const int m = tid & 15;
+      if (m < M) {
+        unsigned long long best = 0ull;
+        for (int q = tid >> 4; q < P; q += kNth / 16) {
+          const unsigned long long key = ld_dev(&a.wg_keys[q * kMaxRows + m]);
+          best = key > best ? key : best;
+        }
+        atomicMax(&s_keys[m], best);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int am[kMaxRows];
+      for (int m = 0; m < M; ++m) {
+        am[m] = (int)(0xFFFFFFFFu - (unsigned)(s_keys[m] & 0xFFFFFFFFull));
+        if (m >= a.argmax_from) a.argmax_out[m - a.argmax_from] = am[m];
+      }
+      if (a.head_out) a.head_out[0] = am[0];
+      if (a.accept_out) {
+        int i = 0;
+        while (i < a.k_draft && a.draft[i] == am[i]) ++i;
+        a.accept_out[0] = i;
+        a.accept_out[1] = am[i];
+      }
+      __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
+
+#undef KQ_PH
 
 // ---------------------------------------------------------------------------
 // Tiled layout. Record (b, t) = block b of 16-row tile t is 2,304 bytes at
@@ -910,10 +1062,20 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream) {
 int launch_gemv(const GemvLaunch &a, void *stream) {
   const dim3 grid((unsigned)a.g.n_wg);
   hipStream_t st = (hipStream_t)stream;
+  if (a.chain) {
+    if (a.g.waves != 8 || a.g.bi != 4 || a.g.depth != 4) return (int)hipErrorInvalidConfiguration;
+    if (a.g.tpw == 1)
+      hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true>), grid, dim3(512), 0, st, a);
+    else if (a.g.tpw == 2)
+      hipLaunchKernelGGL((kq_gemv_kernel<8, 2, 4, 4, true>), grid, dim3(512), 0, st, a);
+    else
+      return (int)hipErrorInvalidConfiguration;
+    return (int)hipGetLastError();
+  }
   switch (a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
 #define KQ_CASE(W_, T_, BI_, D_)                                                                   \
   case W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                                                       \
-    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_>), grid, dim3(64 * W_), 0, st, a);          \
+    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, false>), grid, dim3(64 * W_), 0, st, a);   \
     break;
     KQ_CASE(8, 2, 4, 4)
     KQ_CASE(8, 1, 4, 4)
@@ -927,6 +1089,20 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     default: return (int)hipErrorInvalidConfiguration;
   }
   return (int)hipGetLastError();
+}
+
+// Workgroups of the chain kernel (tpw tiles per wave) that the current
+// device holds at once (resident blocks per CU times CUs), or a negative HIP
+// error.
+int chain_capacity(int tpw) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, tpw == 2 ? kq_gemv_kernel<8, 2, 4, 4, true> : kq_gemv_kernel<8, 1, 4, 4, true>, 512, 0);
+  if (e != hipSuccess) return -(int)e;
+  return per_cu * cus;
 }
 
 }  // namespace kq

@@ -21,10 +21,28 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
             "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
             "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights", "kq_draft_block_argmax",
-            "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes")
+            "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes",
+            "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
+
+MAX_GROUP = 8
+CHAIN_ERROR_OFFSET = 256   # byte offset of the chain's barrier time-out word in its scratch
+
+
+class ChainPhase(ctypes.Structure):
+    """kq_chain_phase (include/kq.h)."""
+    _fields_ = [("count", ctypes.c_int), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("w_q4k", ctypes.c_void_p * MAX_GROUP), ("logits", ctypes.c_void_p * MAX_GROUP),
+                ("staged", ctypes.c_void_p)]
+
+
+class ChainPlan(ctypes.Structure):
+    """kq_chain_plan (include/kq.h)."""
+    _fields_ = [("n_phases", ctypes.c_int32), ("m", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("workgroups", ctypes.c_int32), ("max_groups", ctypes.c_int32), ("tiles_per_wave", ctypes.c_int32),
+                ("table_bytes", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64)]
 
 _lib = None
 
@@ -70,10 +88,14 @@ def load() -> ctypes.CDLL:
     lib.kq_tiled_bytes.argtypes = [I64, I64]
     lib.kq_tiled_bytes.restype = SZ
     lib.kq_tile_weights.argtypes = [P, I64, I64, P, SZ, P]
+    lib.kq_chain_table_bytes.argtypes = [I32]
+    lib.kq_chain_table_bytes.restype = SZ
+    lib.kq_chain_encode.argtypes = [ctypes.POINTER(ChainPhase), I32, I32, I32, P, SZ, ctypes.POINTER(ChainPlan)]
+    lib.kq_gemv_chain.argtypes = [P, ctypes.POINTER(ChainPlan), P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
-                 "kq_stream_probe"):
+                 "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -343,3 +365,68 @@ def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scrat
         _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
         _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_verify_staged")
     return am, acc, lg
+
+
+# ------------------------------------------------------------------- chains
+
+class Chain:
+    """An encoded chain (kq_chain_encode): the device copy of its phase
+    table, its plan, its scratch (zeroed once) and the tensors it refers to
+    (kept alive with it)."""
+
+    def __init__(self, table, plan, scratch, refs):
+        self.table, self.plan, self.scratch, self._refs = table, plan, scratch, refs
+
+    @property
+    def workgroups(self) -> int:
+        return int(self.plan.workgroups)
+
+    def error_word(self) -> int:
+        """The barrier time-out word (synchronises with the device)."""
+        off = CHAIN_ERROR_OFFSET
+        return int(self.scratch[off:off + 4].view(_torch().int32).item())
+
+
+def chain_table_bytes(n_phases: int) -> int:
+    return int(load().kq_chain_table_bytes(n_phases))
+
+
+def chain_encode(phases, m: int, layout=LAYOUT_ROWS, device=None) -> Chain:
+    """Encode a chain of dependent grouped products. `phases` is a sequence
+    of (ws, n, k, staged, logits): ws a list of 1..8 uint8 device weight
+    tensors of n x k (in `layout`), staged the kq_stage_rows block for k,
+    logits a list of fp32 device tensors [>= m][n] (one per weight). The
+    table is copied to the device once here."""
+    torch = _torch()
+    n_ph = len(phases)
+    arr = (ChainPhase * max(1, n_ph))()
+    refs = []
+    for i, (ws, n, k, staged, logits) in enumerate(phases):
+        if len(ws) != len(logits):
+            raise ValueError(f"phase {i}: {len(ws)} weights but {len(logits)} logit buffers")
+        if not 1 <= len(ws) <= MAX_GROUP:
+            raise ValueError(f"phase {i}: 1..{MAX_GROUP} matrices per phase, got {len(ws)}")
+        arr[i].count = len(ws)
+        arr[i].n = int(n)
+        arr[i].k = int(k)
+        for j, (w, lg) in enumerate(zip(ws, logits)):
+            arr[i].w_q4k[j] = _dev_ptr(w, "w", torch.uint8)
+            arr[i].logits[j] = _dev_ptr(lg, "logits", torch.float32)
+        arr[i].staged = _dev_ptr(staged, "staged")
+        refs.extend(list(ws) + list(logits) + [staged])
+    nbytes = max(1, chain_table_bytes(n_ph))
+    host = (ctypes.c_uint8 * nbytes)()
+    plan = ChainPlan()
+    _check(load().kq_chain_encode(arr, n_ph, int(m), int(layout), host, nbytes, ctypes.byref(plan)),
+           "kq_chain_encode")
+    dev = device if device is not None else refs[0].device
+    table = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(dev)
+    scratch = alloc_workspace(int(plan.scratch_bytes), dev)
+    return Chain(table, plan, scratch, refs)
+
+
+def gemv_chain(chain: Chain, stream=None):
+    """Run an encoded chain on the current stream (one launch)."""
+    _check(load().kq_gemv_chain(_dev_ptr(chain.table, "table"), ctypes.byref(chain.plan),
+                                _dev_ptr(chain.scratch, "scratch"), chain.scratch.numel(),
+                                _stream_handle(stream)), "kq_gemv_chain")

@@ -228,3 +228,73 @@ def test_tiling_sizes_and_argument_errors():
     assert tw(FAKE, n, k, out + 4, nb, None) == ALIGN
     assert tw(FAKE, n, k, out, nb - 1, None) == WS
     assert tw(FAKE, n, k, FAKE + 4096, nb, None) == SHAPE    # overlapping buffers
+
+
+def _phase(count=2, n=512, k=1024, w=FAKE, logits=FAKE, staged=FAKE):
+    ph = kq.ChainPhase()
+    ph.count, ph.n, ph.k = count, n, k
+    for j in range(min(count, kq.MAX_GROUP)):
+        ph.w_q4k[j] = w
+        ph.logits[j] = logits
+    ph.staged = staged
+    return ph
+
+
+def _encode(phases, m=16, layout=kq.LAYOUT_ROWS, table_bytes=None, table=True, plan=True):
+    lib = kq.load()
+    n = len(phases)
+    arr = (kq.ChainPhase * max(1, n))(*phases)
+    tb = kq.chain_table_bytes(n) if table_bytes is None else table_bytes
+    host = (ctypes.c_uint8 * max(1, tb))() if table else None
+    pl = kq.ChainPlan()
+    return lib.kq_chain_encode(arr, n, m, layout, host, tb, ctypes.byref(pl) if plan else None)
+
+
+def test_chain_table_bytes():
+    assert kq.chain_table_bytes(0) == 0
+    assert kq.chain_table_bytes(65537) == 0
+    one = kq.chain_table_bytes(1)
+    assert one > 0 and kq.chain_table_bytes(208) == 208 * one
+
+
+def test_chain_encode_argument_errors_before_any_hip_call():
+    good = _phase()
+    assert _encode([good], table=False) == NULL
+    assert _encode([good], plan=False) == NULL
+    assert _encode([good], m=0) == SHAPE
+    assert _encode([good], m=17) == SHAPE
+    assert _encode([good], layout=2) == SHAPE
+    assert _encode([_phase(count=0)]) == SHAPE
+    assert _encode([_phase(count=9)]) == SHAPE
+    assert _encode([good, _phase(k=1000)]) == SHAPE          # k not a multiple of 256
+    assert _encode([good, _phase(n=0)]) == SHAPE
+    assert _encode([good, _phase(w=0)]) == NULL
+    assert _encode([good, _phase(logits=0)]) == NULL
+    assert _encode([good, _phase(staged=0)]) == NULL
+    assert _encode([good, _phase(w=FAKE + 8)]) == ALIGN      # weights 16-byte aligned
+    assert _encode([good, _phase(staged=FAKE + 16)]) == ALIGN  # staged 256-byte aligned
+    assert _encode([good, good], table_bytes=kq.chain_table_bytes(2) - 1) == WS
+    lib = kq.load()
+    pl = kq.ChainPlan()
+    assert lib.kq_chain_encode(None, 1, 16, 0, None, 0, ctypes.byref(pl)) == NULL
+    arr = (kq.ChainPhase * 1)(good)
+    host = (ctypes.c_uint8 * 1024)()
+    assert lib.kq_chain_encode(arr, 0, 16, 0, host, 1024, ctypes.byref(pl)) == SHAPE
+
+
+def test_gemv_chain_argument_errors_before_any_hip_call():
+    lib = kq.load()
+    pl = kq.ChainPlan()
+    pl.n_phases, pl.m, pl.layout, pl.workgroups, pl.max_groups, pl.tiles_per_wave = 2, 16, 0, 256, 4, 1
+    assert lib.kq_gemv_chain(None, ctypes.byref(pl), FAKE, 1 << 30, None) == NULL
+    assert lib.kq_gemv_chain(FAKE, None, FAKE, 1 << 30, None) == NULL
+    assert lib.kq_gemv_chain(FAKE, ctypes.byref(pl), None, 1 << 30, None) == NULL
+    # a plan kq_chain_encode did not write (scratch_bytes inconsistent)
+    assert lib.kq_gemv_chain(FAKE, ctypes.byref(pl), FAKE, 1 << 30, None) == SHAPE
+    for field, bad in (("n_phases", 0), ("m", 0), ("m", 17), ("workgroups", 0), ("layout", 5), ("max_groups", 0),
+                       ("tiles_per_wave", 3)):
+        q = kq.ChainPlan.from_buffer_copy(pl)
+        setattr(q, field, bad)
+        assert lib.kq_gemv_chain(FAKE, ctypes.byref(q), FAKE, 1 << 30, None) == SHAPE, field
+    assert lib.kq_gemv_chain(FAKE + 8, ctypes.byref(pl), FAKE, 1 << 30, None) == ALIGN
+    assert lib.kq_gemv_chain(FAKE, ctypes.byref(pl), FAKE + 16, 1 << 30, None) == ALIGN
