@@ -282,7 +282,7 @@ typedef struct kq_chain_plan {
   int32_t layout;
   int32_t workgroups;     /* grid size: min(device capacity, fewest units of any phase) */
   int32_t max_groups;     /* largest number of row groups of any phase */
-  int32_t tiles_per_wave; /* 16-row tiles per wave (row groups of 128 x this) */
+  int32_t tiles_per_wave; /* 16-row tiles per wave: 1 (row groups of 128 rows) */
   uint64_t table_bytes;   /* bytes of the encoded phase table */
   uint64_t scratch_bytes; /* device scratch the launch needs */
 } kq_chain_plan;

@@ -9,10 +9,6 @@
 
 namespace kq {
 
-#ifndef KQ_CHAIN_TPW
-#define KQ_CHAIN_TPW 1
-#endif
-
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -354,8 +350,9 @@ static Geometry chain_geometry(int64_t n, int64_t k, int count, int tpw) {
   return g;
 }
 
-// Tiles per wave of a chain's phases.
-static int chain_tpw() { return KQ_CHAIN_TPW; }
+// Tiles per wave of a chain's phases: one (two-tile waves, 256-row groups,
+// measured slower on the stack's shapes and need more registers than fit).
+static int chain_tpw() { return 1; }
 
 // Chain scratch: control words, group counters, partials, then one
 // 256-byte line per workgroup for its barrier release flag.
@@ -389,7 +386,7 @@ kq_status kq_chain_encode(const kq_chain_phase *phases, int n_phases, int m, int
     if (g.n_groups > max_groups) max_groups = g.n_groups;
   }
   if (table_bytes < kq_chain_table_bytes(n_phases)) return KQ_ERR_WORKSPACE;
-  const int cap = chain_capacity(tpw);
+  const int cap = chain_capacity();
   if (cap <= 0) return KQ_ERR_LAUNCH;
   const int64_t wg = min_units < cap ? min_units : cap;
   Phase *tab = (Phase *)table_host;
@@ -413,7 +410,7 @@ kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan, void *
                         void *stream) {
   if (!table_dev || !plan || !scratch) return KQ_ERR_NULL;
   if (plan->n_phases < 1 || plan->n_phases > KQ_MAX_CHAIN_PHASES || plan->m < 1 || plan->m > kMaxRows ||
-      plan->workgroups < 1 || plan->max_groups < 1 || (plan->tiles_per_wave != 1 && plan->tiles_per_wave != 2) ||
+      plan->workgroups < 1 || plan->max_groups < 1 || plan->tiles_per_wave != 1 ||
       (plan->layout != KQ_LAYOUT_ROWS && plan->layout != KQ_LAYOUT_TILED16))
     return KQ_ERR_SHAPE;
   if (!al(table_dev, 16) || !al(scratch, 256)) return KQ_ERR_ALIGN;

@@ -118,9 +118,9 @@ ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
 int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ctrl, int64_t n_groups,
                  void *stream);
 int launch_gemv(const GemvLaunch &a, void *stream);
-// Workgroups of the chain kernel (8 waves of tpw 16-row tiles) the current
+// Workgroups of the chain kernel (8 waves of one 16-row tile) the current
 // device holds at once, or a negative HIP error code.
-int chain_capacity(int tpw);
+int chain_capacity();
 int launch_fill(unsigned *p, int64_t n_words, void *stream);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
 int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);

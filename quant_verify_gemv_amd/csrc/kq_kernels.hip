@@ -1063,13 +1063,8 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
   const dim3 grid((unsigned)a.g.n_wg);
   hipStream_t st = (hipStream_t)stream;
   if (a.chain) {
-    if (a.g.waves != 8 || a.g.bi != 4 || a.g.depth != 4) return (int)hipErrorInvalidConfiguration;
-    if (a.g.tpw == 1)
-      hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true>), grid, dim3(512), 0, st, a);
-    else if (a.g.tpw == 2)
-      hipLaunchKernelGGL((kq_gemv_kernel<8, 2, 4, 4, true>), grid, dim3(512), 0, st, a);
-    else
-      return (int)hipErrorInvalidConfiguration;
+    if (a.g.waves != 8 || a.g.tpw != 1 || a.g.bi != 4 || a.g.depth != 4) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true>), grid, dim3(512), 0, st, a);
     return (int)hipGetLastError();
   }
   switch (a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
@@ -1091,16 +1086,14 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
   return (int)hipGetLastError();
 }
 
-// Workgroups of the chain kernel (tpw tiles per wave) that the current
-// device holds at once (resident blocks per CU times CUs), or a negative HIP
-// error.
-int chain_capacity(int tpw) {
+// Workgroups of the chain kernel that the current device holds at once
+// (resident blocks per CU times CUs), or a negative HIP error.
+int chain_capacity() {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, tpw == 2 ? kq_gemv_kernel<8, 2, 4, 4, true> : kq_gemv_kernel<8, 1, 4, 4, true>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_gemv_kernel<8, 1, 4, 4, true>, 512, 0);
   if (e != hipSuccess) return -(int)e;
   return per_cu * cus;
 }
