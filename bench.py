@@ -283,6 +283,80 @@ def draft_block_timing(stack, torch, calls=50):
             "matches_verify_argmax": same_rows}
 
 
+def config_timings(stack, torch, calls=50):
+    """The other configurations of the benchmark definition, each timed on
+    its own (back-to-back launches, HIP events on the launch stream, tiled
+    weights as in the step): the square 6,656 x 6,656 product at every M of
+    its sweep, rotating over 16 copies (399 MB, more than the 256 MB MALL);
+    the DFlash fc projection 33,280 -> 6,656 at M = 16 over 4 copies
+    (498 MB); and the LM-head verify at M = 16 on the resident head (491 MB).
+    Each result: microseconds per call, verify rows/s, weight GB/s and its
+    fraction of the 8 TB/s peak."""
+    kq = stack.kq
+    dev = stack.dev
+    out = {}
+
+    def rate(nbytes, m, us):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us_per_call": round(us, 2), "rows_per_s": round(m / (us * 1e-6), 1),
+                "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    def time_calls(fn):
+        for _ in range(5):
+            fn(0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    def copies(cfg, count):
+        n, k = cfg["n"], cfg["k"]
+        return [kq.tile_weights(torch.from_numpy(synthetic.q4k_matrix(n, k, cfg["seed"] + 100 * c)).to(dev), n, k)
+                for c in range(count)]
+
+    sq = synthetic.SQUARE
+    n, k = sq["n"], sq["k"]
+    ws = copies(sq, 16)
+    wbytes = n * synthetic.q4k_bytes_per_row(k)
+    x = torch.from_numpy(synthetic.activations(16, k, sq["seed"])).to(dev)
+    scratch = kq.new_scratch(n, k, dev)
+    logits = torch.empty((16, n), dtype=torch.float32, device=dev)
+    res = {}
+    for m in sq["ms"]:
+        st = kq.stage_rows(x[:m])
+        us = time_calls(lambda i: kq.gemv_staged(ws[i % 16], n, k, st, m, scratch, logits=logits[:m],
+                                                   layout=kq.LAYOUT_TILED16))
+        res[f"m{m}"] = rate(wbytes, m, us)
+    res["m16_over_m1"] = round(res["m16"]["us_per_call"] / res["m1"]["us_per_call"], 4)
+    out["square_6656x6656"] = res
+    del ws
+    fc = synthetic.FC
+    n, k = fc["n"], fc["k"]
+    ws = copies(fc, 4)
+    xf = torch.from_numpy(synthetic.fc_activations(16, fc["seed"])).to(dev)
+    st = kq.stage_rows(xf)
+    scratch = kq.new_scratch(n, k, dev)
+    logits = torch.empty((16, n), dtype=torch.float32, device=dev)
+    us = time_calls(lambda i: kq.gemv_staged(ws[i % 4], n, k, st, 16, scratch, logits=logits,
+                                               layout=kq.LAYOUT_TILED16))
+    out["fc_33280_to_6656_m16"] = rate(n * synthetic.q4k_bytes_per_row(k), 16, us)
+    del ws
+    h = stack.head
+    sth = stack.staged[h.k]
+    kq.stage_rows(stack.x[h.k][:16], staged=sth)
+    us = time_calls(lambda i: kq.verify_staged(stack.w_head, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
+                                                 out=(stack.am, stack.acc, None), layout=stack.layout))
+    out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us)
+    out["launch"] = "eager, back-to-back"
+    torch.cuda.synchronize()
+    return out
+
+
 def read_ceiling(stack, torch, calls=20):
     """Pure-read rate of this device on the resident LM-head weights (the
     library's read probe: every byte loaded once): the achievable ceiling
@@ -426,10 +500,12 @@ def main():
                   "event_ms_per_step": round(ev * 1e3, 4), "step_spread": spread, "roofline": roof}
         log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s, "
             f"kernel {roof['avg_launch_us']} us/launch, {roof['achieved']} GB/s")
-    draft = ceiling = None
+    draft = ceiling = cfgs = None
     if not args.no_extras:
         draft = draft_block_timing(stack, torch)
         ceiling = read_ceiling(stack, torch)
+        cfgs = config_timings(stack, torch)
+        log("bench: configs " + json.dumps(cfgs))
         log(f"bench: read ceiling {ceiling['gb_s']} GB/s ({ceiling['frac']:.3f} of peak)")
         log(f"bench: draft block proposals {draft['us_per_call']} us/call, {draft['weight_gb_s']} GB/s")
     cpu = None
@@ -465,6 +541,7 @@ def main():
         "roofline": top["roofline"],
         "read_ceiling": ceiling,
         "draft_block_argmax": draft,
+        "configs": cfgs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
