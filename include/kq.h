@@ -252,14 +252,16 @@ kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wa
  *
  * The kernel keeps all of its workgroups resident at once (one per CU);
  * kq_chain_encode sizes the grid from the current device's capacity. Each
- * barrier wait is bounded: a wait longer than one second gives up, sets the
- * 32-bit word at byte KQ_CHAIN_ERROR_OFFSET of the scratch to nonzero and
- * ends the launch early (its logits are then incomplete). That word is
- * sticky: kq_workspace_init clears it, together with the barrier count the
- * failed launch left behind. */
+ * wait (at a barrier, or for another workgroup's partial sums of a row
+ * group) is bounded: a wait longer than one second gives up, sets the 32-bit
+ * word at byte KQ_CHAIN_ERROR_OFFSET of the scratch to nonzero and ends the
+ * launch early (its logits are then incomplete). That word is sticky:
+ * kq_chain_scratch_init clears it, together with the state the failed
+ * launch left behind. */
 
 #define KQ_MAX_GROUP 8
-#define KQ_CHAIN_ERROR_OFFSET 256
+#define KQ_CHAIN_BARRIER_OFFSET 128 /* u32 arrival count of the grid barrier (zero between launches) */
+#define KQ_CHAIN_ERROR_OFFSET 256   /* u32 sticky time-out word */
 #define KQ_MAX_CHAIN_PHASES 65536
 
 /* One phase: 1 <= count <= KQ_MAX_GROUP matrices of n x k (all in the
@@ -302,12 +304,20 @@ size_t kq_chain_table_bytes(int n_phases);
 kq_status kq_chain_encode(const kq_chain_phase *phases, int n_phases, int m, int layout,
                           void *table_host, size_t table_bytes, kq_chain_plan *plan);
 
+/* Initialise a chain's scratch (device, >= plan->scratch_bytes, 256-byte
+ * aligned) once before its first kq_gemv_chain, and again after a launch
+ * that set the error word: control words and release flags to zero, the
+ * partial-sum slots to their empty pattern. Enqueued on `stream`.
+ * KQ_ERR_SHAPE for a plan kq_chain_encode did not write. */
+kq_status kq_chain_scratch_init(const kq_chain_plan *plan, void *scratch, size_t scratch_bytes, void *stream);
+
 /* Run an encoded chain.
  *  table_dev  device copy of the encoded table (read only)
  *  plan       the plan kq_chain_encode wrote for it (host)
- *  scratch    device, >= plan->scratch_bytes, 256-byte aligned, zeroed once
- *             by kq_workspace_init; every successful launch leaves it as it
- *             found it (a timed-out one sets the error word, see above)
+ *  scratch    device, >= plan->scratch_bytes, 256-byte aligned, initialised
+ *             once by kq_chain_scratch_init; every successful launch leaves
+ *             it as it found it (a timed-out one sets the error word, see
+ *             above)
  * Calls sharing a scratch must be ordered (e.g. the same stream). */
 kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan,
                         void *scratch, size_t scratch_bytes, void *stream);

@@ -406,17 +406,42 @@ kq_status kq_chain_encode(const kq_chain_phase *phases, int n_phases, int m, int
   return KQ_OK;
 }
 
+// Scratch bytes a plan needs, or 0 if the plan is not one kq_chain_encode
+// could have written.
+static bool chain_plan_fields_ok(const kq_chain_plan *plan) {
+  return !(plan->n_phases < 1 || plan->n_phases > KQ_MAX_CHAIN_PHASES || plan->m < 1 || plan->m > kMaxRows ||
+           plan->workgroups < 1 || plan->max_groups < 1 || plan->tiles_per_wave != 1 ||
+           (plan->layout != KQ_LAYOUT_ROWS && plan->layout != KQ_LAYOUT_TILED16));
+}
+static size_t chain_plan_scratch(const kq_chain_plan *plan) {
+  const size_t need = chain_flag_off(plan->max_groups, plan->workgroups, plan->tiles_per_wave) +
+                      chain_flag_bytes(plan->workgroups);
+  return plan->scratch_bytes == need ? need : 0;
+}
+
+kq_status kq_chain_scratch_init(const kq_chain_plan *plan, void *scratch, size_t scratch_bytes, void *stream) {
+  if (!plan || !scratch) return KQ_ERR_NULL;
+  if (!chain_plan_fields_ok(plan)) return KQ_ERR_SHAPE;
+  if (!al(scratch, 256)) return KQ_ERR_ALIGN;
+  const size_t need = chain_plan_scratch(plan);
+  if (!need) return KQ_ERR_SHAPE;  // not a plan kq_chain_encode wrote
+  if (scratch_bytes < need) return KQ_ERR_WORKSPACE;
+  uint8_t *sc = (uint8_t *)scratch;
+  const size_t p0 = chain_part_off(plan->max_groups);
+  const size_t p1 = chain_flag_off(plan->max_groups, plan->workgroups, plan->tiles_per_wave);
+  if (launch_fill((unsigned *)sc, (int64_t)(p0 / 4), stream)) return KQ_ERR_LAUNCH;
+  if (launch_fill((unsigned *)(sc + p0), (int64_t)((p1 - p0) / 4), stream, 0xFFFFFFFFu)) return KQ_ERR_LAUNCH;
+  if (launch_fill((unsigned *)(sc + p1), (int64_t)((need - p1) / 4), stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
 kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan, void *scratch, size_t scratch_bytes,
                         void *stream) {
   if (!table_dev || !plan || !scratch) return KQ_ERR_NULL;
-  if (plan->n_phases < 1 || plan->n_phases > KQ_MAX_CHAIN_PHASES || plan->m < 1 || plan->m > kMaxRows ||
-      plan->workgroups < 1 || plan->max_groups < 1 || plan->tiles_per_wave != 1 ||
-      (plan->layout != KQ_LAYOUT_ROWS && plan->layout != KQ_LAYOUT_TILED16))
-    return KQ_ERR_SHAPE;
+  if (!chain_plan_fields_ok(plan)) return KQ_ERR_SHAPE;
   if (!al(table_dev, 16) || !al(scratch, 256)) return KQ_ERR_ALIGN;
-  const size_t need = chain_flag_off(plan->max_groups, plan->workgroups, plan->tiles_per_wave) +
-                      chain_flag_bytes(plan->workgroups);
-  if (plan->scratch_bytes != need) return KQ_ERR_SHAPE;  // not a plan kq_chain_encode wrote
+  const size_t need = chain_plan_scratch(plan);
+  if (!need) return KQ_ERR_SHAPE;  // not a plan kq_chain_encode wrote
   if (scratch_bytes < need) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));

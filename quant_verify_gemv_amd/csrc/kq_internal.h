@@ -42,8 +42,8 @@ constexpr int64_t kStageBytes = 16384 + 512 + 64;  // 16,960 B per block (16-B a
 //              different groups do not queue on one line
 //   keys_off   per-workgroup argmax keys [n_wg][16] (u64)
 //   part_off   partial sums [n_wg][2][16][rows per group] fp32
-constexpr int64_t kBarOff = 128;
-constexpr int64_t kErrOff = 256;
+constexpr int64_t kBarOff = KQ_CHAIN_BARRIER_OFFSET;
+constexpr int64_t kErrOff = KQ_CHAIN_ERROR_OFFSET;
 constexpr int64_t kEpochOff = 384;
 constexpr int64_t kCntOff = 512;
 constexpr int kCntStride = 32;
@@ -121,7 +121,7 @@ int launch_gemv(const GemvLaunch &a, void *stream);
 // Workgroups of the chain kernel (8 waves of one 16-row tile) the current
 // device holds at once, or a negative HIP error code.
 int chain_capacity();
-int launch_fill(unsigned *p, int64_t n_words, void *stream);
+int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value = 0u);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
 int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);
 

@@ -251,10 +251,10 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
 
 // ---------------------------------------------------------------------------
 
-__global__ void kq_fill_kernel(unsigned *p, int64_t n) {
+__global__ void kq_fill_kernel(unsigned *p, int64_t n, unsigned value) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) p[i] = 0u;
+  for (; i < n; i += stride) p[i] = value;
 }
 
 // ---------------------------------------------------------------------------
@@ -848,7 +848,83 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       if (both) finish_group(gb, vb);
     };
 
-    if (have_first || last_partial) {
+    // Chains reduce split row groups by pulling: the first contributor of a
+    // group (the workgroup that owns its first block, which reaches its
+    // part of the group last, at the end of its run) sums the later
+    // contributors' partials as soon as they are present, and every other
+    // contributor just stores its partial (its first group's, slot 0). An
+    // unwritten slot holds the sentinel pattern (all ones, a NaN arithmetic
+    // on finite inputs never produces); the reducer resets each slot it
+    // consumed, so every launch leaves the slots as it found them. This
+    // saves the store acknowledgement and the arrival atomic that the
+    // last-to-arrive hand-off below puts on the critical path of each
+    // phase. The sum runs over the contributors in workgroup order, as
+    // below, so both hand-offs give bitwise identical results.
+    if (CHAIN && (have_first || last_partial)) {
+      const bool red_first = have_first && owner(g_first * KB) == p;
+      if (have_first && !red_first) write_partial(0, acc_first);
+      if (red_first || last_partial) {
+        const int g = red_first ? g_first : g_last;
+        // own partial into LDS (the activation ring is idle after the loop)
+        uint8_t *own = s_x[0];
+        static_assert(kRows * kMaxRows * 4 <= kStageBytes, "own partial fits one ring buffer");
+        const f32x4(&mine)[T] = red_first ? acc_first : acc;
+#pragma unroll
+        for (int t = 0; t < T; ++t) *(f32x4 *)(own + (tile_row(t) * kMaxRows + 4 * kg) * 4) = mine[t];
+        __syncthreads();
+        const int pfg = p, plg = owner(g * KB + KB - 1);
+        f32x4 v[kE];
+#pragma unroll
+        for (int j = 0; j < kE; ++j) v[j] = *(const f32x4 *)(own + (tid + j * kNth) * 16);
+        int bad = 0;
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        for (int c0 = 1; c0 <= plg - pfg; c0 += kC) {
+          f32x4 pv[kE][kC];
+          // loads of up to kC contributors in flight together (past the last
+          // one: re-read it, dropped below)
+#pragma unroll
+          for (int c = 0; c < kC; ++c) {
+            const int q = pfg + c0 + c <= plg ? pfg + c0 + c : plg;
+            const unsigned src = (unsigned)(q * 2 * kMaxRows * kRows) * 4u;
+#pragma unroll
+            for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
+          }
+#pragma unroll
+          for (int c = 0; c < kC; ++c) {
+            if (pfg + c0 + c > plg) continue;
+            const unsigned src = (unsigned)((pfg + c0 + c) * 2 * kMaxRows * kRows) * 4u;
+#pragma unroll
+            for (int j = 0; j < kE; ++j) {
+              // not yet written: poll (bounded)
+              while (true) {
+                const u32x4 w = __builtin_bit_cast(u32x4, pv[j][c]);
+                if (w.x != 0xFFFFFFFFu && w.y != 0xFFFFFFFFu && w.z != 0xFFFFFFFFu && w.w != 0xFFFFFFFFu) break;
+                if (bad || __builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                  bad = 1;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
+              }
+              v[j] = v[j] + pv[j][c];
+            }
+          }
+        }
+        if (__syncthreads_or(bad)) {
+          if (tid == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;  // a partial never arrived: *a.err is set, every workgroup leaves
+        }
+        finish_group(g, v);
+        // reset the consumed slots (written through before this workgroup
+        // arrives at the barrier, so before any contributor reuses its slot)
+        const f32x4 sentinel = __builtin_bit_cast(f32x4, u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+        for (int q = pfg + 1; q <= plg; ++q)
+#pragma unroll
+          for (int j = 0; j < kE; ++j)
+            st_dev16(part_rsrc, (unsigned)(q * 2 * kMaxRows * kRows) * 4u + (unsigned)(tid + j * kNth) * 16u,
+                     sentinel);
+      }
+    } else if (have_first || last_partial) {
       if (have_first) write_partial(0, acc_first);
       if (last_partial) write_partial(1, acc);
       // contributor counts of both groups (computed while the stores drain)
@@ -1050,12 +1126,12 @@ int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ct
   return (int)hipGetLastError();
 }
 
-int launch_fill(unsigned *p, int64_t n_words, void *stream) {
+int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value) {
   int64_t blocks = (n_words + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(kq_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p,
-                     n_words);
+                     n_words, value);
   return (int)hipGetLastError();
 }
 

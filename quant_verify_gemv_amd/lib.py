@@ -22,13 +22,14 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
             "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights", "kq_draft_block_argmax",
             "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes",
-            "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain")
+            "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
 
 MAX_GROUP = 8
-CHAIN_ERROR_OFFSET = 256   # byte offset of the chain's barrier time-out word in its scratch
+CHAIN_BARRIER_OFFSET = 128  # byte offset of the chain's barrier arrival count in its scratch
+CHAIN_ERROR_OFFSET = 256    # byte offset of the chain's barrier time-out word in its scratch
 
 
 class ChainPhase(ctypes.Structure):
@@ -92,10 +93,11 @@ def load() -> ctypes.CDLL:
     lib.kq_chain_table_bytes.restype = SZ
     lib.kq_chain_encode.argtypes = [ctypes.POINTER(ChainPhase), I32, I32, I32, P, SZ, ctypes.POINTER(ChainPlan)]
     lib.kq_gemv_chain.argtypes = [P, ctypes.POINTER(ChainPlan), P, SZ, P]
+    lib.kq_chain_scratch_init.argtypes = [ctypes.POINTER(ChainPlan), P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
-                 "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain"):
+                 "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -381,6 +383,11 @@ class Chain:
     def workgroups(self) -> int:
         return int(self.plan.workgroups)
 
+    def init_scratch(self, stream=None):
+        """kq_chain_scratch_init on this chain's scratch (current stream)."""
+        _check(load().kq_chain_scratch_init(ctypes.byref(self.plan), _dev_ptr(self.scratch, "scratch"),
+                                            self.scratch.numel(), _stream_handle(stream)), "kq_chain_scratch_init")
+
     def error_word(self) -> int:
         """The barrier time-out word (synchronises with the device)."""
         off = CHAIN_ERROR_OFFSET
@@ -422,7 +429,9 @@ def chain_encode(phases, m: int, layout=LAYOUT_ROWS, device=None) -> Chain:
     dev = device if device is not None else refs[0].device
     table = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(dev)
     scratch = alloc_workspace(int(plan.scratch_bytes), dev)
-    return Chain(table, plan, scratch, refs)
+    chain = Chain(table, plan, scratch, refs)
+    chain.init_scratch()
+    return chain
 
 
 def gemv_chain(chain: Chain, stream=None):

@@ -298,3 +298,12 @@ def test_gemv_chain_argument_errors_before_any_hip_call():
         assert lib.kq_gemv_chain(FAKE, ctypes.byref(q), FAKE, 1 << 30, None) == SHAPE, field
     assert lib.kq_gemv_chain(FAKE + 8, ctypes.byref(pl), FAKE, 1 << 30, None) == ALIGN
     assert lib.kq_gemv_chain(FAKE, ctypes.byref(pl), FAKE + 16, 1 << 30, None) == ALIGN
+
+
+def test_chain_scratch_init_argument_errors_before_any_hip_call():
+    lib = kq.load()
+    pl = kq.ChainPlan()
+    pl.n_phases, pl.m, pl.layout, pl.workgroups, pl.max_groups, pl.tiles_per_wave = 2, 16, 0, 256, 4, 1
+    assert lib.kq_chain_scratch_init(None, FAKE, 1 << 30, None) == NULL
+    assert lib.kq_chain_scratch_init(ctypes.byref(pl), None, 1 << 30, None) == NULL
+    assert lib.kq_chain_scratch_init(ctypes.byref(pl), FAKE, 1 << 30, None) == SHAPE  # inconsistent scratch_bytes

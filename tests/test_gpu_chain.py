@@ -154,3 +154,33 @@ def test_chain_many_phases_bitwise_equal_to_single_launches(kq):
             else:
                 L, A = oracle.gemv_rows(ws[i % 4], k, x, rows=rows)
                 check_logits(r[i][:, rows], L, A, what=f"chain many phase {i}")
+
+
+def test_chain_wait_timeout_sets_error_word_and_reinit_recovers(kq):
+    """Failure path, forced from the host: a barrier count preloaded with a
+    value no arrival can complete leaves every workgroup waiting for a
+    release that never comes; each wait gives up after its bound (1 s of the
+    real-time counter), raises the sticky error word and leaves, so the
+    launch ends. kq_chain_scratch_init then restores a working state."""
+    import time
+    n, k = 300, 1024
+    w = synthetic.q4k_matrix(n, k, 61)
+    x = synthetic.activations(16, k, 62)
+    wd = to_dev(w)
+    st = kq.stage_rows(to_dev(x))
+    outs = [torch.empty((16, n), dtype=torch.float32, device=DEV) for _ in range(2)]
+    chain = kq.chain_encode([([wd], n, k, st, [outs[0]]), ([wd], n, k, st, [outs[1]])], 16)
+    first = run_chain(kq, chain, outs)
+    off = kq.lib.CHAIN_BARRIER_OFFSET
+    chain.scratch[off:off + 4].view(torch.int32).fill_(1 << 30)
+    torch.cuda.synchronize()
+    log("chain timeout: launching with an unreachable barrier count (expect ~1 s)")
+    t0 = time.time()
+    kq.gemv_chain(chain)
+    torch.cuda.synchronize()
+    log(f"chain timeout: launch ended after {time.time() - t0:.2f} s")
+    assert chain.error_word() == 1
+    chain.init_scratch()
+    again = run_chain(kq, chain, outs)
+    for a, b in zip(first, again):
+        assert np.array_equal(a, b)
