@@ -235,6 +235,53 @@ kq_status kq_gemv_staged_group(const void *const *w_q4k, int layout, int count, 
 kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave,
                              int *workgroups, int64_t *units);
 
+/* ------------------------------------------------- stochastic verify
+ * The accept / resample rule of ch. 33 section 33.2 at temperature > 0: the
+ * target judges each proposed token against its full probability row for
+ * that position. The data-parallel half runs on the GPU (the probability
+ * rows from the verify step's logits); the decision runs on the host, where
+ * the pages keep it ("every rounding decision is visible"), in 32-bit
+ * arithmetic in a fixed order. */
+
+/* Bytes of device workspace kq_softmax_rows needs (0 for invalid shapes). */
+size_t kq_softmax_workspace_bytes(int m, int64_t n);
+
+/* Target probability rows: probs[r][j] = softmax_j(z[r]) with
+ * z = l / temperature, after the optional soft cap l -> soft_cap *
+ * tanh(l / soft_cap) (soft_cap = 0: none). fp32, every reduction in a fixed
+ * order (deterministic).
+ *  logits     device fp32 [m][n] (e.g. the verify step's logits)
+ *  m, n       1 <= m <= 65535, 1 <= n < 2^31
+ *  temperature > 0 and finite; soft_cap >= 0 and finite (else KQ_ERR_SHAPE)
+ *  probs      device fp32 [m][n] (written; may not alias logits)
+ *  workspace  device, >= kq_softmax_workspace_bytes(m, n), 256-byte aligned
+ * Two launches on `stream`. */
+kq_status kq_softmax_rows(const float *logits, int m, int64_t n, float temperature, float soft_cap, float *probs,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* The decision (host; no HIP call). k = number of proposals (0..15).
+ *  draft_tokens  host int32 [k] in [0, n)
+ *  draft_rows    host fp32 [k][n]: the draft's probability rows q
+ *  target_rows   host fp32 [k + 1][n]: the target's rows p (kq_softmax_rows)
+ *  orders        host int32 [k + 1][n]: the token order each row is walked in
+ *                when it is sampled (entries in [0, n); normally a permutation)
+ *  uniforms      host fp32 [k + 1] in [0, 1): u[i] decides position i; the
+ *                replacement after a rejection at i uses u[i + 1], the bonus
+ *                after k acceptances u[k]
+ *  accepted, next_token  host int32 (written)
+ * Position i is accepted when u[i] <= min(p_i[d_i] / q_i[d_i], 1) (certain
+ * when q_i[d_i] <= 0). On the first rejection the replacement is drawn from
+ * max(p_i - q_i, 0) divided by its fp32 sum (or from p_i when that sum is not
+ * positive), walking orders[i] over the tokens with a positive residual:
+ * the first token whose running fp32 sum exceeds the draw, else the last one
+ * walked. After k acceptances the bonus is drawn the same way from p_k over
+ * all of orders[k]. Every argument is checked before the first draw
+ * (KQ_ERR_NULL / SHAPE / TOKEN); KQ_ERR_SHAPE also when a row to sample has
+ * no positive probability. */
+kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, const float *draft_rows,
+                                const float *target_rows, const int32_t *orders, const float *uniforms,
+                                int32_t *accepted, int32_t *next_token);
+
 /* ---------------------------------------------------------------- chains
  * A chain launch runs a sequence of grouped products in ONE grid, each
  * phase depending on the one before it: phase i + 1 starts reading its

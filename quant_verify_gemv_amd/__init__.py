@@ -2,12 +2,14 @@
 
 The hot path (activation staging, Q4_K dequant + MFMA skinny GEMM, split-K
 combine, row argmax, greedy accept, draft block proposals, chains of
-dependent products in one launch) runs in HIP kernels inside libkq.so,
+dependent products in one launch, target probability rows for the
+stochastic verify) runs in HIP kernels inside libkq.so,
 behind the C ABI of include/kq.h. This package is the thin Python binding.
 """
 from .lib import (CHAIN_ERROR_OFFSET, DRAFT_VERIFY_LENGTHS, LAYOUT_ROWS, LAYOUT_TILED16,  # noqa: F401
                   MAX_GROUP, Chain, ChainPhase, ChainPlan, KQError, chain_encode, chain_table_bytes,
-                  draft_block_argmax, draft_block_argmax_staged, gemv_chain, gemv_rows, gemv_staged, gemv_staged_group, group_scratch_bytes, launch_geometry, load, new_group_scratch,
+                  draft_block_argmax, draft_block_argmax_staged, gemv_chain, gemv_rows, gemv_staged, gemv_staged_group, softmax_rows, softmax_workspace_bytes,
+                  speculative_decide, group_scratch_bytes, launch_geometry, load, new_group_scratch,
                   new_scratch, scratch_bytes, stage_rows, staged_bytes, status_string, stream_probe, tile_weights,
                   tiled_bytes, verify, verify_staged, workspace_bytes)
 

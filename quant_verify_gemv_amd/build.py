@@ -43,7 +43,9 @@ def build(verbose: bool = False) -> str:
     try:
         obj_api = os.path.join(tmp, "kq_api.o")
         obj_k = os.path.join(tmp, "kq_kernels.o")
-        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
+        # -ffp-contract=off: the host decision's float arithmetic is exactly
+        # the sequence written (no fused multiply-adds)
+        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC,
               "-c", os.path.join(CSRC, "kq_api.cpp"), "-o", obj_api], verbose)
         _run([HIPCC] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
               os.path.join(CSRC, "kq_kernels.hip"), "-o", obj_k], verbose)

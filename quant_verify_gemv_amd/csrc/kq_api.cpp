@@ -2,8 +2,11 @@
 // (always before any HIP call), workspace layout, launch geometry.
 #include "kq.h"
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <vector>
 
 #include "kq_internal.h"
 
@@ -460,6 +463,80 @@ kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan, void *
   a.g = chain_geometry(128, kQK, 1, plan->tiles_per_wave);
   a.g.n_wg = plan->workgroups;
   if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+size_t kq_softmax_workspace_bytes(int m, int64_t n) {
+  if (m < 1 || m > 65535 || n < 1 || n >= ((int64_t)1 << 31)) return 0;
+  return align256((size_t)m * (size_t)softmax_chunks(n) * 2 * sizeof(float));
+}
+
+kq_status kq_softmax_rows(const float *logits, int m, int64_t n, float temperature, float soft_cap, float *probs,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  if (!logits || !probs || !workspace) return KQ_ERR_NULL;
+  if (m < 1 || m > 65535 || n < 1 || n >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
+  if (!(temperature > 0.0f) || !isfinite(temperature) || !(soft_cap >= 0.0f) || !isfinite(soft_cap))
+    return KQ_ERR_SHAPE;
+  if (!al(logits, 4) || !al(probs, 4) || !al(workspace, 256)) return KQ_ERR_ALIGN;
+  if (workspace_bytes < kq_softmax_workspace_bytes(m, n)) return KQ_ERR_WORKSPACE;
+  if (launch_softmax(logits, m, n, temperature, soft_cap, (float *)workspace, probs, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+// Draw from `prob` by walking `order` (keeping only tokens with prob > 0 when
+// `positive_only`): fp32 running sum, the first token whose sum exceeds u,
+// else the last token walked. -1 when no token qualifies.
+static int32_t sample_in_order(const float *prob, const int32_t *order, int64_t n, float u, bool positive_only) {
+  float c = 0.0f;
+  int32_t last = -1;
+  for (int64_t j = 0; j < n; ++j) {
+    const int32_t t = order[j];
+    if (positive_only && !(prob[t] > 0.0f)) continue;
+    c = c + prob[t];
+    last = t;
+    if (u < c) return t;
+  }
+  return last;
+}
+
+kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, const float *draft_rows,
+                                const float *target_rows, const int32_t *orders, const float *uniforms,
+                                int32_t *accepted, int32_t *next_token) {
+  if (!target_rows || !orders || !uniforms || !accepted || !next_token) return KQ_ERR_NULL;
+  if (k > 0 && (!draft_tokens || !draft_rows)) return KQ_ERR_NULL;
+  if (k < 0 || k >= kMaxRows || n < 1 || n >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
+  // the whole geometry is checked before the first draw
+  for (int i = 0; i < k; ++i)
+    if (draft_tokens[i] < 0 || (int64_t)draft_tokens[i] >= n) return KQ_ERR_TOKEN;
+  for (int64_t j = 0; j < (int64_t)(k + 1) * n; ++j)
+    if (orders[j] < 0 || (int64_t)orders[j] >= n) return KQ_ERR_TOKEN;
+  for (int i = 0; i < k; ++i) {
+    const float *q = draft_rows + (int64_t)i * n;
+    const float *p = target_rows + (int64_t)i * n;
+    const int32_t t = draft_tokens[i];
+    const float acceptance = q[t] <= 0.0f ? 1.0f : fminf(p[t] / q[t], 1.0f);
+    if (uniforms[i] <= acceptance) continue;
+    // first rejection: the replacement comes from max(p - q, 0), renormalised
+    std::vector<float> residual((size_t)n);
+    float total = 0.0f;
+    for (int64_t j = 0; j < n; ++j) {
+      residual[(size_t)j] = fmaxf(p[j] - q[j], 0.0f);
+      total = total + residual[(size_t)j];
+    }
+    if (total <= 0.0f) {
+      for (int64_t j = 0; j < n; ++j) residual[(size_t)j] = p[j];
+    } else {
+      for (int64_t j = 0; j < n; ++j) residual[(size_t)j] = residual[(size_t)j] / total;
+    }
+    const int32_t tok = sample_in_order(residual.data(), orders + (int64_t)i * n, n, uniforms[i + 1], true);
+    if (tok < 0) return KQ_ERR_SHAPE;  // a row without any positive probability
+    *accepted = i;
+    *next_token = tok;
+    return KQ_OK;
+  }
+  const int32_t tok = sample_in_order(target_rows + (int64_t)k * n, orders + (int64_t)k * n, n, uniforms[k], false);
+  *accepted = k;
+  *next_token = tok;
   return KQ_OK;
 }
 

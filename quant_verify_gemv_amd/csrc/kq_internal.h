@@ -124,5 +124,10 @@ int chain_capacity();
 int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value = 0u);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
 int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);
+// Softmax rows: chunks of a row (4,096 logits each) and the two-pass launch
+// (part: rows x chunks float pairs of workspace).
+int softmax_chunks(int64_t n);
+int launch_softmax(const float *logits, int m, int64_t n, float temperature, float cap, float *part, float *probs,
+                   void *stream);
 
 }  // namespace kq

@@ -1078,6 +1078,96 @@ __global__ __launch_bounds__(256) void kq_tile_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Target probability rows for the stochastic verify: p = softmax(z) per row,
+// z = l / T after the optional soft cap l -> cap * tanh(l / cap). Two
+// passes over chunks of kSmChunk logits (grid: chunks x rows):
+//  1. each chunk's max of z and its sum of exp(z - chunk max) -> partials;
+//  2. each chunk combines its row's partials in chunk order (row max M,
+//     S = sum_c s_c exp(m_c - M)) and writes p = exp(z - M) / S.
+// Every reduction runs in a fixed order, so results are deterministic.
+constexpr int kSmThreads = 256;
+constexpr int kSmPer = 16;  // logits per thread
+constexpr int64_t kSmChunk = (int64_t)kSmThreads * kSmPer;
+
+__device__ __forceinline__ float sm_z(float l, float inv_cap, float cap, float temperature) {
+  if (cap > 0.0f) l = cap * tanhf(l * inv_cap);
+  return l / temperature;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(kSmThreads) void kq_softmax_partial_kernel(const float *__restrict__ logits, int64_t n,
+                                                                        float temperature, float cap,
+                                                                        float2 *__restrict__ part) {
+  __shared__ float red[4];
+  const int64_t c = blockIdx.x, row = blockIdx.y, chunks = gridDim.x;
+  const float *l = logits + row * n;
+  const int64_t base = c * kSmChunk;
+  const float inv_cap = cap > 0.0f ? 1.0f / cap : 0.0f;
+  float z[kSmPer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kSmPer; ++j) {
+    const int64_t i = base + (int64_t)j * kSmThreads + threadIdx.x;
+    z[j] = i < n ? sm_z(l[i], inv_cap, cap, temperature) : -INFINITY;
+    mx = fmaxf(mx, z[j]);
+  }
+  mx = block_max(mx, red);
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSmPer; ++j) sum += z[j] == -INFINITY ? 0.0f : expf(z[j] - mx);
+  sum = block_sum(sum, red);
+  if (threadIdx.x == 0) part[row * chunks + c] = float2{mx, sum};
+}
+
+__global__ __launch_bounds__(kSmThreads) void kq_softmax_write_kernel(const float *__restrict__ logits, int64_t n,
+                                                                      float temperature, float cap,
+                                                                      const float2 *__restrict__ part,
+                                                                      float *__restrict__ probs) {
+  const int64_t c = blockIdx.x, row = blockIdx.y, chunks = gridDim.x;
+  const float2 *pr = part + row * chunks;
+  // row max and denominator, in chunk order (every thread alike)
+  float m = -INFINITY;
+  for (int64_t q = 0; q < chunks; ++q) m = fmaxf(m, pr[q].x);
+  float s = 0.0f;
+  for (int64_t q = 0; q < chunks; ++q) s += pr[q].y * expf(pr[q].x - m);
+  const float *l = logits + row * n;
+  float *p = probs + row * n;
+  const int64_t base = c * kSmChunk;
+  const float inv_cap = cap > 0.0f ? 1.0f / cap : 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSmPer; ++j) {
+    const int64_t i = base + (int64_t)j * kSmThreads + threadIdx.x;
+    if (i < n) p[i] = expf(sm_z(l[i], inv_cap, cap, temperature) - m) / s;
+  }
+}
+
+int softmax_chunks(int64_t n) { return (int)((n + kSmChunk - 1) / kSmChunk); }
+
+int launch_softmax(const float *logits, int m, int64_t n, float temperature, float cap, float *part, float *probs,
+                   void *stream) {
+  const dim3 grid((unsigned)softmax_chunks(n), (unsigned)m);
+  hipLaunchKernelGGL(kq_softmax_partial_kernel, grid, dim3(kSmThreads), 0, (hipStream_t)stream, logits, n,
+                     temperature, cap, (float2 *)part);
+  hipLaunchKernelGGL(kq_softmax_write_kernel, grid, dim3(kSmThreads), 0, (hipStream_t)stream, logits, n,
+                     temperature, cap, (const float2 *)part, probs);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Read probe: every 16-byte chunk of a buffer is loaded once, workgroup b
 // streaming its own contiguous slab (four 1 KB wave loads in flight per
 // wave), XOR-folded, and one word per workgroup is written so the loads are

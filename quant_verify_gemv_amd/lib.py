@@ -22,7 +22,8 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_group_scratch_bytes",
             "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights", "kq_draft_block_argmax",
             "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes",
-            "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init")
+            "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
+            "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -94,10 +95,16 @@ def load() -> ctypes.CDLL:
     lib.kq_chain_encode.argtypes = [ctypes.POINTER(ChainPhase), I32, I32, I32, P, SZ, ctypes.POINTER(ChainPlan)]
     lib.kq_gemv_chain.argtypes = [P, ctypes.POINTER(ChainPlan), P, SZ, P]
     lib.kq_chain_scratch_init.argtypes = [ctypes.POINTER(ChainPlan), P, SZ, P]
+    lib.kq_softmax_workspace_bytes.argtypes = [I32, I64]
+    lib.kq_softmax_workspace_bytes.restype = SZ
+    F = ctypes.c_float
+    lib.kq_softmax_rows.argtypes = [P, I32, I64, F, F, P, P, SZ, P]
+    lib.kq_speculative_decide.argtypes = [I32, P, I64, P, P, P, P, P, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
-                 "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init"):
+                 "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
+                 "kq_softmax_rows", "kq_speculative_decide"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -439,3 +446,46 @@ def gemv_chain(chain: Chain, stream=None):
     _check(load().kq_gemv_chain(_dev_ptr(chain.table, "table"), ctypes.byref(chain.plan),
                                 _dev_ptr(chain.scratch, "scratch"), chain.scratch.numel(),
                                 _stream_handle(stream)), "kq_gemv_chain")
+
+
+# -------------------------------------------------------- stochastic verify
+
+def softmax_workspace_bytes(m: int, n: int) -> int:
+    return int(load().kq_softmax_workspace_bytes(m, n))
+
+
+def softmax_rows(logits, temperature: float = 1.0, soft_cap: float = 0.0, probs=None, workspace=None,
+                 stream=None):
+    """Target probability rows (device fp32 [m, n]) from device logits [m, n]."""
+    torch = _torch()
+    m, n = int(logits.shape[0]), int(logits.shape[1])
+    if probs is None:
+        probs = torch.empty_like(logits)
+    need = softmax_workspace_bytes(m, n)
+    ws = workspace if workspace is not None else _WS.get(max(need, 256), logits.device)
+    _check(load().kq_softmax_rows(_dev_ptr(logits, "logits", torch.float32), m, n, float(temperature),
+                                  float(soft_cap), _dev_ptr(probs, "probs", torch.float32), _dev_ptr(ws, "workspace"),
+                                  ws.numel(), _stream_handle(stream)), "kq_softmax_rows")
+    return probs
+
+
+def speculative_decide(draft, draft_rows, target_rows, orders, uniforms):
+    """The accept / resample decision on host arrays (numpy): draft [k],
+    draft_rows fp32 [k, n], target_rows fp32 [k + 1, n], orders int32
+    [k + 1, n], uniforms fp32 [k + 1]. Returns (accepted, next_token)."""
+    import numpy as np
+    k = len(draft)
+    tr = np.ascontiguousarray(target_rows, dtype=np.float32)
+    n = int(tr.shape[1])
+    dr = np.ascontiguousarray(draft_rows, dtype=np.float32) if k else np.zeros((1, n), np.float32)
+    od = np.ascontiguousarray(orders, dtype=np.int32)
+    un = np.ascontiguousarray(uniforms, dtype=np.float32)
+    dt = np.ascontiguousarray(draft, dtype=np.int32) if k else np.zeros(1, np.int32)
+    if tr.shape[0] != k + 1 or od.shape != (k + 1, n) or un.shape != (k + 1,) or (k and dr.shape != (k, n)):
+        raise ValueError("geometry: need k draft rows, k + 1 target rows, orders and uniforms")
+    acc, nxt = ctypes.c_int32(0), ctypes.c_int32(0)
+    vp = ctypes.c_void_p
+    _check(load().kq_speculative_decide(k, vp(dt.ctypes.data), n, vp(dr.ctypes.data), vp(tr.ctypes.data),
+                                        vp(od.ctypes.data), vp(un.ctypes.data), ctypes.byref(acc),
+                                        ctypes.byref(nxt)), "kq_speculative_decide")
+    return int(acc.value), int(nxt.value)

@@ -1,0 +1,104 @@
+"""The library's host decision of the stochastic verify (kq_speculative_decide)
+against the oracle, bit for bit on the same fp32 inputs (no GPU needed), and
+its argument checks (all before the first draw)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle.stochastic import speculative_decide as oracle_decide
+from quant_verify_gemv_amd import lib as kq
+
+NULL, SHAPE, TOKEN = 1, 2, 4
+
+
+def random_case(rng, n, k, peaked=False):
+    z = rng.normal(size=(k + 1, n)) * (4.0 if peaked else 1.0)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    y = rng.normal(size=(k, n)) * (4.0 if peaked else 1.0)
+    q = np.exp(y - y.max(axis=1, keepdims=True))
+    q = (q / q.sum(axis=1, keepdims=True)).astype(np.float32)
+    # proposals drawn from the draft rows, as a draft would
+    draft = [int(rng.choice(n, p=q[i] / q[i].sum())) for i in range(k)]
+    orders = np.stack([rng.permutation(n) for _ in range(k + 1)]).astype(np.int32)
+    u = rng.random(k + 1).astype(np.float32)
+    return draft, q, p, orders, u
+
+
+@pytest.mark.parametrize("n,k", [(5, 3), (64, 7), (1000, 15), (7, 0)])
+def test_decide_matches_oracle_bitwise(n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    seen = set()
+    for trial in range(300 if n < 1000 else 40):
+        draft, q, p, orders, u = random_case(rng, n, k, peaked=trial % 2 == 1)
+        got = kq.speculative_decide(draft, q, p, orders, u)
+        want = oracle_decide(draft, q, p, orders, u)
+        assert got == want, (trial, got, want)
+        seen.add(got[0])
+    if k:
+        assert len(seen) > 1, "every trial took the same branch"
+
+
+def test_decide_one_hot_is_greedy():
+    n, k = 6, 4
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        am = rng.integers(0, n, k + 1)
+        draft = [int(am[i]) if rng.random() < 0.7 else int(rng.integers(n)) for i in range(k)]
+        p = np.eye(n, dtype=np.float32)[am]
+        q = np.eye(n, dtype=np.float32)[draft]
+        orders = np.tile(np.arange(n, dtype=np.int32), (k + 1, 1))
+        acc, nxt = kq.speculative_decide(draft, q, p, orders, rng.random(k + 1).astype(np.float32) * 0.999)
+        want = next((i for i in range(k) if draft[i] != am[i]), k)
+        assert (acc, nxt) == (want, int(am[want]))
+
+
+def test_decide_argument_errors():
+    lib = kq.load()
+    n, k = 4, 2
+    p = np.full((k + 1, n), 0.25, np.float32)
+    q = np.full((k, n), 0.25, np.float32)
+    o = np.tile(np.arange(n, dtype=np.int32), (k + 1, 1))
+    u = np.full(k + 1, 0.5, np.float32)
+    d = np.array([1, 2], np.int32)
+    acc, nxt = ctypes.c_int32(), ctypes.c_int32()
+    vp = ctypes.c_void_p
+
+    def call(k=k, d=d, n=n, q=q, p=p, o=o, u=u, a=True):
+        return lib.kq_speculative_decide(k, vp(d.ctypes.data) if d is not None else None, n,
+                                         vp(q.ctypes.data) if q is not None else None,
+                                         vp(p.ctypes.data) if p is not None else None,
+                                         vp(o.ctypes.data) if o is not None else None,
+                                         vp(u.ctypes.data) if u is not None else None,
+                                         ctypes.byref(acc) if a else None, ctypes.byref(nxt))
+    assert call() == 0
+    assert call(p=None) == NULL and call(o=None) == NULL and call(u=None) == NULL and call(a=False) == NULL
+    assert call(d=None) == NULL and call(q=None) == NULL
+    assert call(k=-1) == SHAPE and call(k=16) == SHAPE and call(n=0) == SHAPE
+    assert call(d=np.array([1, 4], np.int32)) == TOKEN
+    bad = o.copy()
+    bad[2, 3] = 9
+    assert call(o=bad) == TOKEN
+    # a row to sample without any positive probability
+    assert call(k=0, p=np.zeros((1, n), np.float32), o=o[:1], u=u[:1]) == 0  # bonus walks every token
+    zero = p.copy()
+    zero[0] = 0
+    qq = q.copy()
+    qq[0] = 0.5
+    assert call(p=zero, q=qq, u=np.array([0.9, 0.5, 0.5], np.float32)) == SHAPE
+
+
+def test_softmax_argument_errors_before_any_hip_call():
+    lib = kq.load()
+    FAKE = 0x7F0000000000
+    assert kq.softmax_workspace_bytes(0, 10) == 0 and kq.softmax_workspace_bytes(16, 0) == 0
+    assert kq.softmax_workspace_bytes(16, 131072) >= 16 * 32 * 8
+    ws = kq.softmax_workspace_bytes(16, 131072)
+    assert lib.kq_softmax_rows(None, 16, 131072, 1.0, 0.0, FAKE, FAKE, ws, None) == NULL
+    assert lib.kq_softmax_rows(FAKE, 16, 131072, 0.0, 0.0, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.kq_softmax_rows(FAKE, 16, 131072, 1.0, -1.0, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.kq_softmax_rows(FAKE, 16, 131072, float("inf"), 0.0, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.kq_softmax_rows(FAKE, 0, 131072, 1.0, 0.0, FAKE, FAKE, ws, None) == SHAPE
+    assert lib.kq_softmax_rows(FAKE + 2, 16, 131072, 1.0, 0.0, FAKE, FAKE, ws, None) == 3
+    assert lib.kq_softmax_rows(FAKE, 16, 131072, 1.0, 0.0, FAKE, FAKE, ws - 1, None) == 5
