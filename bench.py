@@ -247,6 +247,35 @@ def run_m(stack, torch, m, steps, warmup, use_graph, extras=True):
     return wall, ev, spread
 
 
+def graph_time(torch, fn, calls, reps=5):
+    """Microseconds per call: `calls` back-to-back calls fn(0..calls-1)
+    captured in one HIP graph, averaged over `reps` replays timed with HIP
+    events on the replay stream (so the host's per-call cost of the Python
+    binding is not in the figure)."""
+    for i in range(3):
+        fn(i)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * calls)
+
+
 def draft_block_timing(stack, torch, calls=50):
     """The draft block's proposals (argmax of rows 1..15 of a 16-row block
     against the LM head, no accept), timed on the resident LM-head weights
@@ -269,23 +298,16 @@ def draft_block_timing(stack, torch, calls=50):
     same_rows = bool(torch.equal(props, stack.am[1:16]) and torch.equal(head, stack.am[:1]))
     if not same_rows:
         raise RuntimeError("draft block proposals differ from the verify step's argmax of the same rows")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(calls):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / calls
+    us = graph_time(torch, lambda i: call(), calls)
     gbs = h.weight_bytes / (us * 1e-6) / 1e9
     return {"verify_length": 15, "us_per_call": round(us, 2), "weight_gb_s": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "calls": calls, "launch": "eager",
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "calls": calls, "launch": "hipgraph, back-to-back",
             "matches_verify_argmax": same_rows}
 
 
 def config_timings(stack, torch, calls=50):
     """The other configurations of the benchmark definition, each timed on
-    its own (back-to-back launches, HIP events on the launch stream, tiled
+    its own (back-to-back launches replayed from a HIP graph, tiled
     weights as in the step): the square 6,656 x 6,656 product at every M of
     its sweep, rotating over 16 copies (399 MB, more than the 256 MB MALL);
     the DFlash fc projection 33,280 -> 6,656 at M = 16 over 4 copies
@@ -302,17 +324,7 @@ def config_timings(stack, torch, calls=50):
                 "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     def time_calls(fn):
-        for _ in range(5):
-            fn(0)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(calls):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / calls
+        return graph_time(torch, fn, calls)
 
     def copies(cfg, count):
         n, k = cfg["n"], cfg["k"]
@@ -352,9 +364,65 @@ def config_timings(stack, torch, calls=50):
     us = time_calls(lambda i: kq.verify_staged(stack.w_head, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
                                                  out=(stack.am, stack.acc, None), layout=stack.layout))
     out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us)
-    out["launch"] = "eager, back-to-back"
+    out["stochastic_lm_head_m16"] = stochastic_timing(stack, torch, time_calls)
+    out["launch"] = "hipgraph, back-to-back"
     torch.cuda.synchronize()
     return out
+
+
+def stochastic_timing(stack, torch, time_calls, temperature=300.0, decisions=20):
+    """The stochastic verify at the LM-head size (16 rows x 131,072): the
+    verify launch with logits out, the target probability rows
+    (kq_softmax_rows: two launches, 8 algorithmic bytes per element, one
+    fp32 read and one write), and the library's host decision
+    (kq_speculative_decide) on rows copied to host memory, with the copy
+    timed on its own. Draft rows are the softmax of perturbed logits."""
+    kq = stack.kq
+    h = stack.head
+    n, m = h.n, 16
+    sth = stack.staged[h.k]
+    lg = torch.empty((m, n), dtype=torch.float32, device=stack.dev)
+    probs = torch.empty_like(lg)
+    ws = torch.empty(max(256, kq.softmax_workspace_bytes(m, n)), dtype=torch.uint8, device=stack.dev)
+    us_verify = time_calls(lambda i: kq.verify_staged(stack.w_head, n, h.k, sth, m, stack.draft[:15],
+                                                      stack.head_scratch, out=(stack.am, stack.acc, lg),
+                                                      layout=stack.layout))
+    us_soft = time_calls(lambda i: kq.softmax_rows(lg, temperature, 0.0, probs=probs, workspace=ws))
+
+    def both(i):
+        kq.verify_staged(stack.w_head, n, h.k, sth, m, stack.draft[:15], stack.head_scratch,
+                         out=(stack.am, stack.acc, lg), layout=stack.layout)
+        kq.softmax_rows(lg, temperature, 0.0, probs=probs, workspace=ws)
+    us_both = time_calls(both)
+    gen = torch.Generator(device=stack.dev).manual_seed(5)
+    noisy = lg[:m - 1] + 60.0 * torch.randn((m - 1, n), generator=gen, device=stack.dev)
+    q = kq.softmax_rows(noisy.contiguous(), temperature).cpu().numpy()
+    torch.cuda.synchronize()
+    host = torch.empty((m, n), dtype=torch.float32, pin_memory=True)
+    t0 = time.perf_counter()
+    for _ in range(decisions):
+        host.copy_(probs)
+    us_copy = (time.perf_counter() - t0) * 1e6 / decisions
+    p = host.numpy()
+    orders = np.argsort(-p, axis=1, kind="stable").astype(np.int32)
+    rng = np.random.default_rng(9)
+    drafts = [[int(np.searchsorted(np.cumsum(q[i], dtype=np.float64), rng.random() * q[i].sum()))
+               for i in range(m - 1)] for _ in range(decisions)]
+    drafts = [[min(t, n - 1) for t in d] for d in drafts]
+    us_ = rng.random((decisions, m)).astype(np.float32)
+    t0 = time.perf_counter()
+    accepted = [kq.speculative_decide(drafts[j], q, p, orders, us_[j])[0] for j in range(decisions)]
+    us_decide = (time.perf_counter() - t0) * 1e6 / decisions
+    soft_bytes = 8 * m * n
+    return {"temperature": temperature,
+            "verify_logits_us": round(us_verify, 2),
+            "softmax_rows_us": round(us_soft, 2),
+            "softmax_gb_s": round(soft_bytes / (us_soft * 1e-6) / 1e9, 1),
+            "softmax_algorithmic_bytes": soft_bytes,
+            "verify_plus_rows_us": round(us_both, 2),
+            "rows_to_host_us": round(us_copy, 1),
+            "host_decide_us": round(us_decide, 1),
+            "mean_accepted": round(float(np.mean(accepted)), 2)}
 
 
 def read_ceiling(stack, torch, calls=20):

@@ -275,9 +275,11 @@ kq_status kq_softmax_rows(const float *logits, int m, int64_t n, float temperatu
  * positive), walking orders[i] over the tokens with a positive residual:
  * the first token whose running fp32 sum exceeds the draw, else the last one
  * walked. After k acceptances the bonus is drawn the same way from p_k over
- * all of orders[k]. Every argument is checked before the first draw
- * (KQ_ERR_NULL / SHAPE / TOKEN); KQ_ERR_SHAPE also when a row to sample has
- * no positive probability. */
+ * all of orders[k]. Pointers, k, n and the draft tokens are checked first;
+ * the one order row that is sampled is checked whole before it is walked
+ * (rows that are not sampled are not read) (KQ_ERR_NULL / SHAPE / TOKEN);
+ * KQ_ERR_SHAPE also when a row to sample has no positive probability. The
+ * outputs are written only on KQ_OK. */
 kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, const float *draft_rows,
                                 const float *target_rows, const int32_t *orders, const float *uniforms,
                                 int32_t *accepted, int32_t *next_token);

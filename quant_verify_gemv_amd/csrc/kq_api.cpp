@@ -6,7 +6,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <vector>
 
 #include "kq_internal.h"
 
@@ -483,16 +482,26 @@ kq_status kq_softmax_rows(const float *logits, int m, int64_t n, float temperatu
   return KQ_OK;
 }
 
-// Draw from `prob` by walking `order` (keeping only tokens with prob > 0 when
-// `positive_only`): fp32 running sum, the first token whose sum exceeds u,
-// else the last token walked. -1 when no token qualifies.
-static int32_t sample_in_order(const float *prob, const int32_t *order, int64_t n, float u, bool positive_only) {
+// Every token of one order row is in [0, n).
+static bool order_row_ok(const int32_t *order, int64_t n) {
+  for (int64_t j = 0; j < n; ++j)
+    if (order[j] < 0 || (int64_t)order[j] >= n) return false;
+  return true;
+}
+
+// Draw by walking `order`. A token's value is p[t], or, when q is given,
+// max(p[t] - q[t], 0) / total; tokens whose value is not positive are skipped
+// when `positive_only`. fp32 running sum, the first token whose sum exceeds
+// u, else the last token walked; -1 when no token qualifies.
+static int32_t sample_in_order(const float *p, const float *q, float total, const int32_t *order, int64_t n,
+                               float u, bool positive_only) {
   float c = 0.0f;
   int32_t last = -1;
   for (int64_t j = 0; j < n; ++j) {
     const int32_t t = order[j];
-    if (positive_only && !(prob[t] > 0.0f)) continue;
-    c = c + prob[t];
+    const float v = q ? fmaxf(p[t] - q[t], 0.0f) / total : p[t];
+    if (positive_only && !(v > 0.0f)) continue;
+    c = c + v;
     last = t;
     if (u < c) return t;
   }
@@ -505,38 +514,31 @@ kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, c
   if (!target_rows || !orders || !uniforms || !accepted || !next_token) return KQ_ERR_NULL;
   if (k > 0 && (!draft_tokens || !draft_rows)) return KQ_ERR_NULL;
   if (k < 0 || k >= kMaxRows || n < 1 || n >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
-  // the whole geometry is checked before the first draw
   for (int i = 0; i < k; ++i)
     if (draft_tokens[i] < 0 || (int64_t)draft_tokens[i] >= n) return KQ_ERR_TOKEN;
-  for (int64_t j = 0; j < (int64_t)(k + 1) * n; ++j)
-    if (orders[j] < 0 || (int64_t)orders[j] >= n) return KQ_ERR_TOKEN;
   for (int i = 0; i < k; ++i) {
     const float *q = draft_rows + (int64_t)i * n;
     const float *p = target_rows + (int64_t)i * n;
     const int32_t t = draft_tokens[i];
     const float acceptance = q[t] <= 0.0f ? 1.0f : fminf(p[t] / q[t], 1.0f);
     if (uniforms[i] <= acceptance) continue;
-    // first rejection: the replacement comes from max(p - q, 0), renormalised
-    std::vector<float> residual((size_t)n);
+    // first rejection: the replacement comes from max(p - q, 0) divided by
+    // its sum (summed in token order), or from p when that sum is not positive
+    const int32_t *order = orders + (int64_t)i * n;
+    if (!order_row_ok(order, n)) return KQ_ERR_TOKEN;
     float total = 0.0f;
-    for (int64_t j = 0; j < n; ++j) {
-      residual[(size_t)j] = fmaxf(p[j] - q[j], 0.0f);
-      total = total + residual[(size_t)j];
-    }
-    if (total <= 0.0f) {
-      for (int64_t j = 0; j < n; ++j) residual[(size_t)j] = p[j];
-    } else {
-      for (int64_t j = 0; j < n; ++j) residual[(size_t)j] = residual[(size_t)j] / total;
-    }
-    const int32_t tok = sample_in_order(residual.data(), orders + (int64_t)i * n, n, uniforms[i + 1], true);
+    for (int64_t j = 0; j < n; ++j) total = total + fmaxf(p[j] - q[j], 0.0f);
+    const int32_t tok = sample_in_order(p, total > 0.0f ? q : nullptr, total, order, n, uniforms[i + 1], true);
     if (tok < 0) return KQ_ERR_SHAPE;  // a row without any positive probability
     *accepted = i;
     *next_token = tok;
     return KQ_OK;
   }
-  const int32_t tok = sample_in_order(target_rows + (int64_t)k * n, orders + (int64_t)k * n, n, uniforms[k], false);
+  const int32_t *order = orders + (int64_t)k * n;
+  if (!order_row_ok(order, n)) return KQ_ERR_TOKEN;
+  const float *p = target_rows + (int64_t)k * n;
   *accepted = k;
-  *next_token = tok;
+  *next_token = sample_in_order(p, nullptr, 0.0f, order, n, uniforms[k], false);
   return KQ_OK;
 }
 

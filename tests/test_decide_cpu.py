@@ -78,8 +78,12 @@ def test_decide_argument_errors():
     assert call(k=-1) == SHAPE and call(k=16) == SHAPE and call(n=0) == SHAPE
     assert call(d=np.array([1, 4], np.int32)) == TOKEN
     bad = o.copy()
-    bad[2, 3] = 9
-    assert call(o=bad) == TOKEN
+    bad[2, 3] = 9  # row k is the one sampled when every proposal is accepted
+    acc.value = nxt.value = -7
+    assert call(o=bad) == TOKEN and acc.value == -7 and nxt.value == -7  # no output on error
+    unread = o.copy()
+    unread[0, 1] = 9  # a row that is not sampled is not read
+    assert call(o=unread) == 0 and acc.value == k
     # a row to sample without any positive probability
     assert call(k=0, p=np.zeros((1, n), np.float32), o=o[:1], u=u[:1]) == 0  # bonus walks every token
     zero = p.copy()

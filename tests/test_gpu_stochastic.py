@@ -96,7 +96,8 @@ def test_stochastic_verify_lm_head(kq):
     for trial in range(24):
         noisy = Lh[:kd] + rng.normal(size=(kd, n)).astype(np.float32) * np.float32(40.0 + 20 * (trial % 4))
         q = oracle_softmax(noisy, T).astype(np.float32)
-        draft = [int(rng.choice(n, p=q[i].astype(np.float64) / q[i].sum())) for i in range(kd)]
+        qd = q.astype(np.float64)
+        draft = [int(rng.choice(n, p=qd[i] / qd[i].sum())) for i in range(kd)]
         u = rng.random(m).astype(np.float32)
         got = kq.speculative_decide(draft, q, Ph, orders, u)
         assert got == oracle_decide(draft, q, Ph, orders, u), f"trial {trial}: library != oracle on the same rows"
