@@ -1082,7 +1082,7 @@ __global__ __launch_bounds__(256) void kq_tile_kernel(const uint8_t *__restrict_
 // z = l / T after the optional soft cap l -> cap * tanh(l / cap). Two
 // passes over chunks of kSmChunk logits (grid: chunks x rows):
 //  1. each chunk's max of z and its sum of exp(z - chunk max) -> partials;
-//  2. each chunk combines its row's partials in chunk order (row max M,
+//  2. each chunk combines its row's partials (row max M,
 //     S = sum_c s_c exp(m_c - M)) and writes p = exp(z - M) / S.
 // Every reduction runs in a fixed order, so results are deterministic.
 constexpr int kSmThreads = 256;
@@ -1139,11 +1139,20 @@ __global__ __launch_bounds__(kSmThreads) void kq_softmax_write_kernel(const floa
                                                                       float *__restrict__ probs) {
   const int64_t c = blockIdx.x, row = blockIdx.y, chunks = gridDim.x;
   const float2 *pr = part + row * chunks;
-  // row max and denominator, in chunk order (every thread alike)
+  // Row max and denominator: lane j takes partials j, j + 64, ... (loads in
+  // parallel across the wave), then an xor butterfly across the wave. Max
+  // and add are commutative, so every lane of every wave ends with the same
+  // bits; the order is fixed, so results are the same on every run.
+  const int lane = threadIdx.x & 63;
   float m = -INFINITY;
-  for (int64_t q = 0; q < chunks; ++q) m = fmaxf(m, pr[q].x);
+  for (int64_t q = lane; q < chunks; q += 64) m = fmaxf(m, pr[q].x);
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   float s = 0.0f;
-  for (int64_t q = 0; q < chunks; ++q) s += pr[q].y * expf(pr[q].x - m);
+  for (int64_t q = lane; q < chunks; q += 64) {
+    const float2 v = pr[q];
+    s += v.x == -INFINITY ? 0.0f : v.y * expf(v.x - m);
+  }
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
   const float *l = logits + row * n;
   float *p = probs + row * n;
   const int64_t base = c * kSmChunk;
