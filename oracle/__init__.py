@@ -1,4 +1,5 @@
-"""CPU oracle for the Q4_K batched verify step (ctypes wrapper over kq_oracle.c).
+"""CPU oracle for the k-quant (Q4_K, Q5_K, Q6_K) batched verify step (ctypes
+wrapper over kq_oracle.c).
 
 TEST INFRASTRUCTURE ONLY. The product library never imports, links or runs
 anything here; only tests/, the smoke check and the bench's CPU-baseline leg
@@ -24,6 +25,13 @@ _LIB = os.path.join(_HERE, "libkq_oracle.so")
 _lib = None
 
 REL_TOL = 1e-4  # declared logit tolerance: |G - L| <= REL_TOL * sum_k |w_k x_k|
+
+# weight formats: name -> (code of the C functions, bytes per 256 weights)
+FORMATS = {"q4k": (4, 144), "q5k": (5, 176), "q6k": (6, 210)}
+
+
+def block_bytes(fmt: str = "q4k") -> int:
+    return FORMATS[fmt][1]
 
 
 def build(force: bool = True) -> str:
@@ -62,6 +70,16 @@ def _load():
     lib.kqo_candidates.restype = i64
     lib.kqo_accept.argtypes = [P, ctypes.c_int, P, P, P]
     lib.kqo_accept.restype = ctypes.c_int
+    lib.kqo_quant_q5k.argtypes = [P, P, ctypes.c_int]
+    lib.kqo_quant_q5k.restype = ctypes.c_int
+    lib.kqo_quant_q6k.argtypes = [P, P, ctypes.c_int]
+    lib.kqo_quant_q6k.restype = ctypes.c_int
+    lib.kqo_decode_block_fmt.argtypes = [ctypes.c_int, P, P]
+    lib.kqo_decode_block_fmt.restype = ctypes.c_int
+    lib.kqo_decode_row_fmt.argtypes = [ctypes.c_int, P, i64, P]
+    lib.kqo_decode_row_fmt.restype = ctypes.c_int
+    lib.kqo_gemv_rows_fmt.argtypes = [ctypes.c_int, P, i64, i64, P, ctypes.c_int, P, i64, P, P, ctypes.c_int]
+    lib.kqo_gemv_rows_fmt.restype = ctypes.c_int
     lib.kqo_num_threads.argtypes = []
     lib.kqo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -89,41 +107,45 @@ def scales_mins(s12: bytes) -> Tuple[np.ndarray, np.ndarray]:
     return sc, mn
 
 
-def decode_block(blk) -> np.ndarray:
+def decode_block(blk, fmt: str = "q4k") -> np.ndarray:
+    """The 256 exact weights (fp64) of one block of format `fmt`."""
+    code, nb = FORMATS[fmt]
     b = np.ascontiguousarray(np.frombuffer(bytes(blk), dtype=np.uint8))
-    assert b.shape == (144,)
+    assert b.shape == (nb,)
     w = np.zeros(256, dtype=np.float64)
-    if _load().kqo_decode_block(_p(b), _p(w)):
-        raise ValueError("non-finite d or dmin")
+    if _load().kqo_decode_block_fmt(code, _p(b), _p(w)):
+        raise ValueError("non-finite block scale")
     return w
 
 
-def decode_matrix(w: np.ndarray, k: int) -> np.ndarray:
-    """Exact fp64 weights [N, K] of a Q4_K matrix (small matrices only)."""
+def decode_matrix(w: np.ndarray, k: int, fmt: str = "q4k") -> np.ndarray:
+    """Exact fp64 weights [N, K] of a matrix of format `fmt` (small matrices only)."""
+    code, _ = FORMATS[fmt]
     w = np.ascontiguousarray(w, dtype=np.uint8)
     n = w.shape[0]
     out = np.zeros((n, k), dtype=np.float64)
     lib = _load()
     for r in range(n):
         row = np.ascontiguousarray(w[r])
-        if lib.kqo_decode_row(_p(row), k, _p(out[r])):
-            raise ValueError("non-finite d or dmin")
+        if lib.kqo_decode_row_fmt(code, _p(row), k, _p(out[r])):
+            raise ValueError("non-finite block scale")
     return out
 
 
 def gemv_rows(w: np.ndarray, k: int, x: np.ndarray, rows: Optional[Sequence[int]] = None,
-              threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+              threads: int = 0, fmt: str = "q4k") -> Tuple[np.ndarray, np.ndarray]:
     """(L, A), each float64 [M, n_out]: L = W x^T in fp64, A = sum |w x|.
 
-    w: uint8 [N, K/256*144]; x: float32 [M, K]; rows: optional subset of the
-    N output rows (outputs then follow that order)."""
+    w: uint8 [N, K/256 * block bytes of `fmt`]; x: float32 [M, K]; rows:
+    optional subset of the N output rows (outputs then follow that order)."""
+    code, nb = FORMATS[fmt]
     w = np.ascontiguousarray(w, dtype=np.uint8)
     x = np.ascontiguousarray(x, dtype=np.float32)
     if x.ndim == 1:
         x = x[None, :]
     n = w.shape[0]
     m = x.shape[0]
-    if x.shape[1] != k or w.shape[1] != (k // 256) * 144:
+    if x.shape[1] != k or w.shape[1] != (k // 256) * nb:
         raise ValueError("shape mismatch")
     if rows is None:
         r_arr = None
@@ -133,13 +155,13 @@ def gemv_rows(w: np.ndarray, k: int, x: np.ndarray, rows: Optional[Sequence[int]
         nout = r_arr.shape[0]
     L = np.zeros((m, nout), dtype=np.float64)
     A = np.zeros((m, nout), dtype=np.float64)
-    rc = _load().kqo_gemv_rows(_p(w), n, k, _p(x), m,
-                               _p(r_arr) if r_arr is not None else None, nout,
-                               _p(L), _p(A), int(threads))
+    rc = _load().kqo_gemv_rows_fmt(code, _p(w), n, k, _p(x), m,
+                                   _p(r_arr) if r_arr is not None else None, nout,
+                                   _p(L), _p(A), int(threads))
     if rc == -3:
         raise ValueError("non-finite activation")
     if rc == -2:
-        raise ValueError("non-finite d or dmin")
+        raise ValueError("non-finite block scale")
     if rc:
         raise ValueError("bad shape")
     return L, A
@@ -180,10 +202,10 @@ def accept(draft: Sequence[int], argmax: Sequence[int]) -> Tuple[int, int]:
 
 
 def verify(w: np.ndarray, k: int, x: np.ndarray, draft: Sequence[int], rel: float = REL_TOL,
-           threads: int = 0):
+           threads: int = 0, fmt: str = "q4k"):
     """The whole step on the CPU: logits, argmax with flags, greedy accept.
     Returns dict(L, A, argmax, n_cand, accepted, next_token)."""
-    L, A = gemv_rows(w, k, x, threads=threads)
+    L, A = gemv_rows(w, k, x, threads=threads, fmt=fmt)
     am, nc = argmax_flags(L, A, rel)
     acc, nxt = accept(draft, am)
     return dict(L=L, A=A, argmax=am, n_cand=nc, accepted=acc, next_token=nxt)

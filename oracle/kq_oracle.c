@@ -27,6 +27,24 @@
  *     and next_token is the argmax of row `accepted` (the last row when all
  *     k are accepted).
  *
+ * Other k-quant formats (the next formats after Q4_K: the pages say the
+ * draft loads Q4_K, Q5_K and Q6_K tensors and that its v projection is
+ * Q6_K, ch. 8 "The DFlash draft", section 8.2; the byte layouts are the
+ * llama.cpp GGUF ones, unpinned against llama.cpp here):
+ *
+ *  Q5_K, 176 bytes per 256 weights: fp16 d, fp16 dmin, the same 12 bytes of
+ *    6-bit scales/mins as Q4_K, 32 bytes of fifth bits, 128 bytes of
+ *    nibbles. Weight i has sub-block j = i / 32, its low four bits where a
+ *    Q4_K block keeps them and its fifth bit in bit j of fifth-bit byte
+ *    i % 32; w = d * sc_j * q - dmin * m_j, q in [0, 31].
+ *  Q6_K, 210 bytes per 256 weights: 128 bytes of low nibbles, 64 bytes of
+ *    2-bit high parts, 16 signed 8-bit scales, fp16 d last. Weight i of
+ *    half h = i / 128 (r = i % 128, quarter c = r / 32, l = r % 32) takes
+ *    its low four bits from nibble byte 64 h + l + 32 (c & 1) (low nibble
+ *    for c < 2, high for c >= 2) and its top two bits from bits 2c, 2c + 1
+ *    of high-part byte 32 h + l; its scale is scale byte i / 16;
+ *    w = d * sc * (q - 32), q in [0, 63].
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no fast-math, no intrinsics).
  */
 #include <math.h>
@@ -39,6 +57,13 @@
 
 #define KQO_QK 256
 #define KQO_BLOCK 144
+#define KQO_BLOCK_Q5K 176
+#define KQO_BLOCK_Q6K 210
+
+/* Weight format codes of the *_fmt functions. */
+#define KQO_Q4K 4
+#define KQO_Q5K 5
+#define KQO_Q6K 6
 
 /* IEEE-754 binary16 bit pattern to double: sign, 5-bit exponent (bias 15),
  * 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24). Returns NaN
@@ -112,21 +137,105 @@ int kqo_decode_row(const uint8_t *row, int64_t k, double *w) {
     return 0;
 }
 
+/* The 5-bit quant of weight i of a Q5_K block: four low bits from the
+ * nibbles (as in Q4_K), the fifth from bit i / 32 of byte i % 32 of qh. */
+int kqo_quant_q5k(const uint8_t *qh32, const uint8_t *q128, int i) {
+    int hi = (qh32[i % 32] >> (i / 32)) & 1;
+    return kqo_quant(q128, i) + 16 * hi;
+}
+
+/* Decode one 176-byte Q5_K block; 0, or -1 when d or dmin is not finite. */
+int kqo_decode_block_q5k(const uint8_t *blk, double *w) {
+    uint16_t dh = (uint16_t)(blk[0] | (blk[1] << 8));
+    uint16_t mh = (uint16_t)(blk[2] | (blk[3] << 8));
+    double d = kqo_half_to_double(dh);
+    double dmin = kqo_half_to_double(mh);
+    if (isnan(d) || isnan(dmin)) return -1;
+    int sc[8], mn[8];
+    kqo_scales_mins(blk + 4, sc, mn);
+    for (int i = 0; i < KQO_QK; ++i) {
+        int j = i / 32;
+        int q = kqo_quant_q5k(blk + 16, blk + 48, i);
+        w[i] = d * (double)sc[j] * (double)q - dmin * (double)mn[j];
+    }
+    return 0;
+}
+
+/* The 6-bit quant (0..63, before the -32 offset) of weight i of a Q6_K
+ * block from its 128 nibble bytes and 64 high-part bytes. */
+int kqo_quant_q6k(const uint8_t *ql, const uint8_t *qh, int i) {
+    int h = i / 128, r = i % 128, c = r / 32, l = r % 32;
+    uint8_t b = ql[64 * h + l + 32 * (c & 1)];
+    int lo = c < 2 ? (b & 15) : (b >> 4);
+    int hi = (qh[32 * h + l] >> (2 * c)) & 3;
+    return lo | (hi << 4);
+}
+
+/* Decode one 210-byte Q6_K block; 0, or -1 when d is not finite. */
+int kqo_decode_block_q6k(const uint8_t *blk, double *w) {
+    const uint8_t *ql = blk, *qh = blk + 128;
+    const int8_t *sc = (const int8_t *)(blk + 192);
+    uint16_t dh = (uint16_t)(blk[208] | (blk[209] << 8));
+    double d = kqo_half_to_double(dh);
+    if (isnan(d)) return -1;
+    for (int i = 0; i < KQO_QK; ++i)
+        w[i] = d * (double)sc[i / 16] * (double)(kqo_quant_q6k(ql, qh, i) - 32);
+    return 0;
+}
+
+/* Bytes per 256-weight block of a format code (0 for an unknown code). */
+int kqo_block_bytes(int fmt) {
+    return fmt == KQO_Q4K ? KQO_BLOCK : fmt == KQO_Q5K ? KQO_BLOCK_Q5K : fmt == KQO_Q6K ? KQO_BLOCK_Q6K : 0;
+}
+
+/* Decode one block of format `fmt`; -1 for a non-finite header, -4 for an
+ * unknown format. */
+int kqo_decode_block_fmt(int fmt, const uint8_t *blk, double *w) {
+    if (fmt == KQO_Q4K) return kqo_decode_block(blk, w);
+    if (fmt == KQO_Q5K) return kqo_decode_block_q5k(blk, w);
+    if (fmt == KQO_Q6K) return kqo_decode_block_q6k(blk, w);
+    return -4;
+}
+
+/* Decode a full row of K weights of format `fmt`. */
+int kqo_decode_row_fmt(int fmt, const uint8_t *row, int64_t k, double *w) {
+    int bb = kqo_block_bytes(fmt);
+    if (!bb) return -4;
+    for (int64_t b = 0; b < k / KQO_QK; ++b) {
+        int rc = kqo_decode_block_fmt(fmt, row + b * bb, w + b * KQO_QK);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
 /* L[m][n] and A[m][n] (row-major [m][n], fp64) for an N x K Q4_K matrix and
  * M fp32 activation rows [m][k]. `rows` may be NULL (all rows 0..n-1) or a
  * list of n_rows row indices, in which case outputs are [m][n_rows].
  * Returns 0; -1 for bad shapes; -2 for a non-finite d/dmin; -3 for a
  * non-finite activation. nthreads <= 0 keeps the OpenMP default. */
+int kqo_gemv_rows_fmt(int fmt, const uint8_t *w, int64_t n, int64_t k, const float *x, int m,
+                      const int64_t *rows, int64_t n_rows, double *L, double *A,
+                      int nthreads);
+
 int kqo_gemv_rows(const uint8_t *w, int64_t n, int64_t k, const float *x, int m,
                   const int64_t *rows, int64_t n_rows, double *L, double *A,
                   int nthreads) {
+    return kqo_gemv_rows_fmt(KQO_Q4K, w, n, k, x, m, rows, n_rows, L, A, nthreads);
+}
+
+/* kqo_gemv_rows for a matrix in format `fmt` (rows of K / 256 blocks of
+ * kqo_block_bytes(fmt) bytes); -4 for an unknown format. */
+int kqo_gemv_rows_fmt(int fmt, const uint8_t *w, int64_t n, int64_t k, const float *x, int m,
+                      const int64_t *rows, int64_t n_rows, double *L, double *A,
+                      int nthreads) {
+    if (!kqo_block_bytes(fmt)) return -4;
     if (n <= 0 || k <= 0 || k % KQO_QK || m <= 0) return -1;
     for (int64_t i = 0; i < (int64_t)m * k; ++i)
         if (!isfinite(x[i])) return -3;
     int64_t nout = rows ? n_rows : n;
     for (int64_t r = 0; r < nout; ++r)
         if (rows && (rows[r] < 0 || rows[r] >= n)) return -1;
-    int64_t row_bytes = (k / KQO_QK) * KQO_BLOCK;
+    int64_t row_bytes = (k / KQO_QK) * kqo_block_bytes(fmt);
     int bad = 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -141,7 +250,7 @@ int kqo_gemv_rows(const uint8_t *w, int64_t n, int64_t k, const float *x, int m,
 #pragma omp for schedule(dynamic, 16)
         for (int64_t r = 0; r < nout; ++r) {
             int64_t nn = rows ? rows[r] : r;
-            if (kqo_decode_row(w + nn * row_bytes, k, wr)) {
+            if (kqo_decode_row_fmt(fmt, w + nn * row_bytes, k, wr)) {
 #pragma omp atomic write
                 bad = 1;
                 continue;

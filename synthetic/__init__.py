@@ -117,6 +117,51 @@ def q4k_matrix(n: int, k: int, seed: int, d_range=(0.001, 0.05)) -> np.ndarray:
     return blocks.reshape(n, (k // QK) * BLOCK_BYTES)
 
 
+Q5K_BLOCK_BYTES = 176
+Q6K_BLOCK_BYTES = 210
+
+
+def _random_blocks(n: int, k: int, seed: int, block_bytes: int, d_offsets, d_range, stream: int) -> np.ndarray:
+    """N x K/256 random blocks of `block_bytes` bytes whose fp16 fields at
+    byte offsets `d_offsets` are ~U(d_range) (53-bit uniforms, rounded to
+    fp16 to nearest even); every other byte uniform random."""
+    if k % QK:
+        raise ValueError(f"K={k} is not a multiple of {QK}")
+    nb = n * (k // QK)
+    words = (nb * block_bytes + 7) // 8
+    blocks = random_u64(words, seed, stream).view(np.uint8)[:nb * block_bytes].reshape(nb, block_bytes).copy()
+    lo, hi = d_range
+    nd = len(d_offsets)
+    step = 1 << 22
+    for b0 in range(0, nb, step):
+        b1 = min(nb, b0 + step)
+        u = random_u64(nd * (b1 - b0), seed * 1000003 + b0 // step, stream + 1)
+        uf = (u >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        dd = (lo + (hi - lo) * uf).astype(np.float16).view(np.uint8).reshape(b1 - b0, nd, 2)
+        for j, off in enumerate(d_offsets):
+            blocks[b0:b1, off:off + 2] = dd[:, j, :]
+    return blocks.reshape(n, (k // QK) * block_bytes)
+
+
+def q5k_matrix(n: int, k: int, seed: int, d_range=(0.001, 0.05)) -> np.ndarray:
+    """Random Q5_K matrix uint8 [N, K/256*176]: d and dmin (bytes 0..3)
+    ~U(d_range) rounded to fp16; scales, fifth bits and nibbles uniform."""
+    return _random_blocks(n, k, seed, Q5K_BLOCK_BYTES, (0, 2), d_range, 10)
+
+
+def q6k_matrix(n: int, k: int, seed: int, d_range=(0.0002, 0.01)) -> np.ndarray:
+    """Random Q6_K matrix uint8 [N, K/256*210]: d (bytes 208..209)
+    ~U(d_range) rounded to fp16; nibbles, high parts and the signed 8-bit
+    scales uniform (a smaller default d keeps |w| = d |sc (q - 32)| <=
+    4,096 d in the range of the other formats)."""
+    return _random_blocks(n, k, seed, Q6K_BLOCK_BYTES, (208,), d_range, 12)
+
+
+def kquant_matrix(fmt: str, n: int, k: int, seed: int) -> np.ndarray:
+    """Random matrix of format "q4k", "q5k" or "q6k"."""
+    return {"q4k": q4k_matrix, "q5k": q5k_matrix, "q6k": q6k_matrix}[fmt](n, k, seed)
+
+
 def activations(m: int, k: int, seed: int) -> np.ndarray:
     """fp32 activation rows [M, K] ~ N(0, 1)."""
     g = np.random.Generator(np.random.PCG64(_seq(seed, 2)))
