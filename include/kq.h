@@ -67,6 +67,12 @@ typedef int kq_status;
 /* Weight layouts accepted by the staged calls. */
 #define KQ_LAYOUT_ROWS    0  /* llama.cpp: row n is k/256 consecutive 144-byte blocks */
 #define KQ_LAYOUT_TILED16 1  /* kq_tile_weights output (same bytes, reordered) */
+/* Q5_K and Q6_K weights (the draft loads Q4_K, Q5_K and Q6_K tensors and its
+ * v projection is Q6_K: muser-book ch. 8 "The DFlash draft", section 8.2),
+ * tiled by kq_tile_weights_fmt from llama.cpp rows (176- and 210-byte
+ * blocks); every entry point that takes a layout accepts them. */
+#define KQ_LAYOUT_Q5K_TILED16 2
+#define KQ_LAYOUT_Q6K_TILED16 3
 
 /* Measurement helper, not part of the verify step: reads every byte of a
  * device buffer once (16-byte loads over the whole GPU) and writes one
@@ -90,7 +96,8 @@ size_t kq_workspace_bytes(int64_t n, int64_t k, int m);
 /* Bytes of a staged activation block for k columns (any m <= 16). */
 size_t kq_staged_bytes(int64_t k);
 
-/* Bytes of device scratch the *_staged calls need for an n x k matrix. */
+/* Bytes of device scratch the *_staged calls need for an n x k matrix (in
+ * any weight format and layout). */
 size_t kq_scratch_bytes(int64_t n, int64_t k);
 
 /* Zero the control words of a workspace or scratch buffer of `bytes` bytes
@@ -156,8 +163,35 @@ size_t kq_tiled_bytes(int64_t n, int64_t k);
 kq_status kq_tile_weights(const void *w_q4k, int64_t n, int64_t k,
                           void *w_tiled, size_t tiled_bytes, void *stream);
 
+/* Bytes of the tiled copy in `layout` (KQ_LAYOUT_TILED16, KQ_LAYOUT_Q5K_TILED16
+ * or KQ_LAYOUT_Q6K_TILED16) of an n x k matrix: ceil(n/16) * (k/256) * 16 *
+ * (144, 176 or 210); 0 for invalid shapes or layouts. */
+size_t kq_tiled_bytes_fmt(int layout, int64_t n, int64_t k);
+
+/* Tile an n x k matrix given as llama.cpp rows of its format (device; Q4_K
+ * 144-, Q5_K 176-, Q6_K 210-byte blocks, layout GGUF) into `layout`
+ * (device, >= kq_tiled_bytes_fmt bytes, 16-byte aligned, not overlapping the
+ * input). KQ_LAYOUT_TILED16 is kq_tile_weights. The Q5_K and Q6_K records
+ * (block b of 16-row tile t at (b * ceil(n/16) + t) * 16 * block bytes) keep
+ * every bit of the 16 blocks, reordered so that lane l = 16 g + r of a wave
+ * (row r, g = 0..3) reads its weights' low four bits exactly where a Q4_K
+ * record keeps them:
+ *  Q5_K (2,816 B): the 16 headers (d, dmin, 12 scale/min bytes) at 16 r;
+ *    quant bytes [16g, 16g+16) at 256 + 16 l and [64+16g, 80+16g) at
+ *    1,280 + 16 l; the lane's 64 fifth bits at 2,304 + 8 l.
+ *  Q6_K (3,360 B): the lane's 4 signed scales at 4 l; the low nibbles in the
+ *    Q4_K order at 256 + 16 l and 1,280 + 16 l; the lane's 64 two-bit high
+ *    parts at 2,304 + 16 l; fp16 d of row r at 3,328 + 2 r.
+ * Rows past n are zero. Q5_K and Q6_K have no row-major kernel path: pass
+ * their tiled copy. Input the row layout requires: the rows are 16-byte
+ * aligned for Q4_K and Q5_K, 2-byte aligned for Q6_K. */
+kq_status kq_tile_weights_fmt(int layout, const void *w_rows, int64_t n, int64_t k,
+                              void *w_tiled, size_t tiled_bytes, void *stream);
+
 /* kq_gemv_rows on staged activations.
- *  layout   KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16 (the layout of w_q4k)
+ *  layout   KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16 (the layout of w_q4k), or
+ *           KQ_LAYOUT_Q5K_TILED16 / KQ_LAYOUT_Q6K_TILED16 (w_q4k is then a
+ *           tiled Q5_K or Q6_K matrix; same staged activations)
  *  scratch  device, >= kq_scratch_bytes(n, k) bytes, 256-byte aligned,
  *           zeroed once by kq_workspace_init */
 kq_status kq_gemv_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
@@ -206,7 +240,7 @@ kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
                            void *scratch, size_t scratch_bytes, void *stream);
 
 /* Bytes of device scratch kq_gemv_staged_group needs for `count` matrices
- * of n x k (0 for invalid arguments). */
+ * of n x k in any weight format (0 for invalid arguments). */
 size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count);
 
 /* kq_gemv_staged for 1 <= count <= 8 matrices of the same shape that share

@@ -6,7 +6,8 @@ dependent products in one launch, target probability rows for the
 stochastic verify) runs in HIP kernels inside libkq.so,
 behind the C ABI of include/kq.h. This package is the thin Python binding.
 """
-from .lib import (CHAIN_ERROR_OFFSET, DRAFT_VERIFY_LENGTHS, LAYOUT_ROWS, LAYOUT_TILED16,  # noqa: F401
+from .lib import (CHAIN_ERROR_OFFSET, DRAFT_VERIFY_LENGTHS, FORMATS, LAYOUT_Q5K_TILED16,  # noqa: F401
+                  LAYOUT_Q6K_TILED16, LAYOUT_ROWS, LAYOUT_TILED16,
                   MAX_GROUP, Chain, ChainPhase, ChainPlan, KQError, chain_encode, chain_table_bytes,
                   draft_block_argmax, draft_block_argmax_staged, gemv_chain, gemv_rows, gemv_staged, gemv_staged_group, softmax_rows, softmax_workspace_bytes,
                   speculative_decide, group_scratch_bytes, launch_geometry, load, new_group_scratch,

@@ -17,11 +17,13 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // The kernels address a weight matrix (either layout, rows rounded up to a
 // 16-row tile) and a staged activation block with 32-bit offsets, so both
 // must be smaller than 4 GiB.
-static bool shape_ok(int64_t n, int64_t k) {
+// Every matrix and every staged block is smaller than 4 GiB: the kernels
+// address them with 32-bit offsets.
+static bool shape_ok(int64_t n, int64_t k, int fmt = kFmtQ4) {
   if (!(n >= 1 && n < ((int64_t)1 << 31) && k > 0 && k % kQK == 0 && k <= ((int64_t)1 << 28))) return false;
   const int64_t kb = k / kQK;
   const int64_t limit = (int64_t)1 << 32;
-  return cdiv(n, 16) * 16 * kb * kBlockBytes < limit && kb * kStageBytes < limit;
+  return cdiv(n, 16) * 16 * kb * fmt_block_bytes(fmt) < limit && kb * kStageBytes < limit;
 }
 
 // Launch geometry: persistent workgroups, one per CU (their LDS activation
@@ -39,7 +41,7 @@ struct Shape {
   int waves, tpw, per_cu, bi, depth;
 };
 
-static Shape pick_shape(int64_t n, int count) {
+static Shape pick_shape(int64_t n, int count, int fmt) {
 #ifdef KQ_GEOM_WAVES  // build-time override for tuning sweeps
 #ifndef KQ_GEOM_BI
 #define KQ_GEOM_BI 1
@@ -49,17 +51,21 @@ static Shape pick_shape(int64_t n, int count) {
 #endif
   (void)n;
   (void)count;
+  (void)fmt;
   return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI, KQ_GEOM_DEPTH};
 #endif
   const int64_t rows = n * count;
+  // Q5_K and Q6_K keep two more registers per tile and register set, so
+  // they run one tile per wave (12 waves from 32,768 rows, else 8)
+  if (fmt != kFmtQ4) return rows >= 32768 ? Shape{12, 1, 1, 4, 4} : Shape{8, 1, 1, 4, 4};
   if (rows >= 131072) return {8, 2, 1, 4, 4};
   if (rows >= 32768) return {12, 1, 1, 4, 4};
   return {8, 1, 1, 4, 4};
 }
 
-Geometry geometry(int64_t n, int64_t k, int count) {
+Geometry geometry(int64_t n, int64_t k, int count, int fmt) {
   Geometry g;
-  const Shape sh = pick_shape(n, count);
+  const Shape sh = pick_shape(n, count, fmt);
   g.count = count;
   g.waves = sh.waves;
   g.tpw = sh.tpw;
@@ -79,8 +85,8 @@ Geometry geometry(int64_t n, int64_t k, int count) {
   return g;
 }
 
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count) {
-  const Geometry g = geometry(n, k, count);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt) {
+  const Geometry g = geometry(n, k, count, fmt);
   ScratchLayout s;
   s.cnt_off = kCntOff;
   s.keys_off = align256(s.cnt_off + sizeof(unsigned) * kCntStride * (size_t)g.n_groups);
@@ -113,14 +119,25 @@ size_t kq_staged_bytes(int64_t k) {
   return (size_t)(k / kQK) * (size_t)kStageBytes;
 }
 
+// Scratch for `count` matrices in whichever format needs the most.
+static size_t scratch_any_fmt(int64_t n, int64_t k, int count) {
+  size_t t = 0;
+  for (int f = kFmtQ4; f <= kFmtQ6; ++f) {
+    if (!shape_ok(n, k, f)) continue;
+    const size_t b = scratch_layout(n, k, count, f).total;
+    t = b > t ? b : t;
+  }
+  return t;
+}
+
 size_t kq_scratch_bytes(int64_t n, int64_t k) {
   if (!shape_ok(n, k)) return 0;
-  return scratch_layout(n, k, 1).total;
+  return scratch_any_fmt(n, k, 1);
 }
 
 size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count) {
   if (!shape_ok(n, k) || count < 1 || count > kMaxGroup) return 0;
-  return scratch_layout(n, k, count).total;
+  return scratch_any_fmt(n, k, count);
 }
 
 size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
@@ -141,22 +158,30 @@ kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wa
 
 static inline bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-size_t kq_tiled_bytes(int64_t n, int64_t k) {
-  if (!shape_ok(n, k)) return 0;
-  return (size_t)cdiv(n, 16) * (size_t)(k / kQK) * (size_t)kTileBlockBytes;
+size_t kq_tiled_bytes(int64_t n, int64_t k) { return kq_tiled_bytes_fmt(KQ_LAYOUT_TILED16, n, k); }
+
+size_t kq_tiled_bytes_fmt(int layout, int64_t n, int64_t k) {
+  if (layout == KQ_LAYOUT_ROWS || layout_fmt(layout) < 0 || !shape_ok(n, k, layout_fmt(layout))) return 0;
+  return (size_t)cdiv(n, 16) * (size_t)(k / kQK) * 16 * (size_t)fmt_block_bytes(layout_fmt(layout));
 }
 
 kq_status kq_tile_weights(const void *w_q4k, int64_t n, int64_t k, void *w_tiled, size_t tiled_bytes,
                           void *stream) {
-  if (!w_q4k || !w_tiled) return KQ_ERR_NULL;
-  if (!shape_ok(n, k)) return KQ_ERR_SHAPE;
-  if (!al(w_q4k, 16) || !al(w_tiled, 16)) return KQ_ERR_ALIGN;
-  const size_t need = kq_tiled_bytes(n, k);
+  return kq_tile_weights_fmt(KQ_LAYOUT_TILED16, w_q4k, n, k, w_tiled, tiled_bytes, stream);
+}
+
+kq_status kq_tile_weights_fmt(int layout, const void *w_rows, int64_t n, int64_t k, void *w_tiled,
+                              size_t tiled_bytes, void *stream) {
+  if (!w_rows || !w_tiled) return KQ_ERR_NULL;
+  const int fmt = layout_fmt(layout);
+  if (layout == KQ_LAYOUT_ROWS || fmt < 0 || !shape_ok(n, k, fmt)) return KQ_ERR_SHAPE;
+  if (!al(w_rows, fmt == kFmtQ6 ? 2 : 16) || !al(w_tiled, 16)) return KQ_ERR_ALIGN;
+  const size_t need = kq_tiled_bytes_fmt(layout, n, k);
   if (tiled_bytes < need) return KQ_ERR_WORKSPACE;
-  const uintptr_t a0 = (uintptr_t)w_q4k, a1 = a0 + (uintptr_t)(n * (k / kQK) * kBlockBytes);
+  const uintptr_t a0 = (uintptr_t)w_rows, a1 = a0 + (uintptr_t)(n * (k / kQK) * fmt_block_bytes(fmt));
   const uintptr_t b0 = (uintptr_t)w_tiled, b1 = b0 + (uintptr_t)need;
   if (a0 < b1 && b0 < a1) return KQ_ERR_SHAPE;  // buffers overlap
-  if (launch_tile((const uint8_t *)w_q4k, n, k, (uint8_t *)w_tiled, stream)) return KQ_ERR_LAUNCH;
+  if (launch_tile((const uint8_t *)w_rows, n, k, (uint8_t *)w_tiled, stream, fmt)) return KQ_ERR_LAUNCH;
   return KQ_OK;
 }
 
@@ -210,7 +235,8 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
                      int32_t *head_out, void *scratch, size_t scratch_bytes, const float *x_to_stage,
                      void *stream) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
-  if (layout != KQ_LAYOUT_ROWS && layout != KQ_LAYOUT_TILED16) return KQ_ERR_SHAPE;
+  const int fmt = layout_fmt(layout);
+  if (fmt < 0) return KQ_ERR_SHAPE;
   if (count < 1 || count > kMaxGroup || (verify && count != 1)) return KQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i) {
     if (!w[i]) return KQ_ERR_NULL;
@@ -218,12 +244,12 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   }
   if (verify && (!argmax || (!accept_out && argmax_from == 0))) return KQ_ERR_NULL;
   if (verify && accept_out && m > 1 && !draft_host) return KQ_ERR_NULL;
-  if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
+  if (!shape_ok(n, k, fmt) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i)
     if (!al(w[i], 16)) return KQ_ERR_ALIGN;
   if (!al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
   if (x_to_stage && !al(x_to_stage, 16)) return KQ_ERR_ALIGN;
-  const ScratchLayout sl = scratch_layout(n, k, count);
+  const ScratchLayout sl = scratch_layout(n, k, count, fmt);
   if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
@@ -233,7 +259,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
       a.draft[i] = draft_host[i];
     }
   }
-  a.g = geometry(n, k, count);
+  a.g = geometry(n, k, count, fmt);
   fill_phase(a.ph, a.g, w, logits, count, n, k, staged);
   a.layout = layout;
   a.m = m;

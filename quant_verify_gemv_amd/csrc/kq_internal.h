@@ -20,6 +20,31 @@ constexpr int64_t kTileBlockBytes = 16 * kBlockBytes;  // 2,304
 constexpr int64_t kTileQ0 = 256;
 constexpr int64_t kTileQ1 = 1280;
 
+// Weight formats of the main kernel: Q4_K (row-major or tiled), Q5_K and
+// Q6_K (tiled only; kq_tile_weights_fmt). Their tiled records keep the Q4_K
+// lane order for the low four bits of every weight (the same staged
+// activations serve every format):
+//   Q5_K (2,816 B): headers as Q4_K | quant halves as Q4_K | 64 lanes x 8 B
+//                   of fifth bits (kTileQH)
+//   Q6_K (3,360 B): 64 lanes x 4 scale bytes | low-nibble halves as Q4_K |
+//                   64 lanes x 16 B of 2-bit high parts (kTileQH) | 16 fp16 d
+//                   (kTileQ6D)
+constexpr int kFmtQ4 = 0, kFmtQ5 = 1, kFmtQ6 = 2;
+constexpr int64_t kBlockBytesQ5 = 176;
+constexpr int64_t kBlockBytesQ6 = 210;
+constexpr int64_t kTileQH = 2304;
+constexpr int64_t kTileQ6D = 3328;
+constexpr int64_t fmt_block_bytes(int fmt) {
+  return fmt == kFmtQ6 ? kBlockBytesQ6 : fmt == kFmtQ5 ? kBlockBytesQ5 : kBlockBytes;
+}
+// format of a layout code (-1 for an unknown code)
+constexpr int layout_fmt(int layout) {
+  return layout == KQ_LAYOUT_ROWS || layout == KQ_LAYOUT_TILED16 ? kFmtQ4
+         : layout == KQ_LAYOUT_Q5K_TILED16                       ? kFmtQ5
+         : layout == KQ_LAYOUT_Q6K_TILED16                       ? kFmtQ6
+                                                                 : -1;
+}
+
 // Staged activations, one record per 256-column block (each row scaled by a
 // power of two 2^e chosen from that row's largest magnitude in the block):
 //   XA  [8 k-steps][hi,lo][64 lanes][8 x fp16]  16,384 B  MFMA A operand
@@ -94,7 +119,7 @@ struct GemvLaunch {
   unsigned *epoch;     // chain: launch epoch (scratch + kEpochOff)
   unsigned long long *flags;  // chain: per-workgroup release flags, 256 bytes apart
   int m;
-  int layout;       // KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16
+  int layout;       // KQ_LAYOUT_* (the weight format and its layout)
   float *partials;
   unsigned *done;
   unsigned *group_cnt;
@@ -109,8 +134,8 @@ struct GemvLaunch {
   Geometry g;
 };
 
-Geometry geometry(int64_t n, int64_t k, int count);
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
+Geometry geometry(int64_t n, int64_t k, int count, int fmt = kFmtQ4);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt = kFmtQ4);
 
 // Kernel launches (return a hipError_t as int).
 // kq_stage_kernel also zeroes the control words of `ctrl` (a scratch area
@@ -122,7 +147,7 @@ int launch_gemv(const GemvLaunch &a, void *stream);
 // device holds at once, or a negative HIP error code.
 int chain_capacity();
 int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value = 0u);
-int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream);
+int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream, int fmt = kFmtQ4);
 int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);
 // Softmax rows: chunks of a row (4,096 logits each) and the two-pass launch
 // (part: rows x chunks float pairs of workspace).

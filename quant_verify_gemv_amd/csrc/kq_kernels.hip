@@ -58,6 +58,25 @@ __device__ __forceinline__ half2v fma_bcast(half2v a, half2v k) {
   return r;
 }
 
+// a * b and a * b - c on fp16 pairs, rounded exactly once each (v_pk_mul_f16,
+// v_pk_fma_f16): the Q6_K operand split needs the rounded product and its
+// exact remainder.
+__device__ __forceinline__ half2v pk_mul(half2v a, half2v b) {
+  half2v r;
+  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ half2v pk_fma_sub(half2v a, half2v b, half2v c) {
+  half2v r;
+  asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// (h >> from) & mask, moved to start at bit `to` (from, to compile-time).
+__device__ __forceinline__ unsigned bit_move(unsigned h, int from, unsigned mask, int to) {
+  return to >= from ? (h << (to - from)) & (mask << to) : (h >> (from - to)) & (mask << to);
+}
+
 // A value the compiler must keep in a VGPR: lets (x & mask) | magic become
 // one v_and_or_b32 (a VOP3 instruction may read one scalar operand only).
 __device__ __forceinline__ unsigned in_vgpr(unsigned c) {
@@ -101,6 +120,16 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned vof
 constexpr int kCpolNt = 2;
 __device__ __forceinline__ u32x4 buf_ld16_w(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCpolNt));
+}
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 buf_ld8_w(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kCpolNt));
+}
+__device__ __forceinline__ unsigned buf_ld4_w(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kCpolNt);
+}
+__device__ __forceinline__ unsigned buf_ld2_w(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, kCpolNt);
 }
 // 16-byte versions for the partial sums: buffer instructions with the same
 // cache policy (sc1) as the agent-scope atomic accesses above
@@ -273,9 +302,13 @@ __global__ void kq_fill_kernel(unsigned *p, int64_t n, unsigned value) {
 // workgroup issues the first weight loads of the next phase before it
 // waits at the barrier.
 
+// One 16-row tile's share of a block in a lane's registers: Q4_K and Q5_K
+// header, two quant chunks; Q5_K fifth bits in hx.x, hx.y; Q6_K: scale
+// dword in hdr.x, d in hdr.y, low nibbles in q0, q1, high parts in hx.
 struct WTile {
-  u32x4 hdr, q0, q1;
+  u32x4 hdr, q0, q1, hx;
 };
+__device__ __forceinline__ unsigned sel4(const u32x4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 constexpr int lcm_int(int a, int b) {
   int x = a, y = b;
@@ -320,9 +353,11 @@ __device__ __forceinline__ int spin_flag(const unsigned long long *flag, unsigne
 // Field f of phase ph: the launch's own phase, or entry ph of a chain's table.
 #define KQ_PH(I_, f) (CHAIN ? ((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f : a.ph.f)
 
-template <int W, int T, int BI, int D, bool CHAIN>
+template <int W, int T, int BI, int D, bool CHAIN, int FMT>
 __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv_kernel(GemvLaunch a) {
   static_assert(W % 4 == 0, "waves spread evenly over the 4 SIMDs");
+  static_assert(FMT == kFmtQ4 || !CHAIN, "chains run Q4_K");
+  constexpr unsigned kTB = 16u * (unsigned)fmt_block_bytes(FMT);  // tiled record bytes
   // D weight register sets: the weights of unit i + D - 1 are loaded while
   // unit i computes. The activations of unit i + BI are stored to LDS in
   // step i from registers loaded kXL steps earlier: loads complete in issue
@@ -387,7 +422,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // the last row) times the row bytes + {0, 16 + 16kg, 80 + 16kg}, soff = 0,
   // stride 144. Tiled: voff = {16 ln, 256 + 16 lane, 1,280 + 16 lane}, soff
   // = the 16-row tile's record, stride = tiles * 2,304.
-  const bool tiled = a.layout == KQ_LAYOUT_TILED16;
+  const bool tiled = FMT != kFmtQ4 || a.layout == KQ_LAYOUT_TILED16;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // The phase fields the stream needs: a single launch reads them from its
   // arguments; a chain keeps the current phase's in registers.
@@ -400,7 +435,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   auto w_kb = [&]() -> int { return CHAIN ? cw_kb : a.ph.kb; };
   auto w_nwg = [&]() -> int { return CHAIN ? cw_nwg : a.ph.n_wg_per; };
   auto block_stride = [&]() -> unsigned {
-    return tiled ? (unsigned)w_nt() * (unsigned)kTileBlockBytes : (unsigned)kBlockBytes;
+    return tiled ? (unsigned)w_nt() * kTB : (unsigned)kBlockBytes;
   };
   unsigned boff = 0;
   __amdgpu_buffer_rsrc_t w_rsrc;
@@ -414,7 +449,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       if (tiled) {
         int ti = (r0 + (t * W + wave_u) * 16) / 16;
         ti = ti < w_nt() ? ti : w_nt() - 1;
-        soff[t] = (unsigned)ti * (unsigned)kTileBlockBytes;
+        soff[t] = (unsigned)ti * kTB;
         voff[t][0] = 16u * ln;
         voff[t][1] = (unsigned)kTileQ0 + 16u * lane;
         voff[t][2] = (unsigned)kTileQ1 + 16u * lane;
@@ -448,9 +483,20 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   auto load_w = [&](WTile(&w)[T]) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      w[t].hdr = buf_ld16_w(w_rsrc, voff[t][0], soff[t] + boff);
+      if constexpr (FMT == kFmtQ6) {
+        w[t].hdr.x = buf_ld4_w(w_rsrc, 4u * lane, soff[t] + boff);
+        w[t].hdr.y = buf_ld2_w(w_rsrc, (unsigned)kTileQ6D + 2u * ln, soff[t] + boff);
+      } else {
+        w[t].hdr = buf_ld16_w(w_rsrc, voff[t][0], soff[t] + boff);
+      }
       w[t].q0 = buf_ld16_w(w_rsrc, voff[t][1], soff[t] + boff);
       w[t].q1 = buf_ld16_w(w_rsrc, voff[t][2], soff[t] + boff);
+      if constexpr (FMT == kFmtQ5) {
+        const u32x2 h = buf_ld8_w(w_rsrc, (unsigned)kTileQH + 8u * lane, soff[t] + boff);
+        w[t].hx.x = h.x;
+        w[t].hx.y = h.y;
+      }
+      if constexpr (FMT == kFmtQ6) w[t].hx = buf_ld16_w(w_rsrc, (unsigned)kTileQH + 16u * lane, soff[t] + boff);
     }
     if (uw < uw_last) {
       ++uw;
@@ -627,78 +673,158 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t *xb = s_x[i % kNB];
       if (i < nu) {
-        float d[T], dmin[T];
-        // per sub-block {scale, offset} pairs; the fma broadcasts each half
-        half2v k00[T], k01[T], k10[T], k11[T];
-        half4 bm[T];
-        const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-        const half2v lo_pair = {(_Float16)1.0f, (_Float16)-1024.0f};
-        const half2v hi_pair = {(_Float16)0.0625f, (_Float16)-64.0f};
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const u32x4 h = cur[t].hdr;
-          d[t] = h2f_lo(h.x);
-          dmin[t] = h2f_hi(h.x);
-          // q0 holds sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
-          // q1 holds 4+2(kg>>1) and 5+2(kg>>1). Their 6-bit scales are bytes
-          // 2(kg>>1), 2(kg>>1)+1 of sc03 and sc47; one byte permute sets each
-          // below an fp16 exponent byte 0x64 (1024 + s), so {s, s'} is exact.
-          const unsigned sc03 = h.y & 0x3F3F3F3Fu;
-          const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
-          const half2v s0 = as_h2(__builtin_amdgcn_perm(sc03, 0x64646464u, sel_sc)) + neg1024;
-          const half2v s1 = as_h2(__builtin_amdgcn_perm(sc47, 0x64646464u, sel_sc)) + neg1024;
-          // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
-          k00[t] = half2v{s0[0], s0[0]} * lo_pair;
-          k01[t] = half2v{s0[1], s0[1]} * hi_pair;
-          k10[t] = half2v{s1[0], s1[0]} * lo_pair;
-          k11[t] = half2v{s1[1], s1[1]} * hi_pair;
-          // min-term B operand: the 6-bit m of sub-blocks 4(kg&1) + {0,2,1,3}
-          const unsigned m03 = h.z & 0x3F3F3F3Fu;
-          const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-          const unsigned msrc = (kg & 1) ? m47 : m03;
-          const half2v p0 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00060004u)) + neg1024;
-          const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
-          bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
-        }
-        // x hi and x lo products accumulate in one fp32 sum per tile
-        f32x4 cq[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
-          const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
-          const bool hi = (s & 2) != 0;
-          const unsigned mask = hi ? mask_hi : mask_lo;
+        if constexpr (FMT == kFmtQ6) {
+          // Q6_K: w = d sc (q - 32), sc a signed 8-bit scale per 16 columns.
+          // Each lane's 8 columns of a k-step share one scale (its 4 scales are
+          // bytes 2 (s >> 2) + ((s >> 1) & 1) of hdr.x). The unpack gives the
+          // fp16 1024 + q (low nibble steps) or 1024 + 16 q (high), minus 1056
+          // or 1536 is q - 32 or 16 (q - 32) exactly; times sc or sc / 16 it
+          // can need 13 significant bits, so the B operand is the rounded
+          // product b_hi plus the exact remainder b_lo (0 or +-1); x_hi b_hi +
+          // x_lo b_hi + x_hi b_lo leaves out x_lo b_lo, below 2^-22 of |w x|.
+          float d6[T];
+          half2v k6[T][4];
 #pragma unroll
           for (int t = 0; t < T; ++t) {
-            const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
-            const unsigned da = (s & 1) ? qq.z : qq.x;
-            const unsigned db = (s & 1) ? qq.w : qq.y;
-            const half2v kk = s < 4 ? (hi ? k01[t] : k00[t]) : (hi ? k11[t] : k10[t]);
-            const unsigned u0_ = (da & mask) | 0x64006400u;
-            const unsigned u1_ = ((da >> 8) & mask) | 0x64006400u;
-            const unsigned u2_ = (db & mask) | 0x64006400u;
-            const unsigned u3_ = ((db >> 8) & mask) | 0x64006400u;
-            const half2v v0 = fma_bcast(as_h2(u0_), kk);
-            const half2v v1 = fma_bcast(as_h2(u1_), kk);
-            const half2v v2 = fma_bcast(as_h2(u2_), kk);
-            const half2v v3 = fma_bcast(as_h2(u3_), kk);
-            const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
-            cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
-            cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
+            const unsigned sw = cur[t].hdr.x;
+            d6[t] = h2f_lo(cur[t].hdr.y);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float sv = (float)(int)(signed char)(sw >> (8 * j)) * ((j & 1) ? 0.0625f : 1.0f);
+              const _Float16 hv = (_Float16)sv;
+              k6[t][j] = half2v{hv, hv};
+            }
           }
-        }
-        // min term and the block's contribution in the row's scaled units
-        const half4 as4 = *(const half4 *)(xb + kXsbOffset + lane * 8);
-        const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
+          f32x4 cq[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const f32x4 c2 =
-              __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const half2v off_lo = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+          const half2v off_hi = {(_Float16)-1536.0f, (_Float16)-1536.0f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
+          for (int s = 0; s < 8; ++s) {
+            const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
+            const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+            const bool hi = (s & 2) != 0;
+            const unsigned mask = hi ? mask_hi : mask_lo;
+            const half2v off = hi ? off_hi : off_lo;
+            const int to = hi ? 8 : 4, c = 8 * (s & 1);
+            const int j = 2 * (s >> 2) + ((s >> 1) & 1);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
+              const unsigned da = (s & 1) ? qq.z : qq.x;
+              const unsigned db = (s & 1) ? qq.w : qq.y;
+              // the two high bits of pairs (0,2), (1,3), (4,6), (5,7) sit at
+              // bits c, c + 2, c + 4, c + 6 (+16) of high-part word s >> 1
+              const unsigned hw = sel4(cur[t].hx, s >> 1);
+              const half2v q0h = as_h2((da & mask) | bit_move(hw, c + 0, 0x00030003u, to) | 0x64006400u) + off;
+              const half2v q1h = as_h2(((da >> 8) & mask) | bit_move(hw, c + 2, 0x00030003u, to) | 0x64006400u) + off;
+              const half2v q2h = as_h2((db & mask) | bit_move(hw, c + 4, 0x00030003u, to) | 0x64006400u) + off;
+              const half2v q3h = as_h2(((db >> 8) & mask) | bit_move(hw, c + 6, 0x00030003u, to) | 0x64006400u) + off;
+              const half2v kk = k6[t][j];
+              const half2v h0 = pk_mul(q0h, kk), h1 = pk_mul(q1h, kk), h2 = pk_mul(q2h, kk), h3 = pk_mul(q3h, kk);
+              const half2v l0 = pk_fma_sub(q0h, kk, h0), l1 = pk_fma_sub(q1h, kk, h1);
+              const half2v l2 = pk_fma_sub(q2h, kk, h2), l3 = pk_fma_sub(q3h, kk, h3);
+              const half8 bhi = make_h8(as_u(h0), as_u(h1), as_u(h2), as_u(h3));
+              const half8 blo = make_h8(as_u(l0), as_u(l1), as_u(l2), as_u(l3));
+              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, cq[t], 0, 0, 0);
+              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, cq[t], 0, 0, 0);
+              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, cq[t], 0, 0, 0);
+            }
+          }
+          const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][r] += xinv[r] * (d6[t] * cq[t][r]);
+          }
+        } else {
+          float d[T], dmin[T];
+          // per sub-block {scale, offset} pairs; the fma broadcasts each half
+          half2v k00[T], k01[T], k10[T], k11[T];
+          half4 bm[T];
+          const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+          const half2v lo_pair = {(_Float16)1.0f, (_Float16)-1024.0f};
+          const half2v hi_pair = {(_Float16)0.0625f, (_Float16)-64.0f};
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const u32x4 h = cur[t].hdr;
+            d[t] = h2f_lo(h.x);
+            dmin[t] = h2f_hi(h.x);
+            // q0 holds sub-blocks 2(kg>>1) (low nibbles) and 2(kg>>1)+1 (high);
+            // q1 holds 4+2(kg>>1) and 5+2(kg>>1). Their 6-bit scales are bytes
+            // 2(kg>>1), 2(kg>>1)+1 of sc03 and sc47; one byte permute sets each
+            // below an fp16 exponent byte 0x64 (1024 + s), so {s, s'} is exact.
+            const unsigned sc03 = h.y & 0x3F3F3F3Fu;
+            const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+            const half2v s0 = as_h2(__builtin_amdgcn_perm(sc03, 0x64646464u, sel_sc)) + neg1024;
+            const half2v s1 = as_h2(__builtin_amdgcn_perm(sc47, 0x64646464u, sel_sc)) + neg1024;
+            // low nibble q: (1024 + q) s - 1024 s; high nibble: (1024 + 16q) s/16 - 64 s
+            k00[t] = half2v{s0[0], s0[0]} * lo_pair;
+            k01[t] = half2v{s0[1], s0[1]} * hi_pair;
+            k10[t] = half2v{s1[0], s1[0]} * lo_pair;
+            k11[t] = half2v{s1[1], s1[1]} * hi_pair;
+            // min-term B operand: the 6-bit m of sub-blocks 4(kg&1) + {0,2,1,3}
+            const unsigned m03 = h.z & 0x3F3F3F3Fu;
+            const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+            const unsigned msrc = (kg & 1) ? m47 : m03;
+            const half2v p0 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00060004u)) + neg1024;
+            const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
+            bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
+          }
+          // x hi and x lo products accumulate in one fp32 sum per tile
+          f32x4 cq[T];
+#pragma unroll
+          for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
+            const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+            const bool hi = (s & 2) != 0;
+            const unsigned mask = hi ? mask_hi : mask_lo;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
+              const unsigned da = (s & 1) ? qq.z : qq.x;
+              const unsigned db = (s & 1) ? qq.w : qq.y;
+              const half2v kk = s < 4 ? (hi ? k01[t] : k00[t]) : (hi ? k11[t] : k10[t]);
+              // Q5_K: the fifth bit of each weight, at bit 4 (low nibble) or 8
+              // (high nibble, 16 q) of its fp16 half; pairs (bytes 0,2), (1,3),
+              // (4,6), (5,7) of the 8 sit at bits c .. c + 3 (+16) of the lane's
+              // fifth-bit word for steps s & ~3
+              unsigned e0 = 0u, e1 = 0u, e2 = 0u, e3 = 0u;
+              if constexpr (FMT == kFmtQ5) {
+                const unsigned hw = s < 4 ? cur[t].hx.x : cur[t].hx.y;
+                const int c = 4 * (s & 3), to = hi ? 8 : 4;
+                e0 = bit_move(hw, c + 0, 0x00010001u, to);
+                e1 = bit_move(hw, c + 1, 0x00010001u, to);
+                e2 = bit_move(hw, c + 2, 0x00010001u, to);
+                e3 = bit_move(hw, c + 3, 0x00010001u, to);
+              }
+              const unsigned u0_ = (da & mask) | e0 | 0x64006400u;
+              const unsigned u1_ = ((da >> 8) & mask) | e1 | 0x64006400u;
+              const unsigned u2_ = (db & mask) | e2 | 0x64006400u;
+              const unsigned u3_ = ((db >> 8) & mask) | e3 | 0x64006400u;
+              const half2v v0 = fma_bcast(as_h2(u0_), kk);
+              const half2v v1 = fma_bcast(as_h2(u1_), kk);
+              const half2v v2 = fma_bcast(as_h2(u2_), kk);
+              const half2v v3 = fma_bcast(as_h2(u3_), kk);
+              const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
+              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
+              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
+            }
+          }
+          // min term and the block's contribution in the row's scaled units
+          const half4 as4 = *(const half4 *)(xb + kXsbOffset + lane * 8);
+          const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const f32x4 c2 =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
+          }
         }
       }
       // end of a row group's segment
@@ -1078,6 +1204,90 @@ __global__ __launch_bounds__(256) void kq_tile_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Q5_K and Q6_K tiled records (layouts in kq.h). One thread per (block,
+// tile, row): it reads the row's block and writes every byte that row owns
+// in the record (its header or scale words, the 16-byte quant chunks of its
+// four lanes, their high-bit words, its d). Lane group g of the row holds,
+// in k-step s at byte p of its 8 bytes, block column lane_col(g, s, p): the
+// column order the Q4_K records and the staged activations use.
+__device__ __forceinline__ int lane_col(int g, int s, int p) {
+  const int gg = (s < 4 ? 0 : 2) + (g >> 1), h = (s >> 1) & 1, l = 16 * (g & 1) + 8 * (s & 1) + p;
+  return 64 * gg + 32 * h + l;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void kq_tile_kq_kernel(const uint8_t *__restrict__ w, int64_t n, int64_t kb,
+                                                         int64_t n_tiles, uint8_t *__restrict__ out) {
+  constexpr int BB = (int)fmt_block_bytes(FMT);
+  // the bytes of a pair of weights in an unpacked word: (0,2), (1,3), (4,6), (5,7)
+  constexpr int kPair[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= kb * n_tiles * 16) return;
+  const int r = (int)(idx & 15);
+  const int64_t tb = idx >> 4, ti = tb % n_tiles, b = tb / n_tiles;
+  const int64_t row = ti * 16 + r;
+  const bool live = row < n;
+  const uint8_t *src = w + (live ? (row * kb + b) * BB : 0);
+  uint8_t *rec = out + (b * n_tiles + ti) * 16 * BB;
+  auto byte = [&](int i) -> unsigned { return live ? (unsigned)src[i] : 0u; };
+  if constexpr (FMT == kFmtQ5) {
+    // d, dmin, 12 scale bytes | qh[32] at 16 | qs[128] at 48
+    for (int i = 0; i < 16; ++i) rec[16 * r + i] = (uint8_t)byte(i);
+    for (int g = 0; g < 4; ++g) {
+      const int ln = 16 * g + r;
+      for (int j = 0; j < 16; ++j) {
+        rec[kTileQ0 + 16 * ln + j] = (uint8_t)byte(48 + 16 * g + j);
+        rec[kTileQ1 + 16 * ln + j] = (uint8_t)byte(48 + 64 + 16 * g + j);
+      }
+      unsigned hw[2] = {0u, 0u};
+      for (int s = 0; s < 8; ++s)
+        for (int q = 0; q < 4; ++q)
+          for (int e = 0; e < 2; ++e) {
+            const int col = lane_col(g, s, kPair[q][e]);
+            const unsigned bit = (byte(16 + col % 32) >> (col / 32)) & 1u;
+            hw[s >> 2] |= bit << (4 * (s & 3) + q + 16 * e);
+          }
+      *(unsigned *)(rec + kTileQH + 8 * ln) = hw[0];
+      *(unsigned *)(rec + kTileQH + 8 * ln + 4) = hw[1];
+    }
+  } else {
+    // ql[128] | qh[64] at 128 | 16 signed scales at 192 | fp16 d at 208
+    auto low4 = [&](int i) -> unsigned {
+      const int h = i >> 7, c = (i & 127) >> 5, l = i & 31;
+      const unsigned v = byte(64 * h + l + 32 * (c & 1));
+      return c < 2 ? (v & 15u) : (v >> 4);
+    };
+    auto hi2 = [&](int i) -> unsigned {
+      const int h = i >> 7, c = (i & 127) >> 5, l = i & 31;
+      return (byte(128 + 32 * h + l) >> (2 * c)) & 3u;
+    };
+    for (int g = 0; g < 4; ++g) {
+      const int ln = 16 * g + r;
+      // scale byte j: k-steps with s >> 2 == j >> 1 and (s >> 1) & 1 == j & 1
+      for (int j = 0; j < 4; ++j) {
+        const int gg = (j >= 2 ? 2 : 0) + (g >> 1);
+        rec[4 * ln + j] = (uint8_t)byte(192 + 4 * gg + 2 * (j & 1) + (g & 1));
+      }
+      // low nibbles where a Q4_K record keeps them: byte 8 (s & 1) + p of a
+      // chunk, low nibble for step s, high nibble for step s + 2
+      for (int j = 0; j < 16; ++j) {
+        const int s = j >> 3, p = j & 7;
+        rec[kTileQ0 + 16 * ln + j] = (uint8_t)(low4(lane_col(g, s, p)) | (low4(lane_col(g, s + 2, p)) << 4));
+        rec[kTileQ1 + 16 * ln + j] = (uint8_t)(low4(lane_col(g, s + 4, p)) | (low4(lane_col(g, s + 6, p)) << 4));
+      }
+      unsigned hw[4] = {0u, 0u, 0u, 0u};
+      for (int s = 0; s < 8; ++s)
+        for (int q = 0; q < 4; ++q)
+          for (int e = 0; e < 2; ++e)
+            hw[s >> 1] |= hi2(lane_col(g, s, kPair[q][e])) << (8 * (s & 1) + 2 * q + 16 * e);
+      for (int i = 0; i < 4; ++i) *(unsigned *)(rec + kTileQH + 16 * ln + 4 * i) = hw[i];
+    }
+    rec[kTileQ6D + 2 * r] = (uint8_t)byte(208);
+    rec[kTileQ6D + 2 * r + 1] = (uint8_t)byte(209);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Target probability rows for the stochastic verify: p = softmax(z) per row,
 // z = l / T after the optional soft cap l -> cap * tanh(l / cap). Two
 // passes over chunks of kSmChunk logits (grid: chunks x rows):
@@ -1207,13 +1417,23 @@ int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int bl
   return (int)hipGetLastError();
 }
 
-int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream) {
+int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream, int fmt) {
   const int64_t kb = k / kQK;
   const int64_t n_tiles = (n + 15) / 16;
-  const int64_t total = kb * n_tiles * 144;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(kq_tile_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, n, kb,
-                     n_tiles, out);
+  if (fmt == kFmtQ4) {
+    const int64_t total = kb * n_tiles * 144;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(kq_tile_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w, n, kb,
+                       n_tiles, out);
+  } else {
+    const int64_t blocks = (kb * n_tiles * 16 + 255) / 256;
+    if (fmt == kFmtQ5)
+      hipLaunchKernelGGL(kq_tile_kq_kernel<kFmtQ5>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
+                         n, kb, n_tiles, out);
+    else
+      hipLaunchKernelGGL(kq_tile_kq_kernel<kFmtQ6>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, w,
+                         n, kb, n_tiles, out);
+  }
   return (int)hipGetLastError();
 }
 
@@ -1239,22 +1459,27 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.chain) {
     if (a.g.waves != 8 || a.g.tpw != 1 || a.g.bi != 4 || a.g.depth != 4) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4>), grid, dim3(512), 0, st, a);
     return (int)hipGetLastError();
   }
-  switch (a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
-#define KQ_CASE(W_, T_, BI_, D_)                                                                   \
-  case W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                                                       \
-    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, false>), grid, dim3(64 * W_), 0, st, a);   \
+  const int fmt = layout_fmt(a.layout);
+  switch (fmt * 65536 + a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
+#define KQ_CASE(F_, W_, T_, BI_, D_)                                                                \
+  case F_ * 65536 + W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                                           \
+    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, false, F_>), grid, dim3(64 * W_), 0, st, a); \
     break;
-    KQ_CASE(8, 2, 4, 4)
-    KQ_CASE(8, 1, 4, 4)
-    KQ_CASE(8, 1, 2, 4)
-    KQ_CASE(8, 2, 2, 4)
-    KQ_CASE(4, 1, 1, 4)
-    KQ_CASE(12, 1, 4, 4)
-    KQ_CASE(4, 2, 2, 3)
-    KQ_CASE(4, 2, 1, 3)
+    KQ_CASE(kFmtQ4, 8, 2, 4, 4)
+    KQ_CASE(kFmtQ4, 8, 1, 4, 4)
+    KQ_CASE(kFmtQ4, 8, 1, 2, 4)
+    KQ_CASE(kFmtQ4, 8, 2, 2, 4)
+    KQ_CASE(kFmtQ4, 4, 1, 1, 4)
+    KQ_CASE(kFmtQ4, 12, 1, 4, 4)
+    KQ_CASE(kFmtQ4, 4, 2, 2, 3)
+    KQ_CASE(kFmtQ4, 4, 2, 1, 3)
+    KQ_CASE(kFmtQ5, 8, 1, 4, 4)
+    KQ_CASE(kFmtQ5, 12, 1, 4, 4)
+    KQ_CASE(kFmtQ6, 8, 1, 4, 4)
+    KQ_CASE(kFmtQ6, 12, 1, 4, 4)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;
   }
@@ -1268,7 +1493,7 @@ int chain_capacity() {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_gemv_kernel<8, 1, 4, 4, true>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4>, 512, 0);
   if (e != hipSuccess) return -(int)e;
   return per_cu * cus;
 }

@@ -23,10 +23,15 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_gemv_staged_group", "kq_tiled_bytes", "kq_tile_weights", "kq_draft_block_argmax",
             "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes",
             "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
-            "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide")
+            "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
+            "kq_tiled_bytes_fmt", "kq_tile_weights_fmt")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
+LAYOUT_Q5K_TILED16 = 2  # kq_tile_weights_fmt output for a Q5_K matrix
+LAYOUT_Q6K_TILED16 = 3  # kq_tile_weights_fmt output for a Q6_K matrix
+# weight format -> (tiled layout, bytes per 256-weight block in llama.cpp rows)
+FORMATS = {"q4k": (LAYOUT_TILED16, 144), "q5k": (LAYOUT_Q5K_TILED16, 176), "q6k": (LAYOUT_Q6K_TILED16, 210)}
 
 MAX_GROUP = 8
 CHAIN_BARRIER_OFFSET = 128  # byte offset of the chain's barrier arrival count in its scratch
@@ -100,11 +105,14 @@ def load() -> ctypes.CDLL:
     F = ctypes.c_float
     lib.kq_softmax_rows.argtypes = [P, I32, I64, F, F, P, P, SZ, P]
     lib.kq_speculative_decide.argtypes = [I32, P, I64, P, P, P, P, P, P]
+    lib.kq_tiled_bytes_fmt.argtypes = [I32, I64, I64]
+    lib.kq_tiled_bytes_fmt.restype = SZ
+    lib.kq_tile_weights_fmt.argtypes = [I32, P, I64, I64, P, SZ, P]
     for name in ("kq_workspace_init", "kq_gemv_rows", "kq_verify_argmax_accept", "kq_stage_rows",
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
-                 "kq_softmax_rows", "kq_speculative_decide"):
+                 "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -135,8 +143,8 @@ def group_scratch_bytes(n: int, k: int, count: int) -> int:
     return int(load().kq_group_scratch_bytes(n, k, count))
 
 
-def tiled_bytes(n: int, k: int) -> int:
-    return int(load().kq_tiled_bytes(n, k))
+def tiled_bytes(n: int, k: int, fmt: str = "q4k") -> int:
+    return int(load().kq_tiled_bytes_fmt(FORMATS[fmt][0], n, k))
 
 
 def launch_geometry(n: int, k: int) -> Tuple[int, int, int, int]:
@@ -297,14 +305,18 @@ def new_scratch(n: int, k: int, device):
     return alloc_workspace(scratch_bytes(n, k), device)
 
 
-def tile_weights(w, n: int, k: int, out=None, stream=None):
-    """The KQ_LAYOUT_TILED16 copy of a Q4_K matrix (uint8 device tensor)."""
+def tile_weights(w, n: int, k: int, out=None, stream=None, fmt: str = "q4k"):
+    """The tiled copy (uint8 device tensor) of a matrix given as llama.cpp
+    rows of format `fmt` ("q4k": KQ_LAYOUT_TILED16, "q5k", "q6k"); pass
+    layout=FORMATS[fmt][0] to the staged calls."""
     torch = _torch()
-    nb = tiled_bytes(n, k)
+    layout = FORMATS[fmt][0]
+    nb = tiled_bytes(n, k, fmt)
     if out is None:
         out = torch.empty(nb, dtype=torch.uint8, device=w.device)
-    _check(load().kq_tile_weights(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(out, "out", torch.uint8),
-                                  out.numel(), _stream_handle(stream)), "kq_tile_weights")
+    _check(load().kq_tile_weights_fmt(layout, _dev_ptr(w, "w", torch.uint8), n, k,
+                                      _dev_ptr(out, "out", torch.uint8), out.numel(), _stream_handle(stream)),
+           "kq_tile_weights_fmt")
     return out
 
 

@@ -148,7 +148,7 @@ def test_draft_block_argument_errors():
     sb = kq.scratch_bytes(n, k)
     st = lib.kq_draft_block_argmax_staged
     assert st(FAKE, 0, n, k, FAKE, 4, FAKE, None, FAKE, sb, None) == SHAPE
-    assert st(FAKE, 2, n, k, FAKE, 3, FAKE, None, FAKE, sb, None) == SHAPE
+    assert st(FAKE, 7, n, k, FAKE, 3, FAKE, None, FAKE, sb, None) == SHAPE
     assert st(FAKE, 0, n, k, None, 3, FAKE, None, FAKE, sb, None) == NULL
     assert st(FAKE, 0, n, k, FAKE, 3, None, None, FAKE, sb, None) == NULL
     assert st(FAKE, 0, n, k, FAKE, 15, FAKE, None, FAKE, sb - 1, None) == WS
@@ -178,7 +178,7 @@ def test_staged_argument_errors():
     sb = kq.scratch_bytes(512, 1024)
     assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, None, 4, FAKE, FAKE, sb, None) == NULL
     assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, FAKE, 4, FAKE, FAKE, sb - 1, None) == WS
-    assert lib.kq_gemv_staged(FAKE, 2, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
+    assert lib.kq_gemv_staged(FAKE, 7, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
     assert lib.kq_gemv_staged(FAKE, -1, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
     d = (ctypes.c_int32 * 3)(0, 1, 600)
     assert lib.kq_verify_staged(FAKE, 0, 512, 1024, FAKE, 4, d, FAKE, FAKE, None, FAKE, sb, None) == TOKEN
@@ -228,6 +228,45 @@ def test_tiling_sizes_and_argument_errors():
     assert tw(FAKE, n, k, out + 4, nb, None) == ALIGN
     assert tw(FAKE, n, k, out, nb - 1, None) == WS
     assert tw(FAKE, n, k, FAKE + 4096, nb, None) == SHAPE    # overlapping buffers
+
+
+def test_q5k_q6k_tiling_sizes_and_argument_errors():
+    lib = kq.load()
+    L5, L6 = kq.LAYOUT_Q5K_TILED16, kq.LAYOUT_Q6K_TILED16
+    assert kq.tiled_bytes(512, 1024, "q5k") == 32 * 4 * 16 * 176
+    assert kq.tiled_bytes(17, 256, "q6k") == 2 * 1 * 16 * 210
+    assert lib.kq_tiled_bytes_fmt(kq.LAYOUT_ROWS, 16, 256) == 0     # not a tiled layout
+    assert lib.kq_tiled_bytes_fmt(9, 16, 256) == 0                  # unknown layout
+    assert lib.kq_tiled_bytes_fmt(kq.LAYOUT_TILED16, 100, 512) == kq.tiled_bytes(100, 512)
+    n, k = 1000, 2048
+    out = FAKE + 0x40000000
+    tf = lib.kq_tile_weights_fmt
+    for lay in (L5, L6):
+        nb = lib.kq_tiled_bytes_fmt(lay, n, k)
+        assert tf(lay, None, n, k, out, nb, None) == NULL
+        assert tf(lay, FAKE, n, k, None, nb, None) == NULL
+        assert tf(lay, FAKE, n, 100, out, nb, None) == SHAPE
+        assert tf(lay, FAKE, n, k, out + 4, nb, None) == ALIGN
+        assert tf(lay, FAKE, n, k, out, nb - 1, None) == WS
+        assert tf(lay, FAKE, n, k, FAKE + 4096, nb, None) == SHAPE  # overlapping buffers
+    assert tf(L5, FAKE + 8, n, k, out, 1 << 30, None) == ALIGN       # Q5_K rows are 16-byte aligned
+    assert tf(L6, FAKE + 1, n, k, out, 1 << 30, None) == ALIGN       # Q6_K rows: 2-byte aligned
+    assert tf(kq.LAYOUT_ROWS, FAKE, n, k, out, 1 << 30, None) == SHAPE
+    assert tf(6, FAKE, n, k, out, 1 << 30, None) == SHAPE
+    # the staged calls take the Q5_K / Q6_K layouts (checked up to the launch)
+    sb = kq.scratch_bytes(n, k)
+    lp = (ctypes.c_void_p * 1)(FAKE)
+    for lay in (L5, L6):
+        assert lib.kq_gemv_staged(FAKE + 8, lay, n, k, FAKE, 16, FAKE, FAKE, sb, None) == ALIGN
+        assert lib.kq_gemv_staged(FAKE, lay, n, k, FAKE, 16, FAKE, FAKE, 256, None) == WS
+        assert lib.kq_gemv_staged(FAKE, lay, n, 100, FAKE, 16, FAKE, FAKE, sb, None) == SHAPE
+    # scratch sized for any format: at least what each format's geometry needs
+    assert kq.scratch_bytes(131072, 6656) > 0 and kq.group_scratch_bytes(2000, 6656, 3) > 0
+
+
+def test_chain_refuses_q5k_q6k_layouts():
+    for lay in (kq.LAYOUT_Q5K_TILED16, kq.LAYOUT_Q6K_TILED16):
+        assert _encode([_phase()], layout=lay) == SHAPE
 
 
 def _phase(count=2, n=512, k=1024, w=FAKE, logits=FAKE, staged=FAKE):
