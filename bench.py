@@ -365,7 +365,52 @@ def config_timings(stack, torch, calls=50):
                                                  out=(stack.am, stack.acc, None), layout=stack.layout))
     out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us)
     out["stochastic_lm_head_m16"] = stochastic_timing(stack, torch, time_calls)
+    out.update(kquant_timings(stack, torch, time_calls))
     out["launch"] = "hipgraph, back-to-back"
+    torch.cuda.synchronize()
+    return out
+
+
+def kquant_timings(stack, torch, time_calls):
+    """The Q5_K and Q6_K paths on the benchmark's shapes: the square
+    6,656 x 6,656 product at M = 1 and 16 over 16 rotating copies of each
+    format, and the LM-head verify (6,656 -> 131,072, M = 16, k = 15) with
+    Q6_K weights (the output layer's usual k-quant). Weight bytes per call
+    are the format's own (176 or 210 per 256 weights)."""
+    kq = stack.kq
+    dev = stack.dev
+    out = {}
+
+    def rate(nbytes, m, us):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us_per_call": round(us, 2), "rows_per_s": round(m / (us * 1e-6), 1),
+                "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    sq = synthetic.SQUARE
+    n, k = sq["n"], sq["k"]
+    x = torch.from_numpy(synthetic.activations(16, k, sq["seed"])).to(dev)
+    scratch = kq.new_scratch(n, k, dev)
+    logits = torch.empty((16, n), dtype=torch.float32, device=dev)
+    for fmt in ("q5k", "q6k"):
+        layout, bb = kq.FORMATS[fmt]
+        ws = [kq.tile_weights(torch.from_numpy(synthetic.kquant_matrix(fmt, n, k, sq["seed"] + 100 * c)).to(dev),
+                              n, k, fmt=fmt) for c in range(16)]
+        res = {}
+        for m in (1, 16):
+            st = kq.stage_rows(x[:m])
+            us = time_calls(lambda i: kq.gemv_staged(ws[i % 16], n, k, st, m, scratch, logits=logits[:m],
+                                                       layout=layout))
+            res[f"m{m}"] = rate(n * (k // 256) * bb, m, us)
+        out[f"square_6656x6656_{fmt}"] = res
+        del ws
+    h = stack.head
+    w6 = kq.tile_weights(torch.from_numpy(synthetic.q6k_matrix(h.n, h.k, h.seed)).to(dev), h.n, h.k, fmt="q6k")
+    sth = stack.staged[h.k]
+    kq.stage_rows(stack.x[h.k][:16], staged=sth)
+    us = time_calls(lambda i: kq.verify_staged(w6, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
+                                                 out=(stack.am, stack.acc, None), layout=kq.LAYOUT_Q6K_TILED16))
+    out["lm_head_verify_m16_q6k"] = rate(h.n * (h.k // 256) * 210, 16, us)
+    del w6
     torch.cuda.synchronize()
     return out
 
