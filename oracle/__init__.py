@@ -80,6 +80,8 @@ def _load():
     lib.kqo_decode_row_fmt.restype = ctypes.c_int
     lib.kqo_gemv_rows_fmt.argtypes = [ctypes.c_int, P, i64, i64, P, ctypes.c_int, P, i64, P, P, ctypes.c_int]
     lib.kqo_gemv_rows_fmt.restype = ctypes.c_int
+    lib.kqo_tree_accept.argtypes = [P, P, ctypes.c_int, P, P, P, P]
+    lib.kqo_tree_accept.restype = ctypes.c_int
     lib.kqo_num_threads.argtypes = []
     lib.kqo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -199,6 +201,23 @@ def accept(draft: Sequence[int], argmax: Sequence[int]) -> Tuple[int, int]:
     nxt = ctypes.c_int32(0)
     _load().kqo_accept(_p(d) if k else None, k, _p(a), ctypes.byref(acc), ctypes.byref(nxt))
     return int(acc.value), int(nxt.value)
+
+
+def tree_accept(parent: Sequence[int], token: Sequence[int], argmax: Sequence[int]) -> Tuple[int, int, list]:
+    """(accepted, next_token, path) of the greedy walk over a token tree
+    (kqo_tree_accept): parent[0] = -1, parent[j] < j, token[j] the token node
+    j proposes, argmax[j] the target's argmax of row j."""
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    tok = np.ascontiguousarray(np.asarray(token, dtype=np.int32))
+    am = np.ascontiguousarray(np.asarray(argmax, dtype=np.int32))
+    m = par.shape[0]
+    if tok.shape[0] != m or am.shape[0] != m:
+        raise ValueError("parent, token and argmax need one entry per node")
+    acc, nxt = ctypes.c_int32(0), ctypes.c_int32(0)
+    path = np.zeros(max(m, 1), dtype=np.int32)
+    if _load().kqo_tree_accept(_p(par), _p(tok), m, _p(am), ctypes.byref(acc), ctypes.byref(nxt), _p(path)):
+        raise ValueError("invalid tree: parent[0] must be -1 and parent[j] in [0, j)")
+    return int(acc.value), int(nxt.value), [int(v) for v in path[:acc.value]]
 
 
 def verify(w: np.ndarray, k: int, x: np.ndarray, draft: Sequence[int], rel: float = REL_TOL,

@@ -321,6 +321,40 @@ int kqo_accept(const int32_t *draft, int k, const int32_t *argmax,
     return 0;
 }
 
+/* Greedy accept over a token tree of m nodes (the hardware-aware token tree
+ * of ch. 33 "Speculation: the local win and the distributed verdict",
+ * section 33.7: the tree covers near-miss branches with batch arithmetic
+ * the weight stream leaves idle, so the target scores every node in one
+ * pass and a round emits along the branch it agrees with). Node 0 is the
+ * root (the last committed position); node j >= 1 proposes token[j] as
+ * the continuation of its parent parent[j] < j. Row j of the target
+ * predicts the token after node j (its argmax). From the root, the walk
+ * moves to a child whose token equals the current node's argmax (the
+ * lowest-index such child when siblings repeat a token) and stops when no
+ * child matches. accepted = nodes moved through, next_token = the argmax of
+ * the node where the walk stops, path[0..accepted) = the nodes moved
+ * through. A chain (parent[j] = j - 1) is the linear rule of kqo_accept.
+ * Returns -1 for an invalid tree (parent[0] != -1 or parent[j] not in
+ * [0, j)). */
+int kqo_tree_accept(const int32_t *parent, const int32_t *token, int m, const int32_t *argmax,
+                    int32_t *accepted, int32_t *next_token, int32_t *path) {
+    if (m < 1 || parent[0] != -1) return -1;
+    for (int j = 1; j < m; ++j)
+        if (parent[j] < 0 || parent[j] >= j) return -1;
+    int cur = 0, n = 0;
+    for (;;) {
+        int nxt = -1;
+        for (int j = 1; j < m; ++j)
+            if (parent[j] == cur && token[j] == argmax[cur]) { nxt = j; break; }
+        if (nxt < 0) break;
+        path[n++] = nxt;
+        cur = nxt;
+    }
+    *accepted = n;
+    *next_token = argmax[cur];
+    return 0;
+}
+
 int kqo_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
