@@ -23,11 +23,13 @@
  * (k if none), next_token = argmax[accepted], emitted = accepted + 1.
  *
  * Conventions (all entry points):
- *  - Shapes: 1 <= m <= 16, k > 0 and k % 256 == 0, k <= 2^28, 1 <= n < 2^31,
+ *  - Shapes: 1 <= m <= 64 (more than 16 only where stated: not for chains
+ *    or the draft block), k > 0 and k % 256 == 0, k <= 2^28, 1 <= n < 2^31,
  *    and the weight matrix (n rounded up to a multiple of 16) and the staged
- *    activations each smaller than 4 GiB: ceil(n/16) * 16 * (k/256) * 144 <
- *    2^32 and (k/256) * 16,960 < 2^32 (the kernels address them with 32-bit
- *    offsets). Other shapes give KQ_ERR_SHAPE (size queries return 0).
+ *    activations each smaller than 4 GiB: ceil(n/16) * 16 * (k/256) * (block
+ *    bytes) < 2^32 and kq_staged_bytes_rows(k, m) < 2^32 (the kernels
+ *    address them with 32-bit offsets). Other shapes give KQ_ERR_SHAPE (size
+ *    queries return 0).
  *  - Layouts: w is [n][k/256] blocks of 144 bytes, row-major, 16-byte aligned;
  *    x is fp32 [m][k] row-major, 16-byte aligned; logits fp32 [m][n].
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
@@ -96,6 +98,14 @@ size_t kq_workspace_bytes(int64_t n, int64_t k, int m);
 /* Bytes of a staged activation block for k columns (any m <= 16). */
 size_t kq_staged_bytes(int64_t k);
 
+/* Bytes of a staged activation block for m <= 64 rows of k columns (0 for
+ * invalid arguments): (k/256) * s * 16,960 with s = 1, 2 or 4 sixteen-row
+ * slices for m <= 16, <= 32, <= 64. Calls of more than 16 rows (the
+ * token-tree verify, kq_verify_tree_staged, or a longer linear verify) run
+ * every weight tile against all slices in the same pass, so the weights are
+ * still read once per call. */
+size_t kq_staged_bytes_rows(int64_t k, int m);
+
 /* Bytes of device scratch the *_staged calls need for an n x k matrix (in
  * any weight format and layout). */
 size_t kq_scratch_bytes(int64_t n, int64_t k);
@@ -119,7 +129,7 @@ kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* The verify step: logits (optional), per-row argmax and greedy accept.
- *  m               k_draft + 1 (1..16): row i < m-1 judges draft[i], row
+ *  m               k_draft + 1 (1..64): row i < m-1 judges draft[i], row
  *                  m-1 supplies the token after a full accept
  *  draft_host      host, m-1 int32 tokens in [0, n) (copied before return;
  *                  may be NULL when m == 1)
@@ -139,7 +149,9 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k,
 /* Stage m fp32 activation rows once for any number of matrices with the same
  * k (projections that share an input: q/k/v, gate/up).
  *  x       device, fp32 [m][k]
- *  staged  device, >= kq_staged_bytes(k) bytes, 256-byte aligned (written)
+ *  m       1..64 (more than 16: see kq_staged_bytes_rows)
+ *  staged  device, >= kq_staged_bytes_rows(k, m) bytes (kq_staged_bytes(k)
+ *          for m <= 16), 256-byte aligned (written)
  * A staged block is valid for the m it was staged with. */
 kq_status kq_stage_rows(const float *x, int m, int64_t k,
                         void *staged, size_t staged_bytes, void *stream);
@@ -238,6 +250,32 @@ kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
                            int32_t *argmax, int32_t *accept_out,
                            float *logits_or_null,
                            void *scratch, size_t scratch_bytes, void *stream);
+
+/* Token-tree verify (ch. 33 "Speculation: the local win and the
+ * distributed verdict", section 33.7: the hardware-aware token tree spends
+ * the batch arithmetic a weight stream leaves idle on near-miss branches,
+ * at 24, 32, 48 or 64 nodes). One pass over the weights scores all m nodes
+ * (m <= 64; activation row i is node i's position), takes every row's
+ * argmax (ties -> lowest index) and walks the tree: from the root (node 0),
+ * move to a child whose token equals the current node's argmax (the lowest
+ * index when siblings repeat a token) until none does.
+ *  staged        kq_stage_rows of the m node rows (kq_staged_bytes_rows)
+ *  parent_host   host int32 [m]: parent_host[0] = -1, parent_host[i] in
+ *                [0, i) (parents before children), else KQ_ERR_SHAPE
+ *  token_host    host int32 [m]: the token node i proposes (i >= 1, in
+ *                [0, n), else KQ_ERR_TOKEN); entry 0 is ignored
+ *  argmax        device int32 [m] (written)
+ *  accept_out    device int32 [2] = {nodes moved through, the argmax of the
+ *                node where the walk stops} (written)
+ *  path_out_or_null  device int32 [m] or NULL: entries 0..accepted-1 are the
+ *                nodes moved through, in order (the rest untouched)
+ *  logits_or_null, scratch: as kq_verify_staged. A chain (parent i - 1)
+ * gives kq_verify_staged's result for the same tokens. Every argument is
+ * checked before any HIP call. */
+kq_status kq_verify_tree_staged(const void *w, int layout, int64_t n, int64_t k, const void *staged, int m,
+                                const int32_t *parent_host, const int32_t *token_host, int32_t *argmax,
+                                int32_t *accept_out, int32_t *path_out_or_null, float *logits_or_null,
+                                void *scratch, size_t scratch_bytes, void *stream);
 
 /* Bytes of device scratch kq_gemv_staged_group needs for `count` matrices
  * of n x k in any weight format (0 for invalid arguments). */

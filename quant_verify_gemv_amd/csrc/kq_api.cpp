@@ -41,7 +41,7 @@ struct Shape {
   int waves, tpw, per_cu, bi, depth;
 };
 
-static Shape pick_shape(int64_t n, int count, int fmt) {
+static Shape pick_shape(int64_t n, int count, int fmt, int ms) {
 #ifdef KQ_GEOM_WAVES  // build-time override for tuning sweeps
 #ifndef KQ_GEOM_BI
 #define KQ_GEOM_BI 1
@@ -52,9 +52,15 @@ static Shape pick_shape(int64_t n, int count, int fmt) {
   (void)n;
   (void)count;
   (void)fmt;
+  (void)ms;
   return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI, KQ_GEOM_DEPTH};
 #endif
   const int64_t rows = n * count;
+  // More than 16 activation rows (2 or 4 slices per tile): one tile per
+  // wave, and the LDS ring shrinks to 4 or 2 blocks (every block now holds
+  // 2 or 4 staged slices) so that it still fits a CU's LDS; at 4 slices,
+  // three weight register sets (the slices' accumulators need the room).
+  if (ms > 1) return ms == 4 ? Shape{8, 1, 1, 1, 3} : Shape{8, 1, 1, 2, 4};
   // Q5_K and Q6_K keep two more registers per tile and register set, so
   // they run one tile per wave (12 waves from 32,768 rows, else 8)
   if (fmt != kFmtQ4) return rows >= 32768 ? Shape{12, 1, 1, 4, 4} : Shape{8, 1, 1, 4, 4};
@@ -63,9 +69,10 @@ static Shape pick_shape(int64_t n, int count, int fmt) {
   return {8, 1, 1, 4, 4};
 }
 
-Geometry geometry(int64_t n, int64_t k, int count, int fmt) {
+Geometry geometry(int64_t n, int64_t k, int count, int fmt, int ms) {
   Geometry g;
-  const Shape sh = pick_shape(n, count, fmt);
+  const Shape sh = pick_shape(n, count, fmt, ms);
+  g.ms = ms;
   g.count = count;
   g.waves = sh.waves;
   g.tpw = sh.tpw;
@@ -85,14 +92,21 @@ Geometry geometry(int64_t n, int64_t k, int count, int fmt) {
   return g;
 }
 
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt) {
-  const Geometry g = geometry(n, k, count, fmt);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt, int ms) {
+  const Geometry g = geometry(n, k, count, fmt, ms);
   ScratchLayout s;
   s.cnt_off = kCntOff;
   s.keys_off = align256(s.cnt_off + sizeof(unsigned) * kCntStride * (size_t)g.n_groups);
-  s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxRows * (size_t)g.n_wg);
-  s.total = s.part_off + align256(sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * (size_t)g.rows);
+  s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxTreeRows * (size_t)g.n_wg);
+  s.total = s.part_off + align256(sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * ms * (size_t)g.rows);
   return s;
+}
+
+// The staged records of k columns for m rows stay below 4 GiB (32-bit
+// offsets).
+static bool staged_ok(int64_t k, int m) {
+  return k > 0 && k % kQK == 0 && k <= ((int64_t)1 << 28) && m >= 1 && m <= kMaxTreeRows &&
+         (k / kQK) * row_slices(m) * kStageBytes < ((int64_t)1 << 32);
 }
 
 }  // namespace kq
@@ -114,18 +128,23 @@ const char *kq_status_string(kq_status s) {
   }
 }
 
-size_t kq_staged_bytes(int64_t k) {
-  if (k <= 0 || k % kQK || k > ((int64_t)1 << 28)) return 0;
-  return (size_t)(k / kQK) * (size_t)kStageBytes;
+size_t kq_staged_bytes(int64_t k) { return kq_staged_bytes_rows(k, kMaxRows); }
+
+size_t kq_staged_bytes_rows(int64_t k, int m) {
+  if (!staged_ok(k, m)) return 0;
+  return (size_t)(k / kQK) * (size_t)row_slices(m) * (size_t)kStageBytes;
 }
 
-// Scratch for `count` matrices in whichever format needs the most.
+// Scratch for `count` matrices in whichever format and slice count needs
+// the most.
 static size_t scratch_any_fmt(int64_t n, int64_t k, int count) {
   size_t t = 0;
   for (int f = kFmtQ4; f <= kFmtQ6; ++f) {
     if (!shape_ok(n, k, f)) continue;
-    const size_t b = scratch_layout(n, k, count, f).total;
-    t = b > t ? b : t;
+    for (int ms = 1; ms <= 4; ms *= 2) {
+      const size_t b = scratch_layout(n, k, count, f, ms).total;
+      t = b > t ? b : t;
+    }
   }
   return t;
 }
@@ -141,8 +160,8 @@ size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count) {
 }
 
 size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
-  if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return 0;
-  return align256(kq_staged_bytes(k)) + kq_scratch_bytes(n, k);
+  if (!shape_ok(n, k) || !staged_ok(k, m)) return 0;
+  return align256(kq_staged_bytes_rows(k, m)) + kq_scratch_bytes(n, k);
 }
 
 kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave,
@@ -196,9 +215,9 @@ kq_status kq_workspace_init(void *workspace, size_t bytes, void *stream) {
 kq_status kq_stage_rows(const float *x, int m, int64_t k, void *staged, size_t staged_bytes,
                         void *stream) {
   if (!x || !staged) return KQ_ERR_NULL;
-  if (m < 1 || m > kMaxRows || k <= 0 || k % kQK || k > ((int64_t)1 << 28)) return KQ_ERR_SHAPE;
+  if (!staged_ok(k, m)) return KQ_ERR_SHAPE;
   if (!al(x, 16) || !al(staged, 256)) return KQ_ERR_ALIGN;
-  if (staged_bytes < kq_staged_bytes(k)) return KQ_ERR_WORKSPACE;
+  if (staged_bytes < kq_staged_bytes_rows(k, m)) return KQ_ERR_WORKSPACE;
   if (launch_stage(x, m, k, (uint8_t *)staged, nullptr, 0, stream)) return KQ_ERR_LAUNCH;
   return KQ_OK;
 }
@@ -233,7 +252,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
                      const void *staged, int m, float *const *logits, bool verify,
                      const int32_t *draft_host, int32_t *argmax, int32_t *accept_out, int argmax_from,
                      int32_t *head_out, void *scratch, size_t scratch_bytes, const float *x_to_stage,
-                     void *stream) {
+                     void *stream, const int32_t *tree_parent = nullptr, int32_t *path_out = nullptr) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
   const int fmt = layout_fmt(layout);
   if (fmt < 0) return KQ_ERR_SHAPE;
@@ -244,22 +263,36 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   }
   if (verify && (!argmax || (!accept_out && argmax_from == 0))) return KQ_ERR_NULL;
   if (verify && accept_out && m > 1 && !draft_host) return KQ_ERR_NULL;
-  if (!shape_ok(n, k, fmt) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
+  if (!shape_ok(n, k, fmt) || !staged_ok(k, m)) return KQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i)
     if (!al(w[i], 16)) return KQ_ERR_ALIGN;
   if (!al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
   if (x_to_stage && !al(x_to_stage, 16)) return KQ_ERR_ALIGN;
-  const ScratchLayout sl = scratch_layout(n, k, count, fmt);
+  const int ms = row_slices(m);
+  const ScratchLayout sl = scratch_layout(n, k, count, fmt, ms);
   if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
-  if (verify && accept_out) {
+  if (verify && accept_out && tree_parent) {
+    // node 0 is the root; every other node names an earlier node as parent
+    if (tree_parent[0] != -1) return KQ_ERR_SHAPE;
+    for (int i = 1; i < m; ++i)
+      if (tree_parent[i] < 0 || tree_parent[i] >= i) return KQ_ERR_SHAPE;
+    for (int i = 1; i < m; ++i) {
+      if (draft_host[i] < 0 || (int64_t)draft_host[i] >= n) return KQ_ERR_TOKEN;
+      a.draft[i] = draft_host[i];
+      a.parent[i] = tree_parent[i];
+    }
+    a.parent[0] = -1;
+    a.tree = 1;
+    a.path_out = path_out;
+  } else if (verify && accept_out) {
     for (int i = 0; i < m - 1; ++i) {
       if (draft_host[i] < 0 || (int64_t)draft_host[i] >= n) return KQ_ERR_TOKEN;
       a.draft[i] = draft_host[i];
     }
   }
-  a.g = geometry(n, k, count, fmt);
+  a.g = geometry(n, k, count, fmt, ms);
   fill_phase(a.ph, a.g, w, logits, count, n, k, staged);
   a.layout = layout;
   a.m = m;
@@ -272,7 +305,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   a.argmax_from = argmax_from;
   a.head_out = head_out;
   a.accept_out = accept_out;
-  a.k_draft = verify && accept_out ? m - 1 : 0;
+  a.k_draft = verify && accept_out && !tree_parent ? m - 1 : 0;
   a.verify = verify ? 1 : 0;
   if (x_to_stage) {
     if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, a.g.n_groups, stream))
@@ -304,14 +337,23 @@ kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k, 
              nullptr, scratch, scratch_bytes, nullptr, stream);
 }
 
+kq_status kq_verify_tree_staged(const void *w, int layout, int64_t n, int64_t k, const void *staged, int m,
+                                const int32_t *parent_host, const int32_t *token_host, int32_t *argmax,
+                                int32_t *accept_out, int32_t *path_out_or_null, float *logits_or_null,
+                                void *scratch, size_t scratch_bytes, void *stream) {
+  if (!parent_host || !token_host || !argmax || !accept_out) return KQ_ERR_NULL;
+  return run(&w, layout, 1, n, k, staged, m, &logits_or_null, true, token_host, argmax, accept_out, 0, nullptr,
+             scratch, scratch_bytes, nullptr, stream, parent_host, path_out_or_null);
+}
+
 static kq_status split_workspace(int64_t n, int64_t k, int m, void *ws, size_t ws_bytes,
                                  void **staged, void **scratch, size_t *scratch_bytes) {
   if (!ws) return KQ_ERR_NULL;
-  if (!shape_ok(n, k) || m < 1 || m > kMaxRows) return KQ_ERR_SHAPE;
+  if (!shape_ok(n, k) || !staged_ok(k, m)) return KQ_ERR_SHAPE;
   if (!al(ws, 256)) return KQ_ERR_ALIGN;
   const size_t need = kq_workspace_bytes(n, k, m);
   if (ws_bytes < need) return KQ_ERR_WORKSPACE;
-  const size_t st = align256(kq_staged_bytes(k));
+  const size_t st = align256(kq_staged_bytes_rows(k, m));
   *staged = ws;
   *scratch = (uint8_t *)ws + st;
   *scratch_bytes = ws_bytes - st;
@@ -369,6 +411,7 @@ static Geometry chain_geometry(int64_t n, int64_t k, int count, int tpw) {
   g.tpw = tpw;
   g.bi = 4;
   g.depth = 4;
+  g.ms = 1;
   g.rows = 128 * tpw;
   g.n_wg_per = (int)cdiv(n, g.rows);
   g.n_groups = count * g.n_wg_per;

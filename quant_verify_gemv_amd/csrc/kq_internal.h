@@ -10,7 +10,10 @@ namespace kq {
 
 constexpr int64_t kQK = 256;          // weights per Q4_K super-block
 constexpr int64_t kBlockBytes = 144;  // bytes per super-block
-constexpr int kMaxRows = 16;          // verify rows per call (block size of the draft)
+constexpr int kMaxRows = 16;          // activation rows per MFMA slice (block size of the draft)
+constexpr int kMaxTreeRows = 64;      // activation rows per call: up to 4 slices (token-tree verify)
+// 16-row slices a call of m activation rows runs: 1, 2 or 4
+constexpr int row_slices(int m) { return m <= 16 ? 1 : m <= 32 ? 2 : 4; }
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
 
 // Tiled weight layout (see kq_tile_weights in kq.h): 2,304-byte records of
@@ -45,8 +48,10 @@ constexpr int layout_fmt(int layout) {
                                                                  : -1;
 }
 
-// Staged activations, one record per 256-column block (each row scaled by a
-// power of two 2^e chosen from that row's largest magnitude in the block):
+// Staged activations, one record per 256-column block and 16-row slice
+// (records [block][slice]; a call of m rows has row_slices(m) slices; each
+// row scaled by a power of two 2^e chosen from that row's largest magnitude
+// in the block):
 //   XA  [8 k-steps][hi,lo][64 lanes][8 x fp16]  16,384 B  MFMA A operand
 //   XSB [64 lanes][4 x fp16]                       512 B  sub-block sums (min-term A operand)
 //   XI  [16] fp32                                    64 B  per-row 2^-e
@@ -65,8 +70,8 @@ constexpr int64_t kStageBytes = 16384 + 512 + 64;  // 16,960 B per block (16-B a
 //   cnt_off    per-row-group arrival counters [n_groups], one u32 per
 //              128-byte line (kCntStride words apart) so that the atomics of
 //              different groups do not queue on one line
-//   keys_off   per-workgroup argmax keys [n_wg][16] (u64)
-//   part_off   partial sums [n_wg][2][16][rows per group] fp32
+//   keys_off   per-workgroup argmax keys [n_wg][kMaxTreeRows] (u64)
+//   part_off   partial sums [n_wg][2][rows per group][16 * slices] fp32
 constexpr int64_t kBarOff = KQ_CHAIN_BARRIER_OFFSET;
 constexpr int64_t kErrOff = KQ_CHAIN_ERROR_OFFSET;
 constexpr int64_t kEpochOff = 384;
@@ -84,6 +89,7 @@ struct Geometry {
   int tpw;        // 16-row tiles per wave (1 or 2)
   int bi;         // units between workgroup barriers (1, 2 or 4; LDS ring of 2 bi blocks)
   int depth;      // weight register sets (prefetch depth + 1: 4 or 8)
+  int ms;         // 16-row activation slices (1, 2 or 4)
   int rows;       // rows per row group = 16 * waves * tpw
   int n_wg_per;   // row groups per matrix
   int n_groups;   // row groups in total = count * n_wg_per
@@ -128,20 +134,23 @@ struct GemvLaunch {
   int argmax_from;
   int32_t *head_out;    // verify only, may be null: row 0's argmax
   int32_t *accept_out;  // verify only, may be null (then no accept decision)
-  int32_t draft[kMaxRows];
-  int k_draft;
+  int32_t draft[kMaxTreeRows];   // linear: draft[i] judged by row i; tree: token of node i (i >= 1)
+  int32_t parent[kMaxTreeRows];  // tree: parent of node i (i >= 1)
+  int k_draft;                   // linear drafts (0: no linear accept)
+  int tree;                      // 1: tree accept over m nodes
+  int32_t *path_out;             // tree, may be null: the accepted path's nodes
   int verify;
   Geometry g;
 };
 
-Geometry geometry(int64_t n, int64_t k, int count, int fmt = kFmtQ4);
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt = kFmtQ4);
+Geometry geometry(int64_t n, int64_t k, int count, int fmt = kFmtQ4, int ms = 1);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt = kFmtQ4, int ms = 1);
 
 // Kernel launches (return a hipError_t as int).
 // kq_stage_kernel also zeroes the control words of `ctrl` (a scratch area
 // laid out as above for n_groups row groups) when ctrl is not null.
 int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ctrl, int64_t n_groups,
-                 void *stream);
+                 void *stream);  // row_slices(m) records per block
 int launch_gemv(const GemvLaunch &a, void *stream);
 // Workgroups of the chain kernel (8 waves of one 16-row tile) the current
 // device holds at once, or a negative HIP error code.

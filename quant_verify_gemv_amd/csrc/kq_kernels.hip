@@ -188,8 +188,10 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, unsigned n) {
 __device__ __forceinline__ constexpr int perm8(int i) { return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1); }
 
 // ---------------------------------------------------------------------------
-// Staging. One workgroup per 256-column block; thread t handles row m = t/16
-// and the 16 columns [16c, 16c+16) of the block, c = t%16.
+// Staging. One workgroup per 256-column block and 16-row slice (grid:
+// blocks x slices, records [block][slice]); thread t handles row
+// 16 slice + t/16 (record row m = t/16) and the 16 columns [16c, 16c+16) of
+// the block, c = t%16.
 __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__ x, int m_rows,
                                                        int64_t k, uint8_t *__restrict__ staged,
                                                        unsigned *__restrict__ ctrl,
@@ -198,9 +200,11 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
   const int m = t >> 4;
   const int c = t & 15;
   const int64_t b = blockIdx.x;
-  const bool active = m < m_rows;  // rows >= m_rows are staged as zeros
+  const int slice = blockIdx.y;
+  const int mg = 16 * slice + m;     // activation row
+  const bool active = mg < m_rows;  // rows >= m_rows are staged as zeros
 
-  if (ctrl && b == 0) {
+  if (ctrl && b == 0 && slice == 0) {
     if (t == 0) ctrl[0] = 0u;
     for (int64_t i = t; i < n_groups; i += 256) ctrl[kCntOff / 4 + i * kCntStride] = 0u;
   }
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
   float v[16];
   float amax = 0.0f;
   if (active) {
-    const f32x4 *src = (const f32x4 *)(x + (int64_t)m * k + b * kQK + 16 * c);
+    const f32x4 *src = (const f32x4 *)(x + (int64_t)mg * k + b * kQK + 16 * c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 f = src[i];
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(256) void kq_stage_kernel(const float *__restrict__
     e = 10 - E;
     e = e > 100 ? 100 : e;
   }
-  uint8_t *rec = staged + b * kStageBytes;
+  uint8_t *rec = staged + (b * gridDim.y + slice) * kStageBytes;
   if (c == 0) *(float *)(rec + kXiOffset + 4 * m) = ldexpf(1.0f, -e);
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = ldexpf(v[i], e);
@@ -353,10 +357,14 @@ __device__ __forceinline__ int spin_flag(const unsigned long long *flag, unsigne
 // Field f of phase ph: the launch's own phase, or entry ph of a chain's table.
 #define KQ_PH(I_, f) (CHAIN ? ((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f : a.ph.f)
 
-template <int W, int T, int BI, int D, bool CHAIN, int FMT>
+template <int W, int T, int BI, int D, bool CHAIN, int FMT, int MS>
 __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv_kernel(GemvLaunch a) {
   static_assert(W % 4 == 0, "waves spread evenly over the 4 SIMDs");
   static_assert(FMT == kFmtQ4 || !CHAIN, "chains run Q4_K");
+  // MS 16-row activation slices: every unpacked weight operand feeds the
+  // MFMAs of all MS slices, so the weights are read once for 16 MS rows
+  static_assert(MS == 1 || (!CHAIN && T == 1), "more than 16 rows: single launches, one tile per wave");
+  constexpr int kRS = 16 * MS;  // activation rows per call at most
   constexpr unsigned kTB = 16u * (unsigned)fmt_block_bytes(FMT);  // tiled record bytes
   // D weight register sets: the weights of unit i + D - 1 are loaded while
   // unit i computes. The activations of unit i + BI are stored to LDS in
@@ -366,21 +374,24 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // workgroups stage twice the activation chunks per thread and keep one
   // set in flight. The unit loop is unrolled kU = lcm(D, BI, kXL + 1) times
   // so that every register set index and every interval position is static.
-  constexpr int kXL = (W >= 8 && T == 1) ? 3 : 1;
+  // Four slices: one register set, loaded at the start of a unit and stored
+  // at its end (the unit's four-fold MFMA work covers the L2 latency).
+  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : MS == 4 ? 0 : 1;
   constexpr int kU = lcm_int(lcm_int(D, BI), kXL + 1);
   constexpr int kNth = 64 * W;
   constexpr int kRows = 16 * T * W;
   // The staged record is kXc 16-byte chunks, copied linearly; thread tid
   // moves chunks tid + j kNth (the last round only partly).
-  constexpr int kXc = (int)(kStageBytes / 16);  // 1,060
+  constexpr int kXc = (int)(kStageBytes * MS / 16);  // 1,060 per slice
   constexpr int kXj = (kXc + kNth - 1) / kNth;   // chunks per thread
   // Activation ring: unit i sits in buffer i % kNB. Workgroups synchronise
   // once every BI units: between two barriers the waves read BI buffers and
   // fill the other BI.
   constexpr int kNB = 2 * BI;
   static_assert(BI == 1 || BI == 2 || BI == 4, "barrier interval");
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[kNB][kStageBytes];
-  __shared__ unsigned long long s_keys[kMaxRows];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[kNB][kStageBytes * MS];
+  __shared__ unsigned long long s_keys[kRS];
+  __shared__ int s_am[kRS];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
@@ -403,7 +414,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   auto run_len = [&](int U) -> int { return U / P + (p < U % P ? 1 : 0); };
   auto tile_row = [&](int t) -> int { return (t * W + wave) * 16 + ln; };  // row within the group
 
-  if (tid < kMaxRows) s_keys[tid] = 0ull;
+  if (tid < kRS) s_keys[tid] = 0ull;
 
   const unsigned mask_lo = in_vgpr(0x000F000Fu);
   // byte-permute selector that puts this lane's two scale bytes 2(kg>>1),
@@ -517,12 +528,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   };
   XRegs xr[kXL + 1];
   WTile wr[D][T];
-  f32x4 acc[T], acc_first[T];
+  f32x4 acc[T][MS], acc_first[T][MS];
   // finished rows of whole row groups: the argmax keys are reduced over the
   // wave's tiles and its 16 rows per lane group into a running maximum per
   // activation row 4kg + r (wave_key[r], held by every lane of the group)
   // that goes to LDS after the loop.
-  unsigned long long wave_key[4] = {0ull, 0ull, 0ull, 0ull};
+  unsigned long long wave_key[MS][4] = {};
   const __amdgpu_buffer_rsrc_t part_rsrc = dev_rsrc(a.partials);
   // Logits of a chain phase are written through to the device coherence
   // point (agent-scope stores), so they are visible to every workgroup once
@@ -567,10 +578,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       return (g - mat * n_wg_per) * kRows;
     };
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc_first[t] = acc[t];
-    }
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int sl = 0; sl < MS; ++sl) {
+        acc[t][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_first[t][sl] = acc[t][sl];
+      }
 
     // Activation stream, two units behind the weights and never past the
     // phase's last unit (in a chain, a phase's activations are read only
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     int bx = u0 % KB;
     const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_PH(ph, staged));
     auto load_x = [&](XRegs &x) {
-      const unsigned src = (unsigned)bx * (unsigned)kStageBytes;
+      const unsigned src = (unsigned)bx * (unsigned)(kStageBytes * MS);
 #pragma unroll
       for (int j = 0; j < kXj; ++j)
         x.a[j] = buf_ld16(x_rsrc, (unsigned)(j < kXj - 1 ? tid + kNth * j : xlast) * 16u, src);
@@ -594,7 +607,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
         if (j < kXj - 1 || tid + kNth * j < kXc) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
     };
 
-    auto write_rows = [&](int g, const f32x4(&v)[T]) {
+    auto write_rows = [&](int g, const f32x4(&v)[T][MS]) {
       int mat;
       const int r0 = group_row0(g, mat);
       float *logits = KQ_PH(ph, logits[mat]);
@@ -604,26 +617,36 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
           const int row = r0 + tile_row(t);
           if (row < N) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int m = 4 * kg + r;
-              if (m < M) put(&logits[(int64_t)m * N + row], v[t][r]);
-            }
+            for (int sl = 0; sl < MS; ++sl)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int m = 16 * sl + 4 * kg + r;
+                if (m < M) put(&logits[(int64_t)m * N + row], v[t][sl][r]);
+              }
           }
         }
       }
       if (!CHAIN && a.verify) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          unsigned long long best = 0ull;
+        for (int sl = 0; sl < MS; ++sl)
 #pragma unroll
-          for (int t = 0; t < T; ++t) {
-            const int row = r0 + tile_row(t);
-            const unsigned long long key = row < N ? argmax_key(v[t][r], (unsigned)row) : 0ull;
-            best = key > best ? key : best;
+          for (int r = 0; r < 4; ++r) {
+            unsigned long long best = 0ull;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              const int row = r0 + tile_row(t);
+              const unsigned long long key = row < N ? argmax_key(v[t][sl][r], (unsigned)row) : 0ull;
+              best = key > best ? key : best;
+            }
+            best = lanes_max(best, 16);
+            if constexpr (MS == 1) {
+              wave_key[sl][r] = best > wave_key[sl][r] ? best : wave_key[sl][r];
+            } else {
+              // more rows: straight into LDS (no running maxima in registers)
+              const int m = 16 * sl + 4 * kg + r;
+              if (ln == 0 && m < M && best) atomicMax(&s_keys[m], best);
+            }
           }
-          best = lanes_max(best, 16);
-          wave_key[r] = best > wave_key[r] ? best : wave_key[r];
-        }
       }
     };
 
@@ -653,6 +676,18 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     const int g_first = u0 / KB;
     int gc = g_first, bc = u0 % KB, seg0 = bc;
     int have_first = 0;
+
+    // A partial is [row of the group][kRS activation rows] fp32: the lane's
+    // four sums of a slice (activation rows 16 sl + 4kg .. +3 of its output
+    // row) are one 16-byte store.
+    auto write_partial = [&](int slot, const f32x4(&v)[T][MS]) {
+      const unsigned base_off = (unsigned)((p * 2 + slot) * kRS * kRows) * 4u;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int sl = 0; sl < MS; ++sl)
+          st_dev16(part_rsrc, base_off + (unsigned)(tile_row(t) * kRS + 16 * sl + 4 * kg) * 4u, v[t][sl]);
+    };
 
     // One unit: prefetch the activations of unit i+BI+kXL (into xl) and the
     // weights of unit i+D-1 (into pf), contract the weights in `cur` with the
@@ -695,15 +730,21 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
               k6[t][j] = half2v{hv, hv};
             }
           }
-          f32x4 cq[T];
+          f32x4 cq[T][MS];
 #pragma unroll
-          for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int sl = 0; sl < MS; ++sl) cq[t][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
           const half2v off_lo = {(_Float16)-1056.0f, (_Float16)-1056.0f};
           const half2v off_hi = {(_Float16)-1536.0f, (_Float16)-1536.0f};
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
-            const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+            half8 ahi[MS], alo[MS];
+#pragma unroll
+            for (int sl = 0; sl < MS; ++sl) {
+              ahi[sl] = *(const half8 *)(xb + sl * kStageBytes + (s * 2 + 0) * 1024 + lane * 16);
+              alo[sl] = *(const half8 *)(xb + sl * kStageBytes + (s * 2 + 1) * 1024 + lane * 16);
+            }
             const bool hi = (s & 2) != 0;
             const unsigned mask = hi ? mask_hi : mask_lo;
             const half2v off = hi ? off_hi : off_lo;
@@ -727,16 +768,22 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
               const half2v l2 = pk_fma_sub(q2h, kk, h2), l3 = pk_fma_sub(q3h, kk, h3);
               const half8 bhi = make_h8(as_u(h0), as_u(h1), as_u(h2), as_u(h3));
               const half8 blo = make_h8(as_u(l0), as_u(l1), as_u(l2), as_u(l3));
-              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, cq[t], 0, 0, 0);
-              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, cq[t], 0, 0, 0);
-              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, cq[t], 0, 0, 0);
+#pragma unroll
+              for (int sl = 0; sl < MS; ++sl) {
+                cq[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sl], bhi, cq[t][sl], 0, 0, 0);
+                cq[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[sl], bhi, cq[t][sl], 0, 0, 0);
+                cq[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sl], blo, cq[t][sl], 0, 0, 0);
+              }
             }
           }
-          const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
 #pragma unroll
-          for (int t = 0; t < T; ++t) {
+          for (int sl = 0; sl < MS; ++sl) {
+            const f32x4 xinv = *(const f32x4 *)(xb + sl * kStageBytes + kXiOffset + 16 * kg);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[t][r] += xinv[r] * (d6[t] * cq[t][r]);
+            for (int t = 0; t < T; ++t) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[t][sl][r] += xinv[r] * (d6[t] * cq[t][sl][r]);
+            }
           }
         } else {
           float d[T], dmin[T];
@@ -772,14 +819,20 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
             const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
             bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
           }
-          // x hi and x lo products accumulate in one fp32 sum per tile
-          f32x4 cq[T];
+          // x hi and x lo products accumulate in one fp32 sum per tile and slice
+          f32x4 cq[T][MS];
 #pragma unroll
-          for (int t = 0; t < T; ++t) cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int sl = 0; sl < MS; ++sl) cq[t][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
-            const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
-            const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+            half8 ahi[MS], alo[MS];
+#pragma unroll
+            for (int sl = 0; sl < MS; ++sl) {
+              ahi[sl] = *(const half8 *)(xb + sl * kStageBytes + (s * 2 + 0) * 1024 + lane * 16);
+              alo[sl] = *(const half8 *)(xb + sl * kStageBytes + (s * 2 + 1) * 1024 + lane * 16);
+            }
             const bool hi = (s & 2) != 0;
             const unsigned mask = hi ? mask_hi : mask_lo;
 #pragma unroll
@@ -810,20 +863,26 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
               const half2v v2 = fma_bcast(as_h2(u2_), kk);
               const half2v v3 = fma_bcast(as_h2(u3_), kk);
               const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
-              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
-              cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
+#pragma unroll
+              for (int sl = 0; sl < MS; ++sl) {
+                cq[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sl], bw8, cq[t][sl], 0, 0, 0);
+                cq[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[sl], bw8, cq[t][sl], 0, 0, 0);
+              }
             }
           }
           // min term and the block's contribution in the row's scaled units
-          const half4 as4 = *(const half4 *)(xb + kXsbOffset + lane * 8);
-          const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
 #pragma unroll
-          for (int t = 0; t < T; ++t) {
-            const f32x4 c2 =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          for (int sl = 0; sl < MS; ++sl) {
+            const half4 as4 = *(const half4 *)(xb + sl * kStageBytes + kXsbOffset + lane * 8);
+            const f32x4 xinv = *(const f32x4 *)(xb + sl * kStageBytes + kXiOffset + 16 * kg);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
+            for (int t = 0; t < T; ++t) {
+              const f32x4 c2 =
+                  __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[t][sl][r] += xinv[r] * (d[t] * cq[t][sl][r] - dmin[t] * c2[r]);
+            }
           }
         }
       }
@@ -833,13 +892,19 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
         if (seg0 == 0 && bc == KB - 1) {
           write_rows(gc, acc);
         } else if (gc == g_first) {
+          if constexpr (MS == 1) {
 #pragma unroll
-          for (int t = 0; t < T; ++t) acc_first[t] = acc[t];
+            for (int t = 0; t < T; ++t) acc_first[t][0] = acc[t][0];
+          } else {
+            write_partial(0, acc);  // more rows: stored now, not kept in registers
+          }
           have_first = 1;
         }
         if (u != u_last) {
 #pragma unroll
-          for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int sl = 0; sl < MS; ++sl) acc[t][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
           seg0 = 0;
         }
       }
@@ -870,30 +935,25 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     // workgroup order.
     if (!CHAIN && a.verify) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (ln == 0 && m < M && wave_key[r]) atomicMax(&s_keys[m], wave_key[r]);
-      }
+      for (int sl = 0; sl < MS; ++sl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * sl + 4 * kg + r;
+          if (ln == 0 && m < M && wave_key[sl][r]) atomicMax(&s_keys[m], wave_key[sl][r]);
+        }
     }
     const int g_last = u_last / KB;
     const int last_partial = (g_last != g_first) && (u_last % KB != KB - 1);
-    // A partial is [row of the group][16 activation rows] fp32: the lane's
-    // four sums (activation rows 4kg..4kg+3 of its output row) are one
-    // 16-byte store.
-    auto write_partial = [&](int slot, const f32x4(&v)[T]) {
-      const unsigned base_off = (unsigned)((p * 2 + slot) * kMaxRows * kRows) * 4u;
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-        st_dev16(part_rsrc, base_off + (unsigned)(tile_row(t) * kMaxRows + 4 * kg) * 4u, v[t]);
-    };
     // Sum the partials of one or two row groups over their contributors in
     // workgroup order, the loads of both groups in flight together. Thread
-    // tid handles the 16-byte chunks c = tid + j kNth of each group (row c / 4
-    // of the group, activation rows 4 (c % 4) .. +3) and issues the loads of
-    // eight contributors per group before it adds any of them.
-    constexpr int kE = kRows * kMaxRows / (4 * kNth);  // chunks per thread
-    constexpr int kC = 8;
-    static_assert(kE * 4 * kNth == kRows * kMaxRows, "chunks must split evenly");
+    // tid handles the 16-byte chunks c = tid + j kNth of each group (row
+    // c / (kRS/4) of the group, activation rows 4 (c % (kRS/4)) .. +3) and
+    // issues the loads of eight contributors per group before it adds any
+    // of them.
+    constexpr int kE = kRows * kRS / (4 * kNth);  // chunks per thread
+    constexpr int kC = 8 / MS;                     // contributors in flight (registers: 2 kE kC chunks)
+    constexpr int kCR = kRS / 4;                   // chunks per output row
+    static_assert(kE * 4 * kNth == kRows * kRS, "chunks must split evenly");
     struct Contributors {
       int pf, pl;  // first and last contributing workgroup
       int pf_slot;     // the first one's slot (the others use slot 0)
@@ -916,7 +976,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       for (int c = 0; c < kC; ++c) {
         const int q = cb.pf + c0 + c <= cb.pl ? cb.pf + c0 + c : cb.pl;
         const int slot = q == cb.pf ? cb.pf_slot : 0;
-        const unsigned src = (unsigned)((q * 2 + slot) * kMaxRows * kRows) * 4u;
+        const unsigned src = (unsigned)((q * 2 + slot) * kRS * kRows) * 4u;
 #pragma unroll
         for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
       }
@@ -938,7 +998,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
 #pragma unroll
       for (int j = 0; j < kE; ++j) {
         const int c = tid + j * kNth;
-        const int row = c >> 2, m0 = 4 * (c & 3);
+        const int row = c / kCR, m0 = 4 * (c % kCR);
         const int n = r0 + row;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -946,10 +1006,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
           const bool ok = m < M && row < nrows;
           if (ok && logits) put(&logits[(int64_t)m * N + n], v[j][r]);
           if (!CHAIN && a.verify) {
-            // max over the wave's 16 rows: the lanes with the same c % 4
+            // max over the wave's 64 / kCR rows: the lanes with the same c % kCR
             unsigned long long best = ok ? argmax_key(v[j][r], (unsigned)n) : 0ull;
-            best = lanes_max(best, 64, 4);
-            if (lane < 4 && m < M) atomicMax(&s_keys[m], best);
+            best = lanes_max(best, 64, kCR);
+            if (lane < kCR && m < M) atomicMax(&s_keys[m], best);
           }
         }
       }
@@ -993,10 +1053,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
         const int g = red_first ? g_first : g_last;
         // own partial into LDS (the activation ring is idle after the loop)
         uint8_t *own = s_x[0];
-        static_assert(kRows * kMaxRows * 4 <= kStageBytes, "own partial fits one ring buffer");
-        const f32x4(&mine)[T] = red_first ? acc_first : acc;
+        static_assert(kRows * kRS * 4 <= kStageBytes * MS, "own partial fits one ring buffer");
+        const f32x4(&mine)[T][MS] = red_first ? acc_first : acc;
 #pragma unroll
-        for (int t = 0; t < T; ++t) *(f32x4 *)(own + (tile_row(t) * kMaxRows + 4 * kg) * 4) = mine[t];
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int sl = 0; sl < MS; ++sl)
+            *(f32x4 *)(own + (tile_row(t) * kRS + 16 * sl + 4 * kg) * 4) = mine[t][sl];
         __syncthreads();
         const int pfg = p, plg = owner(g * KB + KB - 1);
         f32x4 v[kE];
@@ -1011,14 +1074,14 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
 #pragma unroll
           for (int c = 0; c < kC; ++c) {
             const int q = pfg + c0 + c <= plg ? pfg + c0 + c : plg;
-            const unsigned src = (unsigned)(q * 2 * kMaxRows * kRows) * 4u;
+            const unsigned src = (unsigned)(q * 2 * kRS * kRows) * 4u;
 #pragma unroll
             for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
           }
 #pragma unroll
           for (int c = 0; c < kC; ++c) {
             if (pfg + c0 + c > plg) continue;
-            const unsigned src = (unsigned)((pfg + c0 + c) * 2 * kMaxRows * kRows) * 4u;
+            const unsigned src = (unsigned)((pfg + c0 + c) * 2 * kRS * kRows) * 4u;
 #pragma unroll
             for (int j = 0; j < kE; ++j) {
               // not yet written: poll (bounded)
@@ -1047,11 +1110,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
         for (int q = pfg + 1; q <= plg; ++q)
 #pragma unroll
           for (int j = 0; j < kE; ++j)
-            st_dev16(part_rsrc, (unsigned)(q * 2 * kMaxRows * kRows) * 4u + (unsigned)(tid + j * kNth) * 16u,
+            st_dev16(part_rsrc, (unsigned)(q * 2 * kRS * kRows) * 4u + (unsigned)(tid + j * kNth) * 16u,
                      sentinel);
       }
     } else if (have_first || last_partial) {
-      if (have_first) write_partial(0, acc_first);
+      if (MS == 1 && have_first) write_partial(0, acc_first);
       if (last_partial) write_partial(1, acc);
       // contributor counts of both groups (computed while the stores drain)
       int c_first = 0, c_last = 0;
@@ -1128,7 +1191,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
 
     if (!a.verify) return;
     __syncthreads();
-    if (tid < kMaxRows) st_dev(&a.wg_keys[(int64_t)p * kMaxRows + tid], s_keys[tid]);
+    if (tid < kRS) st_dev(&a.wg_keys[(int64_t)p * kMaxTreeRows + tid], s_keys[tid]);
     stores_done_barrier();
     if (tid == 0) {
       const unsigned old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1136,32 +1199,57 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     }
     __syncthreads();
     if (!s_flag) return;
-    if (tid < kMaxRows) s_keys[tid] = 0ull;
+    if (tid < kRS) s_keys[tid] = 0ull;
     __syncthreads();
     {
-      const int m = tid & 15;
+      const int m = tid % kRS;
       if (m < M) {
         unsigned long long best = 0ull;
-        for (int q = tid >> 4; q < P; q += kNth / 16) {
-          const unsigned long long key = ld_dev(&a.wg_keys[q * kMaxRows + m]);
+        for (int q = tid / kRS; q < P; q += kNth / kRS) {
+          const unsigned long long key = ld_dev(&a.wg_keys[(int64_t)q * kMaxTreeRows + m]);
           best = key > best ? key : best;
         }
         atomicMax(&s_keys[m], best);
       }
     }
     __syncthreads();
-    if (tid == 0) {
-      int am[kMaxRows];
-      for (int m = 0; m < M; ++m) {
-        am[m] = (int)(0xFFFFFFFFu - (unsigned)(s_keys[m] & 0xFFFFFFFFull));
-        if (m >= a.argmax_from) a.argmax_out[m - a.argmax_from] = am[m];
+    if (tid < M) {
+      const int am = (int)(0xFFFFFFFFu - (unsigned)(s_keys[tid] & 0xFFFFFFFFull));
+      s_am[tid] = am;
+      if (tid >= a.argmax_from) a.argmax_out[tid - a.argmax_from] = am;
+    }
+    __syncthreads();
+    if (a.accept_out && a.tree) {
+      // Token tree: wave 0 walks from the root; lane j holds node j. Each
+      // move goes to a higher node index (parents precede children), so the
+      // walk ends within M - 1 moves.
+      if (tid < 64) {
+        const int j = lane;
+        const int par = j < M ? a.parent[j] : -1;
+        const int tok = j < M ? a.draft[j] : -1;
+        int cur = 0, n = 0;
+        while (true) {
+          const bool match = j >= 1 && j < M && par == cur && tok == s_am[cur];
+          const unsigned long long bal = __ballot(match);
+          if (!bal) break;
+          const int nxt = __ffsll((long long)bal) - 1;
+          if (lane == 0 && a.path_out) a.path_out[n] = nxt;
+          ++n;
+          cur = nxt;
+        }
+        if (lane == 0) {
+          a.accept_out[0] = n;
+          a.accept_out[1] = s_am[cur];
+        }
       }
-      if (a.head_out) a.head_out[0] = am[0];
-      if (a.accept_out) {
+    }
+    if (tid == 0) {
+      if (a.head_out) a.head_out[0] = s_am[0];
+      if (a.accept_out && !a.tree) {
         int i = 0;
-        while (i < a.k_draft && a.draft[i] == am[i]) ++i;
+        while (i < a.k_draft && a.draft[i] == s_am[i]) ++i;
         a.accept_out[0] = i;
-        a.accept_out[1] = am[i];
+        a.accept_out[1] = s_am[i];
       }
       __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1440,8 +1528,8 @@ int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stre
 int launch_stage(const float *x, int m, int64_t k, uint8_t *staged, unsigned *ctrl, int64_t n_groups,
                  void *stream) {
   const int64_t blocks = k / kQK;
-  hipLaunchKernelGGL(kq_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, m,
-                     k, staged, ctrl, n_groups);
+  hipLaunchKernelGGL(kq_stage_kernel, dim3((unsigned)blocks, (unsigned)row_slices(m)), dim3(256), 0,
+                     (hipStream_t)stream, x, m, k, staged, ctrl, n_groups);
   return (int)hipGetLastError();
 }
 
@@ -1459,27 +1547,31 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.chain) {
     if (a.g.waves != 8 || a.g.tpw != 1 || a.g.bi != 4 || a.g.depth != 4) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4, 1>), grid, dim3(512), 0, st, a);
     return (int)hipGetLastError();
   }
   const int fmt = layout_fmt(a.layout);
-  switch (fmt * 65536 + a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
-#define KQ_CASE(F_, W_, T_, BI_, D_)                                                                \
-  case F_ * 65536 + W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                                           \
-    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, false, F_>), grid, dim3(64 * W_), 0, st, a); \
+  switch (a.g.ms * 1048576 + fmt * 65536 + a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
+#define KQ_CASE(F_, W_, T_, BI_, D_, MS_)                                                              \
+  case MS_ * 1048576 + F_ * 65536 + W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                              \
+    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, false, F_, MS_>), grid, dim3(64 * W_), 0, st, a); \
     break;
-    KQ_CASE(kFmtQ4, 8, 2, 4, 4)
-    KQ_CASE(kFmtQ4, 8, 1, 4, 4)
-    KQ_CASE(kFmtQ4, 8, 1, 2, 4)
-    KQ_CASE(kFmtQ4, 8, 2, 2, 4)
-    KQ_CASE(kFmtQ4, 4, 1, 1, 4)
-    KQ_CASE(kFmtQ4, 12, 1, 4, 4)
-    KQ_CASE(kFmtQ4, 4, 2, 2, 3)
-    KQ_CASE(kFmtQ4, 4, 2, 1, 3)
-    KQ_CASE(kFmtQ5, 8, 1, 4, 4)
-    KQ_CASE(kFmtQ5, 12, 1, 4, 4)
-    KQ_CASE(kFmtQ6, 8, 1, 4, 4)
-    KQ_CASE(kFmtQ6, 12, 1, 4, 4)
+    KQ_CASE(kFmtQ4, 8, 2, 4, 4, 1)
+    KQ_CASE(kFmtQ4, 8, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ4, 8, 1, 2, 4, 1)
+    KQ_CASE(kFmtQ4, 8, 2, 2, 4, 1)
+    KQ_CASE(kFmtQ4, 4, 1, 1, 4, 1)
+    KQ_CASE(kFmtQ4, 12, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ4, 4, 2, 2, 3, 1)
+    KQ_CASE(kFmtQ4, 4, 2, 1, 3, 1)
+    KQ_CASE(kFmtQ5, 8, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ5, 12, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ6, 8, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ6, 12, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ4, 8, 1, 2, 4, 2)
+    KQ_CASE(kFmtQ4, 8, 1, 1, 3, 4)
+    KQ_CASE(kFmtQ6, 8, 1, 2, 4, 2)
+    KQ_CASE(kFmtQ6, 8, 1, 1, 3, 4)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;
   }
@@ -1493,7 +1585,7 @@ int chain_capacity() {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4, 1>, 512, 0);
   if (e != hipSuccess) return -(int)e;
   return per_cu * cus;
 }

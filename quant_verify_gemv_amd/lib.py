@@ -24,7 +24,7 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes",
             "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
             "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
-            "kq_tiled_bytes_fmt", "kq_tile_weights_fmt")
+            "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -105,6 +105,9 @@ def load() -> ctypes.CDLL:
     F = ctypes.c_float
     lib.kq_softmax_rows.argtypes = [P, I32, I64, F, F, P, P, SZ, P]
     lib.kq_speculative_decide.argtypes = [I32, P, I64, P, P, P, P, P, P]
+    lib.kq_staged_bytes_rows.argtypes = [I64, I32]
+    lib.kq_staged_bytes_rows.restype = SZ
+    lib.kq_verify_tree_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, P, P, SZ, P]
     lib.kq_tiled_bytes_fmt.argtypes = [I32, I64, I64]
     lib.kq_tiled_bytes_fmt.restype = SZ
     lib.kq_tile_weights_fmt.argtypes = [I32, P, I64, I64, P, SZ, P]
@@ -112,7 +115,7 @@ def load() -> ctypes.CDLL:
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
-                 "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt"):
+                 "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -131,8 +134,8 @@ def workspace_bytes(n: int, k: int, m: int) -> int:
     return int(load().kq_workspace_bytes(n, k, m))
 
 
-def staged_bytes(k: int) -> int:
-    return int(load().kq_staged_bytes(k))
+def staged_bytes(k: int, m: int = 16) -> int:
+    return int(load().kq_staged_bytes_rows(k, m))
 
 
 def scratch_bytes(n: int, k: int) -> int:
@@ -294,7 +297,7 @@ def stage_rows(x, staged=None, stream=None):
     torch = _torch()
     m, k = int(x.shape[0]), int(x.shape[1])
     if staged is None:
-        staged = alloc_workspace(staged_bytes(k), x.device)
+        staged = alloc_workspace(staged_bytes(k, m), x.device)
     _check(load().kq_stage_rows(_dev_ptr(x, "x", torch.float32), m, k, _dev_ptr(staged, "staged"),
                                 staged.numel(), _stream_handle(stream)), "kq_stage_rows")
     return staged
@@ -386,6 +389,34 @@ def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scrat
         _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
         _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_verify_staged")
     return am, acc, lg
+
+
+def verify_tree_staged(w, n: int, k: int, staged, parent: Sequence[int], token: Sequence[int], scratch,
+                       want_logits=False, want_path=True, stream=None, out=None, layout=LAYOUT_ROWS):
+    """Token-tree verify of m = len(parent) nodes (kq_verify_tree_staged):
+    returns (argmax[m], accept[2] = {accepted, next_token}, path[m] or None,
+    logits [m, n] or None), device int32 / fp32 tensors."""
+    torch = _torch()
+    m = len(parent)
+    if len(token) != m:
+        raise ValueError("parent and token need one entry per node")
+    par = (ctypes.c_int32 * max(1, m))(*[int(v) for v in parent])
+    tok = (ctypes.c_int32 * max(1, m))(*[int(v) for v in token])
+    dev = w.device
+    if out is None:
+        am = torch.empty(m, dtype=torch.int32, device=dev)
+        acc = torch.empty(2, dtype=torch.int32, device=dev)
+        path = torch.full((m,), -1, dtype=torch.int32, device=dev) if want_path else None
+        lg = torch.empty((m, n), dtype=torch.float32, device=dev) if want_logits else None
+    else:
+        am, acc, path, lg = out
+    _check(load().kq_verify_tree_staged(
+        _dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"), m, par, tok,
+        _dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
+        _dev_ptr(path, "path", torch.int32) if path is not None else None,
+        _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
+        _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_verify_tree_staged")
+    return am, acc, path, lg
 
 
 # ------------------------------------------------------------------- chains

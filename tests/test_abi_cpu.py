@@ -50,13 +50,18 @@ def test_status_strings():
 def test_sizes_and_geometry():
     assert kq.workspace_bytes(512, 1000, 4) == 0       # k not a multiple of 256
     assert kq.workspace_bytes(512, 1024, 0) == 0
-    assert kq.workspace_bytes(512, 1024, 17) == 0
+    assert kq.workspace_bytes(512, 1024, 65) == 0      # at most 64 rows
     assert kq.workspace_bytes(0, 1024, 1) == 0
     assert kq.staged_bytes(1024) == 4 * 16960
     assert kq.staged_bytes(6656) == 26 * 16960
+    # more than 16 rows: 2 or 4 sixteen-row slices per block
+    assert [kq.staged_bytes(1024, m) for m in (1, 16, 17, 32, 33, 64)] == [4 * 16960 * s for s in (1, 1, 2, 2, 4, 4)]
+    assert kq.staged_bytes(1024, 65) == 0 and kq.staged_bytes(1024, 0) == 0
+    assert kq.workspace_bytes(512, 1024, 64) - kq.workspace_bytes(512, 1024, 16) == 3 * 4 * 16960
     for n, k in [(512, 1024), (6656, 6656), (6656, 33280), (131072, 6656), (17920, 6656), (6656, 17920), (1, 256),
                  (35840, 6656)]:
         assert kq.workspace_bytes(n, k, 1) == kq.workspace_bytes(n, k, 16) > 0
+        assert kq.workspace_bytes(n, k, 64) > kq.workspace_bytes(n, k, 16)
         waves, tpw, nwg, units = kq.launch_geometry(n, k)
         assert waves in (4, 8, 12) and tpw in (1, 2)
         assert units == -(-n // (16 * waves * tpw)) * (k // 256)
@@ -88,7 +93,7 @@ def test_gemv_argument_errors():
     assert _call_gemv(out=None) == NULL
     assert _call_gemv(ws=None) == NULL
     assert _call_gemv(m=0) == SHAPE
-    assert _call_gemv(m=17) == SHAPE
+    assert _call_gemv(m=65) == SHAPE
     assert _call_gemv(k=1000) == SHAPE
     assert _call_gemv(k=0) == SHAPE
     assert _call_gemv(n=0) == SHAPE
@@ -121,7 +126,7 @@ def test_verify_argument_errors():
     assert _call_verify(am=None) == NULL
     assert _call_verify(acc=None) == NULL
     assert _call_verify(draft=None) == NULL
-    assert _call_verify(m=17, draft=tuple(range(16))) == SHAPE
+    assert _call_verify(m=65, draft=tuple(range(64))) == SHAPE
     assert _call_verify(draft=(1, 2, 512)) == TOKEN
     assert _call_verify(draft=(-1, 2, 3)) == TOKEN
     assert _call_verify(wsb=100) == WS
@@ -151,7 +156,7 @@ def test_draft_block_argument_errors():
     assert st(FAKE, 7, n, k, FAKE, 3, FAKE, None, FAKE, sb, None) == SHAPE
     assert st(FAKE, 0, n, k, None, 3, FAKE, None, FAKE, sb, None) == NULL
     assert st(FAKE, 0, n, k, FAKE, 3, None, None, FAKE, sb, None) == NULL
-    assert st(FAKE, 0, n, k, FAKE, 15, FAKE, None, FAKE, sb - 1, None) == WS
+    assert st(FAKE, 0, n, k, FAKE, 15, FAKE, None, FAKE, 256, None) == WS
     with pytest.raises(ValueError):
         kq.draft_block_argmax(None, n, k, None, 5)
     assert kq.DRAFT_VERIFY_LENGTHS == (3, 7, 15)
@@ -177,7 +182,7 @@ def test_staged_argument_errors():
     assert lib.kq_stage_rows(FAKE, 4, 1024, FAKE, 100, None) == WS
     sb = kq.scratch_bytes(512, 1024)
     assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, None, 4, FAKE, FAKE, sb, None) == NULL
-    assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, FAKE, 4, FAKE, FAKE, sb - 1, None) == WS
+    assert lib.kq_gemv_staged(FAKE, 0, 512, 1024, FAKE, 4, FAKE, FAKE, 256, None) == WS
     assert lib.kq_gemv_staged(FAKE, 7, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
     assert lib.kq_gemv_staged(FAKE, -1, 512, 1024, FAKE, 4, FAKE, FAKE, sb, None) == SHAPE
     d = (ctypes.c_int32 * 3)(0, 1, 600)
@@ -201,7 +206,7 @@ def test_grouped_argument_errors():
         assert call(wp, layout, 0, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
         assert call(wp, layout, 9, n, k, FAKE, m, lp, FAKE, sb, None) == SHAPE
         assert call(wp, layout, 3, n, 100, FAKE, m, lp, FAKE, sb, None) == SHAPE
-        assert call(wp, layout, 3, n, k, FAKE, m, lp, FAKE, sb - 1, None) == WS
+        assert call(wp, layout, 3, n, k, FAKE, m, lp, FAKE, 256, None) == WS
         assert call(None, layout, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
         bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
         assert call(bad, layout, 3, n, k, FAKE, m, lp, FAKE, sb, None) == NULL
@@ -346,3 +351,26 @@ def test_chain_scratch_init_argument_errors_before_any_hip_call():
     assert lib.kq_chain_scratch_init(None, FAKE, 1 << 30, None) == NULL
     assert lib.kq_chain_scratch_init(ctypes.byref(pl), None, 1 << 30, None) == NULL
     assert lib.kq_chain_scratch_init(ctypes.byref(pl), FAKE, 1 << 30, None) == SHAPE  # inconsistent scratch_bytes
+
+
+def test_tree_verify_argument_errors_before_any_hip_call():
+    lib = kq.load()
+    n, k = 512, 1024
+    sb = kq.scratch_bytes(n, k)
+
+    def call(m=5, parent=(-1, 0, 0, 1, 2), token=(0, 1, 2, 3, 4), argmax=FAKE, acc=FAKE, path=None,
+             layout=kq.LAYOUT_TILED16, scratch_bytes=sb):
+        par = (ctypes.c_int32 * max(1, len(parent)))(*parent) if parent is not None else None
+        tok = (ctypes.c_int32 * max(1, len(token)))(*token) if token is not None else None
+        return lib.kq_verify_tree_staged(FAKE, layout, n, k, FAKE, m, par, tok, argmax, acc, path, None, FAKE,
+                                         scratch_bytes, None)
+    assert call(parent=None) == NULL and call(token=None) == NULL
+    assert call(argmax=None) == NULL and call(acc=None) == NULL
+    assert call(parent=(0, 0, 0, 1, 2)) == SHAPE          # the root has no parent
+    assert call(parent=(-1, 0, 3, 1, 2)) == SHAPE         # a parent after its child
+    assert call(parent=(-1, 0, 0, 1, -1)) == SHAPE
+    assert call(token=(0, 1, 2, 3, n)) == TOKEN           # token outside [0, n)
+    assert call(token=(0, 1, -2, 3, 4)) == TOKEN
+    assert call(m=65, parent=(-1,) + tuple(range(64)), token=(0,) * 65) == SHAPE
+    assert call(layout=7) == SHAPE
+    assert call(scratch_bytes=256) == WS

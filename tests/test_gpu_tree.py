@@ -1,0 +1,152 @@
+"""GPU parity of calls with more than 16 activation rows (2 or 4 sixteen-row
+slices in one pass over the weights) and of the token-tree verify
+(kq_verify_tree_staged) against the oracle: every logit on ragged shapes,
+slices bitwise equal to 16-row calls, argmax with flags at the LM-head size
+for 24 to 64 nodes, and the tree walk against the oracle's."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.parity import check_argmax, check_logits, log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import quant_verify_gemv_amd as kq
+    kq.load()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return kq
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("fmt,layout", [("q4k", "rows"), ("q4k", "tiled"), ("q6k", "tiled")])
+@pytest.mark.parametrize("n,k", [(300, 1024), (1000, 2304), (129, 6656)])
+def test_more_rows_every_logit(kq, fmt, layout, n, k):
+    w = synthetic.kquant_matrix(fmt, n, k, 700 + n)
+    x = synthetic.activations(64, k, 710 + k)
+    wd = to_dev(w)
+    if layout == "tiled":
+        wd = kq.tile_weights(wd, n, k, fmt=fmt)
+    lay = kq.FORMATS[fmt][0] if layout == "tiled" else kq.LAYOUT_ROWS
+    sc = kq.new_scratch(n, k, DEV)
+    L, A = oracle.gemv_rows(w, k, x, fmt=fmt)
+    for m in (64, 48, 33, 32, 24, 17):
+        log(f"rows: {fmt} {layout} n={n} k={k} m={m}")
+        st = kq.stage_rows(to_dev(x[:m]))
+        G = kq.gemv_staged(wd, n, k, st, m, sc, layout=lay)
+        torch.cuda.synchronize()
+        r = check_logits(G.cpu().numpy(), L[:m], A[:m], what=f"{fmt} {layout} n={n} k={k} m={m}")
+        log(f"rows: m={m} max |d|/tol = {r:.3g}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+def test_slices_bitwise_equal_to_sixteen_row_calls(kq, fmt):
+    """Each 16-row slice of a 64-row (and 32-row) call equals the 16-row call
+    on the same rows bit for bit: same unit split, same per-slice arithmetic."""
+    n, k = 2000, 6656
+    w = synthetic.kquant_matrix(fmt, n, k, 91)
+    x = synthetic.activations(64, k, 92)
+    wt = kq.tile_weights(to_dev(w), n, k, fmt=fmt)
+    lay = kq.FORMATS[fmt][0]
+    sc = kq.new_scratch(n, k, DEV)
+    g64 = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x)), 64, sc, layout=lay).cpu().numpy()
+    g32 = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x[:32])), 32, sc, layout=lay).cpu().numpy()
+    for s in range(4):
+        g16 = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x[16 * s:16 * s + 16])), 16, sc,
+                             layout=lay).cpu().numpy()
+        assert np.array_equal(g64[16 * s:16 * s + 16], g16), f"slice {s} of 64 rows"
+        if s < 2:
+            assert np.array_equal(g32[16 * s:16 * s + 16], g16), f"slice {s} of 32 rows"
+    again = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x)), 64, sc, layout=lay).cpu().numpy()
+    assert np.array_equal(g64, again), "not deterministic"
+
+
+def make_tree(rng, m, am, n_vocab, p_follow=0.6):
+    """Random tree of m nodes (parent within the 6 previous nodes); a child
+    takes its parent's target argmax with probability p_follow (once per
+    sibling set), so the walk reaches depth."""
+    parent = [-1] + [int(rng.integers(max(0, j - 6), j)) for j in range(1, m)]
+    token = [0] * m
+    for j in range(1, m):
+        used = {token[c] for c in range(1, j) if parent[c] == parent[j]}
+        want = int(am[parent[j]])
+        if want not in used and rng.random() < p_follow:
+            token[j] = want
+        else:
+            t = int(rng.integers(n_vocab))
+            while t in used or t == want:
+                t = int(rng.integers(n_vocab))
+            token[j] = t
+    return parent, token
+
+
+def test_tree_verify_lm_head(kq):
+    """Trees of 24, 32, 48 and 64 nodes on the LM head (6,656 -> 131,072,
+    Q4_K tiled): argmax of every node row against the oracle (flags), the
+    walk equal to the oracle's walk on the GPU's argmax always, and on the
+    oracle's argmax when no row is flagged; the path output lists the nodes
+    moved through; a chain gives the linear verify's result; the Q6_K head
+    at 64 nodes too."""
+    h = synthetic.LM_HEAD
+    n, k = h["n"], h["k"]
+    x = synthetic.activations(64, k, 4242)
+    log("tree: oracle over 64 rows of the LM head")
+    w = synthetic.q4k_matrix(n, k, h["seed"])
+    L, A = oracle.gemv_rows(w, k, x)
+    o_am, o_nc = oracle.argmax_flags(L, A)
+    log(f"tree: oracle flagged rows {int(np.sum(o_nc > 0))}")
+    wt = kq.tile_weights(to_dev(w), n, k)
+    sc = kq.new_scratch(n, k, DEV)
+    rng = np.random.default_rng(11)
+    for m in (24, 32, 48, 64):
+        st = kq.stage_rows(to_dev(x[:m]))
+        for trial in range(3):
+            parent, token = make_tree(rng, m, o_am[:m], n)
+            am, acc, path, lg = kq.verify_tree_staged(wt, n, k, st, parent, token, sc, want_logits=(trial == 0),
+                                                      layout=kq.LAYOUT_TILED16)
+            torch.cuda.synchronize()
+            am, acc, path = am.cpu().numpy(), acc.cpu().numpy(), path.cpu().numpy()
+            if lg is not None:
+                r = check_logits(lg.cpu().numpy(), L[:m], A[:m], what=f"tree logits m={m}")
+                log(f"tree: m={m} logits max |d|/tol = {r:.3g}")
+            check_argmax(am, L[:m], A[:m], what=f"tree m={m} trial {trial}")
+            g_acc, g_nxt, g_path = oracle.tree_accept(parent, token, am)
+            assert (int(acc[0]), int(acc[1])) == (g_acc, g_nxt), f"m={m} trial {trial}: walk != oracle walk on GPU argmax"
+            assert list(path[:g_acc]) == g_path and np.all(path[g_acc:] == -1)
+            if not np.any(o_nc[:m] > 0):
+                assert oracle.tree_accept(parent, token, o_am[:m])[:2] == (g_acc, g_nxt)
+            log(f"tree: m={m} trial {trial}: accepted {g_acc}, path {g_path}")
+        # a chain is the linear verify
+        draft = [int(t) for t in o_am[:m - 1]]
+        draft[min(m - 2, 20)] = (draft[min(m - 2, 20)] + 1) % n
+        am_t, acc_t, _, _ = kq.verify_tree_staged(wt, n, k, st, [-1] + list(range(m - 1)), [0] + draft, sc,
+                                                  layout=kq.LAYOUT_TILED16)
+        am_l, acc_l, _ = kq.verify_staged(wt, n, k, st, m, draft, sc, layout=kq.LAYOUT_TILED16)
+        torch.cuda.synchronize()
+        assert np.array_equal(am_t.cpu().numpy(), am_l.cpu().numpy())
+        assert np.array_equal(acc_t.cpu().numpy(), acc_l.cpu().numpy())
+        assert tuple(acc_l.cpu().numpy()) == oracle.accept(draft, am_l.cpu().numpy())
+    del wt
+    log("tree: Q6_K head, 64 nodes")
+    w6 = synthetic.q6k_matrix(n, k, h["seed"])
+    rows = np.arange(n)
+    L6, A6 = oracle.gemv_rows(w6, k, x, fmt="q6k")
+    o6, n6 = oracle.argmax_flags(L6, A6)
+    wt6 = kq.tile_weights(to_dev(w6), n, k, fmt="q6k")
+    st = kq.stage_rows(to_dev(x))
+    parent, token = make_tree(rng, 64, o6, n)
+    am, acc, path, _ = kq.verify_tree_staged(wt6, n, k, st, parent, token, sc, layout=kq.LAYOUT_Q6K_TILED16)
+    torch.cuda.synchronize()
+    am = am.cpu().numpy()
+    check_argmax(am, L6, A6, what="tree q6k m=64")
+    assert tuple(acc.cpu().numpy()) == oracle.tree_accept(parent, token, am)[:2]
+    del rows
