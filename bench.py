@@ -366,6 +366,8 @@ def config_timings(stack, torch, calls=50):
     out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us)
     out["stochastic_lm_head_m16"] = stochastic_timing(stack, torch, time_calls)
     out.update(kquant_timings(stack, torch, time_calls))
+    tree = out["tree_verify_lm_head"]
+    tree["m64_over_lm_head_m16"] = round(tree["m64"]["us_per_call"] / out["lm_head_verify_m16"]["us_per_call"], 4)
     out["launch"] = "hipgraph, back-to-back"
     torch.cuda.synchronize()
     return out
@@ -376,7 +378,9 @@ def kquant_timings(stack, torch, time_calls):
     6,656 x 6,656 product at M = 1 and 16 over 16 rotating copies of each
     format, and the LM-head verify (6,656 -> 131,072, M = 16, k = 15) with
     Q6_K weights (the output layer's usual k-quant). Weight bytes per call
-    are the format's own (176 or 210 per 256 weights)."""
+    are the format's own (176 or 210 per 256 weights). Then the token-tree
+    verify of 24, 32, 48 and 64 nodes on the resident Q4_K LM head (rows/s
+    counts the tree's nodes)."""
     kq = stack.kq
     dev = stack.dev
     out = {}
@@ -411,6 +415,22 @@ def kquant_timings(stack, torch, time_calls):
                                                  out=(stack.am, stack.acc, None), layout=kq.LAYOUT_Q6K_TILED16))
     out["lm_head_verify_m16_q6k"] = rate(h.n * (h.k // 256) * 210, 16, us)
     del w6
+    # token-tree verify on the resident Q4_K head: a tree of m nodes (parent
+    # within the previous 6 nodes, seeded tokens), all nodes in one pass
+    g = np.random.default_rng(77)
+    x64 = torch.from_numpy(synthetic.activations(64, h.k, 4242)).to(dev)
+    tree = {}
+    for m in (24, 32, 48, 64):
+        parent = [-1] + [int(g.integers(max(0, j - 6), j)) for j in range(1, m)]
+        token = [0] + [int(t) for t in g.integers(0, h.n, m - 1)]
+        st = kq.stage_rows(x64[:m])
+        am = torch.empty(m, dtype=torch.int32, device=dev)
+        acc = torch.empty(2, dtype=torch.int32, device=dev)
+        path = torch.empty(m, dtype=torch.int32, device=dev)
+        us = time_calls(lambda i: kq.verify_tree_staged(stack.w_head, h.n, h.k, st, parent, token, stack.head_scratch,
+                                                          out=(am, acc, path, None), layout=stack.layout))
+        tree[f"m{m}"] = rate(h.weight_bytes, m, us)
+    out["tree_verify_lm_head"] = tree
     torch.cuda.synchronize()
     return out
 
