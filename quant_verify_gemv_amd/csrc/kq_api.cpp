@@ -56,11 +56,13 @@ static Shape pick_shape(int64_t n, int count, int fmt, int ms) {
   return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI, KQ_GEOM_DEPTH};
 #endif
   const int64_t rows = n * count;
-  // More than 16 activation rows (2 or 4 slices per tile): one tile per
-  // wave, and the LDS ring shrinks to 4 or 2 blocks (every block now holds
-  // 2 or 4 staged slices) so that it still fits a CU's LDS; at 4 slices,
-  // three weight register sets (the slices' accumulators need the room).
-  if (ms > 1) return ms == 4 ? Shape{8, 1, 1, 1, 3} : Shape{8, 1, 1, 2, 4};
+  // More than 16 activation rows (2 or 4 slices per tile): the LDS ring
+  // shrinks to 4 or 2 blocks (every block now holds 2 or 4 staged slices)
+  // so that it still fits a CU's LDS, with three weight register sets. At 2
+  // slices two tiles per wave (each activation read from LDS feeds 32 weight
+  // rows: 20 % faster than one tile on the LM head); at 4 slices one tile
+  // (two would spill).
+  if (ms > 1) return ms == 4 ? Shape{8, 1, 1, 1, 3} : Shape{8, 2, 1, 2, 3};
   // Q5_K and Q6_K keep two more registers per tile and register set, so
   // they run one tile per wave (12 waves from 32,768 rows, else 8)
   if (fmt != kFmtQ4) return rows >= 32768 ? Shape{12, 1, 1, 4, 4} : Shape{8, 1, 1, 4, 4};

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   static_assert(FMT == kFmtQ4 || !CHAIN, "chains run Q4_K");
   // MS 16-row activation slices: every unpacked weight operand feeds the
   // MFMAs of all MS slices, so the weights are read once for 16 MS rows
-  static_assert(MS == 1 || (!CHAIN && T == 1), "more than 16 rows: single launches, one tile per wave");
+  static_assert(MS == 1 || !CHAIN, "more than 16 rows: single launches");
   constexpr int kRS = 16 * MS;  // activation rows per call at most
   constexpr unsigned kTB = 16u * (unsigned)fmt_block_bytes(FMT);  // tiled record bytes
   // D weight register sets: the weights of unit i + D - 1 are loaded while
@@ -1568,9 +1568,9 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(kFmtQ5, 12, 1, 4, 4, 1)
     KQ_CASE(kFmtQ6, 8, 1, 4, 4, 1)
     KQ_CASE(kFmtQ6, 12, 1, 4, 4, 1)
-    KQ_CASE(kFmtQ4, 8, 1, 2, 4, 2)
+    KQ_CASE(kFmtQ4, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ4, 8, 1, 1, 3, 4)
-    KQ_CASE(kFmtQ6, 8, 1, 2, 4, 2)
+    KQ_CASE(kFmtQ6, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ6, 8, 1, 1, 3, 4)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;

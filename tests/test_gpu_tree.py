@@ -50,8 +50,11 @@ def test_more_rows_every_logit(kq, fmt, layout, n, k):
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k"])
 def test_slices_bitwise_equal_to_sixteen_row_calls(kq, fmt):
-    """Each 16-row slice of a 64-row (and 32-row) call equals the 16-row call
-    on the same rows bit for bit: same unit split, same per-slice arithmetic."""
+    """Each 16-row slice of a 64-row call equals the 16-row call on the same
+    rows bit for bit (both cut the work into the same 128-row units, and
+    each slice's arithmetic is the 16-row call's); 32-row calls run
+    256-row units, so their slices match the 16-row calls within the
+    oracle's tolerance."""
     n, k = 2000, 6656
     w = synthetic.kquant_matrix(fmt, n, k, 91)
     x = synthetic.activations(64, k, 92)
@@ -60,12 +63,13 @@ def test_slices_bitwise_equal_to_sixteen_row_calls(kq, fmt):
     sc = kq.new_scratch(n, k, DEV)
     g64 = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x)), 64, sc, layout=lay).cpu().numpy()
     g32 = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x[:32])), 32, sc, layout=lay).cpu().numpy()
+    rows = np.array([0, 1, 127, 128, 255, 256, 1999])
+    L, A = oracle.gemv_rows(w, k, x[:32], rows=rows, fmt=fmt)
+    check_logits(g32[:, rows], L, A, what=f"{fmt} 32 rows")
     for s in range(4):
         g16 = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x[16 * s:16 * s + 16])), 16, sc,
                              layout=lay).cpu().numpy()
         assert np.array_equal(g64[16 * s:16 * s + 16], g16), f"slice {s} of 64 rows"
-        if s < 2:
-            assert np.array_equal(g32[16 * s:16 * s + 16], g16), f"slice {s} of 32 rows"
     again = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x)), 64, sc, layout=lay).cpu().numpy()
     assert np.array_equal(g64, again), "not deterministic"
 
