@@ -63,9 +63,11 @@ static Shape pick_shape(int64_t n, int count, int fmt, int ms) {
   // rows: 20 % faster than one tile on the LM head); at 4 slices one tile
   // (two would spill).
   if (ms > 1) return ms == 4 ? Shape{8, 1, 1, 1, 3} : Shape{8, 2, 1, 2, 3};
-  // Q5_K and Q6_K keep two more registers per tile and register set, so
-  // they run one tile per wave (12 waves from 32,768 rows, else 8)
-  if (fmt != kFmtQ4) return rows >= 32768 ? Shape{12, 1, 1, 4, 4} : Shape{8, 1, 1, 4, 4};
+  // Q5_K and Q6_K (two more registers per tile and register set): two
+  // tiles per wave from 131,072 rows (7-9 % faster than 12 one-tile waves on
+  // the LM head), 12 waves of one tile from 32,768 rows, else 8
+  if (fmt != kFmtQ4)
+    return rows >= 131072 ? Shape{8, 2, 1, 4, 4} : rows >= 32768 ? Shape{12, 1, 1, 4, 4} : Shape{8, 1, 1, 4, 4};
   if (rows >= 131072) return {8, 2, 1, 4, 4};
   if (rows >= 32768) return {12, 1, 1, 4, 4};
   return {8, 1, 1, 4, 4};

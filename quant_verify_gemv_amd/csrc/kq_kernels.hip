@@ -49,27 +49,26 @@ __device__ __forceinline__ half8 make_h8(unsigned a, unsigned b, unsigned c, uns
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4 *)p; }
 
-// a * k.x + k.y on both halves of a: one v_pk_fma_f16 whose op_sel
-// modifiers broadcast the two halves of k, so each {scale, offset} pair
-// occupies a single register.
+// a * k.x + k.y on both halves of a: the compiler makes it one
+// v_pk_fma_f16 whose op_sel modifiers broadcast the two halves of k, so each
+// {scale, offset} pair occupies a single register. (Compiler builtins, not
+// inline asm, for every value that feeds an MFMA: the compiler inserts the
+// wait states between a VALU write and an MFMA read only for instructions
+// it can see; an inline-asm product feeding the Q6_K operand once read a
+// stale register under a two-tile schedule.)
 __device__ __forceinline__ half2v fma_bcast(half2v a, half2v k) {
-  half2v r;
-  asm("v_pk_fma_f16 %0, %1, %2, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(k));
-  return r;
+  return __builtin_elementwise_fma(a, half2v{k[0], k[0]}, half2v{k[1], k[1]});
 }
 
-// a * b and a * b - c on fp16 pairs, rounded exactly once each (v_pk_mul_f16,
-// v_pk_fma_f16): the Q6_K operand split needs the rounded product and its
-// exact remainder.
+// a * b and a * b - c on fp16 pairs, rounded exactly once each (v_pk_mul_f16
+// with contraction off, v_pk_fma_f16): the Q6_K operand split needs the
+// rounded product and its exact remainder.
 __device__ __forceinline__ half2v pk_mul(half2v a, half2v b) {
-  half2v r;
-  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+#pragma clang fp contract(off)
+  return a * b;
 }
 __device__ __forceinline__ half2v pk_fma_sub(half2v a, half2v b, half2v c) {
-  half2v r;
-  asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_fma(a, b, -c);
 }
 
 // (h >> from) & mask, moved to start at bit `to` (from, to compile-time).
@@ -1566,8 +1565,10 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(kFmtQ4, 4, 2, 1, 3, 1)
     KQ_CASE(kFmtQ5, 8, 1, 4, 4, 1)
     KQ_CASE(kFmtQ5, 12, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ5, 8, 2, 4, 4, 1)
     KQ_CASE(kFmtQ6, 8, 1, 4, 4, 1)
     KQ_CASE(kFmtQ6, 12, 1, 4, 4, 1)
+    KQ_CASE(kFmtQ6, 8, 2, 4, 4, 1)
     KQ_CASE(kFmtQ4, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ4, 8, 1, 1, 3, 4)
     KQ_CASE(kFmtQ6, 8, 2, 2, 3, 2)
