@@ -73,6 +73,29 @@ def test_one_hot_rows_extract_weights(kq, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_one_hot_rows_at_lm_head_shape(kq, fmt):
+    """One-hot rows at the LM head's shape (131,072 rows: two tiles per
+    wave): every weight column bit-exact for Q6_K (one rounding for Q5_K).
+    A stale or wrong operand remainder in any tile shows here even when the
+    logits stay inside the tolerance."""
+    h = synthetic.LM_HEAD
+    n, k = h["n"], h["k"]
+    w = synthetic.kquant_matrix(fmt, n, k, 57)
+    cols = [0, 15, 16, 31, 255, 256, 1000, 2047, 3333, 4096, 5000, 6000, 6400, 6655, 100, 777]
+    x = np.zeros((16, k), dtype=np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    W, _ = oracle.gemv_rows(w, k, x, fmt=fmt)  # exact columns (fp64 products of exact weights by 1)
+    G = gpu_gemv(kq, fmt, w, n, k, x)
+    for i, c in enumerate(cols):
+        if fmt == "q6k":
+            bad = np.nonzero(G[i].astype(np.float64) != W[i])[0]
+            assert bad.size == 0, f"column {c}: {bad.size} rows differ, first {bad[:5]}"
+        else:
+            assert np.all(np.abs(G[i] - W[i]) <= 2.0 ** -24 * np.abs(W[i])), c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_extreme_fields(kq, fmt):
     """Blocks at the ends of every field's range: Q6_K scales -128 and 127
     with q = 0 and 63 (|sc (q - 32)| up to 4,096, the products that need the
