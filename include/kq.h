@@ -1,6 +1,9 @@
 /*
- * kq.h -- C ABI of libkq: the Q4_K batched speculative-verify step on
- * MI355X (gfx950).
+ * kq.h -- C ABI of libkq: the k-quant (Q4_K, Q5_K, Q6_K) batched
+ * speculative-verify step on MI355X (gfx950): the skinny products, the fused
+ * argmax and greedy accept (linear or over a token tree), the draft block's
+ * proposals, chains of dependent products in one launch, and the stochastic
+ * verify's probability rows and host decision.
  *
  * The operation (muser-book ch. 33 "Speculation: the local win and the
  * distributed verdict", section 33.1; ch. 8 "The DFlash draft", section 8.1):
@@ -30,8 +33,9 @@
  *    bytes) < 2^32 and kq_staged_bytes_rows(k, m) < 2^32 (the kernels
  *    address them with 32-bit offsets). Other shapes give KQ_ERR_SHAPE (size
  *    queries return 0).
- *  - Layouts: w is [n][k/256] blocks of 144 bytes, row-major, 16-byte aligned;
- *    x is fp32 [m][k] row-major, 16-byte aligned; logits fp32 [m][n].
+ *  - Layouts: w is [n][k/256] Q4_K blocks of 144 bytes, row-major, 16-byte
+ *    aligned, or one of the tiled layouts below; x is fp32 [m][k]
+ *    row-major, 16-byte aligned; logits fp32 [m][n].
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
  *    library allocates nothing and keeps no global mutable state.
  *  - Every call is enqueued on `stream` (a hipStream_t; NULL = default
@@ -44,8 +48,10 @@
  *    calls sharing a workspace must be ordered (e.g. the same stream).
  *  - Numerics: fp32 accumulation. |logit - exact| <= 1e-4 * sum_k |w_k x_k|
  *    for finite inputs with |dmin| * 63 <= 65504; results are bitwise
- *    deterministic and row i of an m-row call equals the 1-row call on x[i].
- *    There is no CPU or alternate path.
+ *    deterministic, and for m <= 16 row i of an m-row call equals the 1-row
+ *    call on x[i] bit for bit (calls of more than 16 rows may cut the work
+ *    differently; they meet the same bound). There is no CPU or alternate
+ *    path.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -79,7 +85,7 @@ typedef int kq_status;
 /* Measurement helper, not part of the verify step: reads every byte of a
  * device buffer once (16-byte loads over the whole GPU) and writes one
  * XOR-fold word per workgroup to `sink`, so a caller can time the HBM read
- * rate the weight stream could reach on this device (bench.py reports it
+ * rate the weight stream could reach on this device (a benchmark reports it
  * next to the roofline).
  *  buf   device, `bytes` bytes, 16-byte aligned, bytes % 16 == 0 (else KQ_ERR_SHAPE)
  *  sink  device, >= kq_stream_probe_sink_bytes() bytes (written; contents
@@ -200,7 +206,9 @@ size_t kq_tiled_bytes_fmt(int layout, int64_t n, int64_t k);
 kq_status kq_tile_weights_fmt(int layout, const void *w_rows, int64_t n, int64_t k,
                               void *w_tiled, size_t tiled_bytes, void *stream);
 
-/* kq_gemv_rows on staged activations.
+/* kq_gemv_rows on staged activations (every staged call: `staged` comes from
+ * kq_stage_rows with the same m, since its size and slice layout depend on
+ * m).
  *  layout   KQ_LAYOUT_ROWS or KQ_LAYOUT_TILED16 (the layout of w_q4k), or
  *           KQ_LAYOUT_Q5K_TILED16 / KQ_LAYOUT_Q6K_TILED16 (w_q4k is then a
  *           tiled Q5_K or Q6_K matrix; same staged activations)
