@@ -599,10 +599,24 @@ def cpu_baseline(target_s):
         if spent + float(np.mean(layer_times)) > target_s:
             break
     t_step = synthetic.LAYERS * float(np.mean(layer_times)) + t_head
+    # one core: a 6,656 x 6,656 matrix at 1 thread and at all threads; the
+    # step scales by that ratio
+    g0 = mats[3]
+    w0 = synthetic.q4k_matrix(g0.n, g0.k, g0.seed)
+    t_all = time.perf_counter()
+    oracle.gemv_rows(w0, g0.k, xs[g0.k], threads=threads)
+    t_all = time.perf_counter() - t_all
+    t_one = time.perf_counter()
+    oracle.gemv_rows(w0, g0.k, xs[g0.k], threads=1)
+    t_one = time.perf_counter() - t_one
+    t_step1 = t_step * t_one / t_all
     return {"value": round(16.0 / t_step, 4), "unit": "verify rows/s", "cores": threads, "kind": "oracle",
-            "step_s_extrapolated": round(t_step, 3), "sample_s": round(spent, 2),
+            "step_s_extrapolated": round(t_step, 3), "sample_s": round(spent + t_all + t_one, 2),
             "sample": f"LM head in full + {len(layer_times)} of {synthetic.LAYERS} stack layers in full "
-                      f"(M=16, same bytes as the GPU); step = {synthetic.LAYERS} x mean layer time + head"}
+                      f"(M=16, same bytes as the GPU); step = {synthetic.LAYERS} x mean layer time + head",
+            "single_core": {"value": round(16.0 / t_step1, 5), "step_s_extrapolated": round(t_step1, 2),
+                            "sample": f"one {g0.n} x {g0.k} matrix at 1 thread ({t_one:.2f} s) and at {threads} "
+                                      f"({t_all:.3f} s); the step scaled by that ratio"}}
 
 
 def main():
