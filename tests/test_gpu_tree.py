@@ -74,6 +74,23 @@ def test_slices_bitwise_equal_to_sixteen_row_calls(kq, fmt):
     assert np.array_equal(g64, again), "not deterministic"
 
 
+@pytest.mark.parametrize("m", [40, 64])
+def test_grouped_launch_more_rows(kq, m):
+    """Three matrices on one staged block of more than 16 rows in one launch
+    (kq_gemv_staged_group): every logit of every member against the oracle."""
+    n, k, count = 1000, 2304, 3
+    ws = [synthetic.q4k_matrix(n, k, 820 + i) for i in range(count)]
+    x = synthetic.activations(m, k, 830)
+    wts = [kq.tile_weights(to_dev(w), n, k) for w in ws]
+    st = kq.stage_rows(to_dev(x))
+    gs = kq.new_group_scratch(n, k, count, DEV)
+    got = [g.cpu().numpy() for g in kq.gemv_staged_group(wts, n, k, st, m, gs, layout=kq.LAYOUT_TILED16)]
+    for i in range(count):
+        L, A = oracle.gemv_rows(ws[i], k, x, fmt="q4k")
+        r = check_logits(got[i], L, A, what=f"group m={m} member {i}")
+        log(f"group m={m} member {i}: max |d|/tol = {r:.3g}")
+
+
 def make_tree(rng, m, am, n_vocab, p_follow=0.6):
     """Random tree of m nodes (parent within the 6 previous nodes); a child
     takes its parent's target argmax with probability p_follow (once per
