@@ -259,6 +259,18 @@ kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k,
                            float *logits_or_null,
                            void *scratch, size_t scratch_bytes, void *stream);
 
+/* kq_verify_staged with the draft tokens in device memory (for drafts the
+ * GPU produced, e.g. kq_draft_block_argmax_staged's proposals: draft and
+ * verify then run on one stream with no host round trip).
+ *  draft_dev  device int32 [m-1], 4-byte aligned (may be NULL when m == 1);
+ *             read by the kernel, so the tokens are not range-checked on
+ *             the host: a token outside [0, n) never equals a row's argmax,
+ *             and so counts as a mismatch (it is only compared, never used
+ *             as an index). */
+kq_status kq_verify_staged_dev(const void *w, int layout, int64_t n, int64_t k, const void *staged, int m,
+                               const int32_t *draft_dev, int32_t *argmax, int32_t *accept_out,
+                               float *logits_or_null, void *scratch, size_t scratch_bytes, void *stream);
+
 /* Token-tree verify (ch. 33 "Speculation: the local win and the
  * distributed verdict", section 33.7: the hardware-aware token tree spends
  * the batch arithmetic a weight stream leaves idle on near-miss branches,

@@ -256,7 +256,8 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
                      const void *staged, int m, float *const *logits, bool verify,
                      const int32_t *draft_host, int32_t *argmax, int32_t *accept_out, int argmax_from,
                      int32_t *head_out, void *scratch, size_t scratch_bytes, const float *x_to_stage,
-                     void *stream, const int32_t *tree_parent = nullptr, int32_t *path_out = nullptr) {
+                     void *stream, const int32_t *tree_parent = nullptr, int32_t *path_out = nullptr,
+                     const int32_t *draft_dev = nullptr) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
   const int fmt = layout_fmt(layout);
   if (fmt < 0) return KQ_ERR_SHAPE;
@@ -266,7 +267,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
     if (!verify && (!logits || !logits[i])) return KQ_ERR_NULL;
   }
   if (verify && (!argmax || (!accept_out && argmax_from == 0))) return KQ_ERR_NULL;
-  if (verify && accept_out && m > 1 && !draft_host) return KQ_ERR_NULL;
+  if (verify && accept_out && m > 1 && !draft_host && !draft_dev) return KQ_ERR_NULL;
   if (!shape_ok(n, k, fmt) || !staged_ok(k, m)) return KQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i)
     if (!al(w[i], 16)) return KQ_ERR_ALIGN;
@@ -290,6 +291,9 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
     a.parent[0] = -1;
     a.tree = 1;
     a.path_out = path_out;
+  } else if (verify && accept_out && draft_dev) {
+    if (m > 1 && !al(draft_dev, 4)) return KQ_ERR_ALIGN;
+    a.draft_dev = draft_dev;  // read by the kernel; not validated on the host
   } else if (verify && accept_out) {
     for (int i = 0; i < m - 1; ++i) {
       if (draft_host[i] < 0 || (int64_t)draft_host[i] >= n) return KQ_ERR_TOKEN;
@@ -339,6 +343,15 @@ kq_status kq_verify_staged(const void *w_q4k, int layout, int64_t n, int64_t k, 
                            void *stream) {
   return run(&w_q4k, layout, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax, accept_out, 0,
              nullptr, scratch, scratch_bytes, nullptr, stream);
+}
+
+kq_status kq_verify_staged_dev(const void *w, int layout, int64_t n, int64_t k, const void *staged, int m,
+                               const int32_t *draft_dev, int32_t *argmax, int32_t *accept_out,
+                               float *logits_or_null, void *scratch, size_t scratch_bytes, void *stream) {
+  if (!argmax || !accept_out) return KQ_ERR_NULL;
+  if (m > 1 && !draft_dev) return KQ_ERR_NULL;
+  return run(&w, layout, 1, n, k, staged, m, &logits_or_null, true, nullptr, argmax, accept_out, 0, nullptr,
+             scratch, scratch_bytes, nullptr, stream, nullptr, nullptr, draft_dev);
 }
 
 kq_status kq_verify_tree_staged(const void *w, int layout, int64_t n, int64_t k, const void *staged, int m,

@@ -137,6 +137,7 @@ struct GemvLaunch {
   int32_t draft[kMaxTreeRows];   // linear: draft[i] judged by row i; tree: token of node i (i >= 1)
   int32_t parent[kMaxTreeRows];  // tree: parent of node i (i >= 1)
   int k_draft;                   // linear drafts (0: no linear accept)
+  const int32_t *draft_dev;      // linear, may be null: the k_draft tokens in device memory (else draft[])
   int tree;                      // 1: tree accept over m nodes
   int32_t *path_out;             // tree, may be null: the accepted path's nodes
   int verify;

@@ -1245,8 +1245,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     if (tid == 0) {
       if (a.head_out) a.head_out[0] = s_am[0];
       if (a.accept_out && !a.tree) {
+        // device drafts are only compared, never used as an index, so a
+        // token outside [0, n) is a mismatch
         int i = 0;
-        while (i < a.k_draft && a.draft[i] == s_am[i]) ++i;
+        while (i < a.k_draft && (a.draft_dev ? a.draft_dev[i] : a.draft[i]) == s_am[i]) ++i;
         a.accept_out[0] = i;
         a.accept_out[1] = s_am[i];
       }

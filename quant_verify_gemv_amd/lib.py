@@ -24,7 +24,8 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_draft_block_argmax_staged", "kq_stream_probe", "kq_stream_probe_sink_bytes",
             "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
             "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
-            "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged")
+            "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged",
+            "kq_verify_staged_dev")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -105,6 +106,7 @@ def load() -> ctypes.CDLL:
     F = ctypes.c_float
     lib.kq_softmax_rows.argtypes = [P, I32, I64, F, F, P, P, SZ, P]
     lib.kq_speculative_decide.argtypes = [I32, P, I64, P, P, P, P, P, P]
+    lib.kq_verify_staged_dev.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_staged_bytes_rows.argtypes = [I64, I32]
     lib.kq_staged_bytes_rows.restype = SZ
     lib.kq_verify_tree_staged.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, P, P, SZ, P]
@@ -115,7 +117,8 @@ def load() -> ctypes.CDLL:
                  "kq_gemv_staged", "kq_verify_staged", "kq_launch_geometry", "kq_gemv_staged_group",
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
-                 "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged"):
+                 "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged",
+                 "kq_verify_staged_dev"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -371,23 +374,32 @@ def draft_block_argmax_staged(w, n: int, k: int, staged, verify_length: int, scr
     return props, head
 
 
-def verify_staged(w, n: int, k: int, staged, m: int, draft: Sequence[int], scratch, want_logits=False,
+def verify_staged(w, n: int, k: int, staged, m: int, draft, scratch, want_logits=False,
                   stream=None, out=None, layout=LAYOUT_ROWS):
+    """The verify step on staged activations. `draft` is a sequence of m-1
+    host tokens (kq_verify_staged), or an int32 device tensor of m-1 tokens
+    (kq_verify_staged_dev: no host round trip, no host range check)."""
     torch = _torch()
+    on_device = hasattr(draft, "is_cuda") and draft.is_cuda
     if len(draft) != m - 1:
         raise ValueError(f"need m-1 = {m - 1} draft tokens, got {len(draft)}")
-    dr = (ctypes.c_int32 * max(1, m - 1))(*[int(t) for t in draft])
     if out is None:
         am = torch.empty(m, dtype=torch.int32, device=w.device)
         acc = torch.empty(2, dtype=torch.int32, device=w.device)
         lg = torch.empty((m, n), dtype=torch.float32, device=w.device) if want_logits else None
     else:
         am, acc, lg = out
-    _check(load().kq_verify_staged(
-        _dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"), m, dr,
-        _dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
-        _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
-        _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream)), "kq_verify_staged")
+    common = (_dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
+              _dev_ptr(lg, "logits", torch.float32) if lg is not None else None,
+              _dev_ptr(scratch, "scratch"), scratch.numel(), _stream_handle(stream))
+    if on_device:
+        dp = _dev_ptr(draft, "draft", torch.int32) if m > 1 else None
+        _check(load().kq_verify_staged_dev(_dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"),
+                                           m, dp, *common), "kq_verify_staged_dev")
+    else:
+        dr = (ctypes.c_int32 * max(1, m - 1))(*[int(t) for t in draft])
+        _check(load().kq_verify_staged(_dev_ptr(w, "w", torch.uint8), layout, n, k, _dev_ptr(staged, "staged"), m,
+                                       dr, *common), "kq_verify_staged")
     return am, acc, lg
 
 

@@ -374,3 +374,17 @@ def test_tree_verify_argument_errors_before_any_hip_call():
     assert call(m=65, parent=(-1,) + tuple(range(64)), token=(0,) * 65) == SHAPE
     assert call(layout=7) == SHAPE
     assert call(scratch_bytes=256) == WS
+
+
+def test_verify_staged_dev_argument_errors_before_any_hip_call():
+    lib = kq.load()
+    n, k, m = 512, 1024, 4
+    sb = kq.scratch_bytes(n, k)
+    v = lib.kq_verify_staged_dev
+    assert v(FAKE, 1, n, k, FAKE, m, FAKE, None, FAKE, None, FAKE, sb, None) == NULL
+    assert v(FAKE, 1, n, k, FAKE, m, FAKE, FAKE, None, None, FAKE, sb, None) == NULL
+    assert v(FAKE, 1, n, k, FAKE, m, None, FAKE, FAKE, None, FAKE, sb, None) == NULL   # drafts needed for m > 1
+    assert v(FAKE, 1, n, k, FAKE, m, FAKE + 2, FAKE, FAKE, None, FAKE, sb, None) == ALIGN
+    assert v(FAKE, 1, n, k, FAKE, 65, FAKE, FAKE, FAKE, None, FAKE, sb, None) == SHAPE
+    assert v(FAKE, 9, n, k, FAKE, m, FAKE, FAKE, FAKE, None, FAKE, sb, None) == SHAPE
+    assert v(FAKE, 1, n, k, FAKE, m, FAKE, FAKE, FAKE, None, FAKE, 256, None) == WS

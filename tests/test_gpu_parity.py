@@ -388,3 +388,51 @@ def test_tiled_lm_head_verify_and_group(kq):
     b = kq.gemv_staged_group(wts, n2, k2, st2, 16, gs, layout=kq.LAYOUT_TILED16)
     for u, v in zip(a, b):
         assert np.array_equal(u.cpu().numpy(), v.cpu().numpy())
+
+
+def test_device_drafts_and_draft_block_to_verify_on_device(kq):
+    """Draft tokens in device memory (kq_verify_staged_dev) give the host
+    path's result; tokens outside [0, n) count as mismatches; the draft
+    block's proposals (device) feed the verify with no host round trip."""
+    n, k, m = 3000, 2304, 16
+    w = synthetic.q4k_matrix(n, k, 61)
+    x = synthetic.activations(m, k, 62)
+    L, A = oracle.gemv_rows(w, k, x)
+    o_am, o_nc = oracle.argmax_flags(L, A)
+    wt = kq.tile_weights(to_dev(w), n, k)
+    st = kq.stage_rows(to_dev(x))
+    sc = kq.new_scratch(n, k, DEV)
+    rng = np.random.default_rng(63)
+    for trial in range(6):
+        d = [int(t) for t in synthetic.forced_draft(o_am[:m - 1], int(rng.integers(0, m)), n)]
+        am_h, acc_h, _ = kq.verify_staged(wt, n, k, st, m, d, sc, layout=kq.LAYOUT_TILED16)
+        acc_h = acc_h.cpu().numpy().copy()
+        dd = torch.tensor(d, dtype=torch.int32, device=DEV)
+        am_d, acc_d, _ = kq.verify_staged(wt, n, k, st, m, dd, sc, layout=kq.LAYOUT_TILED16)
+        torch.cuda.synchronize()
+        assert np.array_equal(am_h.cpu().numpy(), am_d.cpu().numpy())
+        assert np.array_equal(acc_h, acc_d.cpu().numpy()), trial
+        check_accept(acc_d.cpu().numpy()[0], acc_d.cpu().numpy()[1], d, am_d.cpu().numpy(), o_am, o_nc,
+                     what=f"device drafts trial {trial}")
+    # out-of-range device tokens are mismatches (compared, never used as an index)
+    for bad in (-1, n, n + 1000, -(1 << 30)):
+        d = [int(t) for t in o_am[:m - 1]]
+        d[5] = bad
+        am_d, acc_d, _ = kq.verify_staged(wt, n, k, st, m, torch.tensor(d, dtype=torch.int32, device=DEV), sc,
+                                          layout=kq.LAYOUT_TILED16)
+        torch.cuda.synchronize()
+        am_d = am_d.cpu().numpy()
+        assert tuple(acc_d.cpu().numpy()) == oracle.accept(d, am_d)
+    # draft block -> verify on one stream: the proposals of a 16-row block
+    # (rows 1..15) verified as the draft of the same block: all accepted
+    props, head = kq.draft_block_argmax_staged(wt, n, k, st, 15, sc, want_head=True, layout=kq.LAYOUT_TILED16)
+    am_b = torch.empty(16, dtype=torch.int32, device=DEV)
+    acc_b = torch.empty(2, dtype=torch.int32, device=DEV)
+    shifted = torch.empty(15, dtype=torch.int32, device=DEV)
+    shifted[0] = head[0]
+    shifted[1:] = props[:14]
+    kq.verify_staged(wt, n, k, st, 16, shifted, sc, out=(am_b, acc_b, None), layout=kq.LAYOUT_TILED16)
+    torch.cuda.synchronize()
+    a = am_b.cpu().numpy()
+    assert tuple(acc_b.cpu().numpy()) == (15, int(a[15]))
+    assert np.array_equal(a[1:16], props.cpu().numpy()) and int(a[0]) == int(head.cpu().numpy()[0])
