@@ -50,8 +50,9 @@
  *    for finite inputs with |dmin| * 63 <= 65504; results are bitwise
  *    deterministic, and for m <= 16 row i of an m-row call equals the 1-row
  *    call on x[i] bit for bit (calls of more than 16 rows may cut the work
- *    differently; they meet the same bound). There is no CPU or alternate
- *    path.
+ *    differently; they meet the same bound). A call of 33 to 64 rows equals
+ *    a 32-row call on rows 0-31 and a call on the remaining rows, bit for
+ *    bit. There is no CPU or alternate path.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -106,10 +107,13 @@ size_t kq_staged_bytes(int64_t k);
 
 /* Bytes of a staged activation block for m <= 64 rows of k columns (0 for
  * invalid arguments): (k/256) * s * 16,960 with s = 1, 2 or 4 sixteen-row
- * slices for m <= 16, <= 32, <= 64. Calls of more than 16 rows (the
- * token-tree verify, kq_verify_tree_staged, or a longer linear verify) run
- * every weight tile against all slices in the same pass, so the weights are
- * still read once per call. */
+ * slices for m <= 16, <= 32, <= 64. Calls of 17 to 32 rows (the token-tree
+ * verify, kq_verify_tree_staged, or a longer linear verify) run every
+ * weight tile against both slices in the same pass, so the weights are
+ * still read once per call. Calls of 33 to 64 rows make two passes (rows
+ * 0-31 at two slices, then the rest at one or two): a single pass at four
+ * slices is bound by the activation reads from LDS and was 5-15 % slower on
+ * MI355X at the LM head's size. */
 size_t kq_staged_bytes_rows(int64_t k, int m);
 
 /* Bytes of device scratch the *_staged calls need for an n x k matrix (in
@@ -274,11 +278,11 @@ kq_status kq_verify_staged_dev(const void *w, int layout, int64_t n, int64_t k, 
 /* Token-tree verify (ch. 33 "Speculation: the local win and the
  * distributed verdict", section 33.7: the hardware-aware token tree spends
  * the batch arithmetic a weight stream leaves idle on near-miss branches,
- * at 24, 32, 48 or 64 nodes). One pass over the weights scores all m nodes
- * (m <= 64; activation row i is node i's position), takes every row's
- * argmax (ties -> lowest index) and walks the tree: from the root (node 0),
- * move to a child whose token equals the current node's argmax (the lowest
- * index when siblings repeat a token) until none does.
+ * at 24, 32, 48 or 64 nodes). One pass over the weights (two above 32 nodes)
+ * scores all m nodes (m <= 64; activation row i is node i's position),
+ * takes every row's argmax (ties -> lowest index) and walks the tree: from
+ * the root (node 0), move to a child whose token equals the current node's
+ * argmax (the lowest index when siblings repeat a token) until none does.
  *  staged        kq_stage_rows of the m node rows (kq_staged_bytes_rows)
  *  parent_host   host int32 [m]: parent_host[0] = -1, parent_host[i] in
  *                [0, i) (parents before children), else KQ_ERR_SHAPE

@@ -56,13 +56,12 @@ static Shape pick_shape(int64_t n, int count, int fmt, int ms) {
   return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI, KQ_GEOM_DEPTH};
 #endif
   const int64_t rows = n * count;
-  // More than 16 activation rows (2 or 4 slices per tile): the LDS ring
-  // shrinks to 4 or 2 blocks (every block now holds 2 or 4 staged slices)
-  // so that it still fits a CU's LDS, with three weight register sets. At 2
-  // slices two tiles per wave (each activation read from LDS feeds 32 weight
-  // rows: 20 % faster than one tile on the LM head); at 4 slices one tile
-  // (two would spill).
-  if (ms > 1) return ms == 4 ? Shape{8, 1, 1, 1, 3} : Shape{8, 2, 1, 2, 3};
+  // Two activation slices (17 to 32 rows, or one pass of a larger call):
+  // the LDS ring shrinks to 4 blocks (every block now holds 2 staged
+  // slices) so that it still fits a CU's LDS, with three weight register
+  // sets and two tiles per wave (each activation read from LDS feeds 32
+  // weight rows: 20 % faster than one tile on the LM head).
+  if (ms > 1) return Shape{8, 2, 1, 2, 3};
   // Q5_K and Q6_K (two more registers per tile and register set): two
   // tiles per wave from 131,072 rows (7-9 % faster than 12 one-tile waves on
   // the LM head), 12 waves of one tile from 32,768 rows, else 8
@@ -139,13 +138,13 @@ size_t kq_staged_bytes_rows(int64_t k, int m) {
   return (size_t)(k / kQK) * (size_t)row_slices(m) * (size_t)kStageBytes;
 }
 
-// Scratch for `count` matrices in whichever format and slice count needs
-// the most.
+// Scratch for `count` matrices in whichever format and launch slice count
+// (1 or 2) needs the most.
 static size_t scratch_any_fmt(int64_t n, int64_t k, int count) {
   size_t t = 0;
   for (int f = kFmtQ4; f <= kFmtQ6; ++f) {
     if (!shape_ok(n, k, f)) continue;
-    for (int ms = 1; ms <= 4; ms *= 2) {
+    for (int ms = 1; ms <= 2; ++ms) {
       const size_t b = scratch_layout(n, k, count, f, ms).total;
       t = b > t ? b : t;
     }
@@ -273,9 +272,14 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
     if (!al(w[i], 16)) return KQ_ERR_ALIGN;
   if (!al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
   if (x_to_stage && !al(x_to_stage, 16)) return KQ_ERR_ALIGN;
+  // staged slices, and the slices of the launch (of each of the two
+  // launches of a call of 33 to 64 rows)
   const int ms = row_slices(m);
-  const ScratchLayout sl = scratch_layout(n, k, count, fmt, ms);
-  if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
+  const bool two_pass = ms == 4;
+  const int ms_a = two_pass ? 2 : ms, ms_b = two_pass ? row_slices(m - 32) : ms;
+  const size_t need_a = scratch_layout(n, k, count, fmt, ms_a).total;
+  const size_t need_b = scratch_layout(n, k, count, fmt, ms_b).total;
+  if (scratch_bytes < need_a || scratch_bytes < need_b) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
   if (verify && accept_out && tree_parent) {
@@ -300,25 +304,59 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
       a.draft[i] = draft_host[i];
     }
   }
-  a.g = geometry(n, k, count, fmt, ms);
-  fill_phase(a.ph, a.g, w, logits, count, n, k, staged);
   a.layout = layout;
-  a.m = m;
-  uint8_t *sc = (uint8_t *)scratch;
-  a.done = (unsigned *)sc;
-  a.group_cnt = (unsigned *)(sc + sl.cnt_off);
-  a.wg_keys = (unsigned long long *)(sc + sl.keys_off);
-  a.partials = (float *)(sc + sl.part_off);
   a.argmax_out = argmax;
   a.argmax_from = argmax_from;
   a.head_out = head_out;
   a.accept_out = accept_out;
   a.k_draft = verify && accept_out && !tree_parent ? m - 1 : 0;
   a.verify = verify ? 1 : 0;
+  a.x_rec = (unsigned)(ms * kStageBytes);
+  // The rows [row0, row0 + rows) of the call, at `pms` slices from staged
+  // slice row0 / 16 on (each launch lays out the scratch for its own
+  // geometry; every layout fits the one sized for the whole call).
+  uint8_t *sc = (uint8_t *)scratch;
+  auto part = [&](GemvLaunch &b, int row0, int rows, int pms) {
+    b.g = geometry(n, k, count, fmt, pms);
+    float *lg[kMaxGroup] = {};
+    for (int i = 0; i < count; ++i) lg[i] = logits && logits[i] ? logits[i] + (int64_t)row0 * n : nullptr;
+    fill_phase(b.ph, b.g, w, lg, count, n, k, staged);
+    const ScratchLayout bl = scratch_layout(n, k, count, fmt, pms);
+    b.done = (unsigned *)sc;
+    b.group_cnt = (unsigned *)(sc + bl.cnt_off);
+    b.wg_keys = (unsigned long long *)(sc + bl.keys_off);
+    b.partials = (float *)(sc + bl.part_off);
+    b.m = rows;
+    b.row0 = row0;
+    b.x_off = (unsigned)((row0 / 16) * kStageBytes);
+  };
+  // 33 to 64 rows: two weight passes, rows 0-31 at two slices and the rest
+  // at one or two, rather than one pass at four slices. With four slices
+  // every weight byte costs 16 bytes of LDS activation reads per wave and
+  // the pass is bound by them: on MI355X two passes took 15 % (40 nodes),
+  // 13 % (48) and 5 % (64) less time on the 131,072-row LM head. The first
+  // pass writes the argmaxes of rows 0-31 (no decision); the second reads
+  // them back for the accept decision over all m rows.
+  GemvLaunch first = a;
+  if (two_pass) {
+    part(first, 0, 32, ms_a);
+    first.accept_out = nullptr;
+    first.tree = 0;
+    first.path_out = nullptr;
+    first.k_draft = 0;
+    part(a, 32, m - 32, ms_b);
+    a.am_prev = argmax;
+    a.argmax_out = argmax ? argmax + 32 : nullptr;
+    a.head_out = nullptr;
+  } else {
+    part(a, 0, m, ms);
+  }
   if (x_to_stage) {
-    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, a.g.n_groups, stream))
+    const int64_t groups = two_pass && first.g.n_groups > a.g.n_groups ? first.g.n_groups : a.g.n_groups;
+    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, groups, stream))
       return KQ_ERR_LAUNCH;
   }
+  if (two_pass && launch_gemv(first, stream)) return KQ_ERR_LAUNCH;
   if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;
   return KQ_OK;
 }

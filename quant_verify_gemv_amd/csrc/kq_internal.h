@@ -12,7 +12,8 @@ constexpr int64_t kQK = 256;          // weights per Q4_K super-block
 constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // activation rows per MFMA slice (block size of the draft)
 constexpr int kMaxTreeRows = 64;      // activation rows per call: up to 4 slices (token-tree verify)
-// 16-row slices a call of m activation rows runs: 1, 2 or 4
+// 16-row slices staged for m activation rows: 1, 2 or 4 (a launch runs one
+// or two of them; 33 to 64 rows take two launches)
 constexpr int row_slices(int m) { return m <= 16 ? 1 : m <= 32 ? 2 : 4; }
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
 
@@ -89,7 +90,7 @@ struct Geometry {
   int tpw;        // 16-row tiles per wave (1 or 2)
   int bi;         // units between workgroup barriers (1, 2 or 4; LDS ring of 2 bi blocks)
   int depth;      // weight register sets (prefetch depth + 1: 4 or 8)
-  int ms;         // 16-row activation slices (1, 2 or 4)
+  int ms;         // 16-row activation slices of the launch (1 or 2)
   int rows;       // rows per row group = 16 * waves * tpw
   int n_wg_per;   // row groups per matrix
   int n_groups;   // row groups in total = count * n_wg_per
@@ -141,6 +142,15 @@ struct GemvLaunch {
   int tree;                      // 1: tree accept over m nodes
   int32_t *path_out;             // tree, may be null: the accepted path's nodes
   int verify;
+  // Staged activations of a single launch: block b's first slice of this
+  // launch at b * x_rec + x_off (x_rec = the staged slices per block times
+  // kStageBytes). A launch that takes slices past the first (the second pass
+  // of a two-pass tree) covers rows row0 .. row0 + m - 1 of the call; the
+  // argmaxes of rows 0 .. row0 - 1 are read from am_prev (device memory,
+  // written by the earlier pass) for the accept decision.
+  unsigned x_rec, x_off;
+  int row0;
+  const int32_t *am_prev;
   Geometry g;
 };
 

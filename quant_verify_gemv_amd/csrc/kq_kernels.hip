@@ -362,6 +362,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   static_assert(FMT == kFmtQ4 || !CHAIN, "chains run Q4_K");
   // MS 16-row activation slices: every unpacked weight operand feeds the
   // MFMAs of all MS slices, so the weights are read once for 16 MS rows
+  // (33 to 64 rows: two launches, rows 0-31 and the rest)
+  static_assert(MS == 1 || MS == 2, "one or two slices per launch");
   static_assert(MS == 1 || !CHAIN, "more than 16 rows: single launches");
   constexpr int kRS = 16 * MS;  // activation rows per call at most
   constexpr unsigned kTB = 16u * (unsigned)fmt_block_bytes(FMT);  // tiled record bytes
@@ -373,9 +375,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // workgroups stage twice the activation chunks per thread and keep one
   // set in flight. The unit loop is unrolled kU = lcm(D, BI, kXL + 1) times
   // so that every register set index and every interval position is static.
-  // Four slices: one register set, loaded at the start of a unit and stored
-  // at its end (the unit's four-fold MFMA work covers the L2 latency).
-  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : MS == 4 ? 0 : 1;
+  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : 1;
   constexpr int kU = lcm_int(lcm_int(D, BI), kXL + 1);
   constexpr int kNth = 64 * W;
   constexpr int kRows = 16 * T * W;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   static_assert(BI == 1 || BI == 2 || BI == 4, "barrier interval");
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kNB][kStageBytes * MS];
   __shared__ unsigned long long s_keys[kRS];
-  __shared__ int s_am[kRS];
+  __shared__ int s_am[kMaxTreeRows];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
@@ -590,8 +590,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     int ux = u0;
     int bx = u0 % KB;
     const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_PH(ph, staged));
+    const unsigned x_rec = CHAIN ? (unsigned)kStageBytes : a.x_rec;
+    const unsigned x_off = CHAIN ? 0u : a.x_off;
     auto load_x = [&](XRegs &x) {
-      const unsigned src = (unsigned)bx * (unsigned)(kStageBytes * MS);
+      const unsigned src = (unsigned)bx * x_rec + x_off;
 #pragma unroll
       for (int j = 0; j < kXj; ++j)
         x.a[j] = buf_ld16(x_rsrc, (unsigned)(j < kXj - 1 ? tid + kNth * j : xlast) * 16u, src);
@@ -1212,23 +1214,27 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       }
     }
     __syncthreads();
+    // rows of this launch at row0 + tid; an earlier pass's rows from am_prev
+    const int R0 = a.row0, MT = R0 + M;
     if (tid < M) {
       const int am = (int)(0xFFFFFFFFu - (unsigned)(s_keys[tid] & 0xFFFFFFFFull));
-      s_am[tid] = am;
+      s_am[R0 + tid] = am;
       if (tid >= a.argmax_from) a.argmax_out[tid - a.argmax_from] = am;
+    } else if (tid - M < R0) {
+      s_am[tid - M] = a.am_prev[tid - M];
     }
     __syncthreads();
     if (a.accept_out && a.tree) {
       // Token tree: wave 0 walks from the root; lane j holds node j. Each
       // move goes to a higher node index (parents precede children), so the
-      // walk ends within M - 1 moves.
+      // walk ends within MT - 1 moves.
       if (tid < 64) {
         const int j = lane;
-        const int par = j < M ? a.parent[j] : -1;
-        const int tok = j < M ? a.draft[j] : -1;
+        const int par = j < MT ? a.parent[j] : -1;
+        const int tok = j < MT ? a.draft[j] : -1;
         int cur = 0, n = 0;
         while (true) {
-          const bool match = j >= 1 && j < M && par == cur && tok == s_am[cur];
+          const bool match = j >= 1 && j < MT && par == cur && tok == s_am[cur];
           const unsigned long long bal = __ballot(match);
           if (!bal) break;
           const int nxt = __ffsll((long long)bal) - 1;
@@ -1572,9 +1578,7 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(kFmtQ6, 12, 1, 4, 4, 1)
     KQ_CASE(kFmtQ6, 8, 2, 4, 4, 1)
     KQ_CASE(kFmtQ4, 8, 2, 2, 3, 2)
-    KQ_CASE(kFmtQ4, 8, 1, 1, 3, 4)
     KQ_CASE(kFmtQ6, 8, 2, 2, 3, 2)
-    KQ_CASE(kFmtQ6, 8, 1, 1, 3, 4)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;
   }
