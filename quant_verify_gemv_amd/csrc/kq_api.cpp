@@ -17,8 +17,6 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // The kernels address a weight matrix (either layout, rows rounded up to a
 // 16-row tile) and a staged activation block with 32-bit offsets, so both
 // must be smaller than 4 GiB.
-// Every matrix and every staged block is smaller than 4 GiB: the kernels
-// address them with 32-bit offsets.
 static bool shape_ok(int64_t n, int64_t k, int fmt = kFmtQ4) {
   if (!(n >= 1 && n < ((int64_t)1 << 31) && k > 0 && k % kQK == 0 && k <= ((int64_t)1 << 28))) return false;
   const int64_t kb = k / kQK;
@@ -337,8 +335,9 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   // 13 % (48) and 5 % (64) less time on the 131,072-row LM head. The first
   // pass writes the argmaxes of rows 0-31 (no decision); the second reads
   // them back for the accept decision over all m rows.
-  GemvLaunch first = a;
+  GemvLaunch first;
   if (two_pass) {
+    first = a;
     part(first, 0, 32, ms_a);
     first.accept_out = nullptr;
     first.tree = 0;

@@ -181,3 +181,41 @@ def test_tree_verify_lm_head(kq):
     check_argmax(am, L6, A6, what="tree q6k m=64")
     assert tuple(acc.cpu().numpy()) == oracle.tree_accept(parent, token, am)[:2]
     del rows
+
+
+@pytest.mark.parametrize("m", [40, 64])
+def test_two_pass_host_staged_and_device_drafts(kq, m):
+    """More than 32 rows through the entry points that stage the host's x
+    themselves (kq_gemv_rows, kq_verify_argmax_accept) and with drafts in
+    device memory (kq_verify_staged_dev): every logit within tolerance, the
+    argmax with flags, the linear accept equal to the oracle's on the GPU's
+    argmax, with a mismatch in either pass's rows and with every draft
+    accepted (the walk crosses from the first pass's rows into the
+    second's); the staged and device-draft forms equal the host-staged one
+    bit for bit."""
+    n, k = 1000, 2304
+    w = synthetic.q4k_matrix(n, k, 840 + m)
+    x = synthetic.activations(m, k, 850 + m)
+    L, A = oracle.gemv_rows(w, k, x)
+    w_d, x_d = to_dev(w), to_dev(x)
+    G = kq.gemv_rows(w_d, n, k, x_d).cpu().numpy()
+    r = check_logits(G, L, A, what=f"gemv_rows m={m}")
+    log(f"two passes: gemv_rows m={m} max |d|/tol = {r:.3g}")
+    am0, _, _ = kq.verify(w_d, n, k, x_d, [0] * (m - 1))
+    am0 = am0.cpu().numpy()
+    check_argmax(am0, L, A, what=f"verify m={m}")
+    sc = kq.new_scratch(n, k, DEV)
+    st = kq.stage_rows(x_d)
+    for miss in (m - 3, 20, None):
+        draft = [int(t) for t in am0[:m - 1]]
+        if miss is not None:
+            draft[miss] = (draft[miss] + 1) % n
+        am, acc, lg = kq.verify(w_d, n, k, x_d, draft, want_logits=True)
+        torch.cuda.synchronize()
+        am, acc = am.cpu().numpy(), acc.cpu().numpy()
+        assert np.array_equal(am, am0) and np.array_equal(lg.cpu().numpy(), G)
+        assert tuple(acc) == oracle.accept(draft, am), f"m={m} miss={miss}"
+        am2, acc2, _ = kq.verify_staged(w_d, n, k, st, m, torch.tensor(draft, dtype=torch.int32, device=DEV), sc)
+        torch.cuda.synchronize()
+        assert np.array_equal(am2.cpu().numpy(), am) and np.array_equal(acc2.cpu().numpy(), acc)
+        log(f"two passes: m={m} mismatch at {miss}: accepted {int(acc[0])}, next {int(acc[1])}")
