@@ -117,7 +117,11 @@ size_t kq_staged_bytes(int64_t k);
 size_t kq_staged_bytes_rows(int64_t k, int m);
 
 /* Bytes of device scratch the *_staged calls need for an n x k matrix (in
- * any weight format and layout). */
+ * any weight format and layout). The scratch is laid out for the shape
+ * alone: every single-matrix call on n x k may share it (any format,
+ * layout and m, ordered on one stream). A call on another shape, or a
+ * grouped call, needs its own scratch, or this one zeroed again with
+ * kq_workspace_init first. */
 size_t kq_scratch_bytes(int64_t n, int64_t k);
 
 /* Zero the control words of a workspace or scratch buffer of `bytes` bytes
@@ -302,7 +306,9 @@ kq_status kq_verify_tree_staged(const void *w, int layout, int64_t n, int64_t k,
                                 void *scratch, size_t scratch_bytes, void *stream);
 
 /* Bytes of device scratch kq_gemv_staged_group needs for `count` matrices
- * of n x k in any weight format (0 for invalid arguments). */
+ * of n x k in any weight format (0 for invalid arguments).
+ * The layout depends on n, k and count: calls with another shape or count
+ * need their own scratch, or this one zeroed again with kq_workspace_init. */
 size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count);
 
 /* kq_gemv_staged for 1 <= count <= 8 matrices of the same shape that share

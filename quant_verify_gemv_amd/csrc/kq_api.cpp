@@ -93,13 +93,30 @@ Geometry geometry(int64_t n, int64_t k, int count, int fmt, int ms) {
   return g;
 }
 
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt, int ms) {
-  const Geometry g = geometry(n, k, count, fmt, ms);
+// One layout for every call on `count` matrices of n x k, whatever the
+// weight format and the launch's slice count: the arrival counters cover the
+// most row groups, the keys the most workgroups and the partials the largest
+// size of any of these geometries. The offsets then never depend on the
+// call, so a scratch shared by calls of different row counts or formats (or
+// by the two passes of one call) never has one launch's argmax keys or
+// partials where another expects its zeroed counters.
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count) {
+  size_t groups = 0, wgs = 0, part = 0;
+  for (int f = kFmtQ4; f <= kFmtQ6; ++f) {
+    if (!shape_ok(n, k, f)) continue;
+    for (int ms = 1; ms <= 2; ++ms) {
+      const Geometry g = geometry(n, k, count, f, ms);
+      const size_t pb = sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * ms * (size_t)g.rows;
+      groups = (size_t)g.n_groups > groups ? (size_t)g.n_groups : groups;
+      wgs = (size_t)g.n_wg > wgs ? (size_t)g.n_wg : wgs;
+      part = pb > part ? pb : part;
+    }
+  }
   ScratchLayout s;
   s.cnt_off = kCntOff;
-  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * kCntStride * (size_t)g.n_groups);
-  s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxTreeRows * (size_t)g.n_wg);
-  s.total = s.part_off + align256(sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * ms * (size_t)g.rows);
+  s.keys_off = align256(s.cnt_off + sizeof(unsigned) * kCntStride * groups);
+  s.part_off = align256(s.keys_off + sizeof(unsigned long long) * kMaxTreeRows * wgs);
+  s.total = s.part_off + align256(part);
   return s;
 }
 
@@ -136,19 +153,9 @@ size_t kq_staged_bytes_rows(int64_t k, int m) {
   return (size_t)(k / kQK) * (size_t)row_slices(m) * (size_t)kStageBytes;
 }
 
-// Scratch for `count` matrices in whichever format and launch slice count
-// (1 or 2) needs the most.
-static size_t scratch_any_fmt(int64_t n, int64_t k, int count) {
-  size_t t = 0;
-  for (int f = kFmtQ4; f <= kFmtQ6; ++f) {
-    if (!shape_ok(n, k, f)) continue;
-    for (int ms = 1; ms <= 2; ++ms) {
-      const size_t b = scratch_layout(n, k, count, f, ms).total;
-      t = b > t ? b : t;
-    }
-  }
-  return t;
-}
+// Scratch for `count` matrices: the one layout of every format and slice
+// count.
+static size_t scratch_any_fmt(int64_t n, int64_t k, int count) { return scratch_layout(n, k, count).total; }
 
 size_t kq_scratch_bytes(int64_t n, int64_t k) {
   if (!shape_ok(n, k)) return 0;
@@ -275,9 +282,8 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   const int ms = row_slices(m);
   const bool two_pass = ms == 4;
   const int ms_a = two_pass ? 2 : ms, ms_b = two_pass ? row_slices(m - 32) : ms;
-  const size_t need_a = scratch_layout(n, k, count, fmt, ms_a).total;
-  const size_t need_b = scratch_layout(n, k, count, fmt, ms_b).total;
-  if (scratch_bytes < need_a || scratch_bytes < need_b) return KQ_ERR_WORKSPACE;
+  const ScratchLayout sl = scratch_layout(n, k, count);
+  if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
   if (verify && accept_out && tree_parent) {
@@ -311,19 +317,17 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   a.verify = verify ? 1 : 0;
   a.x_rec = (unsigned)(ms * kStageBytes);
   // The rows [row0, row0 + rows) of the call, at `pms` slices from staged
-  // slice row0 / 16 on (each launch lays out the scratch for its own
-  // geometry; every layout fits the one sized for the whole call).
+  // slice row0 / 16 on.
   uint8_t *sc = (uint8_t *)scratch;
   auto part = [&](GemvLaunch &b, int row0, int rows, int pms) {
     b.g = geometry(n, k, count, fmt, pms);
     float *lg[kMaxGroup] = {};
     for (int i = 0; i < count; ++i) lg[i] = logits && logits[i] ? logits[i] + (int64_t)row0 * n : nullptr;
     fill_phase(b.ph, b.g, w, lg, count, n, k, staged);
-    const ScratchLayout bl = scratch_layout(n, k, count, fmt, pms);
     b.done = (unsigned *)sc;
-    b.group_cnt = (unsigned *)(sc + bl.cnt_off);
-    b.wg_keys = (unsigned long long *)(sc + bl.keys_off);
-    b.partials = (float *)(sc + bl.part_off);
+    b.group_cnt = (unsigned *)(sc + sl.cnt_off);
+    b.wg_keys = (unsigned long long *)(sc + sl.keys_off);
+    b.partials = (float *)(sc + sl.part_off);
     b.m = rows;
     b.row0 = row0;
     b.x_off = (unsigned)((row0 / 16) * kStageBytes);

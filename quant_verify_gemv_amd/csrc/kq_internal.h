@@ -155,7 +155,8 @@ struct GemvLaunch {
 };
 
 Geometry geometry(int64_t n, int64_t k, int count, int fmt = kFmtQ4, int ms = 1);
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int fmt = kFmtQ4, int ms = 1);
+// the one scratch layout of every call on `count` matrices of n x k
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
 
 // Kernel launches (return a hipError_t as int).
 // kq_stage_kernel also zeroes the control words of `ctrl` (a scratch area

@@ -121,8 +121,8 @@ def make_tree(rng, m, am, n_vocab, p_follow=0.6):
 
 
 def test_tree_verify_lm_head(kq):
-    """Trees of 24, 32, 48 and 64 nodes on the LM head (6,656 -> 131,072,
-    Q4_K tiled): argmax of every node row against the oracle (flags), the
+    """Trees of 24, 32, 33, 40, 48 and 64 nodes on the LM head (6,656 ->
+    131,072, Q4_K tiled; above 32 nodes two passes over the weights): argmax of every node row against the oracle (flags), the
     walk equal to the oracle's walk on the GPU's argmax always, and on the
     oracle's argmax when no row is flagged; the path output lists the nodes
     moved through; a chain gives the linear verify's result; the Q6_K head
@@ -138,7 +138,7 @@ def test_tree_verify_lm_head(kq):
     wt = kq.tile_weights(to_dev(w), n, k)
     sc = kq.new_scratch(n, k, DEV)
     rng = np.random.default_rng(11)
-    for m in (24, 32, 48, 64):
+    for m in (24, 32, 33, 40, 48, 64):
         st = kq.stage_rows(to_dev(x[:m]))
         for trial in range(3):
             parent, token = make_tree(rng, m, o_am[:m], n)
@@ -219,3 +219,31 @@ def test_two_pass_host_staged_and_device_drafts(kq, m):
         torch.cuda.synchronize()
         assert np.array_equal(am2.cpu().numpy(), am) and np.array_equal(acc2.cpu().numpy(), acc)
         log(f"two passes: m={m} mismatch at {miss}: accepted {int(acc[0])}, next {int(acc[1])}")
+
+
+def test_scratch_shared_across_row_counts(kq):
+    """One scratch for verify calls of 32, 16, 48, 16, 32 and 48 rows in
+    turn. On this shape the one- and two-slice geometries have different
+    numbers of row groups, and each call leaves its argmax keys in the
+    scratch; with one layout for every call they never land where another
+    call expects its zeroed arrival counters. Every call's argmax and accept
+    equal the same call on a fresh scratch."""
+    n, k = 2000, 2304
+    w = synthetic.q4k_matrix(n, k, 870)
+    x = synthetic.activations(48, k, 871)
+    wt = kq.tile_weights(to_dev(w), n, k)
+    shared = kq.new_scratch(n, k, DEV)
+    for m in (32, 16, 48, 16, 32, 48):
+        st = kq.stage_rows(to_dev(x[:m]))
+        fresh = kq.new_scratch(n, k, DEV)
+        am_f, acc_f, _ = kq.verify_staged(wt, n, k, st, m, [0] * (m - 1), fresh, layout=kq.LAYOUT_TILED16)
+        draft = [int(t) for t in am_f.cpu().numpy()[:m - 1]]
+        draft[m - 3] = (draft[m - 3] + 1) % n
+        am_f, acc_f, _ = kq.verify_staged(wt, n, k, st, m, draft, fresh, layout=kq.LAYOUT_TILED16)
+        am_s, acc_s, _ = kq.verify_staged(wt, n, k, st, m, draft, shared, layout=kq.LAYOUT_TILED16)
+        torch.cuda.synchronize()
+        assert np.array_equal(am_s.cpu().numpy(), am_f.cpu().numpy()), f"m={m}: argmax on the shared scratch"
+        assert np.array_equal(acc_s.cpu().numpy(), acc_f.cpu().numpy()), f"m={m}: accept on the shared scratch"
+        assert tuple(acc_s.cpu().numpy()) == (m - 3, int(am_f.cpu().numpy()[m - 3]))
+    L, A = oracle.gemv_rows(w, k, x)
+    check_argmax(am_s.cpu().numpy(), L, A, what="shared scratch, 48 rows")
