@@ -441,7 +441,11 @@ def stochastic_timing(stack, torch, time_calls, temperature=300.0, decisions=20)
     (kq_softmax_rows: two launches, 8 algorithmic bytes per element, one
     fp32 read and one write), and the library's host decision
     (kq_speculative_decide) on rows copied to host memory, with the copy
-    timed on its own. Draft rows are the softmax of perturbed logits."""
+    timed on its own; then the same decisions in two steps (kq_gather_rows
+    of p_i[d_i] on the device, those k values and the one row the decision
+    walks copied to the host, kq_speculative_first_reject and
+    kq_speculative_resample), checked equal. Draft rows are the softmax of
+    perturbed logits."""
     kq = stack.kq
     h = stack.head
     n, m = h.n, 16
@@ -476,8 +480,30 @@ def stochastic_timing(stack, torch, time_calls, temperature=300.0, decisions=20)
     drafts = [[min(t, n - 1) for t in d] for d in drafts]
     us_ = rng.random((decisions, m)).astype(np.float32)
     t0 = time.perf_counter()
-    accepted = [kq.speculative_decide(drafts[j], q, p, orders, us_[j])[0] for j in range(decisions)]
+    decided = [kq.speculative_decide(drafts[j], q, p, orders, us_[j]) for j in range(decisions)]
     us_decide = (time.perf_counter() - t0) * 1e6 / decisions
+    accepted = [a for a, _ in decided]
+    # the same decisions in two steps: p_i[d_i] gathered on the device, k
+    # values and then the one row the decision walks copied to the host
+    kd = m - 1
+    drafts_d = [torch.tensor(d, dtype=torch.int32, device=stack.dev) for d in drafts]
+    q_at = [q[np.arange(kd), d] for d in drafts]
+    pat_h = torch.empty(kd, dtype=torch.float32, pin_memory=True)
+    row_h = torch.empty(n, dtype=torch.float32, pin_memory=True)
+    torch.cuda.synchronize()
+    t_copy = t_host = 0.0
+    for j in range(decisions):
+        t0 = time.perf_counter()
+        pat_h.copy_(kq.gather_rows(probs[:kd], drafts_d[j]))
+        pos = kq.speculative_first_reject(pat_h.numpy(), q_at[j], us_[j][:kd])
+        row_h.copy_(probs[pos])
+        t1 = time.perf_counter()
+        tok = (kq.speculative_resample(row_h.numpy(), q[pos], orders[pos], us_[j][pos + 1]) if pos < kd
+               else kq.speculative_resample(row_h.numpy(), None, orders[kd], us_[j][kd]))
+        t_host += time.perf_counter() - t1
+        t_copy += t1 - t0
+        if (pos, tok) != decided[j]:
+            raise RuntimeError("the two-step decision differs from the full-row decision")
     soft_bytes = 8 * m * n
     return {"temperature": temperature,
             "verify_logits_us": round(us_verify, 2),
@@ -487,6 +513,8 @@ def stochastic_timing(stack, torch, time_calls, temperature=300.0, decisions=20)
             "verify_plus_rows_us": round(us_both, 2),
             "rows_to_host_us": round(us_copy, 1),
             "host_decide_us": round(us_decide, 1),
+            "gather_and_one_row_to_host_us": round(t_copy * 1e6 / decisions, 1),
+            "host_resample_us": round(t_host * 1e6 / decisions, 1),
             "mean_accepted": round(float(np.mean(accepted)), 2)}
 
 

@@ -386,6 +386,46 @@ kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, c
                                 const float *target_rows, const int32_t *orders, const float *uniforms,
                                 int32_t *accepted, int32_t *next_token);
 
+/* The same decision in two host steps, for callers that copy to the host
+ * only what the decision reads: the accept tests need p_i[d_i] and
+ * q_i[d_i] alone, and only the row pair of the first rejected position (or
+ * target row k) is ever walked. kq_speculative_decide is exactly
+ * kq_speculative_first_reject followed by kq_speculative_resample.
+ *
+ * kq_gather_rows (device, one launch): out[i] = rows[i][tokens[i]] for
+ * i < count, e.g. p_i[d_i] from kq_softmax_rows' output.
+ *  rows    device fp32 [m][n], 1 <= m <= 65535, 1 <= n < 2^31
+ *  tokens  device int32 [count], 0 <= count <= m (count = 0: nothing is
+ *          enqueued)
+ *  out     device fp32 [count] (written); a token outside [0, n) gives a
+ *          NaN, which kq_speculative_first_reject counts as a rejection */
+kq_status kq_gather_rows(const float *rows, int m, int64_t n, const int32_t *tokens, int count, float *out,
+                         void *stream);
+
+/* The first rejected position: the first i < k with u[i] > min(p_at[i] /
+ * q_at[i], 1) (accepted when q_at[i] <= 0; a NaN rejects), else k.
+ *  p_at, q_at  host fp32 [k]: p_i[d_i] and q_i[d_i]
+ *  uniforms    host fp32 [>= k]: u[0 .. k-1]
+ *  position    host int32 (written)
+ * KQ_ERR_NULL, KQ_ERR_SHAPE (k outside 0..15). */
+kq_status kq_speculative_first_reject(int k, const float *p_at, const float *q_at, const float *uniforms,
+                                      int32_t *position);
+
+/* The token drawn where the decision stops. With q_row (a rejection): from
+ * max(p_row - q_row, 0) divided by its fp32 sum in index order over the
+ * tokens with a positive value, or from p_row when that sum is not positive;
+ * without q_row (the bonus after k acceptances): from p_row over all of
+ * `order`. The walk is kq_speculative_decide's.
+ *  p_row          host fp32 [n]; q_row_or_null host fp32 [n] or NULL
+ *  order          host int32 [n], entries in [0, n) (checked whole first)
+ *  u              the draw: u[i + 1] after a rejection at i, u[k] for the
+ *                 bonus
+ *  token          host int32 (written only on KQ_OK)
+ * KQ_ERR_NULL, KQ_ERR_SHAPE (n; a row with no positive value to draw),
+ * KQ_ERR_TOKEN (an order entry outside [0, n)). */
+kq_status kq_speculative_resample(int64_t n, const float *p_row, const float *q_row_or_null, const int32_t *order,
+                                  float u, int32_t *token);
+
 /* ---------------------------------------------------------------- chains
  * A chain launch runs a sequence of grouped products in ONE grid, each
  * phase depending on the one before it: phase i + 1 starts reading its

@@ -635,6 +635,53 @@ static int32_t sample_in_order(const float *p, const float *q, float total, cons
   return last;
 }
 
+kq_status kq_gather_rows(const float *rows, int m, int64_t n, const int32_t *tokens, int count, float *out,
+                         void *stream) {
+  if (m < 1 || m > 65535 || n < 1 || n >= ((int64_t)1 << 31) || count < 0 || count > m) return KQ_ERR_SHAPE;
+  if (count == 0) return KQ_OK;
+  if (!rows || !tokens || !out) return KQ_ERR_NULL;
+  if (!al(rows, 4) || !al(tokens, 4) || !al(out, 4)) return KQ_ERR_ALIGN;
+  if (launch_gather(rows, n, tokens, count, out, stream)) return KQ_ERR_LAUNCH;
+  return KQ_OK;
+}
+
+kq_status kq_speculative_first_reject(int k, const float *p_at, const float *q_at, const float *uniforms,
+                                      int32_t *position) {
+  if (!position || (k > 0 && (!p_at || !q_at || !uniforms))) return KQ_ERR_NULL;
+  if (k < 0 || k >= kMaxRows) return KQ_ERR_SHAPE;
+  // min(p / q, 1) that keeps a NaN ratio (fminf would return 1), so a NaN
+  // (e.g. a gathered token outside the row) rejects
+  int i = 0;
+  for (; i < k; ++i) {
+    const float r = p_at[i] / q_at[i];
+    const float acceptance = q_at[i] <= 0.0f ? 1.0f : (r >= 1.0f ? 1.0f : r);
+    if (!(uniforms[i] <= acceptance)) break;
+  }
+  *position = i;
+  return KQ_OK;
+}
+
+kq_status kq_speculative_resample(int64_t n, const float *p_row, const float *q_row_or_null, const int32_t *order,
+                                  float u, int32_t *token) {
+  if (!p_row || !order || !token) return KQ_ERR_NULL;
+  if (n < 1 || n >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
+  if (!order_row_ok(order, n)) return KQ_ERR_TOKEN;
+  int32_t t;
+  if (q_row_or_null) {
+    // the replacement comes from max(p - q, 0) divided by its sum (summed in
+    // token order), or from p when that sum is not positive
+    const float *q = q_row_or_null;
+    float total = 0.0f;
+    for (int64_t j = 0; j < n; ++j) total = total + fmaxf(p_row[j] - q[j], 0.0f);
+    t = sample_in_order(p_row, total > 0.0f ? q : nullptr, total, order, n, u, true);
+    if (t < 0) return KQ_ERR_SHAPE;  // a row without any positive probability
+  } else {
+    t = sample_in_order(p_row, nullptr, 0.0f, order, n, u, false);
+  }
+  *token = t;
+  return KQ_OK;
+}
+
 kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, const float *draft_rows,
                                 const float *target_rows, const int32_t *orders, const float *uniforms,
                                 int32_t *accepted, int32_t *next_token) {
@@ -643,29 +690,21 @@ kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, c
   if (k < 0 || k >= kMaxRows || n < 1 || n >= ((int64_t)1 << 31)) return KQ_ERR_SHAPE;
   for (int i = 0; i < k; ++i)
     if (draft_tokens[i] < 0 || (int64_t)draft_tokens[i] >= n) return KQ_ERR_TOKEN;
+  float p_at[kMaxRows], q_at[kMaxRows];
   for (int i = 0; i < k; ++i) {
-    const float *q = draft_rows + (int64_t)i * n;
-    const float *p = target_rows + (int64_t)i * n;
-    const int32_t t = draft_tokens[i];
-    const float acceptance = q[t] <= 0.0f ? 1.0f : fminf(p[t] / q[t], 1.0f);
-    if (uniforms[i] <= acceptance) continue;
-    // first rejection: the replacement comes from max(p - q, 0) divided by
-    // its sum (summed in token order), or from p when that sum is not positive
-    const int32_t *order = orders + (int64_t)i * n;
-    if (!order_row_ok(order, n)) return KQ_ERR_TOKEN;
-    float total = 0.0f;
-    for (int64_t j = 0; j < n; ++j) total = total + fmaxf(p[j] - q[j], 0.0f);
-    const int32_t tok = sample_in_order(p, total > 0.0f ? q : nullptr, total, order, n, uniforms[i + 1], true);
-    if (tok < 0) return KQ_ERR_SHAPE;  // a row without any positive probability
-    *accepted = i;
-    *next_token = tok;
-    return KQ_OK;
+    p_at[i] = target_rows[(int64_t)i * n + draft_tokens[i]];
+    q_at[i] = draft_rows[(int64_t)i * n + draft_tokens[i]];
   }
-  const int32_t *order = orders + (int64_t)k * n;
-  if (!order_row_ok(order, n)) return KQ_ERR_TOKEN;
-  const float *p = target_rows + (int64_t)k * n;
-  *accepted = k;
-  *next_token = sample_in_order(p, nullptr, 0.0f, order, n, uniforms[k], false);
+  int32_t j = 0, tok = 0;
+  kq_status st = kq_speculative_first_reject(k, p_at, q_at, uniforms, &j);
+  if (st != KQ_OK) return st;
+  const float *p = target_rows + (int64_t)j * n;
+  const int32_t *order = orders + (int64_t)j * n;
+  st = j < k ? kq_speculative_resample(n, p, draft_rows + (int64_t)j * n, order, uniforms[j + 1], &tok)
+             : kq_speculative_resample(n, p, nullptr, order, uniforms[k], &tok);
+  if (st != KQ_OK) return st;
+  *accepted = j;
+  *next_token = tok;
   return KQ_OK;
 }
 

@@ -173,6 +173,8 @@ int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int bl
 // Softmax rows: chunks of a row (4,096 logits each) and the two-pass launch
 // (part: rows x chunks float pairs of workspace).
 int softmax_chunks(int64_t n);
+// out[i] = rows[i][tokens[i]], i < count (NaN for a token outside [0, n))
+int launch_gather(const float *rows, int64_t n, const int32_t *tokens, int count, float *out, void *stream);
 int launch_softmax(const float *logits, int m, int64_t n, float temperature, float cap, float *part, float *probs,
                    void *stream);
 

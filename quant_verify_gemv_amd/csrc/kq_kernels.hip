@@ -1549,6 +1549,23 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value) {
   return (int)hipGetLastError();
 }
 
+// out[i] = rows[i][tokens[i]] (the accept tests' p_i[d_i]); a token outside
+// [0, n) gives a NaN.
+__global__ __launch_bounds__(256) void kq_gather_kernel(const float *__restrict__ rows, int64_t n,
+                                                        const int32_t *__restrict__ tokens, int count,
+                                                        float *__restrict__ out) {
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (i >= count) return;
+  const int32_t t = tokens[i];
+  out[i] = (t >= 0 && (int64_t)t < n) ? rows[(int64_t)i * n + t] : __builtin_nanf("");
+}
+
+int launch_gather(const float *rows, int64_t n, const int32_t *tokens, int count, float *out, void *stream) {
+  hipLaunchKernelGGL(kq_gather_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     rows, n, tokens, count, out);
+  return (int)hipGetLastError();
+}
+
 int launch_gemv(const GemvLaunch &a, void *stream) {
   const dim3 grid((unsigned)a.g.n_wg);
   hipStream_t st = (hipStream_t)stream;

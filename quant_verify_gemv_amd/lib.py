@@ -25,7 +25,7 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
             "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
             "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged",
-            "kq_verify_staged_dev")
+            "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject", "kq_speculative_resample")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -106,6 +106,9 @@ def load() -> ctypes.CDLL:
     F = ctypes.c_float
     lib.kq_softmax_rows.argtypes = [P, I32, I64, F, F, P, P, SZ, P]
     lib.kq_speculative_decide.argtypes = [I32, P, I64, P, P, P, P, P, P]
+    lib.kq_gather_rows.argtypes = [P, I32, I64, P, I32, P, P]
+    lib.kq_speculative_first_reject.argtypes = [I32, P, P, P, P]
+    lib.kq_speculative_resample.argtypes = [I64, P, P, P, F, P]
     lib.kq_verify_staged_dev.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_staged_bytes_rows.argtypes = [I64, I32]
     lib.kq_staged_bytes_rows.restype = SZ
@@ -118,7 +121,8 @@ def load() -> ctypes.CDLL:
                  "kq_tile_weights", "kq_draft_block_argmax", "kq_draft_block_argmax_staged",
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
                  "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged",
-                 "kq_verify_staged_dev"):
+                 "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject",
+                 "kq_speculative_resample"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -544,3 +548,54 @@ def speculative_decide(draft, draft_rows, target_rows, orders, uniforms):
                                         vp(od.ctypes.data), vp(un.ctypes.data), ctypes.byref(acc),
                                         ctypes.byref(nxt)), "kq_speculative_decide")
     return int(acc.value), int(nxt.value)
+
+
+def gather_rows(rows, tokens, out=None, stream=None):
+    """out[i] = rows[i, tokens[i]] on the device (kq_gather_rows): rows fp32
+    [m, n], tokens int32 [count <= m] (device tensors). NaN for a token
+    outside [0, n)."""
+    torch = _torch()
+    m, n = int(rows.shape[0]), int(rows.shape[1])
+    count = int(tokens.numel())
+    if out is None:
+        out = torch.empty(max(count, 1), dtype=torch.float32, device=rows.device)
+    if count:
+        _check(load().kq_gather_rows(_dev_ptr(rows, "rows", torch.float32), m, n,
+                                     _dev_ptr(tokens, "tokens", torch.int32), count,
+                                     _dev_ptr(out, "out", torch.float32), _stream_handle(stream)), "kq_gather_rows")
+    return out[:count]
+
+
+def speculative_first_reject(p_at, q_at, uniforms):
+    """The first rejected position (host arrays): p_at, q_at fp32 [k] =
+    p_i[d_i], q_i[d_i]; uniforms fp32 [>= k]. Returns k when all accept."""
+    import numpy as np
+    pa = np.ascontiguousarray(p_at, dtype=np.float32)
+    qa = np.ascontiguousarray(q_at, dtype=np.float32)
+    un = np.ascontiguousarray(uniforms, dtype=np.float32)
+    k = int(pa.shape[0])
+    if qa.shape != (k,) or un.shape[0] < k:
+        raise ValueError("need k values of p, of q and k draws")
+    pos = ctypes.c_int32(0)
+    vp = ctypes.c_void_p
+    _check(load().kq_speculative_first_reject(k, vp(pa.ctypes.data), vp(qa.ctypes.data), vp(un.ctypes.data),
+                                              ctypes.byref(pos)), "kq_speculative_first_reject")
+    return int(pos.value)
+
+
+def speculative_resample(p_row, q_row, order, u):
+    """The token drawn where the decision stops (host arrays): from the
+    residual of p_row and q_row, or from p_row alone when q_row is None."""
+    import numpy as np
+    p = np.ascontiguousarray(p_row, dtype=np.float32)
+    n = int(p.shape[0])
+    q = np.ascontiguousarray(q_row, dtype=np.float32) if q_row is not None else None
+    od = np.ascontiguousarray(order, dtype=np.int32)
+    if od.shape != (n,) or (q is not None and q.shape != (n,)):
+        raise ValueError("p_row, q_row and order must have the same length")
+    tok = ctypes.c_int32(0)
+    vp = ctypes.c_void_p
+    _check(load().kq_speculative_resample(n, vp(p.ctypes.data), vp(q.ctypes.data) if q is not None else None,
+                                          vp(od.ctypes.data), ctypes.c_float(float(u)), ctypes.byref(tok)),
+           "kq_speculative_resample")
+    return int(tok.value)

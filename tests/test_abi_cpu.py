@@ -388,3 +388,19 @@ def test_verify_staged_dev_argument_errors_before_any_hip_call():
     assert v(FAKE, 1, n, k, FAKE, 65, FAKE, FAKE, FAKE, None, FAKE, sb, None) == SHAPE
     assert v(FAKE, 9, n, k, FAKE, m, FAKE, FAKE, FAKE, None, FAKE, sb, None) == SHAPE
     assert v(FAKE, 1, n, k, FAKE, m, FAKE, FAKE, FAKE, None, FAKE, 256, None) == WS
+
+
+def test_gather_argument_errors():
+    """kq_gather_rows checks its arguments before any HIP call; count = 0
+    enqueues nothing."""
+    lib = kq.load()
+    p = ctypes.c_void_p(256)
+    assert lib.kq_gather_rows(p, 0, 10, p, 0, p, None) == 2          # m < 1
+    assert lib.kq_gather_rows(p, 4, 0, p, 1, p, None) == 2           # n < 1
+    assert lib.kq_gather_rows(p, 4, 10, p, 5, p, None) == 2          # count > m
+    assert lib.kq_gather_rows(p, 4, 10, p, -1, p, None) == 2         # count < 0
+    assert lib.kq_gather_rows(None, 4, 10, p, 2, p, None) == 1
+    assert lib.kq_gather_rows(p, 4, 10, None, 2, p, None) == 1
+    assert lib.kq_gather_rows(p, 4, 10, p, 2, None, None) == 1
+    assert lib.kq_gather_rows(ctypes.c_void_p(258), 4, 10, p, 2, p, None) == 3
+    assert lib.kq_gather_rows(None, 4, 10, None, 0, None, None) == 0  # nothing to do

@@ -106,3 +106,47 @@ def test_softmax_argument_errors_before_any_hip_call():
     assert lib.kq_softmax_rows(FAKE, 0, 131072, 1.0, 0.0, FAKE, FAKE, ws, None) == SHAPE
     assert lib.kq_softmax_rows(FAKE + 2, 16, 131072, 1.0, 0.0, FAKE, FAKE, ws, None) == 3
     assert lib.kq_softmax_rows(FAKE, 16, 131072, 1.0, 0.0, FAKE, FAKE, ws - 1, None) == 5
+
+
+@pytest.mark.parametrize("n,k", [(5, 3), (64, 7), (1000, 15), (7, 0)])
+def test_two_step_decision_matches_oracle(n, k):
+    """kq_speculative_first_reject on p_i[d_i], q_i[d_i] alone, then
+    kq_speculative_resample on the one row pair (or target row k) it names,
+    equals the oracle's decision on the full rows, bit for bit."""
+    rng = np.random.default_rng(n * 37 + k)
+    for trial in range(200 if n < 1000 else 30):
+        draft, q, p, orders, u = random_case(rng, n, k, peaked=trial % 2 == 1)
+        p_at = np.array([p[i, d] for i, d in enumerate(draft)], dtype=np.float32)
+        q_at = np.array([q[i, d] for i, d in enumerate(draft)], dtype=np.float32)
+        j = kq.speculative_first_reject(p_at, q_at, u[:k])
+        if j < k:
+            tok = kq.speculative_resample(p[j], q[j], orders[j], u[j + 1])
+        else:
+            tok = kq.speculative_resample(p[k], None, orders[k], u[k])
+        assert (j, tok) == oracle_decide(draft, q, p, orders, u), trial
+
+
+def test_two_step_decision_errors():
+    lib = kq.load()
+    pos = ctypes.c_int32(-7)
+    one = np.ones(4, dtype=np.float32)
+    vp = lambda a: ctypes.c_void_p(a.ctypes.data)
+    assert lib.kq_speculative_first_reject(2, None, vp(one), vp(one), ctypes.byref(pos)) == NULL
+    assert lib.kq_speculative_first_reject(16, vp(one), vp(one), vp(one), ctypes.byref(pos)) == SHAPE
+    assert lib.kq_speculative_first_reject(0, None, None, None, ctypes.byref(pos)) == 0 and pos.value == 0
+    # a NaN probability rejects; q <= 0 accepts
+    nan = np.array([np.nan, 1.0], dtype=np.float32)
+    assert kq.speculative_first_reject(nan, np.ones(2, np.float32), np.zeros(2, np.float32)) == 0
+    assert kq.speculative_first_reject(np.zeros(2, np.float32), np.zeros(2, np.float32), np.full(2, 0.99, np.float32)) == 2
+    tok = ctypes.c_int32(-7)
+    p = np.array([0.5, 0.5, 0.0], dtype=np.float32)
+    bad = np.array([0, 3, 1], dtype=np.int32)
+    assert lib.kq_speculative_resample(3, vp(p), None, vp(bad), ctypes.c_float(0.1), ctypes.byref(tok)) == TOKEN
+    assert lib.kq_speculative_resample(0, vp(p), None, vp(bad), ctypes.c_float(0.1), ctypes.byref(tok)) == SHAPE
+    zero = np.zeros(3, dtype=np.float32)
+    order = np.array([2, 0, 1], dtype=np.int32)
+    # residual of p against itself is zero: falls back to p, whose walk skips the zero entry
+    assert kq.speculative_resample(p, p, order, 0.75) == 1
+    assert lib.kq_speculative_resample(3, vp(zero), vp(zero), vp(order), ctypes.c_float(0.1), ctypes.byref(tok)) == SHAPE
+    assert tok.value == -7, "written on an error"
+    assert kq.speculative_resample(p, None, order, 0.25) == 0

@@ -1,7 +1,8 @@
 """GPU tests of the stochastic verify: the target probability rows
 (kq_softmax_rows) against the oracle's fp64 softmax within the bound the fp32
-arithmetic allows, and the whole step at the LM-head size (verify logits ->
-probability rows -> host decision) against the oracle's decision."""
+arithmetic allows, the whole step at the LM-head size (verify logits ->
+probability rows -> host decision) against the oracle's decision, also in
+two steps from gathered p_i[d_i] and one copied row, and kq_gather_rows."""
 import numpy as np
 import pytest
 
@@ -101,6 +102,14 @@ def test_stochastic_verify_lm_head(kq):
         u = rng.random(m).astype(np.float32)
         got = kq.speculative_decide(draft, q, Ph, orders, u)
         assert got == oracle_decide(draft, q, Ph, orders, u), f"trial {trial}: library != oracle on the same rows"
+        # the same decision from p_i[d_i] gathered on the device and one row copied
+        p_at = kq.gather_rows(P[:kd], torch.tensor(draft, dtype=torch.int32, device=DEV)).cpu().numpy()
+        assert np.array_equal(p_at, Ph[np.arange(kd), draft])
+        j = kq.speculative_first_reject(p_at, q[np.arange(kd), draft], u[:kd])
+        row = P[j].cpu().numpy()
+        tok = (kq.speculative_resample(row, q[j], orders[j], u[j + 1]) if j < kd
+               else kq.speculative_resample(row, None, orders[kd], u[kd]))
+        assert (j, tok) == got, f"trial {trial}: two-step decision"
         same_gpu += 1
         want = oracle_decide(draft, q, Pref, orders, u)
         if got == want:
@@ -116,3 +125,20 @@ def test_stochastic_verify_lm_head(kq):
     log(f"stochastic LM head: {same_gpu} trials bitwise with the oracle on the GPU rows, {same_ref} equal "
         f"on the oracle's rows, {boundary} at a boundary; accepted lengths {sorted(accepted_hist)}")
     assert same_ref >= 20
+
+
+def test_gather_rows(kq):
+    """kq_gather_rows equals indexing on the host bit for bit; tokens
+    outside the row give NaN; a count below m reads only the first rows."""
+    rng = np.random.default_rng(3)
+    m, n = 16, 70001
+    R = rng.random((m, n)).astype(np.float32)
+    tok = rng.integers(0, n, m).astype(np.int32)
+    tok[3], tok[9] = -1, n
+    Rd = torch.from_numpy(R).to(DEV)
+    got = kq.gather_rows(Rd, torch.from_numpy(tok).to(DEV)).cpu().numpy()
+    ok = (tok >= 0) & (tok < n)
+    assert np.array_equal(got[ok], R[np.arange(m)[ok], tok[ok]])
+    assert np.all(np.isnan(got[~ok]))
+    few = kq.gather_rows(Rd, torch.from_numpy(tok[:5].copy()).to(DEV)).cpu().numpy()
+    assert few.shape == (5,) and np.array_equal(few[[0, 1, 2, 4]], R[[0, 1, 2, 4], tok[[0, 1, 2, 4]]])
