@@ -73,21 +73,35 @@ def log(*a):
 class Stack:
     """Device-resident weights, staged activations, outputs and scratch."""
 
-    def __init__(self, kq, torch, dev, layers, layout, launch="chain"):
+    def __init__(self, kq, torch, dev, layers, layout, launch="chain", on_matrix=None, keep_rows=False):
+        """`on_matrix(i, gemv, w_host)` is called with each matrix's host
+        bytes before they are uploaded (a parity check computes its oracle
+        rows there, so the 16 GB of host bytes need not be kept)."""
         self.kq, self.torch, self.dev = kq, torch, dev
         self.layout = layout
         self.launch = launch
+        # keep_rows: also keep the llama.cpp row-layout copy of every matrix
+        # resident (the row-layout figures)
+        self.keep_rows = keep_rows and layout == kq.LAYOUT_TILED16
+        self.w_rows = []
         self.mats = synthetic.stack_matrices(layers)
         head = synthetic.LM_HEAD
         self.head = synthetic.Gemv(n=head["n"], k=head["k"], seed=head["seed"])
         t0 = time.time()
         self.w = []
         for i, g in enumerate(self.mats):
-            self.w.append(self.resident(synthetic.q4k_matrix(g.n, g.k, g.seed), g.n, g.k))
+            w_host = synthetic.q4k_matrix(g.n, g.k, g.seed)
+            if on_matrix is not None:
+                on_matrix(i, g, w_host)
+            self.w.append(self.resident(w_host, g.n, g.k))
+            del w_host
             if i % 50 == 0:
                 log(f"bench: generated {i + 1}/{len(self.mats)} matrices ({time.time() - t0:.1f} s)")
-        self.w_head = self.resident(synthetic.q4k_matrix(self.head.n, self.head.k, self.head.seed),
-                                    self.head.n, self.head.k)
+        w_host = synthetic.q4k_matrix(self.head.n, self.head.k, self.head.seed)
+        if on_matrix is not None:
+            on_matrix(len(self.mats), self.head, w_host)
+        self.w_head = self.resident(w_host, self.head.n, self.head.k)
+        del w_host
         torch.cuda.synchronize()
         log(f"bench: weights resident ({time.time() - t0:.1f} s)")
         self.ks = sorted({g.k for g in self.mats} | {self.head.k})
@@ -101,8 +115,9 @@ class Stack:
             for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
                 self.groups.append(tuple(base + i for i in idx))
         keys = sorted({(self.mats[g[0]].n, self.mats[g[0]].k, len(g)) for g in self.groups})
-        self.out = {kk: [torch.empty((16, kk[0]), dtype=torch.float32, device=dev) for _ in range(kk[2])]
-                    for kk in keys}
+        # one output buffer per matrix (every logit of the step stays
+        # available for the parity check: 230 MB at M = 16)
+        self.out = [torch.empty((16, g.n), dtype=torch.float32, device=dev) for g in self.mats]
         self.scratch = {kk: kq.new_group_scratch(kk[0], kk[1], kk[2], dev) for kk in keys}
         self.chains = {}
         self.head_scratch = kq.new_scratch(self.head.n, self.head.k, dev)
@@ -121,6 +136,8 @@ class Stack:
         w = self.torch.from_numpy(w_host).to(self.dev)
         if self.layout == self.kq.LAYOUT_TILED16:
             t = self.kq.tile_weights(w, n, k)
+            if self.keep_rows:
+                self.w_rows.append(w)
             del w
             return t
         return w
@@ -136,9 +153,8 @@ class Stack:
             phases = []
             for grp in self.groups:
                 g = self.mats[grp[0]]
-                key = (g.n, g.k, len(grp))
                 phases.append(([self.w[j] for j in grp], g.n, g.k, self.staged[g.k],
-                               [o[:m] for o in self.out[key]]))
+                               [self.out[j][:m] for j in grp]))
             self.chains[m] = self.kq.chain_encode(phases, m, layout=self.layout)
         return self.chains[m]
 
@@ -153,7 +169,7 @@ class Stack:
                 g = self.mats[grp[0]]
                 key = (g.n, g.k, len(grp))
                 kq.gemv_staged_group([self.w[j] for j in grp], g.n, g.k, self.staged[g.k], m, self.scratch[key],
-                                     logits=[o[:m] for o in self.out[key]], layout=self.layout)
+                                     logits=[self.out[j][:m] for j in grp], layout=self.layout)
         h = self.head
         kq.verify_staged(self.w_head, h.n, h.k, self.staged[h.k], m, self.draft[:m - 1],
                          self.head_scratch, out=(self.am[:m], self.acc, None), layout=self.layout)
@@ -174,8 +190,7 @@ class Stack:
     def snapshot(self, m):
         self.torch.cuda.synchronize()
         return (self.am[:m].cpu().numpy().copy(), self.acc.cpu().numpy().copy(),
-                {(key, j): o[:m, :64].cpu().numpy().copy() for key, outs in self.out.items()
-                 for j, o in enumerate(outs)})
+                {j: o[:m, :64].cpu().numpy().copy() for j, o in enumerate(self.out)})
 
 
 def same(a, b):
@@ -229,8 +244,8 @@ def run_m(stack, torch, m, steps, warmup, use_graph, extras=True):
     wall, ev = timed(torch, fn, steps)
     if not same(stack.snapshot(m), eager):
         raise RuntimeError(f"timed steps at M={m} changed the results")
-    if stack.launch == "chain" and stack.chain(m).error_word() != 0:
-        raise RuntimeError(f"a chain barrier timed out at M={m}")
+    if stack.launch == "chain":
+        stack.chain(m).status()  # raises KQError when a chain wait gave up
     if not extras:
         return wall, ev, None
     # spread over steps: each of `steps` further steps between its own events
@@ -318,10 +333,15 @@ def config_timings(stack, torch, calls=50):
     dev = stack.dev
     out = {}
 
-    def rate(nbytes, m, us):
+    def rate(nbytes, m, us, alg=None, kernel="kq_gemv_kernel"):
+        """nbytes: weight bytes per call; alg: algorithmic bytes per call
+        (weights + activations + outputs) for the roofline point."""
         gbs = nbytes / (us * 1e-6) / 1e9
-        return {"us_per_call": round(us, 2), "rows_per_s": round(m / (us * 1e-6), 1),
-                "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        r = {"us_per_call": round(us, 2), "rows_per_s": round(m / (us * 1e-6), 1),
+             "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if alg is not None:
+            r["roofline"] = roofline_entry(kernel, alg, us)
+        return r
 
     def time_calls(fn):
         return graph_time(torch, fn, calls)
@@ -343,7 +363,7 @@ def config_timings(stack, torch, calls=50):
         st = kq.stage_rows(x[:m])
         us = time_calls(lambda i: kq.gemv_staged(ws[i % 16], n, k, st, m, scratch, logits=logits[:m],
                                                    layout=kq.LAYOUT_TILED16))
-        res[f"m{m}"] = rate(wbytes, m, us)
+        res[f"m{m}"] = rate(wbytes, m, us, wbytes + 4 * m * (n + k))
     res["m16_over_m1"] = round(res["m16"]["us_per_call"] / res["m1"]["us_per_call"], 4)
     out["square_6656x6656"] = res
     del ws
@@ -356,14 +376,15 @@ def config_timings(stack, torch, calls=50):
     logits = torch.empty((16, n), dtype=torch.float32, device=dev)
     us = time_calls(lambda i: kq.gemv_staged(ws[i % 4], n, k, st, 16, scratch, logits=logits,
                                                layout=kq.LAYOUT_TILED16))
-    out["fc_33280_to_6656_m16"] = rate(n * synthetic.q4k_bytes_per_row(k), 16, us)
+    out["fc_33280_to_6656_m16"] = rate(n * synthetic.q4k_bytes_per_row(k), 16, us,
+                                       n * synthetic.q4k_bytes_per_row(k) + 4 * 16 * (n + k))
     del ws
     h = stack.head
     sth = stack.staged[h.k]
     kq.stage_rows(stack.x[h.k][:16], staged=sth)
     us = time_calls(lambda i: kq.verify_staged(stack.w_head, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
                                                  out=(stack.am, stack.acc, None), layout=stack.layout))
-    out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us)
+    out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us, h.weight_bytes + 4 * 16 * h.k + 4 * 18)
     out["stochastic_lm_head_m16"] = stochastic_timing(stack, torch, time_calls)
     out.update(kquant_timings(stack, torch, time_calls))
     tree = out["tree_verify_lm_head"]
@@ -385,10 +406,13 @@ def kquant_timings(stack, torch, time_calls):
     dev = stack.dev
     out = {}
 
-    def rate(nbytes, m, us):
+    def rate(nbytes, m, us, alg=None):
         gbs = nbytes / (us * 1e-6) / 1e9
-        return {"us_per_call": round(us, 2), "rows_per_s": round(m / (us * 1e-6), 1),
-                "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        r = {"us_per_call": round(us, 2), "rows_per_s": round(m / (us * 1e-6), 1),
+             "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if alg is not None:
+            r["roofline"] = roofline_entry("kq_gemv_kernel", alg, us)
+        return r
 
     sq = synthetic.SQUARE
     n, k = sq["n"], sq["k"]
@@ -404,7 +428,7 @@ def kquant_timings(stack, torch, time_calls):
             st = kq.stage_rows(x[:m])
             us = time_calls(lambda i: kq.gemv_staged(ws[i % 16], n, k, st, m, scratch, logits=logits[:m],
                                                        layout=layout))
-            res[f"m{m}"] = rate(n * (k // 256) * bb, m, us)
+            res[f"m{m}"] = rate(n * (k // 256) * bb, m, us, n * (k // 256) * bb + 4 * m * (n + k))
         out[f"square_6656x6656_{fmt}"] = res
         del ws
     h = stack.head
@@ -413,7 +437,8 @@ def kquant_timings(stack, torch, time_calls):
     kq.stage_rows(stack.x[h.k][:16], staged=sth)
     us = time_calls(lambda i: kq.verify_staged(w6, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
                                                  out=(stack.am, stack.acc, None), layout=kq.LAYOUT_Q6K_TILED16))
-    out["lm_head_verify_m16_q6k"] = rate(h.n * (h.k // 256) * 210, 16, us)
+    out["lm_head_verify_m16_q6k"] = rate(h.n * (h.k // 256) * 210, 16, us,
+                                         h.n * (h.k // 256) * 210 + 4 * 16 * h.k + 4 * 18)
     del w6
     # token-tree verify on the resident Q4_K head: a tree of m nodes (parent
     # within the previous 6 nodes, seeded tokens), all nodes in one pass
@@ -429,7 +454,7 @@ def kquant_timings(stack, torch, time_calls):
         path = torch.empty(m, dtype=torch.int32, device=dev)
         us = time_calls(lambda i: kq.verify_tree_staged(stack.w_head, h.n, h.k, st, parent, token, stack.head_scratch,
                                                           out=(am, acc, path, None), layout=stack.layout))
-        tree[f"m{m}"] = rate(h.weight_bytes, m, us)
+        tree[f"m{m}"] = rate(h.weight_bytes, m, us, h.weight_bytes + 4 * m * h.k + 4 * (2 * m + 2))
     out["tree_verify_lm_head"] = tree
     torch.cuda.synchronize()
     return out
@@ -518,6 +543,75 @@ def stochastic_timing(stack, torch, time_calls, temperature=300.0, decisions=20)
             "mean_accepted": round(float(np.mean(accepted)), 2)}
 
 
+def rows_layout_timing(stack, torch, steps):
+    """The step streamed from llama.cpp's row-major blocks, next to the
+    tiled headline: (a) the same chain with KQ_LAYOUT_ROWS (its outputs are
+    checked bitwise against the tiled chain's: the layouts give identical
+    results), and (b) the step as the boundary's two all-in-one entry
+    points make it, kq_gemv_rows per stack matrix (each stages its own
+    activations) and kq_verify_argmax_accept on the LM head, 365 calls in
+    one HIP graph. M = 16 and M = 1; milliseconds per step and weight GB/s."""
+    kq = stack.kq
+    out = {}
+    if not stack.w_rows:
+        return None
+    w_head_rows = stack.w_rows[-1]
+    ws = {}
+    for g in stack.mats + [stack.head]:
+        key = (g.n, g.k)
+        if key not in ws:
+            ws[key] = kq.lib.alloc_workspace(kq.workspace_bytes(g.n, g.k, 16), stack.dev)
+    for m in (16, 1):
+        for k in stack.ks:
+            kq.stage_rows(stack.x[k][:m], staged=stack.staged[k])
+        phases = []
+        for grp in stack.groups:
+            g = stack.mats[grp[0]]
+            phases.append(([stack.w_rows[j] for j in grp], g.n, g.k, stack.staged[g.k],
+                           [stack.out[j][:m] for j in grp]))
+        chain = kq.chain_encode(phases, m, layout=kq.LAYOUT_ROWS)
+        ref = None
+        if stack.launch == "chain":
+            kq.gemv_chain(stack.chain(m))
+            torch.cuda.synchronize()
+            ref = [o[:m, :64].cpu().numpy().copy() for o in stack.out]
+        us_chain = event_us(torch, lambda: kq.gemv_chain(chain), max(3, steps // 4))
+        chain.status()
+        if ref is not None:
+            for j, o in enumerate(stack.out):
+                if not np.array_equal(o[:m, :64].cpu().numpy(), ref[j]):
+                    raise RuntimeError(f"row-layout chain differs from the tiled chain (matrix {j}, M={m})")
+        h = stack.head
+        am = torch.empty(m, dtype=torch.int32, device=stack.dev)
+        acc = torch.empty(2, dtype=torch.int32, device=stack.dev)
+
+        def boundary_step(_i):
+            for j, g in enumerate(stack.mats):
+                kq.gemv_rows(stack.w_rows[j], g.n, g.k, stack.x[g.k][:m], logits=stack.out[j][:m],
+                             workspace=ws[(g.n, g.k)])
+            kq.verify(w_head_rows, h.n, h.k, stack.x[h.k][:m], stack.draft[:m - 1], workspace=ws[(h.n, h.k)],
+                      out=(am, acc, None))
+        us_b = graph_time(torch, boundary_step, 1, reps=max(3, steps // 4))
+        # the head verify is not in the chain launch: add its row-layout time
+        us_head = graph_time(torch, lambda i: kq.verify_staged(w_head_rows, h.n, h.k, stack.staged[h.k], m,
+                                                                stack.draft[:m - 1], stack.head_scratch,
+                                                                out=(am, acc, None), layout=kq.LAYOUT_ROWS), 20)
+        step_chain = us_chain + us_head
+        out[f"m{m}"] = {
+            "chain_rows_ms_per_step": round(step_chain * 1e-3, 4),
+            "chain_rows_weight_gb_s": round(stack.weight_bytes / (step_chain * 1e-6) / 1e9, 1),
+            "chain_rows_hbm_frac": round(stack.weight_bytes / (step_chain * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "boundary_calls_ms_per_step": round(us_b * 1e-3, 4),
+            "boundary_calls_weight_gb_s": round(stack.weight_bytes / (us_b * 1e-6) / 1e9, 1),
+            "boundary_calls_hbm_frac": round(stack.weight_bytes / (us_b * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del chain
+    out["note"] = ("chain_rows: the headline's chain launch plus the LM-head verify, weights in llama.cpp rows; "
+                   "boundary_calls: kq_gemv_rows x 364 + kq_verify_argmax_accept (each call stages its own "
+                   "activations), one HIP graph")
+    torch.cuda.synchronize()
+    return out
+
+
 def read_ceiling(stack, torch, calls=20):
     """Pure-read rate of this device on the resident LM-head weights (the
     library's read probe: every byte loaded once): the achievable ceiling
@@ -572,20 +666,66 @@ def stored_traffic(workload, m, layout_name):
     return float(v) if v else None
 
 
-def kernel_roofline(stack, m, ev_step, workload, layout_name):
-    """The main kernel's roofline point. Its average launch duration is the
-    timed region's HIP-event time per step divided by its launches per step
-    (the kernels run back to back in the graph; the two small staging
-    launches per step are included, so this slightly overstates the
-    duration); achieved = algorithmic bytes per launch / that duration."""
-    n = stack.launches
-    avg_s = ev_step / n
-    avg_b = float(np.mean(stack.algorithmic_bytes(m)))
-    ach = avg_b / avg_s / 1e9
+def roofline_entry(kernel, algorithmic_bytes, us, launches=1, traffic=None):
+    """One kernel's roofline point: algorithmic bytes per launch / its own
+    average launch duration (HIP events on the stream it runs on)."""
+    ach = algorithmic_bytes / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": stored_traffic(workload, m, layout_name),
-            "kernel": "kq_gemv_kernel", "launches_per_step": n, "avg_launch_us": round(avg_s * 1e6, 3),
-            "avg_algorithmic_bytes": int(avg_b)}
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "avg_launch_us": round(us, 3), "launches": launches, "algorithmic_bytes": int(algorithmic_bytes)}
+
+
+def event_us(torch, fn, reps):
+    """Microseconds per call of fn(), eager, between two HIP events on the
+    current stream (for launches long enough that the host's per-call cost
+    hides behind the GPU: the chain launch)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def kernel_rooflines(stack, torch, m, reps, workload, layout_name):
+    """Every kernel of the step timed on its own, at M = m: the stack (one
+    chain launch, or the 208 grouped launches), the LM-head verify, and the
+    activation staging (one launch per distinct K). Each gets its own
+    roofline point; their sum is compared with the step time."""
+    kq = stack.kq
+    for k in stack.ks:
+        kq.stage_rows(stack.x[k][:m], staged=stack.staged[k])
+    out = {}
+    if stack.launch == "chain":
+        ch = stack.chain(m)
+        us = event_us(torch, lambda: kq.gemv_chain(ch), reps)
+        ch.status()
+        out["stack_chain"] = roofline_entry("kq_gemv_kernel (chain, 208 phases)", stack.algorithmic_bytes(m)[0], us,
+                                            1, stored_traffic(workload, m, layout_name))
+    else:
+        def grouped():
+            for grp in stack.groups:
+                g = stack.mats[grp[0]]
+                key = (g.n, g.k, len(grp))
+                kq.gemv_staged_group([stack.w[j] for j in grp], g.n, g.k, stack.staged[g.k], m, stack.scratch[key],
+                                     logits=[stack.out[j][:m] for j in grp], layout=stack.layout)
+        us = graph_time(torch, lambda i: grouped(), 1, reps=reps) / len(stack.groups)
+        out["stack_grouped"] = roofline_entry("kq_gemv_kernel (grouped, per launch)",
+                                              float(np.mean(stack.algorithmic_bytes(m)[:-1])), us, len(stack.groups))
+    h = stack.head
+    us = graph_time(torch, lambda i: kq.verify_staged(stack.w_head, h.n, h.k, stack.staged[h.k], m,
+                                                      stack.draft[:m - 1], stack.head_scratch,
+                                                      out=(stack.am[:m], stack.acc, None), layout=stack.layout), 20)
+    out["lm_head_verify"] = roofline_entry("kq_gemv_kernel (LM-head verify)", stack.algorithmic_bytes(m)[-1], us)
+    x_bytes = sum(4 * m * k + kq.staged_bytes(k) for k in stack.ks)
+    us = graph_time(torch, lambda i: [kq.stage_rows(stack.x[k][:m], staged=stack.staged[k]) for k in stack.ks], 20)
+    out["stage"] = roofline_entry("kq_stage_kernel (all distinct K)", x_bytes, us, len(stack.ks))
+    out["sum_us"] = round(sum(v["avg_launch_us"] * v["launches"] for v in out.values() if isinstance(v, dict)), 2)
+    return out
 
 
 def copy_probe(torch, dev, nbytes=1 << 30):
@@ -599,29 +739,35 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     log(f"bench: copy probe {nbytes} bytes x 3")
 
 
-def cpu_baseline(target_s):
+def cpu_baseline(target_s, check=None):
     """The oracle (plain C, fp64, OpenMP) on a bounded sample of the step, at
     M = 16, on the same bytes the GPU gets: the LM head in full and whole
     stack layers, as many as fit in about target_s seconds. The step time is
-    52 x the mean layer time + the head time (exact when all layers ran)."""
+    52 x the mean layer time + the head time (exact when all layers ran).
+    check(i, L, A) is called, outside the timed calls, with the oracle's
+    logits and tolerance mass of every matrix it ran (i = stack index, or
+    None for the LM head)."""
     import oracle
     threads = oracle.num_threads()
     head = synthetic.LM_HEAD
     xs = {k: synthetic.activations(16, k, synthetic.stack_activation_seed(k))
           for k in (synthetic.HIDDEN, synthetic.FFN)}
 
-    def timed_gemv(n, k, seed):
+    def timed_gemv(i, n, k, seed):
         w = synthetic.q4k_matrix(n, k, seed)
         t0 = time.perf_counter()
-        oracle.gemv_rows(w, k, xs[k])
-        return time.perf_counter() - t0
+        L, A = oracle.gemv_rows(w, k, xs[k])
+        t = time.perf_counter() - t0
+        if check is not None:
+            check(i, L, A)
+        return t
 
-    t_head = timed_gemv(head["n"], head["k"], head["seed"])
+    t_head = timed_gemv(None, head["n"], head["k"], head["seed"])
     mats = synthetic.stack_matrices(synthetic.LAYERS)
     layer_times = []
     spent = t_head
     for layer in range(synthetic.LAYERS):
-        t = sum(timed_gemv(g.n, g.k, g.seed) for g in mats[7 * layer:7 * layer + 7])
+        t = sum(timed_gemv(7 * layer + j, g.n, g.k, g.seed) for j, g in enumerate(mats[7 * layer:7 * layer + 7]))
         layer_times.append(t)
         spent += t
         if spent + float(np.mean(layer_times)) > target_s:
@@ -647,6 +793,58 @@ def cpu_baseline(target_s):
                                       f"({t_all:.3f} s); the step scaled by that ratio"}}
 
 
+class StepCheck:
+    """Parity of the timed step at M = 16 against the oracle outputs the CPU
+    baseline computes anyway: every logit of every stack matrix it ran
+    within 1e-4 * sum_k |w_k x_k|, and the LM head's argmax (ties within the
+    tolerance may resolve to any candidate) and accept decision."""
+
+    def __init__(self, stack, outs, am, acc):
+        self.stack, self.outs, self.am, self.acc = stack, outs, am, acc
+        self.matrices = 0
+        self.logits = 0
+        self.worst = 0.0
+        self.head = None
+
+    def __call__(self, i, L, A):
+        import oracle
+        if i is None:
+            o_am, o_nc = oracle.argmax_flags(L, A)
+            flagged = []
+            for r in range(L.shape[0]):
+                ok = int(self.am[r]) == int(o_am[r])
+                if o_nc[r]:
+                    flagged.append(r)
+                    ok = ok or int(self.am[r]) in set(int(c) for c in oracle.candidates(L[r], A[r], int(o_am[r])))
+                if not ok:
+                    raise RuntimeError(f"parity: LM-head row {r} argmax {self.am[r]} != oracle {o_am[r]}")
+            draft = self.stack.draft[:15]
+            acc_g = oracle.accept(draft, [int(v) for v in self.am])
+            if tuple(int(v) for v in self.acc) != acc_g:
+                raise RuntimeError("parity: the accept decision does not follow the GPU's argmaxes")
+            acc_o = oracle.accept(draft, [int(v) for v in o_am])
+            exact = not any(o_nc[:acc_o[0] + 1])
+            if exact and acc_g != acc_o:
+                raise RuntimeError(f"parity: accept {acc_g} != oracle {acc_o}")
+            self.head = {"argmax_rows": int(L.shape[0]), "flagged_rows": flagged, "accept": list(acc_g),
+                         "accept_equals_oracle": acc_g == acc_o}
+            return
+        G = self.outs[i].astype(np.float64)
+        err = np.abs(G - L)
+        tol = 1e-4 * A
+        if not np.all(err <= tol):
+            bad = np.argwhere(err > tol)[0]
+            raise RuntimeError(f"parity: stack matrix {i} logit {tuple(bad)} off by {err[tuple(bad)]!r} "
+                               f"> tolerance {tol[tuple(bad)]!r}")
+        self.worst = max(self.worst, float(np.max(err / np.maximum(tol, 1e-300))))
+        self.matrices += 1
+        self.logits += int(G.size)
+
+    def result(self):
+        return {"against": "oracle (cpu_baseline's own outputs, M = 16)", "stack_matrices": self.matrices,
+                "logits": self.logits, "max_err_over_tol": float(f"{self.worst:.3g}"), "lm_head": self.head}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -662,33 +860,56 @@ def main():
     if args.copy_probe:
         copy_probe(torch, dev)
     layout = kq.LAYOUT_TILED16 if args.layout == "tiled" else kq.LAYOUT_ROWS
-    stack = Stack(kq, torch, dev, args.layers, layout, args.launch)
+    stack = Stack(kq, torch, dev, args.layers, layout, args.launch, keep_rows=not args.no_extras)
     use_graph = not args.no_graph
     workload = f"stack{args.layers}_q4k+lmhead_verify"
+    layout_name = "tiled16" if layout == kq.LAYOUT_TILED16 else "rows"
     res = {}
+    snap16 = None
     for m in ((16, 1) if args.m == "both" else (int(args.m),)):
         wall, ev, spread = run_m(stack, torch, m, args.steps, args.warmup, use_graph, not args.no_extras)
-        roof = kernel_roofline(stack, m, ev, workload, "tiled16" if layout == kq.LAYOUT_TILED16 else "rows")
+        if m == 16 and not args.no_cpu:
+            # every output of the timed steps, for the parity check against
+            # the oracle outputs of the CPU baseline (outside the timed region)
+            torch.cuda.synchronize()
+            snap16 = ([o.cpu().numpy() for o in stack.out], stack.am.cpu().numpy().copy(),
+                      stack.acc.cpu().numpy().copy())
         gbs = stack.weight_bytes / wall / 1e9
         res[m] = {"ms_per_step": round(wall * 1e3, 4), "rows_per_s": round(m / wall, 2),
                   "weight_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                  "event_ms_per_step": round(ev * 1e3, 4), "step_spread": spread, "roofline": roof}
-        log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s, "
-            f"kernel {roof['avg_launch_us']} us/launch, {roof['achieved']} GB/s")
-    draft = ceiling = cfgs = None
+                  "event_ms_per_step": round(ev * 1e3, 4), "step_spread": spread}
+        if not args.no_extras:
+            kr = kernel_rooflines(stack, torch, m, max(5, args.steps // 2), workload, layout_name)
+            res[m]["kernels"] = kr
+            res[m]["roofline"] = kr["stack_chain" if args.launch == "chain" else "stack_grouped"]
+            log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s; kernels "
+                + ", ".join(f"{k} {v['avg_launch_us']} us ({v['frac']})" for k, v in kr.items() if isinstance(v, dict)))
+        else:
+            log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s")
+    draft = ceiling = cfgs = rows_fig = None
     if not args.no_extras:
         draft = draft_block_timing(stack, torch)
         ceiling = read_ceiling(stack, torch)
+        rows_fig = rows_layout_timing(stack, torch, args.steps)
+        log("bench: row layout " + json.dumps(rows_fig))
         cfgs = config_timings(stack, torch)
         log("bench: configs " + json.dumps(cfgs))
         log(f"bench: read ceiling {ceiling['gb_s']} GB/s ({ceiling['frac']:.3f} of peak)")
         log(f"bench: draft block proposals {draft['us_per_call']} us/call, {draft['weight_gb_s']} GB/s")
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu:
+        check = StepCheck(stack, *snap16) if snap16 is not None else None
         try:
-            cpu = cpu_baseline(args.cpu_seconds)
+            cpu = cpu_baseline(args.cpu_seconds, check)
+        except RuntimeError as e:
+            if str(e).startswith("parity:"):
+                raise  # a wrong result produces no bench line
+            cpu = {"error": repr(e)}
         except Exception as e:  # the baseline must not hide the GPU result
             cpu = {"error": repr(e)}
+        if check is not None and "error" not in cpu:
+            parity = check.result()
+            log(f"bench: parity vs oracle: {json.dumps(parity)}")
     head_m = 16 if 16 in res else min(res)
     top = res[head_m]
     rec = {
@@ -713,11 +934,13 @@ def main():
         "m16": res.get(16),
         "m1": res.get(1),
         "m16_over_m1": round(res[16]["ms_per_step"] / res[1]["ms_per_step"], 4) if len(res) == 2 else None,
-        "roofline": top["roofline"],
+        "roofline": top.get("roofline"),
         "read_ceiling": ceiling,
         "draft_block_argmax": draft,
         "configs": cfgs,
+        "rows_layout": rows_fig,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(rec), flush=True)
 

@@ -46,13 +46,32 @@
  *    failure (hipGetLastError after enqueue).
  *  - Concurrency: calls on different streams need different workspaces;
  *    calls sharing a workspace must be ordered (e.g. the same stream).
- *  - Numerics: fp32 accumulation. |logit - exact| <= 1e-4 * sum_k |w_k x_k|
- *    for finite inputs with |dmin| * 63 <= 65504; results are bitwise
- *    deterministic, and for m <= 16 row i of an m-row call equals the 1-row
- *    call on x[i] bit for bit (calls of more than 16 rows may cut the work
- *    differently; they meet the same bound). A call of 33 to 64 rows equals
- *    a 32-row call on rows 0-31 and a call on the remaining rows, bit for
- *    bit. There is no CPU or alternate path.
+ *  - Numerics: every product of a weight operand and an activation operand
+ *    is exact (fp16 x fp16, the activations split into an exact fp16 pair),
+ *    sums are fp32. The scale term d sc_j q_k and the min term dmin m_j of
+ *    each weight are contracted apart and subtracted once per 256-column
+ *    block, so the rounding error is bounded by the mass of both terms,
+ *    B = sum_k (|d sc_j q_k| + |dmin m_j|) |x_k| (B = sum_k |w_k x_k| for
+ *    Q6_K, which has no min term):
+ *        |logit - exact| <= 2^-24 (544 + k/128) B
+ *    for finite inputs with |dmin| * 63 <= 65504 (a worst case that lets
+ *    every fp32 addition round; activations smaller than 2^-12 of the
+ *    largest magnitude of their row in their 256-column block may each add
+ *    an absolute error of 2^-34 of that magnitude times their weight's term
+ *    mass). This guarantees the tolerance 1e-4 * sum_k |w_k x_k| whenever B
+ *    is at most 2 times sum_k |w_k x_k| (k <= 33,280), which covers weights
+ *    that are mostly of one sign (every configured workload: B is about 1.3
+ *    times that mass). Weights centred on zero, as quantizers fit real
+ *    weights (B about 4 times), are outside that guarantee but are held to
+ *    the tolerance by the tests (tests/test_gpu_cancel.py). Weights whose
+ *    two terms cancel (w = 0 with d, dmin nonzero) contribute to B but not
+ *    to the tolerance, so a row of them can exceed 1e-4 * sum_k |w_k x_k|,
+ *    never the bound above. Results are bitwise deterministic, and for
+ *    m <= 16 row i of an m-row call equals the 1-row call on x[i] bit for
+ *    bit (calls of more than 16 rows may cut the work differently; they
+ *    meet the same bound). A call of 33 to 64 rows equals a 32-row call on
+ *    rows 0-31 and a call on the remaining rows, bit for bit. There is no
+ *    CPU or alternate path.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -441,12 +460,16 @@ kq_status kq_speculative_resample(int64_t n, const float *p_row, const float *q_
  * that call uses the same geometry: 8 waves of one 16-row tile and the
  * same number of workgroups).
  *
- * The kernel keeps all of its workgroups resident at once (one per CU);
- * kq_chain_encode sizes the grid from the current device's capacity. Each
- * wait (at a barrier, or for another workgroup's partial sums of a row
- * group) is bounded: a wait longer than one second gives up, sets the 32-bit
- * word at byte KQ_CHAIN_ERROR_OFFSET of the scratch to nonzero and ends the
- * launch early (its logits are then incomplete). That word is sticky:
+ * Precondition: every workgroup of a chain launch is resident at once (one
+ * per CU); kq_chain_encode sizes the grid from the current device's
+ * capacity, assuming the chain has the device to itself while it runs.
+ * Work from another stream that occupies CUs meanwhile (another chain, a
+ * kernel that holds a CU) can keep workgroups from starting and the others
+ * from passing a barrier. Each wait (at a barrier, or for another
+ * workgroup's partial sums of a row group) is bounded: a wait longer than
+ * one second gives up, sets the 32-bit word at byte KQ_CHAIN_ERROR_OFFSET of
+ * the scratch to nonzero and ends the launch early (its logits are then
+ * incomplete). kq_chain_status reports that word; it is sticky:
  * kq_chain_scratch_init clears it, together with the state the failed
  * launch left behind. */
 
@@ -512,6 +535,17 @@ kq_status kq_chain_scratch_init(const kq_chain_plan *plan, void *scratch, size_t
  * Calls sharing a scratch must be ordered (e.g. the same stream). */
 kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan,
                         void *scratch, size_t scratch_bytes, void *stream);
+
+/* Outcome of the chain launches on `scratch` so far: KQ_OK, or KQ_ERR_LAUNCH
+ * when a wait of one of them gave up (the time-out word is set; the logits
+ * of that launch are incomplete, and the scratch needs
+ * kq_chain_scratch_init before the next launch). Unlike every other call,
+ * this one waits: it copies the word to the host on `stream` and
+ * synchronises that stream, so it reports every launch enqueued before it.
+ *  plan, scratch  as for kq_gemv_chain (the scratch of those launches)
+ * KQ_ERR_NULL / SHAPE / ALIGN / WORKSPACE for invalid arguments (nothing
+ * enqueued); KQ_ERR_LAUNCH also when the copy itself fails. */
+kq_status kq_chain_status(const kq_chain_plan *plan, const void *scratch, size_t scratch_bytes, void *stream);
 
 #ifdef __cplusplus
 }

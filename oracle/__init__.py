@@ -82,6 +82,8 @@ def _load():
     lib.kqo_gemv_rows_fmt.restype = ctypes.c_int
     lib.kqo_tree_accept.argtypes = [P, P, ctypes.c_int, P, P, P, P]
     lib.kqo_tree_accept.restype = ctypes.c_int
+    lib.kqo_term_mass_q4k.argtypes = [P, i64, i64, P, ctypes.c_int, P, i64, P]
+    lib.kqo_term_mass_q4k.restype = ctypes.c_int
     lib.kqo_num_threads.argtypes = []
     lib.kqo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -167,6 +169,30 @@ def gemv_rows(w: np.ndarray, k: int, x: np.ndarray, rows: Optional[Sequence[int]
     if rc:
         raise ValueError("bad shape")
     return L, A
+
+
+def term_mass(w: np.ndarray, k: int, x: np.ndarray, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """B, float64 [M, n_out]: sum_k (|d sc_j q_k| + |dmin m_j|) |x_k| for a
+    Q4_K matrix (kqo_term_mass_q4k), the mass the rounding error of a kernel
+    that forms a block's scale and min terms apart is proportional to."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    n, m = w.shape[0], x.shape[0]
+    if x.shape[1] != k or w.shape[1] != (k // 256) * 144:
+        raise ValueError("shape mismatch")
+    r_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nout = n if r_arr is None else r_arr.shape[0]
+    B = np.zeros((m, nout), dtype=np.float64)
+    rc = _load().kqo_term_mass_q4k(_p(w), n, k, _p(x), m, _p(r_arr) if r_arr is not None else None, nout, _p(B))
+    if rc == -3:
+        raise ValueError("non-finite activation")
+    if rc == -2:
+        raise ValueError("non-finite block scale")
+    if rc:
+        raise ValueError("bad shape")
+    return B
 
 
 def argmax_flags(L: np.ndarray, A: np.ndarray, rel: float = REL_TOL) -> Tuple[np.ndarray, np.ndarray]:

@@ -273,6 +273,54 @@ int kqo_gemv_rows_fmt(int fmt, const uint8_t *w, int64_t n, int64_t k, const flo
     return bad ? -2 : 0;
 }
 
+/* Mass of the two terms of each Q4_K weight: B[m][n] = sum_k (|d sc_j q_k|
+ * + |dmin m_j|) |x[m][k]|, where w_k = d sc_j q_k - dmin m_j (the same
+ * decode as kqo_decode_block, its two terms kept apart). This is not part
+ * of what the method computes. It is the quantity a kernel that forms the
+ * scale term and the min term of a block separately (each from exact
+ * products) and subtracts them in floating point has its rounding error
+ * proportional to; B >= A, with equality when no weight mixes a positive
+ * scale term with a positive min term (dmin = 0, or q = 0 everywhere).
+ * Outputs [m][n_rows] (rows may be NULL: all n rows); returns as
+ * kqo_gemv_rows. */
+int kqo_term_mass_q4k(const uint8_t *w, int64_t n, int64_t k, const float *x, int m,
+                      const int64_t *rows, int64_t n_rows, double *B) {
+    if (n <= 0 || k <= 0 || k % KQO_QK || m <= 0) return -1;
+    for (int64_t i = 0; i < (int64_t)m * k; ++i)
+        if (!isfinite(x[i])) return -3;
+    int64_t nout = rows ? n_rows : n;
+    for (int64_t r = 0; r < nout; ++r)
+        if (rows && (rows[r] < 0 || rows[r] >= n)) return -1;
+    int64_t row_bytes = (k / KQO_QK) * KQO_BLOCK;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nout; ++r) {
+        int64_t nn = rows ? rows[r] : r;
+        for (int mm = 0; mm < m; ++mm) B[(int64_t)mm * nout + r] = 0.0;
+        for (int64_t b = 0; b < k / KQO_QK; ++b) {
+            const uint8_t *blk = w + nn * row_bytes + b * KQO_BLOCK;
+            double d = kqo_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+            double dmin = kqo_half_to_double((uint16_t)(blk[2] | (blk[3] << 8)));
+            if (isnan(d) || isnan(dmin)) {
+#pragma omp atomic write
+                bad = 1;
+                break;
+            }
+            int sc[8], mn[8];
+            kqo_scales_mins(blk + 4, sc, mn);
+            for (int i = 0; i < KQO_QK; ++i) {
+                int j = i / 32;
+                double term = fabs(d * (double)sc[j] * (double)kqo_quant(blk + 16, i)) +
+                              fabs(dmin * (double)mn[j]);
+                int64_t kk = b * KQO_QK + i;
+                for (int mm = 0; mm < m; ++mm)
+                    B[(int64_t)mm * nout + r] += term * fabs((double)x[(int64_t)mm * k + kk]);
+            }
+        }
+    }
+    return bad ? -2 : 0;
+}
+
 /* Per row m: argmax[m] = lowest index attaining the maximum of L[m][:],
  * n_cand[m] = number of other indices j with
  * L[i*] - L[j] <= rel * (A[i*] + A[j]) (0 means the row is unflagged). */

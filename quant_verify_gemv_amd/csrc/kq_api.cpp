@@ -592,6 +592,18 @@ kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan, void *
   return KQ_OK;
 }
 
+kq_status kq_chain_status(const kq_chain_plan *plan, const void *scratch, size_t scratch_bytes, void *stream) {
+  if (!plan || !scratch) return KQ_ERR_NULL;
+  if (!chain_plan_fields_ok(plan)) return KQ_ERR_SHAPE;
+  if (!al(scratch, 256)) return KQ_ERR_ALIGN;
+  const size_t need = chain_plan_scratch(plan);
+  if (!need) return KQ_ERR_SHAPE;  // not a plan kq_chain_encode wrote
+  if (scratch_bytes < need) return KQ_ERR_WORKSPACE;
+  unsigned word = 0;
+  if (read_device_word((const unsigned *)((const uint8_t *)scratch + kErrOff), &word, stream)) return KQ_ERR_LAUNCH;
+  return word ? KQ_ERR_LAUNCH : KQ_OK;
+}
+
 size_t kq_softmax_workspace_bytes(int m, int64_t n) {
   if (m < 1 || m > 65535 || n < 1 || n >= ((int64_t)1 << 31)) return 0;
   return align256((size_t)m * (size_t)softmax_chunks(n) * 2 * sizeof(float));

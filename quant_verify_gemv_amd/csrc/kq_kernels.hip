@@ -1549,6 +1549,12 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value) {
   return (int)hipGetLastError();
 }
 
+int read_device_word(const unsigned *dev, unsigned *host, void *stream) {
+  hipError_t e = hipMemcpyAsync(host, dev, sizeof(unsigned), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  return (int)e;
+}
+
 // out[i] = rows[i][tokens[i]] (the accept tests' p_i[d_i]); a token outside
 // [0, n) gives a NaN.
 __global__ __launch_bounds__(256) void kq_gather_kernel(const float *__restrict__ rows, int64_t n,

@@ -25,7 +25,8 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_chain_table_bytes", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
             "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
             "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged",
-            "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject", "kq_speculative_resample")
+            "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject", "kq_speculative_resample",
+            "kq_chain_status")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -101,6 +102,7 @@ def load() -> ctypes.CDLL:
     lib.kq_chain_encode.argtypes = [ctypes.POINTER(ChainPhase), I32, I32, I32, P, SZ, ctypes.POINTER(ChainPlan)]
     lib.kq_gemv_chain.argtypes = [P, ctypes.POINTER(ChainPlan), P, SZ, P]
     lib.kq_chain_scratch_init.argtypes = [ctypes.POINTER(ChainPlan), P, SZ, P]
+    lib.kq_chain_status.argtypes = [ctypes.POINTER(ChainPlan), P, SZ, P]
     lib.kq_softmax_workspace_bytes.argtypes = [I32, I64]
     lib.kq_softmax_workspace_bytes.restype = SZ
     F = ctypes.c_float
@@ -122,7 +124,7 @@ def load() -> ctypes.CDLL:
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
                  "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged",
                  "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject",
-                 "kq_speculative_resample"):
+                 "kq_speculative_resample", "kq_chain_status"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -458,6 +460,13 @@ class Chain:
         """The barrier time-out word (synchronises with the device)."""
         off = CHAIN_ERROR_OFFSET
         return int(self.scratch[off:off + 4].view(_torch().int32).item())
+
+    def status(self, stream=None):
+        """kq_chain_status: waits for the stream, raises KQError
+        (KQ_ERR_LAUNCH) when a wait of an earlier launch on this chain's
+        scratch gave up (its logits are incomplete)."""
+        _check(load().kq_chain_status(ctypes.byref(self.plan), _dev_ptr(self.scratch, "scratch"),
+                                      self.scratch.numel(), _stream_handle(stream)), "kq_chain_status")
 
 
 def chain_table_bytes(n_phases: int) -> int:

@@ -117,6 +117,27 @@ def q4k_matrix(n: int, k: int, seed: int, d_range=(0.001, 0.05)) -> np.ndarray:
     return blocks.reshape(n, (k // QK) * BLOCK_BYTES)
 
 
+def q4k_matrix_centred(n: int, k: int, seed: int, d_range=(0.001, 0.05), centre: float = 7.5) -> np.ndarray:
+    """Random Q4_K matrix whose weights are centred on zero, as a quantizer
+    fitting real weights makes them: every sub-block's min equals its scale
+    (m_j = sc_j) and dmin = centre * d (rounded to fp16), so w = d sc_j q -
+    dmin m_j is about d sc_j (q - centre), q uniform in [0, 15].
+
+    Built from q4k_matrix's bytes by copying fields where the format keeps
+    them: scale/min bytes 0-3 (six low bits: sc_0..3, two top bits: the top
+    of sc_4..7) go to bytes 4-7 (m_0..3 and the top of m_4..7), and the low
+    nibble of bytes 8-11 (low bits of sc_4..7) to their high nibble (low bits
+    of m_4..7)."""
+    w = q4k_matrix(n, k, seed, d_range).reshape(-1, BLOCK_BYTES).copy()
+    s = w[:, 4:16]
+    s[:, 4:8] = s[:, 0:4]
+    lo = s[:, 8:12] & np.uint8(0x0F)
+    s[:, 8:12] = lo | (lo << np.uint8(4))
+    d = w[:, 0:2].copy().view(np.float16).astype(np.float64)
+    w[:, 2:4] = (d * centre).astype(np.float16).view(np.uint8)
+    return w.reshape(n, (k // QK) * BLOCK_BYTES)
+
+
 Q5K_BLOCK_BYTES = 176
 Q6K_BLOCK_BYTES = 210
 

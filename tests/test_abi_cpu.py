@@ -353,6 +353,19 @@ def test_chain_scratch_init_argument_errors_before_any_hip_call():
     assert lib.kq_chain_scratch_init(ctypes.byref(pl), FAKE, 1 << 30, None) == SHAPE  # inconsistent scratch_bytes
 
 
+def test_chain_status_argument_errors_before_any_hip_call():
+    lib = kq.load()
+    pl = kq.ChainPlan()
+    pl.n_phases, pl.m, pl.layout, pl.workgroups, pl.max_groups, pl.tiles_per_wave = 2, 16, 0, 256, 4, 1
+    assert lib.kq_chain_status(None, FAKE, 1 << 30, None) == NULL
+    assert lib.kq_chain_status(ctypes.byref(pl), None, 1 << 30, None) == NULL
+    assert lib.kq_chain_status(ctypes.byref(pl), FAKE, 1 << 30, None) == SHAPE  # inconsistent scratch_bytes
+    q = kq.ChainPlan.from_buffer_copy(pl)
+    q.m = 0
+    assert lib.kq_chain_status(ctypes.byref(q), FAKE, 1 << 30, None) == SHAPE
+    assert lib.kq_chain_status(ctypes.byref(pl), FAKE + 16, 1 << 30, None) == ALIGN
+
+
 def test_tree_verify_argument_errors_before_any_hip_call():
     lib = kq.load()
     n, k = 512, 1024

@@ -35,6 +35,7 @@ def run_chain(kq, chain, outs):
     kq.gemv_chain(chain)
     torch.cuda.synchronize()
     assert chain.error_word() == 0, "a chain barrier timed out"
+    chain.status()
     return [o.cpu().numpy().copy() for o in outs]
 
 
@@ -180,7 +181,11 @@ def test_chain_wait_timeout_sets_error_word_and_reinit_recovers(kq):
     torch.cuda.synchronize()
     log(f"chain timeout: launch ended after {time.time() - t0:.2f} s")
     assert chain.error_word() == 1
+    with pytest.raises(kq.KQError) as e:
+        chain.status()
+    assert e.value.status == 6  # KQ_ERR_LAUNCH, reported at the C boundary
     chain.init_scratch()
+    chain.status()  # cleared: KQ_OK
     again = run_chain(kq, chain, outs)
     for a, b in zip(first, again):
         assert np.array_equal(a, b)

@@ -87,3 +87,21 @@ def test_injection_and_forced_draft():
         f = synthetic.forced_draft(t, acc, 100)
         am = list(t) + [5]
         assert oracle.accept(f, am)[0] == acc
+
+
+def test_centred_matrix_fields():
+    """q4k_matrix_centred: every sub-block's min equals its scale, dmin is
+    7.5 d rounded to fp16, d and the quants are q4k_matrix's; the decoded
+    weights are centred on zero."""
+    base = synthetic.q4k_matrix(12, 1024, 31).reshape(-1, 144)
+    w = synthetic.q4k_matrix_centred(12, 1024, 31).reshape(-1, 144)
+    assert np.array_equal(w[:, 0:2], base[:, 0:2]) and np.array_equal(w[:, 16:], base[:, 16:])
+    d = w[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    dmin = w[:, 2:4].copy().view(np.float16)[:, 0]
+    assert np.array_equal(dmin, (7.5 * d).astype(np.float16))
+    for b in range(w.shape[0]):
+        sc, mn = oracle.scales_mins(bytes(w[b, 4:16]))
+        sc0, _ = oracle.scales_mins(bytes(base[b, 4:16]))
+        assert np.array_equal(sc, mn) and np.array_equal(sc, sc0)
+    W = oracle.decode_matrix(synthetic.q4k_matrix_centred(64, 2048, 32), 2048)
+    assert abs(W.mean()) < 0.02 * np.abs(W).mean()
