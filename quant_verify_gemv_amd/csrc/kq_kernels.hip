@@ -295,15 +295,6 @@ __global__ void kq_fill_kernel(unsigned *p, int64_t n, unsigned value) {
 // u % kb). Wave w owns the T 16-row tiles t W + w of the current row group;
 // the activations of each block are staged once in LDS per workgroup and
 // every A-operand read from LDS feeds all T tiles of the wave.
-//
-// A chain launch (CHAIN) runs a sequence of such phases in one grid: each
-// phase is split among all workgroups as above, and a grid-wide barrier
-// separates consecutive phases, so a phase starts reading its activations
-// only after every output of the previous one is complete and visible
-// device-wide, as when one projection's input is computed from the
-// previous one's output. Weights do not depend on earlier phases: each
-// workgroup issues the first weight loads of the next phase before it
-// waits at the barrier.
 
 // One 16-row tile's share of a block in a lane's registers: Q4_K and Q5_K
 // header, two quant chunks; Q5_K fifth bits in hx.x, hx.y; Q6_K: scale
@@ -323,7 +314,8 @@ constexpr int lcm_int(int a, int b) {
   return a / x * b;
 }
 
-// Grid barrier between chain phases. Every workgroup adds one arrival to a
+// Grid barrier between the phases of a chain launch (kq_chain_kernel). Every
+// workgroup adds one arrival to a
 // device-wide count (agent-scope atomic); the phase is complete when the
 // count reaches (phase + 1) times the workgroups. The workgroup whose
 // arrival completes the count releases the others: its threads write every
@@ -353,18 +345,16 @@ __device__ __forceinline__ int spin_flag(const unsigned long long *flag, unsigne
   }
 }
 
-// Field f of phase ph: the launch's own phase, or entry ph of a chain's table.
-#define KQ_PH(I_, f) (CHAIN ? ((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f : a.ph.f)
+// Field f of the launch's phase.
+#define KQ_PH(I_, f) (a.ph.f)
 
-template <int W, int T, int BI, int D, bool CHAIN, int FMT, int MS>
+template <int W, int T, int BI, int D, int FMT, int MS>
 __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv_kernel(GemvLaunch a) {
   static_assert(W % 4 == 0, "waves spread evenly over the 4 SIMDs");
-  static_assert(FMT == kFmtQ4 || !CHAIN, "chains run Q4_K");
   // MS 16-row activation slices: every unpacked weight operand feeds the
   // MFMAs of all MS slices, so the weights are read once for 16 MS rows
   // (33 to 64 rows: two launches, rows 0-31 and the rest)
   static_assert(MS == 1 || MS == 2, "one or two slices per launch");
-  static_assert(MS == 1 || !CHAIN, "more than 16 rows: single launches");
   constexpr int kRS = 16 * MS;  // activation rows per call at most
   constexpr unsigned kTB = 16u * (unsigned)fmt_block_bytes(FMT);  // tiled record bytes
   // D weight register sets: the weights of unit i + D - 1 are loaded while
@@ -403,7 +393,6 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // phase has fewer than 2^31 units
   const int P = gridDim.x;
   const int p = blockIdx.x;
-  const int n_ph = CHAIN ? a.n_phases : 1;
 
   // this workgroup's run of the U units of a phase
   auto run_start = [&](int U) -> int {
@@ -421,10 +410,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   const unsigned sel_sc = (kg >> 1) ? 0x00070006u : 0x00050004u;
   const unsigned mask_hi = in_vgpr(0x00F000F0u);
 
-  // Weight stream: the weights run D - 1 units ahead of the compute (in a
-  // chain, across the end of a phase into the next one), clamped to the
-  // phase's last unit, so every load is unconditional and outstanding loads
-  // are counted statically. It keeps its own copy of its phase's geometry.
+  // Weight stream: the weights run D - 1 units ahead of the compute,
+  // clamped to the launch's last unit, so every load is unconditional and
+  // outstanding loads are counted statically.
   // Addressing, one code path for both layouts, through buffer loads from
   // the current matrix (every matrix is smaller than 4 GiB): the lane's
   // bytes of block b of tile t sit at voff[t][0..2] + soff[t] + b *
@@ -434,16 +422,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // = the 16-row tile's record, stride = tiles * 2,304.
   const bool tiled = FMT != kFmtQ4 || a.layout == KQ_LAYOUT_TILED16;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // The phase fields the stream needs: a single launch reads them from its
-  // arguments; a chain keeps the current phase's in registers.
-  int wp = 0;  // the weight stream's phase
   int uw = 0, uw_last = 0, gw = 0, bw = 0;
-  int cw_n = 1, cw_rb = 0, cw_nt = 1, cw_kb = 1, cw_nwg = 1;
-  auto w_n = [&]() -> int { return CHAIN ? cw_n : a.ph.n; };
-  auto w_rb = [&]() -> int { return CHAIN ? cw_rb : a.ph.row_bytes; };
-  auto w_nt = [&]() -> int { return CHAIN ? cw_nt : a.ph.n_tiles; };
-  auto w_kb = [&]() -> int { return CHAIN ? cw_kb : a.ph.kb; };
-  auto w_nwg = [&]() -> int { return CHAIN ? cw_nwg : a.ph.n_wg_per; };
+  auto w_n = [&]() -> int { return a.ph.n; };
+  auto w_rb = [&]() -> int { return a.ph.row_bytes; };
+  auto w_nt = [&]() -> int { return a.ph.n_tiles; };
+  auto w_kb = [&]() -> int { return a.ph.kb; };
+  auto w_nwg = [&]() -> int { return a.ph.n_wg_per; };
   auto block_stride = [&]() -> unsigned {
     return tiled ? (unsigned)w_nt() * kTB : (unsigned)kBlockBytes;
   };
@@ -474,15 +458,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     }
   };
   auto begin_w = [&](int ph) {
-    wp = ph;
     const int U = KQ_PH(ph, units);
-    if (CHAIN) {
-      cw_n = KQ_PH(ph, n);
-      cw_rb = KQ_PH(ph, row_bytes);
-      cw_nt = KQ_PH(ph, n_tiles);
-      cw_kb = KQ_PH(ph, kb);
-      cw_nwg = KQ_PH(ph, n_wg_per);
-    }
     uw = run_start(U);
     uw_last = uw + run_len(U) - 1;
     gw = uw / w_kb();
@@ -534,32 +510,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // that goes to LDS after the loop.
   unsigned long long wave_key[MS][4] = {};
   const __amdgpu_buffer_rsrc_t part_rsrc = dev_rsrc(a.partials);
-  // Logits of a chain phase are written through to the device coherence
-  // point (agent-scope stores), so they are visible to every workgroup once
-  // the writer's stores have completed, before it arrives at the barrier.
-  auto put = [&](float *q, float v) {
-    if (CHAIN)
-      st_dev(q, v);
-    else
-      *q = v;
-  };
-
-  // chain launches: the launch epoch, read by thread 0 before this
-  // workgroup's first arrival (the final arrival of the launch increments
-  // it) and shared through LDS (the prologue's barrier publishes it)
-  __shared__ unsigned long long s_epoch;
-  if (CHAIN && tid == 0) {
-    s_epoch = (unsigned long long)__hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 32;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): read before any arrival
-  }
+  auto put = [&](float *q, float v) { *q = v; };
 
   begin_w(0);
-  if (CHAIN) {
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) load_w(wr[d]);
-  }
 
-  for (int ph = 0; ph < n_ph; ++ph) {
+  {
+    const int ph = 0;
     const int N = KQ_PH(ph, n);
     const int KB = KQ_PH(ph, kb);
     const int n_wg_per = KQ_PH(ph, n_wg_per);
@@ -585,13 +541,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       }
 
     // Activation stream, two units behind the weights and never past the
-    // phase's last unit (in a chain, a phase's activations are read only
-    // after the barrier that ends the previous phase).
+    // launch's last unit.
     int ux = u0;
     int bx = u0 % KB;
     const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_PH(ph, staged));
-    const unsigned x_rec = CHAIN ? (unsigned)kStageBytes : a.x_rec;
-    const unsigned x_off = CHAIN ? 0u : a.x_off;
+    const unsigned x_rec = a.x_rec;
+    const unsigned x_off = a.x_off;
     auto load_x = [&](XRegs &x) {
       const unsigned src = (unsigned)bx * x_rec + x_off;
 #pragma unroll
@@ -627,7 +582,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
           }
         }
       }
-      if (!CHAIN && a.verify) {
+      if (a.verify) {
 #pragma unroll
         for (int sl = 0; sl < MS; ++sl)
 #pragma unroll
@@ -655,18 +610,14 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     // of unit 0 (from HBM, the longest wait, needed first), the activations
     // of units 0..BI-1 (to buffers 0..BI-1 before the first barrier), the
     // weights of units 1..D-2, then the activations of units BI..BI+kXL-1,
-    // which stay in registers (set u % (kXL + 1)). A chain issued the
-    // weights of units 0..D-2 already (before its first phase, or before
-    // the barrier that ended the previous phase).
+    // which stay in registers (set u % (kXL + 1)).
     {
       XRegs xp[BI];
-      if (!CHAIN) load_w(wr[0]);
+      load_w(wr[0]);
 #pragma unroll
       for (int j = 0; j < BI; ++j) load_x(xp[j]);
-      if (!CHAIN) {
 #pragma unroll
-        for (int d = 1; d < D - 1; ++d) load_w(wr[d]);
-      }
+      for (int d = 1; d < D - 1; ++d) load_w(wr[d]);
 #pragma unroll
       for (int q = 0; q < kXL; ++q) load_x(xr[(BI + q) % (kXL + 1)]);
 #pragma unroll
@@ -934,7 +885,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     // goes to slot 0 (first group) or 1 (last group) of this workgroup; the
     // last contributor of a group to arrive sums all contributors' partials in
     // workgroup order.
-    if (!CHAIN && a.verify) {
+    if (a.verify) {
 #pragma unroll
       for (int sl = 0; sl < MS; ++sl)
 #pragma unroll
@@ -1006,7 +957,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
           const int m = m0 + r;
           const bool ok = m < M && row < nrows;
           if (ok && logits) put(&logits[(int64_t)m * N + n], v[j][r]);
-          if (!CHAIN && a.verify) {
+          if (a.verify) {
             // max over the wave's 64 / kCR rows: the lanes with the same c % kCR
             unsigned long long best = ok ? argmax_key(v[j][r], (unsigned)n) : 0ull;
             best = lanes_max(best, 64, kCR);
@@ -1035,86 +986,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       if (both) finish_group(gb, vb);
     };
 
-    // Chains reduce split row groups by pulling: the first contributor of a
-    // group (the workgroup that owns its first block, which reaches its
-    // part of the group last, at the end of its run) sums the later
-    // contributors' partials as soon as they are present, and every other
-    // contributor just stores its partial (its first group's, slot 0). An
-    // unwritten slot holds the sentinel pattern (all ones, a NaN arithmetic
-    // on finite inputs never produces); the reducer resets each slot it
-    // consumed, so every launch leaves the slots as it found them. This
-    // saves the store acknowledgement and the arrival atomic that the
-    // last-to-arrive hand-off below puts on the critical path of each
-    // phase. The sum runs over the contributors in workgroup order, as
-    // below, so both hand-offs give bitwise identical results.
-    if (CHAIN && (have_first || last_partial)) {
-      const bool red_first = have_first && owner(g_first * KB) == p;
-      if (have_first && !red_first) write_partial(0, acc_first);
-      if (red_first || last_partial) {
-        const int g = red_first ? g_first : g_last;
-        // own partial into LDS (the activation ring is idle after the loop)
-        uint8_t *own = s_x[0];
-        static_assert(kRows * kRS * 4 <= kStageBytes * MS, "own partial fits one ring buffer");
-        const f32x4(&mine)[T][MS] = red_first ? acc_first : acc;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-          for (int sl = 0; sl < MS; ++sl)
-            *(f32x4 *)(own + (tile_row(t) * kRS + 16 * sl + 4 * kg) * 4) = mine[t][sl];
-        __syncthreads();
-        const int pfg = p, plg = owner(g * KB + KB - 1);
-        f32x4 v[kE];
-#pragma unroll
-        for (int j = 0; j < kE; ++j) v[j] = *(const f32x4 *)(own + (tid + j * kNth) * 16);
-        int bad = 0;
-        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-        for (int c0 = 1; c0 <= plg - pfg; c0 += kC) {
-          f32x4 pv[kE][kC];
-          // loads of up to kC contributors in flight together (past the last
-          // one: re-read it, dropped below)
-#pragma unroll
-          for (int c = 0; c < kC; ++c) {
-            const int q = pfg + c0 + c <= plg ? pfg + c0 + c : plg;
-            const unsigned src = (unsigned)(q * 2 * kRS * kRows) * 4u;
-#pragma unroll
-            for (int j = 0; j < kE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
-          }
-#pragma unroll
-          for (int c = 0; c < kC; ++c) {
-            if (pfg + c0 + c > plg) continue;
-            const unsigned src = (unsigned)((pfg + c0 + c) * 2 * kRS * kRows) * 4u;
-#pragma unroll
-            for (int j = 0; j < kE; ++j) {
-              // not yet written: poll (bounded)
-              while (true) {
-                const u32x4 w = __builtin_bit_cast(u32x4, pv[j][c]);
-                if (w.x != 0xFFFFFFFFu && w.y != 0xFFFFFFFFu && w.z != 0xFFFFFFFFu && w.w != 0xFFFFFFFFu) break;
-                if (bad || __builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-                  bad = 1;
-                  break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(tid + j * kNth) * 16u);
-              }
-              v[j] = v[j] + pv[j][c];
-            }
-          }
-        }
-        if (__syncthreads_or(bad)) {
-          if (tid == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          return;  // a partial never arrived: *a.err is set, every workgroup leaves
-        }
-        finish_group(g, v);
-        // reset the consumed slots (written through before this workgroup
-        // arrives at the barrier, so before any contributor reuses its slot)
-        const f32x4 sentinel = __builtin_bit_cast(f32x4, u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
-        for (int q = pfg + 1; q <= plg; ++q)
-#pragma unroll
-          for (int j = 0; j < kE; ++j)
-            st_dev16(part_rsrc, (unsigned)(q * 2 * kRS * kRows) * 4u + (unsigned)(tid + j * kNth) * 16u,
-                     sentinel);
-      }
-    } else if (have_first || last_partial) {
+    if (have_first || last_partial) {
       if (MS == 1 && have_first) write_partial(0, acc_first);
       if (last_partial) write_partial(1, acc);
       // contributor counts of both groups (computed while the stores drain)
@@ -1153,42 +1025,6 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       }
     }
 
-    if (CHAIN) {
-      // Grid barrier: this workgroup's stores of phase ph have completed
-      // (logits and the group-counter resets written through to the device
-      // coherence point); arrive, issue the first weights of the next
-      // phase, then wait for the release flag (or release everyone when
-      // this arrival completed the count). The final arrival of the last
-      // phase resets the count and advances the epoch for the next launch
-      // (every workgroup has then passed every barrier).
-      stores_done_barrier();
-      const unsigned target = (unsigned)(ph + 1) * (unsigned)P;
-      unsigned old = 0;
-      if (tid == 0) old = __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (ph + 1 < n_ph) {
-        begin_w(ph + 1);
-#pragma unroll
-        for (int d = 0; d < D - 1; ++d) load_w(wr[d]);
-        if (tid == 0) s_flag = old + 1 == target;
-        __syncthreads();
-        const unsigned long long want = s_epoch | (unsigned long long)(ph + 1);
-        if (s_flag) {
-          // last to arrive: release every other workgroup
-          for (int q = tid; q < P; q += kNth)
-            if (q != p) st_dev(a.flags + (int64_t)q * kFlagStride, want);
-        }
-        int ok = 1;
-        if (tid == 0 && !s_flag) ok = spin_flag(a.flags + (int64_t)p * kFlagStride, want, a.err);
-        __syncthreads();
-        if (tid == 0) s_flag = ok;
-        __syncthreads();
-        if (!s_flag) return;  // a barrier timed out: *a.err is set, every workgroup leaves
-      } else if (tid == 0 && old + 1 == target) {
-        __hip_atomic_store(a.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(a.epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      continue;
-    }
 
     if (!a.verify) return;
     __syncthreads();
@@ -1264,6 +1100,562 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
 }
 
 #undef KQ_PH
+
+// ---------------------------------------------------------------------------
+// Chain launches with specialised waves (kq_chain_kernel). A workgroup has
+// kCwW compute waves (one 16-row tile each: row groups of 128 rows, units
+// as in kq_gemv_kernel) and kCwP producer waves:
+//  * compute waves only load weights and compute: kCwD register sets, the
+//    weights of a unit issued kCwD - 1 units before it is computed, in one
+//    stream that runs through the phases (a phase's last units already
+//    carry the next phase's first weights, which do not depend on the
+//    barrier). Their memory counter holds nothing but weight loads, so
+//    waiting for one unit's weights never waits for anything younger: the
+//    reason this prefetch can run deeper than kq_gemv_kernel's, where the
+//    activation loads and the stores share the counter;
+//  * producer waves move each unit's staged activations from L2 into the
+//    LDS ring one barrier interval ahead, and do every global store: the
+//    results the compute waves hand over through LDS (a finished row group's
+//    logits, a later contributor's partial sums), the pull reduction of a
+//    split row group, and the grid barrier between phases.
+// A phase's units, its row-group arithmetic and its summation orders are
+// those of kq_gemv_kernel, so the results are bitwise equal to it.
+// ---------------------------------------------------------------------------
+
+constexpr int kCwW = 8;                                // compute waves
+constexpr int kCwT = 1;                                // 16-row tiles per compute wave
+constexpr int kCwP = 4;                                // producer waves
+constexpr int kCwD = 4;                                // weight register sets per compute wave
+constexpr int kCwBI = 4;                               // most units between workgroup barriers
+constexpr int kCwRows = 16 * kCwW * kCwT;              // rows per row group (128)
+constexpr int kCwPT = 64 * kCwP;                       // producer threads
+constexpr int kCwXc = (int)(kStageBytes / 16);         // 16-byte chunks of a staged block (1,060)
+constexpr int kCwXj = (kCwXc + kCwPT - 1) / kCwPT;     // chunks per producer thread and unit (5)
+constexpr int kCwChunks = kCwRows * kMaxRows / 4;      // 16-byte chunks of a row group's result (512)
+constexpr int kCwE = kCwChunks / kCwPT;                // of them per producer thread (2)
+constexpr int kCwC = 8;                                // contributors' partials in flight in a pull
+static_assert(kCwE * kCwPT == kCwChunks, "result chunks split evenly over the producer threads");
+static_assert((kCwBI & (kCwBI - 1)) == 0, "barrier interval a power of two");
+
+// One unit of T 16-row tiles of Q4_K weights: per tile, block d, dmin, the
+// 6-bit scales and mins unpacked in registers, the 4-bit quants times their
+// scale as exact fp16 B operands, contracted with the staged activations xb
+// (hi and lo halves into one fp32 sum; every A operand read from LDS feeds
+// all T tiles), the min term as one 16x16x16 MFMA; acc[t] gains
+// 2^-e (d C - dmin C_m). Per tile, the same operations in the same order as
+// the Q4_K path of kq_gemv_kernel.
+template <int T>
+__device__ __forceinline__ void q4_unit(const WTile (&cur)[T], const uint8_t *xb, int lane, int kg, unsigned sel_sc,
+                                        unsigned mask_lo, unsigned mask_hi, f32x4 (&acc)[T]) {
+  const half2v neg1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const half2v lo_pair = {(_Float16)1.0f, (_Float16)-1024.0f};
+  const half2v hi_pair = {(_Float16)0.0625f, (_Float16)-64.0f};
+  float d[T], dmin[T];
+  half2v k00[T], k01[T], k10[T], k11[T];
+  half4 bm[T];
+  f32x4 cq[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const u32x4 h = cur[t].hdr;
+    d[t] = h2f_lo(h.x);
+    dmin[t] = h2f_hi(h.x);
+    const unsigned sc03 = h.y & 0x3F3F3F3Fu;
+    const unsigned sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    const half2v s0 = as_h2(__builtin_amdgcn_perm(sc03, 0x64646464u, sel_sc)) + neg1024;
+    const half2v s1 = as_h2(__builtin_amdgcn_perm(sc47, 0x64646464u, sel_sc)) + neg1024;
+    k00[t] = half2v{s0[0], s0[0]} * lo_pair;
+    k01[t] = half2v{s0[1], s0[1]} * hi_pair;
+    k10[t] = half2v{s1[0], s1[0]} * lo_pair;
+    k11[t] = half2v{s1[1], s1[1]} * hi_pair;
+    const unsigned m03 = h.z & 0x3F3F3F3Fu;
+    const unsigned m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+    const unsigned msrc = (kg & 1) ? m47 : m03;
+    const half2v p0 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00060004u)) + neg1024;
+    const half2v p1 = as_h2(__builtin_amdgcn_perm(msrc, 0x64646464u, 0x00070005u)) + neg1024;
+    bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
+    cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
+    const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+    const bool hi = (s & 2) != 0;
+    const unsigned mask = hi ? mask_hi : mask_lo;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const u32x4 qq = s < 4 ? cur[t].q0 : cur[t].q1;
+      const unsigned da = (s & 1) ? qq.z : qq.x;
+      const unsigned db = (s & 1) ? qq.w : qq.y;
+      const half2v kk = s < 4 ? (hi ? k01[t] : k00[t]) : (hi ? k11[t] : k10[t]);
+      const half2v v0 = fma_bcast(as_h2((da & mask) | 0x64006400u), kk);
+      const half2v v1 = fma_bcast(as_h2(((da >> 8) & mask) | 0x64006400u), kk);
+      const half2v v2 = fma_bcast(as_h2((db & mask) | 0x64006400u), kk);
+      const half2v v3 = fma_bcast(as_h2(((db >> 8) & mask) | 0x64006400u), kk);
+      const half8 bw8 = make_h8(as_u(v0), as_u(v1), as_u(v2), as_u(v3));
+      cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bw8, cq[t], 0, 0, 0);
+      cq[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bw8, cq[t], 0, 0, 0);
+    }
+  }
+  const half4 as4 = *(const half4 *)(xb + kXsbOffset + lane * 8);
+  const f32x4 xinv = *(const f32x4 *)(xb + kXiOffset + 16 * kg);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const f32x4 c2 = __builtin_amdgcn_mfma_f32_16x16x16f16(as4, bm[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] += xinv[r] * (d[t] * cq[t][r] - dmin[t] * c2[r]);
+  }
+}
+
+// Barrier of the producer waves alone (the compute waves are meanwhile at a
+// workgroup barrier of their own, which an s_barrier here would complete):
+// an LDS arrival count. Bounded like every wait; false after a time-out.
+__device__ __forceinline__ bool producer_bar(unsigned *cnt, unsigned &target) {
+  target += kCwP;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  while ((int)(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) - target) < 0) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return true;
+}
+
+#define KQ_CPH(I_, f) (((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f)
+
+__global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLaunch a) {
+  // LDS: the activation ring (two halves of up to kCwBI staged blocks: the
+  // compute waves read one half while the producers fill the other; after
+  // a phase's last unit the unused half takes the final hand-over), two
+  // hand-over slots for results finished inside a run, and control words.
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2 * kCwBI][kStageBytes];
+  __shared__ __attribute__((aligned(16))) float s_hand[2][kCwRows * kMaxRows];
+  __shared__ int s_hdesc[2];   // hand-over in slot i: group * 4 + kind
+  __shared__ int s_htag[2];    // ... written in the launch's interval s_htag[i]
+  __shared__ int s_fdesc;      // the final hand-over of a phase
+  __shared__ unsigned s_pbar;  // producer barrier count
+  __shared__ unsigned s_bad;   // producer broadcast words: a partial never arrived,
+  __shared__ unsigned s_last;  // this arrival completed the grid barrier,
+  __shared__ unsigned s_ok;    // the barrier wait ended with a release
+  __shared__ int s_abort;      // set by the producers when a wait gave up
+  __shared__ unsigned long long s_epoch;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int kg = lane >> 4;
+  const int ln = lane & 15;
+  const int M = a.m;
+  const int P = gridDim.x;
+  const int p = blockIdx.x;
+  const int n_ph = a.n_phases;
+  const bool tiled = a.layout == KQ_LAYOUT_TILED16;
+  // hand-over kinds: a row group finished here (its logits), a later
+  // contributor's partial (to its slot 0, pulled by the group's first
+  // contributor), a group this workgroup reduces (pull, then logits)
+  constexpr int kKindDone = 0, kKindPartial = 1, kKindReduce = 2;
+
+  auto run_start = [&](int U) -> int {
+    const int b = U / P, r = U % P;
+    return p * b + (p < r ? p : r);
+  };
+  auto run_len = [&](int U) -> int { return U / P + (p < U % P ? 1 : 0); };
+  // log2 of the units between barriers: kCwBI, fewer (a power of two) for
+  // rows of fewer blocks, so that at most one row group ends inside an
+  // interval and two hand-over slots suffice
+  auto interval_log2 = [&](int KB) -> int { return KB >= 4 ? 2 : KB >= 2 ? 1 : 0; };
+  // LDS buffer of unit i of a phase (interval 2^lb)
+  auto ring_buf = [&](int i, int lb) -> int { return ((i >> lb) & 1) * kCwBI + (i & ((1 << lb) - 1)); };
+  // row of tile t of a compute wave within its row group
+  auto tile_row = [&](int t) -> int { return (t * kCwW + wave) * 16 + ln; };
+
+  if (tid == 0) {
+    s_htag[0] = s_htag[1] = -1;
+    s_pbar = 0u;
+    s_bad = 0u;
+    s_abort = 0;
+    s_epoch = (unsigned long long)__hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 32;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the epoch is read before any arrival
+  }
+
+  if (wave < kCwW) {
+    // ------------------------------------------------------------ compute
+    const unsigned mask_lo = in_vgpr(0x000F000Fu);
+    const unsigned mask_hi = in_vgpr(0x00F000F0u);
+    const unsigned sel_sc = (kg >> 1) ? 0x00070006u : 0x00050004u;
+    // the weight stream (its own copy of its phase's geometry)
+    int wp = 0, uw = 0, uw_last = 0, gw = 0, bw = 0;
+    int cw_n = 1, cw_rb = 0, cw_nt = 1, cw_kb = 1, cw_nwg = 1;
+    unsigned boff = 0, bstride = 0;
+    __amdgpu_buffer_rsrc_t w_rsrc;
+    unsigned voff[kCwT][3], soff[kCwT];
+    auto set_rowp = [&]() {
+      const int mat = gw / cw_nwg;
+      const int r0 = (gw - mat * cw_nwg) * kCwRows;
+      w_rsrc = dev_rsrc(KQ_CPH(wp, w[mat]));
+#pragma unroll
+      for (int t = 0; t < kCwT; ++t) {
+        if (tiled) {
+          int ti = (r0 + (t * kCwW + wave) * 16) / 16;
+          ti = ti < cw_nt ? ti : cw_nt - 1;
+          soff[t] = (unsigned)ti * (unsigned)kTileBlockBytes;
+          voff[t][0] = 16u * ln;
+          voff[t][1] = (unsigned)kTileQ0 + 16u * lane;
+          voff[t][2] = (unsigned)kTileQ1 + 16u * lane;
+        } else {
+          const int row = r0 + tile_row(t);
+          const unsigned rb = (unsigned)(row < cw_n ? row : cw_n - 1) * (unsigned)cw_rb;
+          soff[t] = 0u;
+          voff[t][0] = rb;
+          voff[t][1] = rb + 16u + 16u * kg;
+          voff[t][2] = rb + 80u + 16u * kg;
+        }
+      }
+    };
+    auto begin_w = [&](int ph) {
+      wp = ph;
+      const int U = KQ_CPH(ph, units);
+      cw_n = KQ_CPH(ph, n);
+      cw_rb = KQ_CPH(ph, row_bytes);
+      cw_nt = KQ_CPH(ph, n_tiles);
+      cw_kb = KQ_CPH(ph, kb);
+      cw_nwg = KQ_CPH(ph, n_wg_per);
+      bstride = tiled ? (unsigned)cw_nt * (unsigned)kTileBlockBytes : (unsigned)kBlockBytes;
+      uw = run_start(U);
+      uw_last = uw + run_len(U) - 1;
+      gw = uw / cw_kb;
+      bw = uw % cw_kb;
+      boff = (unsigned)bw * bstride;
+      set_rowp();
+    };
+    // issue the loads of the stream's next unit and advance (into the next
+    // phase after this one's last unit; the last phase's last unit repeats)
+    auto load_w = [&](WTile (&w)[kCwT]) {
+#pragma unroll
+      for (int t = 0; t < kCwT; ++t) {
+        w[t].hdr = buf_ld16_w(w_rsrc, voff[t][0], soff[t] + boff);
+        w[t].q0 = buf_ld16_w(w_rsrc, voff[t][1], soff[t] + boff);
+        w[t].q1 = buf_ld16_w(w_rsrc, voff[t][2], soff[t] + boff);
+      }
+      if (uw < uw_last) {
+        ++uw;
+        boff += bstride;
+        if (++bw == cw_kb) {
+          bw = 0;
+          boff = 0u;
+          ++gw;
+          set_rowp();
+        }
+      } else if (wp + 1 < n_ph) {
+        begin_w(wp + 1);
+      }
+    };
+
+    // One loop over the launch's steps (every unit of every phase in order),
+    // unrolled kCwD times so that the register set of each step is static.
+    // Each step issues the loads of the stream's unit kCwD - 1 steps ahead
+    // unconditionally (past the last phase the last unit repeats), so the
+    // memory counter waits are static too; the phase tail (hand-over,
+    // barriers) is a branch inside the step of a phase's last unit.
+    WTile wr[kCwD][kCwT];
+    int S = 0;  // this workgroup's units over all phases
+    for (int q = 0; q < n_ph; ++q) S += run_len(KQ_CPH(q, units));
+    begin_w(0);
+#pragma unroll
+    for (int d = 0; d < kCwD - 1; ++d) load_w(wr[d]);
+
+    // phase state: ph; KB, nu, lb of the phase; gc, bc, seg0 the current
+    // row group, block and segment start; i the unit, ib its place in its
+    // barrier interval, kint the interval; gint the launch's intervals
+    // before this phase (hand-over tags)
+    int ph = 0, gint = 0, KB = 1, nu = 1, lb = 0, gc = 0, bc = 0, seg0 = 0, i = 0, ib = 0, kint = 0;
+    auto enter = [&](int q) {
+      KB = KQ_CPH(q, kb);
+      const int U = KQ_CPH(q, units);
+      const int u0 = run_start(U);
+      nu = run_len(U);
+      lb = interval_log2(KB);
+      gc = u0 / KB;
+      bc = u0 - gc * KB;
+      seg0 = bc;
+      i = ib = kint = 0;
+    };
+    enter(0);
+    f32x4 acc[kCwT];
+#pragma unroll
+    for (int t = 0; t < kCwT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // the first phase's first activations are in the ring
+    if (s_abort) return;
+    for (int s0 = 0; s0 < S; s0 += kCwD) {
+#pragma unroll
+      for (int j = 0; j < kCwD; ++j) {
+        load_w(wr[(j + kCwD - 1) % kCwD]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s0 + j < S) {
+          q4_unit<kCwT>(wr[j], s_x[((kint & 1) * kCwBI) + ib], lane, kg, sel_sc, mask_lo, mask_hi, acc);
+          // end of a row group's segment: hand the result to the producers
+          if (bc == KB - 1 || i == nu - 1) {
+            const int kind = (seg0 == 0 && bc == KB - 1) ? kKindDone : seg0 > 0 ? kKindPartial : kKindReduce;
+            const int gi = gint + kint;  // the launch's interval of this unit
+            float *dst = i == nu - 1 ? (float *)s_x[((kint + 1) & 1) * kCwBI] : s_hand[gi & 1];
+#pragma unroll
+            for (int t = 0; t < kCwT; ++t) {
+              *(f32x4 *)(dst + tile_row(t) * kMaxRows + 4 * kg) = acc[t];
+              acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if (tid == 0) {
+              if (i == nu - 1) {
+                s_fdesc = gc * 4 + kind;
+              } else {
+                s_hdesc[gi & 1] = gc * 4 + kind;
+                s_htag[gi & 1] = gi;
+              }
+            }
+            seg0 = 0;
+          }
+          if (++bc == KB) {
+            bc = 0;
+            ++gc;
+          }
+          if (i == nu - 1) {
+            // phase tail: the producers store, reduce and pass the grid
+            // barrier; the weights of the next phase stay in flight
+            gint += kint + 1;
+            __syncthreads();  // the phase's results are handed over
+            if (ph + 1 < n_ph) {
+              enter(++ph);
+              __syncthreads();  // the next phase's first activations are in the ring
+              if (s_abort) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                return;
+              }
+            }
+          } else {
+            ++i;
+            if (++ib == (1 << lb)) {
+              ib = 0;
+              ++kint;
+              __syncthreads();  // the next interval's activations are in
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the repeated last loads
+    return;
+  }
+
+  // -------------------------------------------------------------- producers
+  const int pt = tid - 64 * kCwW;
+  unsigned pbar_target = 0;
+  const __amdgpu_buffer_rsrc_t part_rsrc = dev_rsrc(a.partials);
+  // Activations of units i .. i_end - 1 (< i + kCwBI) of phase ph into the
+  // ring (their blocks' staged records, copied linearly): all loads first,
+  // then `between` (hand-over stores overlap the loads), then the LDS writes.
+  auto move_x = [&](int ph, int i, int i_end, int lb, auto between) {
+    const int KB = KQ_CPH(ph, kb);
+    const int u0 = run_start(KQ_CPH(ph, units));
+    const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_CPH(ph, staged));
+    u32x4 xr[kCwBI][kCwXj];
+#pragma unroll
+    for (int q = 0; q < kCwBI; ++q) {
+      if (i + q < i_end) {
+        const unsigned src = (unsigned)((u0 + i + q) % KB) * (unsigned)kStageBytes;
+#pragma unroll
+        for (int j = 0; j < kCwXj; ++j) {
+          const int c = pt + kCwPT * j < kCwXc ? pt + kCwPT * j : kCwXc - 1;
+          xr[q][j] = buf_ld16(x_rsrc, (unsigned)c * 16u, src);
+        }
+      }
+    }
+    between();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+    for (int q = 0; q < kCwBI; ++q) {
+      if (i + q < i_end) {
+        uint8_t *dst = s_x[ring_buf(i + q, lb)];
+#pragma unroll
+        for (int j = 0; j < kCwXj; ++j)
+          if (pt + kCwPT * j < kCwXc) *(u32x4 *)(dst + (pt + kCwPT * j) * 16) = xr[q][j];
+      }
+    }
+  };
+  // logits of row group g of phase ph from a result ([row][16] fp32, the
+  // thread's chunks pt + j kCwPT)
+  auto store_logits = [&](int ph, int g, const f32x4 (&v)[kCwE]) {
+    const int N = KQ_CPH(ph, n);
+    const int nwg = KQ_CPH(ph, n_wg_per);
+    const int mat = g / nwg;
+    const int r0 = (g - mat * nwg) * kCwRows;
+    float *logits = KQ_CPH(ph, logits[mat]);
+#pragma unroll
+    for (int j = 0; j < kCwE; ++j) {
+      const int c = pt + j * kCwPT;
+      const int row = c >> 2, m0 = 4 * (c & 3);
+      if (r0 + row < N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (m0 + r < M) st_dev(&logits[(int64_t)(m0 + r) * N + r0 + row], v[j][r]);
+      }
+    }
+  };
+  auto load_hand = [&](const float *src, f32x4 (&v)[kCwE]) {
+#pragma unroll
+    for (int j = 0; j < kCwE; ++j) v[j] = *(const f32x4 *)(src + 4 * (pt + j * kCwPT));
+  };
+  auto slot0 = [&](int q) -> unsigned { return (unsigned)(q * 2 * kMaxRows * kCwRows) * 4u; };
+  // a hand-over finished inside a run: logits, or this workgroup's partial
+  auto store_hand = [&](int ph, int desc, const float *src) {
+    f32x4 v[kCwE];
+    load_hand(src, v);
+    if ((desc & 3) == kKindDone) {
+      store_logits(ph, desc >> 2, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kCwE; ++j) st_dev16(part_rsrc, slot0(p) + (unsigned)(pt + j * kCwPT) * 16u, v[j]);
+    }
+  };
+  // every producer wave ends here when a wait gave up: the compute waves
+  // leave at their next phase barrier
+  auto abort_all = [&]() {
+    if (pt == 0) {
+      __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_abort = 1;
+    }
+    __syncthreads();
+  };
+
+  {
+    const int nu = run_len(KQ_CPH(0, units));
+    const int lb = interval_log2(KQ_CPH(0, kb));
+    move_x(0, 0, nu < (1 << lb) ? nu : (1 << lb), lb, [] {});
+  }
+  int gint = 0;  // barrier intervals of the earlier phases (hand-over tags)
+  for (int ph = 0; ph < n_ph; ++ph) {
+    const int KB = KQ_CPH(ph, kb);
+    const int U = KQ_CPH(ph, units);
+    const int nu = run_len(U);
+    const int lb = interval_log2(KB);
+    const int bi = 1 << lb;
+    const int n_int = (nu + bi - 1) >> lb;
+    // a hand-over written in the launch's interval gi, if any (slots are
+    // tagged with the interval that wrote them, so nothing is cleared)
+    auto hand_of = [&](int gi) {
+      if (gi >= 0 && s_htag[gi & 1] == gi) store_hand(ph, s_hdesc[gi & 1], s_hand[gi & 1]);
+    };
+    __syncthreads();  // the phase starts
+    for (int k = 0; k < n_int; ++k) {
+      // the activations of interval k + 1; meanwhile the hand-over of
+      // interval k - 1 (published by the barrier that ended it)
+      const int i1 = (k + 1) * bi;
+      move_x(ph, i1, nu < i1 + bi ? nu : i1 + bi, lb, [&] {
+        if (k > 0) hand_of(gint + k - 1);
+      });
+      __syncthreads();  // interval k's units done; interval k + 1's activations in
+    }
+    // ---- phase tail (producer waves only; the compute waves wait at the
+    // next phase's barrier)
+    hand_of(gint + n_int - 1);
+    gint += n_int;
+    const int fdesc = s_fdesc;
+    const float *fin = (const float *)s_x[(n_int & 1) * kCwBI];
+    int bad = 0;
+    if ((fdesc & 3) == kKindReduce) {
+      // pull: sum the later contributors' partials of group g in workgroup
+      // order after this workgroup's own (the group's first part)
+      const int g = fdesc >> 2;
+      const int big = (U % P) * (U / P + 1);
+      auto owner = [&](int u) -> int { return u < big ? u / (U / P + 1) : U % P + (u - big) / (U / P); };
+      const int plg = owner(g * KB + KB - 1);
+      f32x4 v[kCwE];
+      load_hand(fin, v);
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      for (int c0 = 1; c0 <= plg - p; c0 += kCwC) {
+        f32x4 pv[kCwE][kCwC];
+#pragma unroll
+        for (int c = 0; c < kCwC; ++c) {
+          const int q = p + c0 + c <= plg ? p + c0 + c : plg;
+#pragma unroll
+          for (int j = 0; j < kCwE; ++j) pv[j][c] = ld_dev16(part_rsrc, slot0(q) + (unsigned)(pt + j * kCwPT) * 16u);
+        }
+#pragma unroll
+        for (int c = 0; c < kCwC; ++c) {
+          if (p + c0 + c > plg) continue;
+#pragma unroll
+          for (int j = 0; j < kCwE; ++j) {
+            while (true) {  // not yet written: poll (bounded)
+              const u32x4 w = __builtin_bit_cast(u32x4, pv[j][c]);
+              if (w.x != 0xFFFFFFFFu && w.y != 0xFFFFFFFFu && w.z != 0xFFFFFFFFu && w.w != 0xFFFFFFFFu) break;
+              if (bad || __builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                bad = 1;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+              pv[j][c] = ld_dev16(part_rsrc, slot0(p + c0 + c) + (unsigned)(pt + j * kCwPT) * 16u);
+            }
+            v[j] = v[j] + pv[j][c];
+          }
+        }
+      }
+      if (!bad) {
+        store_logits(ph, g, v);
+        // consumed slots back to the sentinel before this workgroup arrives
+        const f32x4 sentinel =
+            __builtin_bit_cast(f32x4, u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu});
+        for (int q = p + 1; q <= plg; ++q)
+#pragma unroll
+          for (int j = 0; j < kCwE; ++j) st_dev16(part_rsrc, slot0(q) + (unsigned)(pt + j * kCwPT) * 16u, sentinel);
+      }
+    } else {
+      store_hand(ph, fdesc, fin);
+    }
+    if (bad) __hip_atomic_fetch_or(&s_bad, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
+    if (!producer_bar(&s_pbar, pbar_target) || s_bad) {
+      abort_all();
+      return;  // a partial never arrived (or the producers lost each other)
+    }
+    // grid barrier: arrive; the arrival that completes the count releases
+    // every other workgroup through its own flag (see kq_gemv_kernel)
+    const unsigned target = (unsigned)(ph + 1) * (unsigned)P;
+    if (ph + 1 < n_ph) {
+      if (pt == 0) {
+        const unsigned old = __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old + 1 == target ? 1u : 0u;
+      }
+      if (!producer_bar(&s_pbar, pbar_target)) {
+        abort_all();
+        return;
+      }
+      const unsigned long long want = s_epoch | (unsigned long long)(ph + 1);
+      if (s_last) {
+        for (int q = pt; q < P; q += kCwPT)
+          if (q != p) st_dev(a.flags + (int64_t)q * kFlagStride, want);
+        if (pt == 0) s_ok = 1u;
+      } else if (pt == 0) {
+        s_ok = spin_flag(a.flags + (int64_t)p * kFlagStride, want, a.err) ? 1u : 0u;
+      }
+      if (pt == 0) s_bad = 0u;  // every producer read it before the last barrier
+      if (!producer_bar(&s_pbar, pbar_target) || !s_ok) {
+        abort_all();
+        return;  // the barrier wait gave up
+      }
+      // the next phase's first activations, read only now
+      const int nu1 = run_len(KQ_CPH(ph + 1, units));
+      const int lb1 = interval_log2(KQ_CPH(ph + 1, kb));
+      move_x(ph + 1, 0, nu1 < (1 << lb1) ? nu1 : (1 << lb1), lb1, [] {});
+    } else if (pt == 0) {
+      const unsigned old = __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1 == target) {
+        __hip_atomic_store(a.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+#undef KQ_CPH
 
 // ---------------------------------------------------------------------------
 // Tiled layout. Record (b, t) = block b of 16-row tile t is 2,304 bytes at
@@ -1576,15 +1968,15 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
   const dim3 grid((unsigned)a.g.n_wg);
   hipStream_t st = (hipStream_t)stream;
   if (a.chain) {
-    if (a.g.waves != 8 || a.g.tpw != 1 || a.g.bi != 4 || a.g.depth != 4) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4, 1>), grid, dim3(512), 0, st, a);
+    if (a.g.rows != kCwRows) return (int)hipErrorInvalidConfiguration;  // row groups of the chain geometry
+    hipLaunchKernelGGL(kq_chain_kernel, grid, dim3(64 * (kCwW + kCwP)), 0, st, a);
     return (int)hipGetLastError();
   }
   const int fmt = layout_fmt(a.layout);
   switch (a.g.ms * 1048576 + fmt * 65536 + a.g.waves * 4096 + a.g.tpw * 256 + a.g.bi * 16 + a.g.depth) {
 #define KQ_CASE(F_, W_, T_, BI_, D_, MS_)                                                              \
   case MS_ * 1048576 + F_ * 65536 + W_ * 4096 + T_ * 256 + BI_ * 16 + D_:                              \
-    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, false, F_, MS_>), grid, dim3(64 * W_), 0, st, a); \
+    hipLaunchKernelGGL((kq_gemv_kernel<W_, T_, BI_, D_, F_, MS_>), grid, dim3(64 * W_), 0, st, a); \
     break;
     KQ_CASE(kFmtQ4, 8, 2, 4, 4, 1)
     KQ_CASE(kFmtQ4, 8, 1, 4, 4, 1)
@@ -1615,7 +2007,7 @@ int chain_capacity() {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_gemv_kernel<8, 1, 4, 4, true, kFmtQ4, 1>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_chain_kernel, 64 * (kCwW + kCwP), 0);
   if (e != hipSuccess) return -(int)e;
   return per_cu * cus;
 }
