@@ -179,6 +179,26 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k,
                                   void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* kq_verify_argmax_accept without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). The workspace is a
+ * file-scope device array of KQ_NOALLOC_MAX_BYTES inside the library, one
+ * per GPU (held until the process ends); its address is looked up once per
+ * device, on the first call with that device current. Nothing is allocated.
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (different streams, or different threads without ordering) race and
+ * give wrong results; calls ordered on one stream are safe. Each call
+ * re-zeroes the control words it needs, so the array's earlier contents
+ * do not matter. Arguments as for kq_verify_argmax_accept; KQ_ERR_WORKSPACE
+ * (before any HIP call) when kq_workspace_bytes(n, k, m) exceeds
+ * KQ_NOALLOC_MAX_BYTES; KQ_ERR_LAUNCH when the address lookup fails. */
+#define KQ_NOALLOC_MAX_BYTES (24u << 20)
+kq_status kq_verify_argmax_accept_noalloc(const void *w_q4k, int64_t n, int64_t k,
+                                          const float *x, int m,
+                                          const int32_t *draft_host,
+                                          int32_t *argmax, int32_t *accept_out,
+                                          float *logits_or_null, void *stream);
+
 /* Stage m fp32 activation rows once for any number of matrices with the same
  * k (projections that share an input: q/k/v, gate/up).
  *  x       device, fp32 [m][k]

@@ -261,7 +261,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
                      const int32_t *draft_host, int32_t *argmax, int32_t *accept_out, int argmax_from,
                      int32_t *head_out, void *scratch, size_t scratch_bytes, const float *x_to_stage,
                      void *stream, const int32_t *tree_parent = nullptr, int32_t *path_out = nullptr,
-                     const int32_t *draft_dev = nullptr) {
+                     const int32_t *draft_dev = nullptr, bool dry = false) {
   if (!w || !staged || !scratch) return KQ_ERR_NULL;
   const int fmt = layout_fmt(layout);
   if (fmt < 0) return KQ_ERR_SHAPE;
@@ -354,6 +354,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   } else {
     part(a, 0, m, ms);
   }
+  if (dry) return KQ_OK;  // every check passed; nothing enqueued
   if (x_to_stage) {
     const int64_t groups = two_pass && first.g.n_groups > a.g.n_groups ? first.g.n_groups : a.g.n_groups;
     if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, groups, stream))
@@ -429,10 +430,11 @@ kq_status kq_gemv_rows(const void *w_q4k, int64_t n, int64_t k, const float *x, 
              nullptr, scratch, sb, x, stream);
 }
 
-kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
-                                  const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
-                                  float *logits_or_null, void *workspace, size_t workspace_bytes,
-                                  void *stream) {
+// kq_verify_argmax_accept; dry: every argument check, nothing enqueued
+static kq_status verify_rows(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
+                             const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
+                             float *logits_or_null, void *workspace, size_t workspace_bytes, void *stream,
+                             bool dry) {
   if (!w_q4k || !x || !argmax || !accept_out) return KQ_ERR_NULL;
   if (m > 1 && !draft_host) return KQ_ERR_NULL;
   void *staged, *scratch;
@@ -440,7 +442,34 @@ kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const
   kq_status s = split_workspace(n, k, m, workspace, workspace_bytes, &staged, &scratch, &sb);
   if (s != KQ_OK) return s;
   return run(&w_q4k, KQ_LAYOUT_ROWS, 1, n, k, staged, m, &logits_or_null, true, draft_host, argmax,
-             accept_out, 0, nullptr, scratch, sb, x, stream);
+             accept_out, 0, nullptr, scratch, sb, x, stream, nullptr, nullptr, nullptr, dry);
+}
+
+kq_status kq_verify_argmax_accept(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
+                                  const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
+                                  float *logits_or_null, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  return verify_rows(w_q4k, n, k, x, m, draft_host, argmax, accept_out, logits_or_null, workspace,
+                     workspace_bytes, stream, false);
+}
+
+kq_status kq_verify_argmax_accept_noalloc(const void *w_q4k, int64_t n, int64_t k, const float *x, int m,
+                                          const int32_t *draft_host, int32_t *argmax, int32_t *accept_out,
+                                          float *logits_or_null, void *stream) {
+  if (!w_q4k || !x || !argmax || !accept_out) return KQ_ERR_NULL;
+  if (m > 1 && !draft_host) return KQ_ERR_NULL;
+  const size_t need = kq_workspace_bytes(n, k, m);
+  if (!need) return KQ_ERR_SHAPE;
+  if (need > (size_t)KQ_NOALLOC_MAX_BYTES) return KQ_ERR_WORKSPACE;
+  // every argument check of the call below, on a stand-in workspace address
+  // (256-byte aligned, never used), so that a refused call makes no HIP call
+  kq_status s = verify_rows(w_q4k, n, k, x, m, draft_host, argmax, accept_out, logits_or_null,
+                            (void *)(uintptr_t)256, need, stream, true);
+  if (s != KQ_OK) return s;
+  void *ws = nullptr;
+  if (noalloc_workspace(&ws) || !ws) return KQ_ERR_LAUNCH;
+  return kq_verify_argmax_accept(w_q4k, n, k, x, m, draft_host, argmax, accept_out, logits_or_null, ws, need,
+                                 stream);
 }
 
 size_t kq_stream_probe_sink_bytes(void) { return 4 * 8192; }

@@ -171,6 +171,10 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value = 0u)
 // Copy one 32-bit device word to the host on `stream` and wait for the
 // stream (a hipError_t as int).
 int read_device_word(const unsigned *dev, unsigned *host, void *stream);
+// Device address of the current device's copy of the library's fixed
+// workspace (KQ_NOALLOC_MAX_BYTES, 256-byte aligned), looked up once per
+// device (a hipError_t as int).
+int noalloc_workspace(void **ptr);
 int launch_tile(const uint8_t *w, int64_t n, int64_t k, uint8_t *out, void *stream, int fmt = kFmtQ4);
 int launch_stream_probe(const uint8_t *p, int64_t chunks, unsigned *sink, int blocks, void *stream);
 // Softmax rows: chunks of a row (4,096 logits each) and the two-pass launch

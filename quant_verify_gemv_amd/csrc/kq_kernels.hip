@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kq_internal.h"
 
 namespace kq {
@@ -1939,6 +1941,30 @@ int launch_fill(unsigned *p, int64_t n_words, void *stream, unsigned value) {
   hipLaunchKernelGGL(kq_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p,
                      n_words, value);
   return (int)hipGetLastError();
+}
+
+// The fixed workspace of kq_verify_argmax_accept_noalloc: one copy per GPU.
+// Host code never uses the array's name as a device address; it uses the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[KQ_NOALLOC_MAX_BYTES];
+
+int noalloc_workspace(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int read_device_word(const unsigned *dev, unsigned *host, void *stream) {

@@ -26,7 +26,7 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
             "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged",
             "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject", "kq_speculative_resample",
-            "kq_chain_status")
+            "kq_chain_status", "kq_verify_argmax_accept_noalloc")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -103,6 +103,7 @@ def load() -> ctypes.CDLL:
     lib.kq_gemv_chain.argtypes = [P, ctypes.POINTER(ChainPlan), P, SZ, P]
     lib.kq_chain_scratch_init.argtypes = [ctypes.POINTER(ChainPlan), P, SZ, P]
     lib.kq_chain_status.argtypes = [ctypes.POINTER(ChainPlan), P, SZ, P]
+    lib.kq_verify_argmax_accept_noalloc.argtypes = [P, I64, I64, P, I32, P, P, P, P, P]
     lib.kq_softmax_workspace_bytes.argtypes = [I32, I64]
     lib.kq_softmax_workspace_bytes.restype = SZ
     F = ctypes.c_float
@@ -124,7 +125,7 @@ def load() -> ctypes.CDLL:
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
                  "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged",
                  "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject",
-                 "kq_speculative_resample", "kq_chain_status"):
+                 "kq_speculative_resample", "kq_chain_status", "kq_verify_argmax_accept_noalloc"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib

@@ -366,6 +366,31 @@ def test_chain_status_argument_errors_before_any_hip_call():
     assert lib.kq_chain_status(ctypes.byref(pl), FAKE + 16, 1 << 30, None) == ALIGN
 
 
+def test_noalloc_verify_argument_errors_before_any_hip_call():
+    """The allocation-free verify refuses every bad argument with the code
+    kq_verify_argmax_accept gives, and a shape whose workspace exceeds the
+    library's fixed array with KQ_ERR_WORKSPACE, before any HIP call (there
+    is no GPU here: a call that reached the device lookup would report
+    KQ_ERR_LAUNCH)."""
+    lib = kq.load()
+    n, k = 512, 1024
+    dr = (ctypes.c_int32 * 3)(1, 2, 3)
+
+    def call(w=FAKE, n=n, k=k, x=FAKE, m=4, draft=dr, am=FAKE, acc=FAKE):
+        return lib.kq_verify_argmax_accept_noalloc(w, n, k, x, m, draft, am, acc, None, None)
+    assert call(w=None) == NULL and call(x=None) == NULL
+    assert call(am=None) == NULL and call(acc=None) == NULL
+    assert call(draft=None) == NULL
+    assert call(k=1000) == SHAPE and call(m=0) == SHAPE and call(m=65) == SHAPE and call(n=0) == SHAPE
+    assert call(w=FAKE + 8) == ALIGN and call(x=FAKE + 4) == ALIGN
+    bad = (ctypes.c_int32 * 3)(1, n, 3)
+    assert call(draft=bad) == TOKEN
+    # 4,096 blocks per row: 69 MB of staged activations, over the fixed array
+    big_k = 256 * 4096
+    assert kq.workspace_bytes(n, big_k, 4) > 24 << 20
+    assert call(k=big_k) == WS
+
+
 def test_tree_verify_argument_errors_before_any_hip_call():
     lib = kq.load()
     n, k = 512, 1024
