@@ -489,17 +489,17 @@ size_t kq_chain_table_bytes(int n_phases) {
   return (size_t)n_phases * sizeof(Phase);
 }
 
-// Chain geometry: 8 waves of `tpw` 16-row tiles (row groups of 128 tpw
-// rows), barriers every 4 units, 4 weight register sets.
+// Chain geometry: row groups of kChainRows rows (kq_chain_kernel's compute
+// waves of one 16-row tile each; `tpw` is 1).
 static Geometry chain_geometry(int64_t n, int64_t k, int count, int tpw) {
   Geometry g;
   g.count = count;
-  g.waves = 8;
+  g.waves = kChainRows / 16;
   g.tpw = tpw;
   g.bi = 4;
   g.depth = 4;
   g.ms = 1;
-  g.rows = 128 * tpw;
+  g.rows = kChainRows * tpw;
   g.n_wg_per = (int)cdiv(n, g.rows);
   g.n_groups = count * g.n_wg_per;
   g.kb = (int)(k / kQK);
@@ -518,7 +518,7 @@ static size_t chain_part_off(int max_groups) {
   return align256((size_t)kCntOff + sizeof(unsigned) * kCntStride * (size_t)max_groups);
 }
 static size_t chain_flag_off(int max_groups, int64_t wg, int tpw) {
-  return chain_part_off(max_groups) + align256(sizeof(float) * (size_t)wg * 2 * kMaxRows * 128 * (size_t)tpw);
+  return chain_part_off(max_groups) + align256(sizeof(float) * (size_t)wg * 2 * kMaxRows * kChainRows * (size_t)tpw);
 }
 static size_t chain_flag_bytes(int64_t wg) { return (size_t)wg * 256; }
 
@@ -615,7 +615,7 @@ kq_status kq_gemv_chain(const void *table_dev, const kq_chain_plan *plan, void *
   a.partials = (float *)(sc + chain_part_off(plan->max_groups));
   a.epoch = (unsigned *)(sc + kEpochOff);
   a.flags = (unsigned long long *)(sc + chain_flag_off(plan->max_groups, plan->workgroups, plan->tiles_per_wave));
-  a.g = chain_geometry(128, kQK, 1, plan->tiles_per_wave);
+  a.g = chain_geometry(kChainRows, kQK, 1, plan->tiles_per_wave);
   a.g.n_wg = plan->workgroups;
   if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;
   return KQ_OK;

@@ -16,6 +16,9 @@ constexpr int kMaxTreeRows = 64;      // activation rows per call: up to 4 slice
 // or two of them; 33 to 64 rows take two launches)
 constexpr int row_slices(int m) { return m <= 16 ? 1 : m <= 32 ? 2 : 4; }
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
+// Rows per row group of a chain launch (kq_chain_kernel's compute waves times
+// 16-row tiles)
+constexpr int kChainRows = 128;
 
 // Tiled weight layout (see kq_tile_weights in kq.h): 2,304-byte records of
 // one block of one 16-row tile: headers, then the two quant halves in lane

@@ -1138,6 +1138,7 @@ constexpr int kCwE = kCwChunks / kCwPT;                // of them per producer t
 constexpr int kCwC = 8;                                // contributors' partials in flight in a pull
 static_assert(kCwE * kCwPT == kCwChunks, "result chunks split evenly over the producer threads");
 static_assert((kCwBI & (kCwBI - 1)) == 0, "barrier interval a power of two");
+static_assert(kCwRows == kChainRows, "row groups of the chain geometry");
 
 // One unit of T 16-row tiles of Q4_K weights: per tile, block d, dmin, the
 // 6-bit scales and mins unpacked in registers, the 4-bit quants times their
@@ -1177,10 +1178,26 @@ __device__ __forceinline__ void q4_unit(const WTile (&cur)[T], const uint8_t *xb
     bm[t] = half4{p0[0], p0[1], p1[0], p1[1]};
     cq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // A operands (x hi and lo of k-step s) read from LDS two k-steps before
+  // their MFMAs, in three rotating register pairs; the scheduling fences
+  // keep each read ahead of the work it should overlap with
+  constexpr int kAP = 2;
+  half8 ahi_r[kAP + 1], alo_r[kAP + 1];
+  const uint8_t *xa = xb + lane * 16;
+#pragma unroll
+  for (int s = 0; s < kAP; ++s) {
+    ahi_r[s] = *(const half8 *)(xa + (s * 2 + 0) * 1024);
+    alo_r[s] = *(const half8 *)(xa + (s * 2 + 1) * 1024);
+  }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const half8 ahi = *(const half8 *)(xb + (s * 2 + 0) * 1024 + lane * 16);
-    const half8 alo = *(const half8 *)(xb + (s * 2 + 1) * 1024 + lane * 16);
+    if (s + kAP < 8) {
+      ahi_r[(s + kAP) % (kAP + 1)] = *(const half8 *)(xa + ((s + kAP) * 2 + 0) * 1024);
+      alo_r[(s + kAP) % (kAP + 1)] = *(const half8 *)(xa + ((s + kAP) * 2 + 1) * 1024);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const half8 ahi = ahi_r[s % (kAP + 1)];
+    const half8 alo = alo_r[s % (kAP + 1)];
     const bool hi = (s & 2) != 0;
     const unsigned mask = hi ? mask_hi : mask_lo;
 #pragma unroll
@@ -1392,6 +1409,13 @@ __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLau
     for (int s0 = 0; s0 < S; s0 += kCwD) {
 #pragma unroll
       for (int j = 0; j < kCwD; ++j) {
+        // the two compute waves of a SIMD take turns at the higher issue
+        // priority, one step each, so that one of them runs ahead and their
+        // memory waits and MFMA chains do not line up
+        if ((wave >> 2) == (j & 1))
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
         load_w(wr[(j + kCwD - 1) % kCwD]);
         __builtin_amdgcn_sched_barrier(0);
         if (s0 + j < S) {
