@@ -1115,8 +1115,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
 //    waiting for one unit's weights never waits for anything younger: the
 //    reason this prefetch can run deeper than kq_gemv_kernel's, where the
 //    activation loads and the stores share the counter;
-//  * producer waves move each unit's staged activations from L2 into the
-//    LDS ring one barrier interval ahead, and do every global store: the
+//  * producer waves copy each unit's staged activations into the LDS ring
+//    one barrier interval ahead (direct-to-LDS buffer loads, no register
+//    staging), and do every global store: the
 //    results the compute waves hand over through LDS (a finished row group's
 //    logits, a later contributor's partial sums), the pull reduction of a
 //    split row group, and the grid barrier between phases.
@@ -1132,12 +1133,13 @@ constexpr int kCwBI = 4;                               // most units between wor
 constexpr int kCwRows = 16 * kCwW * kCwT;              // rows per row group (128)
 constexpr int kCwPT = 64 * kCwP;                       // producer threads
 constexpr int kCwXc = (int)(kStageBytes / 16);         // 16-byte chunks of a staged block (1,060)
-constexpr int kCwXj = (kCwXc + kCwPT - 1) / kCwPT;     // chunks per producer thread and unit (5)
+constexpr int kCwXj = (kCwXc + kCwPT - 1) / kCwPT;     // LDS copy instructions per producer wave and block (5)
 constexpr int kCwChunks = kCwRows * kMaxRows / 4;      // 16-byte chunks of a row group's result (512)
 constexpr int kCwE = kCwChunks / kCwPT;                // of them per producer thread (2)
 constexpr int kCwC = 8;                                // contributors' partials in flight in a pull
 static_assert(kCwE * kCwPT == kCwChunks, "result chunks split evenly over the producer threads");
 static_assert((kCwBI & (kCwBI - 1)) == 0, "barrier interval a power of two");
+static_assert(kCwP == 4 && kCwXc <= 64 * 4 * kCwXj, "4 producer waves cover a block in kCwXj KiB runs each");
 static_assert(kCwRows == kChainRows, "row groups of the chain geometry");
 
 // One unit of T 16-row tiles of Q4_K weights: per tile, block d, dmin, the
@@ -1483,29 +1485,26 @@ __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLau
     const int KB = KQ_CPH(ph, kb);
     const int u0 = run_start(KQ_CPH(ph, units));
     const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_CPH(ph, staged));
-    u32x4 xr[kCwBI][kCwXj];
+    // buffer_load_dwordx4 ... lds: every lane's 16 bytes go straight to LDS
+    // at the wave's base + 16 x lane, so instruction j of producer wave pw
+    // copies chunks 64 (4 j + pw) .. + 63 of a block (one contiguous KiB)
+    const int pw = __builtin_amdgcn_readfirstlane(pt >> 6), ln = pt & 63;
 #pragma unroll
     for (int q = 0; q < kCwBI; ++q) {
       if (i + q < i_end) {
         const unsigned src = (unsigned)((u0 + i + q) % KB) * (unsigned)kStageBytes;
+        uint8_t *dst = s_x[ring_buf(i + q, lb)];
 #pragma unroll
         for (int j = 0; j < kCwXj; ++j) {
-          const int c = pt + kCwPT * j < kCwXc ? pt + kCwPT * j : kCwXc - 1;
-          xr[q][j] = buf_ld16(x_rsrc, (unsigned)c * 16u, src);
+          const int cb = 64 * (4 * j + pw);
+          if (cb < kCwXc && cb + ln < kCwXc)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (__attribute__((address_space(3))) void *)(dst + cb * 16),
+                                                     16, (unsigned)(cb + ln) * 16u, src, 0, 0);
         }
       }
     }
     between();
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-#pragma unroll
-    for (int q = 0; q < kCwBI; ++q) {
-      if (i + q < i_end) {
-        uint8_t *dst = s_x[ring_buf(i + q, lb)];
-#pragma unroll
-        for (int j = 0; j < kCwXj; ++j)
-          if (pt + kCwPT * j < kCwXc) *(u32x4 *)(dst + (pt + kCwPT * j) * 16) = xr[q][j];
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the blocks are in LDS
   };
   // logits of row group g of phase ph from a result ([row][16] fp32, the
   // thread's chunks pt + j kCwPT)
