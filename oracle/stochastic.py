@@ -27,11 +27,12 @@ handoff", section 32.6):
 Readings where the pages leave a step open (each stated again in the
 design notes):
 
-* Uniform draws are inputs: u[i] is the draw of the attempt at position i;
-  the draw that samples the replacement after a rejection at position i is
-  u[i + 1], and the bonus after k acceptances uses u[k] (k + 1 draws cover
-  every path). The pages' generator and its conversion to a float are not
-  given.
+* Uniform draws: u[i] is the draw of the attempt at position i; the draw
+  that samples the replacement after a rejection at position i is u[i + 1],
+  and the bonus after k acceptances uses u[k] (k + 1 draws cover every
+  path). speculative_decide takes them as inputs; speculative_decide_mt
+  takes them one at a time from an MT19937 stream (oracle.mt19937, whose
+  float conversion is a reading of its own), which is the same rule.
 * Sampling walks the order accumulating c = c + p[t] in fp32 and returns the
   first token with u < c; if rounding leaves u >= c after the last token,
   the last token of the order is returned.
@@ -90,22 +91,40 @@ def speculative_decide(draft: Sequence[int], q_rows: np.ndarray, p_rows: np.ndar
     q_rows [k, N] and p_rows [k + 1, N] are fp32 probability rows (draft and
     target), orders [k + 1, N] token orders per target row, uniforms k + 1
     draws in [0, 1)."""
+    if len(uniforms) != len(draft) + 1:
+        raise ValueError("geometry: need k draft rows, k + 1 target rows, orders and uniforms")
+    draws = iter(uniforms)
+    return _decide(draft, q_rows, p_rows, orders, lambda: F32(next(draws)))
+
+
+def speculative_decide_mt(draft: Sequence[int], q_rows: np.ndarray, p_rows: np.ndarray,
+                          orders: np.ndarray, rng) -> Tuple[int, int]:
+    """The same decision taking its draws from a generator (an
+    oracle.mt19937.MT19937) in the pages' order, one per attempted proposal
+    and one for the token drawn where the decision stops: rng advances by
+    accepted + 2 draws after a rejection, by k + 1 when all k are accepted,
+    and by none when the geometry is refused."""
+    return _decide(draft, q_rows, p_rows, orders, rng.uniform_f32)
+
+
+def _decide(draft, q_rows, p_rows, orders, draw) -> Tuple[int, int]:
     k = len(draft)
     q_rows = np.asarray(q_rows, dtype=F32)
     p_rows = np.asarray(p_rows, dtype=F32)
-    if q_rows.shape[0] != k or p_rows.shape[0] != k + 1 or len(orders) != k + 1 or len(uniforms) != k + 1:
+    if q_rows.shape[0] != k or p_rows.shape[0] != k + 1 or len(orders) != k + 1:
         raise ValueError("geometry: need k draft rows, k + 1 target rows, orders and uniforms")
     n = p_rows.shape[1]
     if q_rows.shape[1] != n:
         raise ValueError("draft and target rows differ in width")
+    for tok in draft:
+        if not 0 <= int(tok) < n:
+            raise ValueError(f"draft token {int(tok)} outside [0, {n})")
     for i, tok in enumerate(draft):
         tok = int(tok)
-        if not 0 <= tok < n:
-            raise ValueError(f"draft token {tok} outside [0, {n})")
         q = q_rows[i, tok]
         p = p_rows[i, tok]
         acceptance = F32(1.0) if q <= 0 else min(F32(p / q), F32(1.0))
-        if F32(uniforms[i]) <= acceptance:
+        if draw() <= acceptance:
             continue
         residual = np.maximum(p_rows[i] - q_rows[i], F32(0.0)).astype(F32)
         total = _f32_sum(residual)
@@ -114,5 +133,5 @@ def speculative_decide(draft: Sequence[int], q_rows: np.ndarray, p_rows: np.ndar
         else:
             residual = (residual / total).astype(F32)
         order = [int(t) for t in orders[i] if residual[int(t)] > 0]
-        return i, sample_ordered(residual, order, uniforms[i + 1])
-    return k, sample_ordered(p_rows[k], list(orders[k]), uniforms[k])
+        return i, sample_ordered(residual, order, draw())
+    return k, sample_ordered(p_rows[k], list(orders[k]), draw())
