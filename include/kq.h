@@ -465,6 +465,52 @@ kq_status kq_speculative_first_reject(int k, const float *p_at, const float *q_a
 kq_status kq_speculative_resample(int64_t n, const float *p_row, const float *q_row_or_null, const int32_t *order,
                                   float u, int32_t *token);
 
+/* ------------------------------------------------- the pinned draw stream
+ * The book's chapter 33, section 33.2 takes every acceptance draw and every
+ * resample draw from one MT19937 stream, consumed in order; chapter 8,
+ * section 8.6 (guarantee 1) requires that stream to be reimplemented bit
+ * for bit and kept apart from any generic random source. This is the
+ * published generator (Matsumoto and Nishimura, ACM TOMACS 8(1), 1998) with
+ * its reference-code seeding, which std::mt19937 also uses: seeded with
+ * 5489, its 10,000th output is 4,123,659,995.
+ *
+ * The float draw of one 32-bit output w is (w >> 8) * 2^-24 (fp32, exact, in
+ * [0, 1 - 2^-24]); the pages do not give the conversion, so this is a
+ * reading of this library.
+ *
+ * The state is a plain struct the caller owns (copy it to snapshot or
+ * replay a stream). index is the next word to temper; 624 means the block is
+ * spent and is regenerated before the next output. A state with index above
+ * 624 is refused (KQ_ERR_SHAPE) and left as it is. */
+#define KQ_MT19937_WORDS 624
+typedef struct kq_mt19937 {
+  uint32_t mt[KQ_MT19937_WORDS];
+  uint32_t index;
+} kq_mt19937;
+
+/* state = the stream of `seed` (x[0] = seed, x[i] = 1812433253 (x[i-1] xor
+ * (x[i-1] >> 30)) + i mod 2^32, index 624). KQ_ERR_NULL. */
+kq_status kq_mt19937_seed(kq_mt19937 *state, uint32_t seed);
+
+/* The next `count` outputs (count >= 0): 32-bit words, or float draws.
+ *  out  host [count] (written); NULL allowed when count = 0
+ * KQ_ERR_NULL, KQ_ERR_SHAPE (count < 0, or a corrupt state); nothing is
+ * drawn on an error. */
+kq_status kq_mt19937_u32(kq_mt19937 *state, uint32_t *out, int64_t count);
+kq_status kq_mt19937_uniform_f32(kq_mt19937 *state, float *out, int64_t count);
+
+/* kq_speculative_decide with its draws taken from `rng` in the pages'
+ * order: the draw of each attempted proposal, then the draw of the token
+ * chosen where the decision stops. rng advances by accepted + 2 draws after
+ * a rejection, by k + 1 after k acceptances; the decision equals
+ * kq_speculative_decide with uniforms[i] = the i-th float draw of rng.
+ * Every argument check of kq_speculative_decide is made first, and on any
+ * error (KQ_ERR_NULL for a null rng, KQ_ERR_SHAPE for a corrupt state) rng
+ * is left unchanged and nothing is written. */
+kq_status kq_speculative_decide_mt(int k, const int32_t *draft_tokens, int64_t n, const float *draft_rows,
+                                   const float *target_rows, const int32_t *orders, kq_mt19937 *rng,
+                                   int32_t *accepted, int32_t *next_token);
+
 /* ---------------------------------------------------------------- chains
  * A chain launch runs a sequence of grouped products in ONE grid, each
  * phase depending on the one before it: phase i + 1 starts reading its

@@ -749,6 +749,80 @@ kq_status kq_speculative_decide(int k, const int32_t *draft_tokens, int64_t n, c
   return KQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// MT19937 (Matsumoto and Nishimura 1998): 624-word state, the twist
+// x[k + 624] = x[k + 397] ^ ((x[k] & 0x80000000 | x[k + 1] & 0x7fffffff) A)
+// with A the companion matrix of 0x9908b0df, and the tempering of each
+// output word.
+kq_status kq_mt19937_seed(kq_mt19937 *state, uint32_t seed) {
+  if (!state) return KQ_ERR_NULL;
+  state->mt[0] = seed;
+  for (uint32_t i = 1; i < KQ_MT19937_WORDS; ++i) {
+    const uint32_t prev = state->mt[i - 1];
+    state->mt[i] = 1812433253u * (prev ^ (prev >> 30)) + i;
+  }
+  state->index = KQ_MT19937_WORDS;
+  return KQ_OK;
+}
+
+static void mt_twist(kq_mt19937 *s) {
+  constexpr int kN = KQ_MT19937_WORDS, kM = 397;
+  for (int k = 0; k < kN; ++k) {
+    const uint32_t y = (s->mt[k] & 0x80000000u) | (s->mt[(k + 1) % kN] & 0x7FFFFFFFu);
+    s->mt[k] = s->mt[(k + kM) % kN] ^ (y >> 1) ^ ((y & 1u) ? 0x9908B0DFu : 0u);
+  }
+  s->index = 0;
+}
+
+static uint32_t mt_next(kq_mt19937 *s) {
+  if (s->index >= KQ_MT19937_WORDS) mt_twist(s);
+  uint32_t y = s->mt[s->index++];
+  y ^= y >> 11;
+  y ^= (y << 7) & 0x9D2C5680u;
+  y ^= (y << 15) & 0xEFC60000u;
+  y ^= y >> 18;
+  return y;
+}
+
+static float mt_float(uint32_t w) { return (float)(w >> 8) * 0x1.0p-24f; }
+
+kq_status kq_mt19937_u32(kq_mt19937 *state, uint32_t *out, int64_t count) {
+  if (!state || (count > 0 && !out)) return KQ_ERR_NULL;
+  if (count < 0 || state->index > KQ_MT19937_WORDS) return KQ_ERR_SHAPE;
+  for (int64_t i = 0; i < count; ++i) out[i] = mt_next(state);
+  return KQ_OK;
+}
+
+kq_status kq_mt19937_uniform_f32(kq_mt19937 *state, float *out, int64_t count) {
+  if (!state || (count > 0 && !out)) return KQ_ERR_NULL;
+  if (count < 0 || state->index > KQ_MT19937_WORDS) return KQ_ERR_SHAPE;
+  for (int64_t i = 0; i < count; ++i) out[i] = mt_float(mt_next(state));
+  return KQ_OK;
+}
+
+kq_status kq_speculative_decide_mt(int k, const int32_t *draft_tokens, int64_t n, const float *draft_rows,
+                                   const float *target_rows, const int32_t *orders, kq_mt19937 *rng,
+                                   int32_t *accepted, int32_t *next_token) {
+  // the outputs are checked here: the decision below writes to locals
+  if (!rng || !accepted || !next_token) return KQ_ERR_NULL;
+  if (rng->index > KQ_MT19937_WORDS) return KQ_ERR_SHAPE;
+  if (k < 0 || k >= kMaxRows) return KQ_ERR_SHAPE;
+  // the k + 1 draws any path can use, from a copy: position i reads draw i,
+  // the token drawn after a rejection at i draw i + 1, the bonus draw k
+  kq_mt19937 ahead = *rng;
+  float u[kMaxRows + 1];
+  for (int i = 0; i <= k; ++i) u[i] = mt_float(mt_next(&ahead));
+  int32_t acc = 0, tok = 0;
+  const kq_status st =
+      kq_speculative_decide(k, draft_tokens, n, draft_rows, target_rows, orders, u, &acc, &tok);
+  if (st != KQ_OK) return st;  // every check precedes the first draw: rng untouched
+  const int used = acc < k ? acc + 2 : k + 1;
+  for (int i = 0; i < used; ++i) (void)mt_next(rng);
+  *accepted = acc;
+  *next_token = tok;
+  return KQ_OK;
+}
+
 static bool verify_length_ok(int length) { return length == 3 || length == 7 || length == 15; }
 
 kq_status kq_draft_block_argmax(const void *w_q4k, int64_t n, int64_t k, const float *x, int verify_length,

@@ -26,7 +26,8 @@ EXPORTED = ("kq_status_string", "kq_workspace_bytes", "kq_staged_bytes", "kq_scr
             "kq_softmax_workspace_bytes", "kq_softmax_rows", "kq_speculative_decide",
             "kq_tiled_bytes_fmt", "kq_tile_weights_fmt", "kq_staged_bytes_rows", "kq_verify_tree_staged",
             "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject", "kq_speculative_resample",
-            "kq_chain_status", "kq_verify_argmax_accept_noalloc")
+            "kq_chain_status", "kq_verify_argmax_accept_noalloc", "kq_mt19937_seed", "kq_mt19937_u32",
+            "kq_mt19937_uniform_f32", "kq_speculative_decide_mt")
 
 LAYOUT_ROWS = 0      # llama.cpp row-major blocks
 LAYOUT_TILED16 = 1   # kq_tile_weights output
@@ -52,6 +53,12 @@ class ChainPlan(ctypes.Structure):
     _fields_ = [("n_phases", ctypes.c_int32), ("m", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("workgroups", ctypes.c_int32), ("max_groups", ctypes.c_int32), ("tiles_per_wave", ctypes.c_int32),
                 ("table_bytes", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64)]
+
+
+class MT19937State(ctypes.Structure):
+    """kq_mt19937 (include/kq.h): 624 state words and the next index."""
+    _fields_ = [("mt", ctypes.c_uint32 * 624), ("index", ctypes.c_uint32)]
+
 
 _lib = None
 
@@ -112,6 +119,11 @@ def load() -> ctypes.CDLL:
     lib.kq_gather_rows.argtypes = [P, I32, I64, P, I32, P, P]
     lib.kq_speculative_first_reject.argtypes = [I32, P, P, P, P]
     lib.kq_speculative_resample.argtypes = [I64, P, P, P, F, P]
+    MTP = ctypes.POINTER(MT19937State)
+    lib.kq_mt19937_seed.argtypes = [MTP, ctypes.c_uint32]
+    lib.kq_mt19937_u32.argtypes = [MTP, P, I64]
+    lib.kq_mt19937_uniform_f32.argtypes = [MTP, P, I64]
+    lib.kq_speculative_decide_mt.argtypes = [I32, P, I64, P, P, P, MTP, P, P]
     lib.kq_verify_staged_dev.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P, SZ, P]
     lib.kq_staged_bytes_rows.argtypes = [I64, I32]
     lib.kq_staged_bytes_rows.restype = SZ
@@ -125,7 +137,8 @@ def load() -> ctypes.CDLL:
                  "kq_stream_probe", "kq_chain_encode", "kq_gemv_chain", "kq_chain_scratch_init",
                  "kq_softmax_rows", "kq_speculative_decide", "kq_tile_weights_fmt", "kq_verify_tree_staged",
                  "kq_verify_staged_dev", "kq_gather_rows", "kq_speculative_first_reject",
-                 "kq_speculative_resample", "kq_chain_status", "kq_verify_argmax_accept_noalloc"):
+                 "kq_speculative_resample", "kq_chain_status", "kq_verify_argmax_accept_noalloc",
+                 "kq_mt19937_seed", "kq_mt19937_u32", "kq_mt19937_uniform_f32", "kq_speculative_decide_mt"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -557,6 +570,55 @@ def speculative_decide(draft, draft_rows, target_rows, orders, uniforms):
     _check(load().kq_speculative_decide(k, vp(dt.ctypes.data), n, vp(dr.ctypes.data), vp(tr.ctypes.data),
                                         vp(od.ctypes.data), vp(un.ctypes.data), ctypes.byref(acc),
                                         ctypes.byref(nxt)), "kq_speculative_decide")
+    return int(acc.value), int(nxt.value)
+
+
+class MT19937:
+    """The library's pinned draw stream (kq_mt19937_*): a host-owned state
+    that the calls below advance. copy() snapshots it."""
+
+    def __init__(self, seed: int = 5489):
+        self.state = MT19937State()
+        _check(load().kq_mt19937_seed(ctypes.byref(self.state), int(seed) & 0xFFFFFFFF), "kq_mt19937_seed")
+
+    def copy(self) -> "MT19937":
+        c = MT19937.__new__(MT19937)
+        c.state = MT19937State()
+        ctypes.memmove(ctypes.byref(c.state), ctypes.byref(self.state), ctypes.sizeof(MT19937State))
+        return c
+
+    def u32(self, count: int):
+        import numpy as np
+        out = np.zeros(max(int(count), 1), dtype=np.uint32)
+        _check(load().kq_mt19937_u32(ctypes.byref(self.state), ctypes.c_void_p(out.ctypes.data), int(count)),
+               "kq_mt19937_u32")
+        return out[:int(count)]
+
+    def uniform_f32(self, count: int):
+        import numpy as np
+        out = np.zeros(max(int(count), 1), dtype=np.float32)
+        _check(load().kq_mt19937_uniform_f32(ctypes.byref(self.state), ctypes.c_void_p(out.ctypes.data),
+                                             int(count)), "kq_mt19937_uniform_f32")
+        return out[:int(count)]
+
+
+def speculative_decide_mt(draft, draft_rows, target_rows, orders, rng: MT19937):
+    """kq_speculative_decide_mt: the decision with its draws taken from rng
+    (advanced by the draws consumed). Returns (accepted, next_token)."""
+    import numpy as np
+    k = len(draft)
+    tr = np.ascontiguousarray(target_rows, dtype=np.float32)
+    n = int(tr.shape[1])
+    dr = np.ascontiguousarray(draft_rows, dtype=np.float32) if k else np.zeros((1, n), np.float32)
+    od = np.ascontiguousarray(orders, dtype=np.int32)
+    dt = np.ascontiguousarray(draft, dtype=np.int32) if k else np.zeros(1, np.int32)
+    if tr.shape[0] != k + 1 or od.shape != (k + 1, n) or (k and dr.shape != (k, n)):
+        raise ValueError("geometry: need k draft rows, k + 1 target rows and orders")
+    acc, nxt = ctypes.c_int32(0), ctypes.c_int32(0)
+    vp = ctypes.c_void_p
+    _check(load().kq_speculative_decide_mt(k, vp(dt.ctypes.data), n, vp(dr.ctypes.data), vp(tr.ctypes.data),
+                                           vp(od.ctypes.data), ctypes.byref(rng.state), ctypes.byref(acc),
+                                           ctypes.byref(nxt)), "kq_speculative_decide_mt")
     return int(acc.value), int(nxt.value)
 
 
