@@ -1,0 +1,94 @@
+"""Concurrent calls on two HIP streams, each with its own workspace (GPU).
+
+The single-launch kernels combine split row groups by last arrival (an
+atomic count, never a wait on another workgroup), so two launches may share
+the CUs in any proportion. Two unrelated problems are enqueued alternately
+on two default-priority streams with no synchronisation between them, eight
+rounds each, every round writing fresh output buffers:
+
+* stream 1: kq_gemv_rows on the 6,656 x 6,656 square matrix, M = 16
+  (workspace 1);
+* stream 2: kq_verify_argmax_accept on a 32,768 x 6,656 head, M = 8 with 7
+  draft tokens (workspace 2), and kq_gemv_staged on the tiled square matrix
+  with a scratch of its own.
+
+Every output of every round must equal, bit for bit, the same call made
+alone on one stream beforehand (the kernels are deterministic), and those
+reference outputs are checked against the oracle on sampled rows."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.parity import check_argmax, check_logits, log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import quant_verify_gemv_amd as kq
+    kq.load()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return kq
+
+
+def test_two_streams_with_separate_workspaces(kq):
+    nA = kA = synthetic.HIDDEN
+    nB, kB, mB = 32768, synthetic.HIDDEN, 8
+    wA_h = synthetic.q4k_matrix(nA, kA, 301)
+    wB_h = synthetic.q4k_matrix(nB, kB, 302)
+    xA_h = synthetic.activations(16, kA, 303)
+    xB_h = synthetic.activations(mB, kB, 304)
+    wA, wB = torch.from_numpy(wA_h).to(DEV), torch.from_numpy(wB_h).to(DEV)
+    xA, xB = torch.from_numpy(xA_h).to(DEV), torch.from_numpy(xB_h).to(DEV)
+    wA_t = kq.tile_weights(wA, nA, kA)
+    stA = kq.stage_rows(xA)
+    draft = list(range(100, 100 + mB - 1))
+
+    ws1 = kq.lib.alloc_workspace(kq.workspace_bytes(nA, kA, 16), DEV)
+    ws2 = kq.lib.alloc_workspace(kq.workspace_bytes(nB, kB, mB), DEV)
+    sc2 = kq.new_scratch(nA, kA, DEV)
+
+    # references: each call alone
+    refA = kq.gemv_rows(wA, nA, kA, xA, workspace=ws1)
+    amB, accB, lgB = kq.verify(wB, nB, kB, xB, draft, want_logits=True, workspace=ws2)
+    refS = kq.gemv_staged(wA_t, nA, kA, stA, 16, sc2, layout=kq.LAYOUT_TILED16)
+    torch.cuda.synchronize()
+    refA, refS = refA.clone(), refS.clone()
+    amB, accB, lgB = amB.clone(), accB.clone(), lgB.clone()
+
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, nA - 1], np.random.default_rng(305).integers(0, nA, 40)]))
+    L, A = oracle.gemv_rows(wA_h, kA, xA_h, rows=rows)
+    check_logits(refA.cpu().numpy()[:, rows], L, A, what="square (stream reference)")
+    check_logits(refS.cpu().numpy()[:, rows], L, A, what="square staged (stream reference)")
+    LB, AB = oracle.gemv_rows(wB_h, kB, xB_h)
+    check_logits(lgB.cpu().numpy(), LB, AB, what="head verify (stream reference)")
+    check_argmax(amB.cpu().numpy(), LB, AB, what="head verify (stream reference)")
+
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(8):
+        oA = torch.full((16, nA), float("nan"), device=DEV)
+        oS = torch.full((16, nA), float("nan"), device=DEV)
+        oam = torch.full((mB,), -1, dtype=torch.int32, device=DEV)
+        oacc = torch.full((2,), -1, dtype=torch.int32, device=DEV)
+        olg = torch.full((mB, nB), float("nan"), device=DEV)
+        torch.cuda.synchronize()  # the fills are done before either stream starts
+        kq.gemv_rows(wA, nA, kA, xA, logits=oA, workspace=ws1, stream=s1)
+        kq.verify(wB, nB, kB, xB, draft, want_logits=True, workspace=ws2, stream=s2, out=(oam, oacc, olg))
+        kq.gemv_staged(wA_t, nA, kA, stA, 16, sc2, logits=oS, stream=s2, layout=kq.LAYOUT_TILED16)
+        kq.gemv_rows(wA, nA, kA, xA, logits=oA, workspace=ws1, stream=s1)  # again, the same result
+        outs.append((oA, oS, oam, oacc, olg))
+    torch.cuda.synchronize()
+    for rep, (oA, oS, oam, oacc, olg) in enumerate(outs):
+        assert torch.equal(oA, refA), f"round {rep}: stream-1 logits differ from the call alone"
+        assert torch.equal(oS, refS), f"round {rep}: stream-2 staged logits differ from the call alone"
+        assert torch.equal(oam, amB) and torch.equal(oacc, accB), f"round {rep}: stream-2 argmax / accept differ"
+        assert torch.equal(olg, lgB), f"round {rep}: stream-2 verify logits differ"
+    log("streams: 8 concurrent rounds on two streams equal the calls made alone")
