@@ -647,12 +647,12 @@ def source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload, m, layout_name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), or None
-    when there is none for this workload and M or the kernel source changed
-    since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"kq_gemv_kernel.{workload}.traffic.md")
+def stored_traffic(workload, m, layout_name, launch):
+    """HBM bytes of one launch (`launch`: "chain" or "lm_head") from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE scaled by the
+    copy-kernel calibration), or None when there is none for this workload
+    and M or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"kq_chain_kernel.{workload}.traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -662,7 +662,7 @@ def stored_traffic(workload, m, layout_name):
             vals[k.strip()] = v.strip().strip("`")
     if vals.get("source_sha256") != source_digest() or vals.get("weight_layout") != layout_name:
         return None
-    v = vals.get(f"traffic_bytes_per_launch_m{m}")
+    v = vals.get(f"traffic_bytes_{launch}_m{m}")
     return float(v) if v else None
 
 
@@ -704,8 +704,8 @@ def kernel_rooflines(stack, torch, m, reps, workload, layout_name):
         ch = stack.chain(m)
         us = event_us(torch, lambda: kq.gemv_chain(ch), reps)
         ch.status()
-        out["stack_chain"] = roofline_entry("kq_gemv_kernel (chain, 208 phases)", stack.algorithmic_bytes(m)[0], us,
-                                            1, stored_traffic(workload, m, layout_name))
+        out["stack_chain"] = roofline_entry("kq_chain_kernel (208 phases)", stack.algorithmic_bytes(m)[0], us,
+                                            1, stored_traffic(workload, m, layout_name, "chain"))
     else:
         def grouped():
             for grp in stack.groups:
@@ -719,8 +719,9 @@ def kernel_rooflines(stack, torch, m, reps, workload, layout_name):
     h = stack.head
     us = graph_time(torch, lambda i: kq.verify_staged(stack.w_head, h.n, h.k, stack.staged[h.k], m,
                                                       stack.draft[:m - 1], stack.head_scratch,
-                                                      out=(stack.am[:m], stack.acc, None), layout=stack.layout), 20)
-    out["lm_head_verify"] = roofline_entry("kq_gemv_kernel (LM-head verify)", stack.algorithmic_bytes(m)[-1], us)
+                                                      out=(stack.am[:m], stack.acc, None), layout=stack.layout), 50)
+    out["lm_head_verify"] = roofline_entry("kq_gemv_kernel (LM-head verify)", stack.algorithmic_bytes(m)[-1], us, 1,
+                                           stored_traffic(workload, m, layout_name, "lm_head"))
     x_bytes = sum(4 * m * k + kq.staged_bytes(k) for k in stack.ks)
     us = graph_time(torch, lambda i: [kq.stage_rows(stack.x[k][:m], staged=stack.staged[k]) for k in stack.ks], 20)
     out["stage"] = roofline_entry("kq_stage_kernel (all distinct K)", x_bytes, us, len(stack.ks))

@@ -37,7 +37,9 @@
  *    aligned, or one of the tiled layouts below; x is fp32 [m][k]
  *    row-major, 16-byte aligned; logits fp32 [m][n].
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
- *    library allocates nothing and keeps no global mutable state.
+ *    library allocates nothing and keeps no global mutable state, except the
+ *    fixed workspace of kq_verify_argmax_accept_noalloc (a device array per
+ *    GPU and its looked-up address, see there).
  *  - Every call is enqueued on `stream` (a hipStream_t; NULL = default
  *    stream) and returns without synchronising; results are valid once the
  *    stream reaches that point.
