@@ -154,6 +154,10 @@ struct GemvLaunch {
   unsigned x_rec, x_off;
   int row0;
   const int32_t *am_prev;
+  // single launches (no chain table): 1 runs the launch's one phase on
+  // kq_chain_kernel (plain Q4_K products of the 128-row geometry, m <= 16),
+  // with kq_gemv_kernel's last-arrival reduction of split row groups
+  int chain_single;
   Geometry g;
 };
 

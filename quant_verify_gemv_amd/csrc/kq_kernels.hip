@@ -1270,9 +1270,14 @@ __device__ __forceinline__ bool producer_bar(unsigned *cnt, unsigned &target) {
   return true;
 }
 
-#define KQ_CPH(I_, f) (((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f)
+#define KQ_CPH(I_, f) (SINGLE ? a.ph.f : ((const __attribute__((address_space(4))) Phase *)a.chain)[(I_)].f)
 
-template <bool ROWS>  // Q4_K weights in llama.cpp rows (else tiled), as for kq_gemv_kernel
+// ROWS: Q4_K weights in llama.cpp rows (else tiled), as for kq_gemv_kernel.
+// SINGLE: a single launch's one phase (a.ph, no table, no grid barrier);
+// split row groups are then combined as kq_gemv_kernel combines them, by the
+// last contributor to arrive, so no workgroup ever waits for another and the
+// launch needs no co-residency.
+template <bool ROWS, bool SINGLE>
 __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLaunch a) {
   // LDS: the activation ring (two halves of up to kCwBI staged blocks: the
   // compute waves read one half while the producers fill the other; after
@@ -1285,7 +1290,7 @@ __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLau
   __shared__ int s_fdesc;      // the final hand-over of a phase
   __shared__ unsigned s_pbar;  // producer barrier count
   __shared__ unsigned s_bad;   // producer broadcast words: a partial never arrived,
-  __shared__ unsigned s_last;  // this arrival completed the grid barrier,
+  __shared__ unsigned s_last;  // this arrival completed the grid barrier (single launches: the groups it reduces),
   __shared__ unsigned s_ok;    // the barrier wait ended with a release
   __shared__ int s_abort;      // set by the producers when a wait gave up
   __shared__ unsigned long long s_epoch;
@@ -1298,7 +1303,7 @@ __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLau
   const int M = a.m;
   const int P = gridDim.x;
   const int p = blockIdx.x;
-  const int n_ph = a.n_phases;
+  const int n_ph = SINGLE ? 1 : a.n_phases;
   constexpr bool tiled = !ROWS;
   // hand-over kinds: a row group finished here (its logits), a later
   // contributor's partial (to its slot 0, pulled by the group's first
@@ -1320,12 +1325,15 @@ __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLau
   auto tile_row = [&](int t) -> int { return (t * kCwW + wave) * 16 + ln; };
 
   if (tid == 0) {
+    s_last = 0u;
     s_htag[0] = s_htag[1] = -1;
     s_pbar = 0u;
     s_bad = 0u;
     s_abort = 0;
-    s_epoch = (unsigned long long)__hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 32;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the epoch is read before any arrival
+    if (!SINGLE) {
+      s_epoch = (unsigned long long)__hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) << 32;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the epoch is read before any arrival
+    }
   }
 
   if (wave < kCwW) {
@@ -1611,6 +1619,94 @@ __global__ __launch_bounds__(64 * (kCwW + kCwP), 1) void kq_chain_kernel(GemvLau
     gint += n_int;
     const int fdesc = s_fdesc;
     const float *fin = (const float *)s_x[(n_int & 1) * kCwBI];
+    if constexpr (SINGLE) {
+      // A single launch combines split row groups as kq_gemv_kernel does:
+      // this workgroup's partial of its first group (when that group is not
+      // complete here) is in slot 0, its partial of a later last group in
+      // slot 1; once they are written, it arrives at each group's count, and
+      // the last contributor to arrive sums all of them in workgroup order.
+      const int base = U / P, rem = U % P;
+      const int big = rem * (base + 1);
+      auto owner = [&](int u) -> int { return u < big ? u / (base + 1) : rem + (u - big) / base; };
+      auto start_of = [&](int q) -> int { return q * base + (q < rem ? q : rem); };
+      const int u0 = start_of(p), u_last = u0 + nu - 1;
+      const int g_first = u0 / KB, g_last = u_last / KB;
+      const int have_first = (u0 % KB != 0) || (u_last < g_first * KB + KB - 1);
+      const int last_partial = (g_last != g_first) && (u_last % KB != KB - 1);
+      constexpr unsigned kSlotBytes = (unsigned)(kMaxRows * kCwRows) * 4u;
+      if ((fdesc & 3) == kKindReduce) {
+        // the final segment opened its group: slot 1 unless it is also the
+        // first segment (then its group is the first group: slot 0)
+        f32x4 v[kCwE];
+        load_hand(fin, v);
+        const unsigned slot = (fdesc >> 2) != g_first ? kSlotBytes : 0u;
+#pragma unroll
+        for (int j = 0; j < kCwE; ++j) st_dev16(part_rsrc, slot0(p) + slot + (unsigned)(pt + j * kCwPT) * 16u, v[j]);
+      } else {
+        store_hand(ph, fdesc, fin);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
+      if (!producer_bar(&s_pbar, pbar_target)) {
+        abort_all();
+        return;
+      }
+      if (pt == 0) {
+        unsigned flags = 0u;
+        if (have_first || last_partial) {
+          unsigned *cnt_f = a.group_cnt + (int64_t)g_first * kCntStride;
+          unsigned *cnt_l = a.group_cnt + (int64_t)g_last * kCntStride;
+          const unsigned old_f =
+              __hip_atomic_fetch_add(cnt_f, have_first ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const unsigned old_l =
+              __hip_atomic_fetch_add(cnt_l, last_partial ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int c_first = owner(g_first * KB + KB - 1) - owner(g_first * KB) + 1;
+          const int c_last = owner(g_last * KB + KB - 1) - owner(g_last * KB) + 1;
+          if (have_first && old_f == (unsigned)(c_first - 1)) {
+            __hip_atomic_store(cnt_f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            flags |= 1u;
+          }
+          if (last_partial && old_l == (unsigned)(c_last - 1)) {
+            __hip_atomic_store(cnt_l, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            flags |= 2u;
+          }
+        }
+        s_last = flags;
+      }
+      if (!producer_bar(&s_pbar, pbar_target)) {
+        abort_all();
+        return;
+      }
+      const unsigned flags = s_last;
+      // sum group g over its contributors pf .. pl (pf's partial in its
+      // slot 1 when its run starts before g, the others' in slot 0), the
+      // loads of kCwC contributors in flight together
+      auto reduce = [&](int g) {
+        const int pf = owner(g * KB), pl = owner(g * KB + KB - 1);
+        const unsigned pf_slot = start_of(pf) < g * KB ? kSlotBytes : 0u;
+        f32x4 v[kCwE];
+#pragma unroll
+        for (int j = 0; j < kCwE; ++j) v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 <= pl - pf; c0 += kCwC) {
+          f32x4 pv[kCwE][kCwC];
+#pragma unroll
+          for (int c = 0; c < kCwC; ++c) {
+            const int q = pf + c0 + c <= pl ? pf + c0 + c : pl;
+            const unsigned src = slot0(q) + (q == pf ? pf_slot : 0u);
+#pragma unroll
+            for (int j = 0; j < kCwE; ++j) pv[j][c] = ld_dev16(part_rsrc, src + (unsigned)(pt + j * kCwPT) * 16u);
+          }
+#pragma unroll
+          for (int c = 0; c < kCwC; ++c)
+#pragma unroll
+            for (int j = 0; j < kCwE; ++j)
+              if (pf + c0 + c <= pl) v[j] = c0 + c == 0 ? pv[j][c] : v[j] + pv[j][c];
+        }
+        store_logits(ph, g, v);
+      };
+      if (flags & 1u) reduce(g_first);
+      if (flags & 2u) reduce(g_last);
+      continue;  // one phase: the loop ends here
+    }
     int bad = 0;
     if ((fdesc & 3) == kKindReduce) {
       // pull: sum the later contributors' partials of group g in workgroup
@@ -2042,12 +2138,23 @@ int launch_gather(const float *rows, int64_t n, const int32_t *tokens, int count
 int launch_gemv(const GemvLaunch &a, void *stream) {
   const dim3 grid((unsigned)a.g.n_wg);
   hipStream_t st = (hipStream_t)stream;
-  if (a.chain) {
+  if (a.chain || a.chain_single) {
     if (a.g.rows != kCwRows) return (int)hipErrorInvalidConfiguration;  // row groups of the chain geometry
-    if (a.layout == KQ_LAYOUT_ROWS)
-      hipLaunchKernelGGL(kq_chain_kernel<true>, grid, dim3(64 * (kCwW + kCwP)), 0, st, a);
-    else
-      hipLaunchKernelGGL(kq_chain_kernel<false>, grid, dim3(64 * (kCwW + kCwP)), 0, st, a);
+    const dim3 block(64 * (kCwW + kCwP));
+    if (a.chain_single) {
+      // one phase, m <= 16, plain products of Q4_K weights
+      if (a.verify || a.g.ms != 1 || a.x_rec != (unsigned)kStageBytes || a.x_off != 0u ||
+          layout_fmt(a.layout) != kFmtQ4)
+        return (int)hipErrorInvalidConfiguration;
+      if (a.layout == KQ_LAYOUT_ROWS)
+        hipLaunchKernelGGL((kq_chain_kernel<true, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((kq_chain_kernel<false, true>), grid, block, 0, st, a);
+    } else if (a.layout == KQ_LAYOUT_ROWS) {
+      hipLaunchKernelGGL((kq_chain_kernel<true, false>), grid, block, 0, st, a);
+    } else {
+      hipLaunchKernelGGL((kq_chain_kernel<false, false>), grid, block, 0, st, a);
+    }
     return (int)hipGetLastError();
   }
   const int fmt = layout_fmt(a.layout);
@@ -2089,7 +2196,7 @@ int chain_capacity() {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_chain_kernel<false>, 64 * (kCwW + kCwP), 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_chain_kernel<false, false>, 64 * (kCwW + kCwP), 0);
   if (e != hipSuccess) return -(int)e;
   return per_cu * cus;
 }
