@@ -41,6 +41,9 @@ if ROOT not in sys.path:
 import synthetic  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# plain Q4_K products of the 128-row geometry (the square and fc shapes) run
+# on the chain kernel's one-phase mode
+ONE_PHASE = "kq_chain_kernel (one-phase launch)"
 METRIC = "verify rows/s + weight HBM GB/s (% of peak) at M=1/16; M16÷M1 step-time ratio"
 
 
@@ -363,7 +366,7 @@ def config_timings(stack, torch, calls=50):
         st = kq.stage_rows(x[:m])
         us = time_calls(lambda i: kq.gemv_staged(ws[i % 16], n, k, st, m, scratch, logits=logits[:m],
                                                    layout=kq.LAYOUT_TILED16))
-        res[f"m{m}"] = rate(wbytes, m, us, wbytes + 4 * m * (n + k))
+        res[f"m{m}"] = rate(wbytes, m, us, wbytes + 4 * m * (n + k), kernel=ONE_PHASE)
     res["m16_over_m1"] = round(res["m16"]["us_per_call"] / res["m1"]["us_per_call"], 4)
     out["square_6656x6656"] = res
     del ws
@@ -377,14 +380,15 @@ def config_timings(stack, torch, calls=50):
     us = time_calls(lambda i: kq.gemv_staged(ws[i % 4], n, k, st, 16, scratch, logits=logits,
                                                layout=kq.LAYOUT_TILED16))
     out["fc_33280_to_6656_m16"] = rate(n * synthetic.q4k_bytes_per_row(k), 16, us,
-                                       n * synthetic.q4k_bytes_per_row(k) + 4 * 16 * (n + k))
+                                       n * synthetic.q4k_bytes_per_row(k) + 4 * 16 * (n + k), kernel=ONE_PHASE)
     del ws
     h = stack.head
     sth = stack.staged[h.k]
     kq.stage_rows(stack.x[h.k][:16], staged=sth)
     us = time_calls(lambda i: kq.verify_staged(stack.w_head, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
                                                  out=(stack.am, stack.acc, None), layout=stack.layout))
-    out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us, h.weight_bytes + 4 * 16 * h.k + 4 * 18)
+    out["lm_head_verify_m16"] = rate(h.weight_bytes, 16, us, h.weight_bytes + 4 * 16 * h.k + 4 * 18,
+                                     kernel="kq_gemv_kernel (LM-head verify)")
     out["stochastic_lm_head_m16"] = stochastic_timing(stack, torch, time_calls)
     out.update(kquant_timings(stack, torch, time_calls))
     tree = out["tree_verify_lm_head"]
