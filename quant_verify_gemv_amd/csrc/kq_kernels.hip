@@ -544,7 +544,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   begin_w(0);
 
   {
-    const int ph = 0;
+    [[maybe_unused]] const int ph = 0;  // single phase: KQ_PH reads the launch's own fields
     const int N = KQ_PH(ph, n);
     const int KB = KQ_PH(ph, kb);
     const int n_wg_per = KQ_PH(ph, n_wg_per);
@@ -2182,6 +2182,7 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(kFmtQ6, 12, 1, 4, 4, 1)
     KQ_CASE(kFmtQ6, 8, 2, 4, 4, 1)
     KQ_CASE(kFmtQ4, 8, 2, 2, 3, 2)
+    KQ_CASE(kFmtQ5, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ6, 8, 2, 2, 3, 2)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;

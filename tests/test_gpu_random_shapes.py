@@ -1,0 +1,154 @@
+"""Seeded random shapes against the oracle.
+
+Row counts are drawn log-uniform from 1 to 150,000, depths from one block up
+to a bounded matrix size, activation rows from 1 to 64 and the format from
+Q4_K, Q5_K and Q6_K. That mixes launches with fewer units than workgroups,
+row groups split over one to many workgroups, ragged last tiles, every row
+geometry and the one- and two-pass paths for more than 16 rows, in
+combinations no hand-picked shape list covers. Each case checks every logit
+of the staged product, the row-major calls bitwise against the tiled one,
+the verify's argmax (with flags) and accept, and for more than 16 rows a
+random token tree's walk. Chains of several phases of mixed random shapes
+are checked the same way, phase by phase."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.parity import check_accept, check_argmax, check_logits, log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MAX_WEIGHTS = 24_000_000  # weights per matrix: keeps the oracle at a second or so
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import quant_verify_gemv_amd as kq
+    kq.load()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return kq
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def draw_shape(rng, max_m=64, n_max=150_000):
+    n = max(1, int(np.exp(rng.uniform(0.0, np.log(n_max)))))
+    kb = int(rng.integers(1, max(1, min(48, MAX_WEIGHTS // (256 * n))) + 1))
+    if max_m <= 16 or rng.random() < 0.75:
+        m = int(rng.integers(1, min(16, max_m) + 1))
+    else:
+        m = int(rng.integers(17, max_m + 1))
+    return n, 256 * kb, m
+
+
+def random_tree(rng, m, am, n_vocab, p_follow=0.6):
+    """m nodes, each node's parent among the 6 before it; a child takes its
+    parent's target argmax with probability p_follow, else a uniform token
+    (siblings may repeat a token; the walk then takes the lowest index)."""
+    parent = [-1] + [int(rng.integers(max(0, j - 6), j)) for j in range(1, m)]
+    token = [0] * m
+    for j in range(1, m):
+        token[j] = int(am[parent[j]]) if rng.random() < p_follow else int(rng.integers(n_vocab))
+    return parent, token
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_shape(kq, seed):
+    rng = np.random.default_rng(50_000 + seed)
+    n, k, m = draw_shape(rng)
+    fmt = ("q4k", "q4k", "q5k", "q6k")[int(rng.integers(4))]
+    geom = kq.launch_geometry(n, k)
+    log(f"random shape seed={seed}: {fmt} n={n} k={k} m={m} geometry {geom}")
+    w = synthetic.kquant_matrix(fmt, n, k, 51_000 + seed)
+    x = synthetic.activations(m, k, 52_000 + seed)
+    L, A = oracle.gemv_rows(w, k, x, fmt=fmt)
+    o_am, o_nc = oracle.argmax_flags(L, A)
+    lay = kq.FORMATS[fmt][0]
+    w_d, x_d = to_dev(w), to_dev(x)
+    wt = kq.tile_weights(w_d, n, k, fmt=fmt)
+    st = kq.stage_rows(x_d)
+    sc = kq.new_scratch(n, k, DEV)
+
+    G = kq.gemv_staged(wt, n, k, st, m, sc, layout=lay)
+    torch.cuda.synchronize()
+    G = G.cpu().numpy()
+    r = check_logits(G, L, A, what=f"seed {seed} {fmt} n={n} k={k} m={m}")
+    log(f"random shape seed={seed}: max |d|/tol = {r:.3g}")
+    if fmt == "q4k":
+        R = kq.gemv_staged(w_d, n, k, st, m, sc)
+        torch.cuda.synchronize()
+        assert np.array_equal(R.cpu().numpy(), G), "row-major weights give other logits than tiled"
+        if m <= 16:
+            R2 = kq.gemv_rows(w_d, n, k, x_d)
+            torch.cuda.synchronize()
+            assert np.array_equal(R2.cpu().numpy(), G), "kq_gemv_rows differs from the staged call"
+
+    draft = synthetic.inject_mismatches(o_am[:m - 1], n, seed=53_000 + seed) if m > 1 else []
+    if fmt == "q4k" and m <= 16:
+        am, acc, lg = kq.verify(w_d, n, k, x_d, list(draft), want_logits=True)
+    else:
+        am, acc, lg = kq.verify_staged(wt, n, k, st, m, list(draft), sc, want_logits=True, layout=lay)
+    torch.cuda.synchronize()
+    am, acc = am.cpu().numpy(), acc.cpu().numpy()
+    assert np.array_equal(lg.cpu().numpy(), G), "verify logits differ from the product's"
+    check_argmax(am, L, A, what=f"seed {seed} verify")
+    check_accept(acc[0], acc[1], draft, am, o_am, o_nc, what=f"seed {seed} verify")
+
+    if m > 16:
+        parent, token = random_tree(rng, m, o_am, n)
+        tam, tacc, path, _ = kq.verify_tree_staged(wt, n, k, st, parent, token, sc, layout=lay)
+        torch.cuda.synchronize()
+        tam, tacc, path = tam.cpu().numpy(), tacc.cpu().numpy(), path.cpu().numpy()
+        assert np.array_equal(tam, am), "tree verify argmax differs from the linear verify's"
+        g_acc, g_nxt, g_path = oracle.tree_accept(parent, token, tam)
+        assert (int(tacc[0]), int(tacc[1])) == (g_acc, g_nxt), "walk differs from the oracle's walk"
+        assert list(path[:g_acc]) == g_path and np.all(path[g_acc:] == -1)
+        if not np.any(o_nc > 0):
+            assert oracle.tree_accept(parent, token, o_am)[:2] == (g_acc, g_nxt)
+        log(f"random shape seed={seed}: tree of {m} nodes accepted {g_acc}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_chain(kq, seed):
+    """3 to 6 dependent phases of random shapes (1 to 3 matrices each, Q4_K,
+    rows or tiled), one launch: every logit of every matrix against the
+    oracle; a second launch of the same chain gives the same bits."""
+    rng = np.random.default_rng(60_000 + seed)
+    m = int(rng.integers(1, 17))
+    tiled = bool(rng.integers(2))
+    lay = kq.LAYOUT_TILED16 if tiled else kq.LAYOUT_ROWS
+    phases, expect = [], []
+    for ph in range(int(rng.integers(3, 7))):
+        n, k, _ = draw_shape(rng, max_m=16, n_max=40_000)
+        count = int(rng.integers(1, 4))
+        x = synthetic.activations(m, k, 61_000 + 10 * seed + ph)
+        st = kq.stage_rows(to_dev(x))
+        ws, outs = [], []
+        for i in range(count):
+            w = synthetic.q4k_matrix(n, k, 62_000 + 100 * seed + 10 * ph + i)
+            expect.append((ph, i, n, k) + oracle.gemv_rows(w, k, x))
+            wd = to_dev(w)
+            ws.append(kq.tile_weights(wd, n, k) if tiled else wd)
+            outs.append(torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV))
+        phases.append((ws, n, k, st, outs))
+    log(f"random chain seed={seed}: m={m} {'tiled' if tiled else 'rows'} phases "
+        + ", ".join(f"{len(p[0])}x{p[1]}x{p[2]}" for p in phases))
+    chain = kq.chain_encode(phases, m, layout=lay)
+    kq.gemv_chain(chain)
+    chain.status()
+    torch.cuda.synchronize()
+    first = [o.cpu().numpy() for p in phases for o in p[4]]
+    for got, (ph, i, n, k, L, A) in zip(first, expect):
+        check_logits(got, L, A, what=f"chain seed {seed} phase {ph} member {i} ({n}x{k})")
+    for o in (o for p in phases for o in p[4]):
+        o.fill_(float("nan"))
+    kq.gemv_chain(chain)
+    chain.status()
+    torch.cuda.synchronize()
+    again = [o.cpu().numpy() for p in phases for o in p[4]]
+    assert all(np.array_equal(a, b) for a, b in zip(first, again)), "second launch differs"

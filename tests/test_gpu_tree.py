@@ -29,7 +29,7 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-@pytest.mark.parametrize("fmt,layout", [("q4k", "rows"), ("q4k", "tiled"), ("q6k", "tiled")])
+@pytest.mark.parametrize("fmt,layout", [("q4k", "rows"), ("q4k", "tiled"), ("q5k", "tiled"), ("q6k", "tiled")])
 @pytest.mark.parametrize("n,k", [(300, 1024), (1000, 2304), (129, 6656)])
 def test_more_rows_every_logit(kq, fmt, layout, n, k):
     w = synthetic.kquant_matrix(fmt, n, k, 700 + n)
@@ -49,7 +49,7 @@ def test_more_rows_every_logit(kq, fmt, layout, n, k):
         log(f"rows: m={m} max |d|/tol = {r:.3g}")
 
 
-@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("fmt", ["q4k", "q5k", "q6k"])
 def test_passes_bitwise_equal_to_smaller_calls(kq, fmt):
     """A call of 33 to 64 rows makes two passes over the weights: rows 0-31
     as a 32-row call, the rest as a call on those rows alone. Both parts
