@@ -152,3 +152,65 @@ def test_random_chain(kq, seed):
     torch.cuda.synchronize()
     again = [o.cpu().numpy() for p in phases for o in p[4]]
     assert all(np.array_equal(a, b) for a, b in zip(first, again)), "second launch differs"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_entry_points(kq, seed):
+    """The other entry points on random Q4_K shapes: a grouped launch of 1 to
+    8 matrices (every logit of every member), the draft block's proposals and
+    head, the verify with drafts in device memory (bitwise the host-draft
+    call's result), and probability rows plus the gather on the verify's
+    logits at a random temperature, with or without a soft cap."""
+    from tests.test_gpu_stochastic import check_probs
+    rng = np.random.default_rng(70_000 + seed)
+    n, k, m = draw_shape(rng, max_m=16)
+    n = max(n, 2)
+    count = int(rng.integers(1, 9))
+    count = max(1, min(count, MAX_WEIGHTS // (n * k)))
+    tiled = bool(rng.integers(2))
+    lay = kq.LAYOUT_TILED16 if tiled else kq.LAYOUT_ROWS
+    log(f"random entry points seed={seed}: n={n} k={k} m={m} group of {count} ({'tiled' if tiled else 'rows'})")
+    ws = [synthetic.q4k_matrix(n, k, 71_000 + 10 * seed + i) for i in range(count)]
+    x = synthetic.activations(16, k, 72_000 + seed)
+    wds = [to_dev(w) for w in ws]
+    wus = [kq.tile_weights(wd, n, k) for wd in wds] if tiled else wds
+    st = kq.stage_rows(to_dev(x[:m]))
+    gs = kq.new_group_scratch(n, k, count, DEV)
+    outs = kq.gemv_staged_group(wus, n, k, st, m, gs, layout=lay)
+    torch.cuda.synchronize()
+    for i in range(count):
+        L, A = oracle.gemv_rows(ws[i], k, x[:m])
+        check_logits(outs[i].cpu().numpy(), L, A, what=f"seed {seed} group member {i}")
+
+    L16, A16 = oracle.gemv_rows(ws[0], k, x)
+    vl = (3, 7, 15)[int(rng.integers(3))]
+    props, head = kq.draft_block_argmax(wds[0], n, k, to_dev(x), vl, want_head=True)
+    torch.cuda.synchronize()
+    check_argmax(props.cpu().numpy(), L16[1:vl + 1], A16[1:vl + 1], what=f"seed {seed} draft block vl={vl}")
+    check_argmax(head.cpu().numpy(), L16[:1], A16[:1], what=f"seed {seed} draft block head")
+
+    o_am, o_nc = oracle.argmax_flags(L16[:m], A16[:m])
+    draft = synthetic.inject_mismatches(o_am[:m - 1], n, seed=73_000 + seed) if m > 1 else np.zeros(0, np.int32)
+    sc = kq.new_scratch(n, k, DEV)
+    host = kq.verify_staged(wus[0], n, k, st, m, [int(t) for t in draft], sc, want_logits=True, layout=lay)
+    on_dev = kq.verify_staged(wus[0], n, k, st, m, to_dev(np.asarray(draft, dtype=np.int32)), sc,
+                              want_logits=True, layout=lay)
+    torch.cuda.synchronize()
+    for a, b in zip(host, on_dev):
+        assert np.array_equal(a.cpu().numpy(), b.cpu().numpy()), "device drafts give another result"
+    am, acc = host[0].cpu().numpy(), host[1].cpu().numpy()
+    check_argmax(am, L16[:m], A16[:m], what=f"seed {seed} verify")
+    check_accept(acc[0], acc[1], draft, am, o_am, o_nc, what=f"seed {seed} verify")
+
+    lg = host[2]
+    lh = lg.cpu().numpy()
+    temperature = max(1e-3, float(np.std(lh)) * float(rng.uniform(0.2, 2.0)))
+    cap = 0.0 if rng.random() < 0.5 else float(np.abs(lh).max()) * float(rng.uniform(0.3, 1.0))
+    P = kq.softmax_rows(lg, temperature, cap)
+    torch.cuda.synchronize()
+    ph = P.cpu().numpy()
+    r = check_probs(ph, lh, temperature, cap, f"seed {seed} rows T={temperature:.3g} cap={cap:.3g}")
+    log(f"random entry points seed={seed}: probability rows max err / tol = {r:.3g}")
+    tok = rng.integers(0, n, m).astype(np.int32)
+    got = kq.gather_rows(P, to_dev(tok)).cpu().numpy()
+    assert np.array_equal(got, ph[np.arange(m), tok]), "gather differs from indexing the rows"
