@@ -69,3 +69,50 @@ def test_noalloc_verify_matches_workspace_call_twice(kq):
         if n <= 4096:
             L, A = oracle.gemv_rows(w, k, x)
             check_logits(lg_a, L, A, what=f"noalloc n={n} k={k} m={m}")
+
+
+def test_noalloc_verify_replays_from_a_graph(kq):
+    """The caller it is for: the call captured in a HIP graph (nothing is
+    allocated during capture; the draft tokens travel in the kernel
+    arguments). Every replay gives the eager call's argmax, accept and
+    logits bit for bit, also after an eager call of another shape has used
+    the same device array in between."""
+    lib = kq.lib.load()
+    n, k, m = 3000, 2304, 8
+    w = torch.from_numpy(synthetic.q4k_matrix(n, k, 77)).to(DEV)
+    x = torch.from_numpy(synthetic.activations(m, k, 78)).to(DEV)
+    draft = [int(t) for t in np.random.default_rng(79).integers(0, n, m - 1)]
+    dr = (ctypes.c_int32 * (m - 1))(*draft)
+    am = torch.full((m,), -7, dtype=torch.int32, device=DEV)
+    acc = torch.full((2,), -7, dtype=torch.int32, device=DEV)
+    lg = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+
+    def call():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = lib.kq_verify_argmax_accept_noalloc(p(w), n, k, p(x), m, dr, p(am), p(acc), p(lg), s)
+        assert rc == 0, kq.status_string(rc)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (am.cpu().numpy(), acc.cpu().numpy(), lg.cpu().numpy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    other_w = torch.from_numpy(synthetic.q4k_matrix(700, 1024, 80)).to(DEV)
+    other_x = torch.from_numpy(synthetic.activations(5, 1024, 81)).to(DEV)
+    for r in range(3):
+        am.fill_(-7)
+        acc.fill_(-7)
+        lg.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = (am.cpu().numpy(), acc.cpu().numpy(), lg.cpu().numpy())
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), f"replay {r}: argmax or accept"
+        assert np.array_equal(got[2].view(np.uint32), ref[2].view(np.uint32)), f"replay {r}: logits"
+        verify_both(kq, other_w, 700, 1024, other_x, [1, 2, 3, 4])  # another shape on the same array
