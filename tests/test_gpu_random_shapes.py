@@ -57,7 +57,7 @@ def random_tree(rng, m, am, n_vocab, p_follow=0.6):
     return parent, token
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_shape(kq, seed):
     rng = np.random.default_rng(50_000 + seed)
     n, k, m = draw_shape(rng)
@@ -113,7 +113,7 @@ def test_random_shape(kq, seed):
         log(f"random shape seed={seed}: tree of {m} nodes accepted {g_acc}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_chain(kq, seed):
     """3 to 6 dependent phases of random shapes (1 to 3 matrices each, Q4_K,
     rows or tiled), one launch: every logit of every matrix against the
@@ -154,7 +154,7 @@ def test_random_chain(kq, seed):
     assert all(np.array_equal(a, b) for a, b in zip(first, again)), "second launch differs"
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_entry_points(kq, seed):
     """The other entry points on random Q4_K shapes: a grouped launch of 1 to
     8 matrices (every logit of every member), the draft block's proposals and
