@@ -92,3 +92,63 @@ def test_two_streams_with_separate_workspaces(kq):
         assert torch.equal(oam, amB) and torch.equal(oacc, accB), f"round {rep}: stream-2 argmax / accept differ"
         assert torch.equal(olg, lgB), f"round {rep}: stream-2 verify logits differ"
     log("streams: 8 concurrent rounds on two streams equal the calls made alone")
+
+
+def test_four_host_threads_each_with_its_own_stream(kq):
+    """Host reentrancy: four Python threads enter the library at once (ctypes
+    releases the interpreter lock during each call), each enqueueing twelve
+    rounds of kq_gemv_rows and kq_verify_argmax_accept on a stream and a
+    workspace of its own, for problems of different shapes, with no ordering
+    between the threads. Every output equals its call made alone, bit for
+    bit; those references match the oracle on sampled rows."""
+    import threading
+
+    shapes = [(synthetic.HIDDEN, synthetic.HIDDEN, 16), (2048, 9216, 4), (30000, 2304, 8), (513, 3328, 1)]
+    probs = []
+    for i, (n, k, m) in enumerate(shapes):
+        w_h = synthetic.q4k_matrix(n, k, 400 + i)
+        x_h = synthetic.activations(m, k, 410 + i)
+        w, x = torch.from_numpy(w_h).to(DEV), torch.from_numpy(x_h).to(DEV)
+        ws = kq.lib.alloc_workspace(kq.workspace_bytes(n, k, m), DEV)
+        draft = [int(t) for t in np.random.default_rng(420 + i).integers(0, n, m - 1)]
+        lg = kq.gemv_rows(w, n, k, x, workspace=ws)
+        am, acc, vl = kq.verify(w, n, k, x, draft, want_logits=True, workspace=ws)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(430 + i).integers(0, n, 24)]))
+        L, A = oracle.gemv_rows(w_h, k, x_h, rows=rows)
+        check_logits(lg.cpu().numpy()[:, rows], L, A, what=f"thread problem {i} (reference)")
+        assert torch.equal(vl, lg), f"problem {i}: verify logits differ from the product's"
+        probs.append(dict(n=n, k=k, m=m, w=w, x=x, ws=ws, draft=draft, ref=(lg.clone(), am.clone(), acc.clone())))
+
+    errors = []
+    start = threading.Barrier(len(probs))
+
+    def worker(i):
+        try:
+            p = probs[i]
+            n, k, m = p["n"], p["k"], p["m"]
+            s = torch.cuda.Stream()
+            outs = []
+            with torch.cuda.stream(s):
+                start.wait()
+                for _ in range(12):
+                    lg = torch.full((m, n), float("nan"), device=DEV)
+                    kq.gemv_rows(p["w"], n, k, p["x"], logits=lg, workspace=p["ws"], stream=s)
+                    am, acc, _ = kq.verify(p["w"], n, k, p["x"], p["draft"], workspace=p["ws"], stream=s)
+                    outs.append((lg, am, acc))
+                s.synchronize()
+                ref_lg, ref_am, ref_acc = p["ref"]
+                for r, (lg, am, acc) in enumerate(outs):
+                    if not (torch.equal(lg, ref_lg) and torch.equal(am, ref_am) and torch.equal(acc, ref_acc)):
+                        errors.append(f"thread {i} round {r}: differs from the call made alone")
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(probs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
+    log("threads: 4 host threads x 12 rounds equal the calls made alone")
