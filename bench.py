@@ -6,7 +6,8 @@ Workload: the synthetic ~16 GB target stack -- 52 layers x (4 x 6,656^2 +
 the 6,656 -> 131,072 LM head (argmax of every row + greedy accept of 15 draft
 tokens). One step = stage the activation rows (one block per distinct K, the
 stack matrices being independent products of a shared input), 364 GEMVs in
-208 launches, one LM-head verify. It runs at M = 16 rows (the headline) and M = 1 (the ratio).
+208 dependent phases (one chain launch by default), one LM-head verify. It
+runs at M = 16 rows (the headline) and M = 1 (the ratio).
 
 The stack follows a transformer layer's data dependencies: the three
 projections that read the same hidden state (q, k, v) form one phase, the
