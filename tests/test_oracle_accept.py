@@ -166,6 +166,18 @@ def test_argmax_flags_and_candidates_hand_cases():
     assert list(oracle.candidates(L[0], A[0], 0, rel=1e-4)) == [4]
 
 
+def test_flag_tolerance_is_the_sum_of_both_rows():
+    """The flag rule sums both rows' tolerances: j is a candidate iff
+    L[i*] - L[j] <= rel (A[i*] + A[j]). With rel = 1e-3 the tolerances are
+    0.3, 0.1, 0.01, 1.0, 0.1; the gaps 0.35, 0.305 and 1.2 fit only the sum
+    (each is above either row's tolerance alone), the gap 0.5 fits neither."""
+    L = np.array([[5.0, 4.65, 4.695, 3.8, 4.5]])
+    A = np.array([[300.0, 100.0, 10.0, 1000.0, 100.0]])
+    am, nc = oracle.argmax_flags(L, A, rel=1e-3)
+    assert am[0] == 0 and nc[0] == 3
+    assert list(oracle.candidates(L[0], A[0], 0, rel=1e-3)) == [1, 2, 3]
+
+
 def test_argmax_through_gemv_duplicated_rows():
     n, k = 32, 512
     w = synthetic.q4k_matrix(n, k, seed=30)
