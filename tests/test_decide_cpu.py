@@ -150,3 +150,28 @@ def test_two_step_decision_errors():
     assert lib.kq_speculative_resample(3, vp(zero), vp(zero), vp(order), ctypes.c_float(0.1), ctypes.byref(tok)) == SHAPE
     assert tok.value == -7, "written on an error"
     assert kq.speculative_resample(p, None, order, 0.25) == 0
+
+
+def test_decide_edge_cases_match_oracle():
+    """The library's decision on the boundary cases the oracle's pins fix:
+    a draw equal to the acceptance probability accepts; a zero residual
+    resamples from the target row; a walk that rounding lets run off the end
+    returns the last token that has residual mass, never the rejected one."""
+    o4 = np.array([list(range(4))] * 2, dtype=np.int32)
+    q = np.array([[0.5, 0.5, 0.0, 0.0]], dtype=np.float32)
+    p = np.array([[0.25] * 4, [0.1, 0.2, 0.3, 0.4]], dtype=np.float32)
+    half_up = float(np.nextafter(np.float32(0.5), np.float32(1)))
+    r = [14.628571510314941, 21.571428298950195, 27.14285659790039]
+    p5 = np.array([[r[0], r[1], r[2], 0.0, 1.0], [0.2] * 5], dtype=np.float32)
+    q5 = np.array([[0.0, 0.0, 0.0, 0.0, 2.0]], dtype=np.float32)
+    o5 = np.array([list(range(5))] * 2, dtype=np.int32)
+    top = float(np.float32(1.0) - np.float32(2.0 ** -24))
+    p3 = np.array([[0.1, 0.2, 0.3, 0.4]] * 3, dtype=np.float32)
+    q_big = np.array([[0.5] * 4, [0.25] * 4], dtype=np.float32)
+    o3 = np.array([list(range(4))] * 3, dtype=np.int32)
+    cases = [([0], q, p, o4, [0.5, 0.05], (1, 0)), ([0], q, p, o4, [half_up, 0.05], (0, 2)),
+             ([4], q5, p5, o5, [0.9, top], (0, 2)), ([3, 0], q_big, p3, o3, [0.9, 0.35, 0.5], (0, 2))]
+    for draft, qq, pp, oo, u, want in cases:
+        uu = np.array(u, dtype=np.float32)
+        assert oracle_decide(draft, qq, pp, oo, uu) == want
+        assert kq.speculative_decide(draft, qq, pp, oo, uu) == want

@@ -109,3 +109,66 @@ def test_every_planted_mistake_fails_a_pin():
     broken = [f"{name}: exit {rc} ({last})" for name, rc, last in results if rc not in (0, 1)]
     assert not broken, broken
     assert not survivors, "mutants no pin caught: " + "; ".join(survivors)
+
+
+PY_PINS = ["tests/test_oracle_stochastic.py", "tests/test_oracle_mt19937.py"]
+
+# (file in oracle/, name, text to replace, replacement)
+PY_MUTANTS = [
+    ("stochastic.py", "softmax: no temperature", "    z = z / temperature\n", "    z = z / 1.0\n"),
+    ("stochastic.py", "softmax: cap without its factor", "z = soft_cap * np.tanh(z / soft_cap)", "z = np.tanh(z / soft_cap)"),
+    ("stochastic.py", "ordered walk: u <= cumulative sum", "        if u < c:\n", "        if u <= c:\n"),
+    ("stochastic.py", "ordered walk: falls back to the first token", "    return int(order[-1])", "    return int(order[0])"),
+    ("stochastic.py", "acceptance q / p", "min(F32(p / q), F32(1.0))", "min(F32(q / p), F32(1.0))"),
+    ("stochastic.py", "acceptance: strict draw test", "if draw() <= acceptance:", "if draw() < acceptance:"),
+    ("stochastic.py", "residual q - p", "np.maximum(p_rows[i] - q_rows[i], F32(0.0))", "np.maximum(q_rows[i] - p_rows[i], F32(0.0))"),
+    ("stochastic.py", "zero residual falls back to q", "residual = p_rows[i].copy()", "residual = q_rows[i].copy()"),
+    ("stochastic.py", "bonus from row k - 1", "return k, sample_ordered(p_rows[k], list(orders[k]), draw())",
+     "return k, sample_ordered(p_rows[k - 1], list(orders[k]), draw())"),
+    ("stochastic.py", "order keeps zero-probability tokens", "if residual[int(t)] > 0]", "if residual[int(t)] >= 0]"),
+    ("stochastic.py", "q = 0 rejects", "F32(1.0) if q <= 0 else", "F32(0.0) if q <= 0 else"),
+    ("mt19937.py", "tempering mask", "y ^= (y << 7) & 0x9D2C5680", "y ^= (y << 7) & 0x1D2C5680"),
+    ("mt19937.py", "seeding multiplier", "(1812433253 * (prev ^ (prev >> 30)) + i)", "(1812433255 * (prev ^ (prev >> 30)) + i)"),
+    ("mt19937.py", "recurrence offset", "v = mt[(k + M) % N] ^ (y >> 1)", "v = mt[(k + M + 1) % N] ^ (y >> 1)"),
+    ("mt19937.py", "last tempering shift", "y ^= y >> 18", "y ^= y >> 17"),
+    ("mt19937.py", "float conversion keeps 23 bits", "np.float32((int(word) >> 8) * 2.0 ** -24)",
+     "np.float32((int(word) >> 9) * 2.0 ** -23)"),
+]
+
+
+def run_py_pins(tmp, tag, fname, old, new):
+    """Copy oracle/ to tmp/<tag>/oracle with one mistake planted in `fname`
+    (old -> new; None keeps it unchanged) and run the Python oracle's pins
+    against the copy in a fresh interpreter."""
+    import shutil
+    dst = os.path.join(tmp, tag)
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(dst, "oracle"),
+                    ignore=shutil.ignore_patterns("__pycache__", "*.tmp*"))
+    if fname is not None:
+        p = os.path.join(dst, "oracle", fname)
+        with open(p) as f:
+            text = f.read()
+        assert text.count(old) == 1, f"mutation site not found once: {old!r}"
+        with open(p, "w") as f:
+            f.write(text.replace(old, new))
+    code = (f"import sys\nsys.path.insert(0, {dst!r})\nimport oracle\n"
+            f"assert oracle.__file__.startswith({dst!r})\n"
+            "import pytest\n"
+            f"sys.exit(pytest.main({PY_PINS + ['-x', '-q', '-p', 'no:cacheprovider']!r}))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True, timeout=600)
+    lines = r.stdout.strip().splitlines()
+    return r.returncode, lines[-1] if lines else ""
+
+
+def test_every_planted_mistake_in_the_python_oracle_fails_a_pin():
+    with tempfile.TemporaryDirectory() as tmp:
+        rc, last = run_py_pins(tmp, "control", None, None, None)
+        assert rc == 0, f"the unmutated oracle must pass its pins: {last}"
+        jobs = [(i,) + m for i, m in enumerate(PY_MUTANTS)]
+        with ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(lambda j: (j[2],) + run_py_pins(tmp, f"p{j[0]}", j[1], j[3], j[4]), jobs))
+    survivors = [f"{name} ({last})" for name, rc, last in results if rc == 0]
+    broken = [f"{name}: exit {rc} ({last})" for name, rc, last in results if rc not in (0, 1)]
+    assert not broken, broken
+    assert not survivors, "mutants no pin caught: " + "; ".join(survivors)

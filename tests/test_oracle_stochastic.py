@@ -130,8 +130,48 @@ def test_decide_special_cases():
     q_big = np.array([[0.5, 0.5, 0.5, 0.5], [0.25] * 4], dtype=np.float32)
     acc, nxt = speculative_decide([3, 0], q_big, p, orders, [0.9, 0.05, 0.5])
     assert acc == 0 and nxt == sample_ordered(p[0], list(range(n)), 0.05) == 0
+    # ... and at a draw where walking the draft row instead would differ
+    # (target cumulative 0.1, 0.3, 0.6: token 2; draft cumulative 0.5: token 0)
+    assert speculative_decide([3, 0], q_big, p, orders, [0.9, 0.35, 0.5]) == (0, 2)
     # geometry is checked before any draw
     with pytest.raises(ValueError):
         speculative_decide([1], p[:1], p[:1], orders[:2], [0.5, 0.5])
     with pytest.raises(ValueError):
         speculative_decide([7], p[:1], p[:2], orders[:2], [0.5, 0.5])
+
+
+
+def test_decide_accepts_a_draw_equal_to_the_acceptance():
+    """The page's rule accepts when the draw is at most the acceptance
+    probability: p/q = 0.25/0.5 = 0.5 exactly, and the draw 0.5 accepts
+    (the bonus then comes from row 1); a strict comparison would reject and
+    resample from the residual (tokens 2 and 3)."""
+    orders = np.array([list(range(4))] * 2)
+    q = np.array([[0.5, 0.5, 0.0, 0.0]], dtype=np.float32)
+    p = np.array([[0.25] * 4, [0.1, 0.2, 0.3, 0.4]], dtype=np.float32)
+    assert speculative_decide([0], q, p, orders, [0.5, 0.05]) == (1, 0)
+    assert speculative_decide([0], q, p, orders, [np.nextafter(np.float32(0.5), np.float32(1)), 0.05]) == (0, 2)
+
+
+def test_decide_never_emits_a_token_without_residual_mass():
+    """After a rejection the replacement is drawn from the renormalised
+    residual max(p - q, 0), so a token whose residual is zero is never
+    emitted, even when fp32 rounding leaves the walk's sum below the draw.
+    Here the residual is [r0, r1, r2, 0, 0] whose normalised fp32 walk sums
+    to exactly 1 - 2^-24, the largest draw, so that draw runs off the end
+    and the last token with residual mass (2) is the answer; tokens 3
+    (p = 0) and 4 (the rejected proposal, p < q) have none."""
+    r = [14.628571510314941, 21.571428298950195, 27.14285659790039]
+    p = np.array([[r[0], r[1], r[2], 0.0, 1.0], [0.2] * 5], dtype=np.float32)
+    q = np.array([[0.0, 0.0, 0.0, 0.0, 2.0]], dtype=np.float32)
+    orders = np.array([list(range(5))] * 2)
+    top = float(np.float32(1.0) - np.float32(2.0 ** -24))
+    resid = np.maximum(p[0] - q[0], np.float32(0.0)).astype(np.float32)
+    total = np.float32(0.0)
+    for v in resid:
+        total = np.float32(total + v)
+    c = np.float32(0.0)
+    for v in (resid / total).astype(np.float32):
+        c = np.float32(c + v)
+    assert c == np.float32(top)  # the walk cannot pass the top draw
+    assert speculative_decide([4], q, p, orders, [0.9, top]) == (0, 2)
