@@ -756,6 +756,18 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     log(f"bench: copy probe {nbytes} bytes x 3")
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s, check=None):
     """The oracle (plain C, fp64, OpenMP) on a bounded sample of the step, at
     M = 16, on the same bytes the GPU gets: the LM head in full and whole
@@ -801,11 +813,14 @@ def cpu_baseline(target_s, check=None):
     oracle.gemv_rows(w0, g0.k, xs[g0.k], threads=1)
     t_one = time.perf_counter() - t_one
     t_step1 = t_step * t_one / t_all
+    wbytes = sum(g.weight_bytes for g in mats) + head["n"] * synthetic.q4k_bytes_per_row(head["k"])
     return {"value": round(16.0 / t_step, 4), "unit": "verify rows/s", "cores": threads, "kind": "oracle",
+            "cpu_model": host_cpu_model(), "weight_gb_s": round(wbytes / t_step / 1e9, 3),
             "step_s_extrapolated": round(t_step, 3), "sample_s": round(spent + t_all + t_one, 2),
             "sample": f"LM head in full + {len(layer_times)} of {synthetic.LAYERS} stack layers in full "
                       f"(M=16, same bytes as the GPU); step = {synthetic.LAYERS} x mean layer time + head",
-            "single_core": {"value": round(16.0 / t_step1, 5), "step_s_extrapolated": round(t_step1, 2),
+            "single_core": {"value": round(16.0 / t_step1, 5), "weight_gb_s": round(wbytes / t_step1 / 1e9, 4),
+                            "step_s_extrapolated": round(t_step1, 2),
                             "sample": f"one {g0.n} x {g0.k} matrix at 1 thread ({t_one:.2f} s) and at {threads} "
                                       f"({t_all:.3f} s); the step scaled by that ratio"}}
 

@@ -76,3 +76,8 @@ def test_step_algorithmic_bytes():
     x = sum(4 * m * g.k for g in phases)
     lg = sum(4 * m * g.n for g in mats)
     assert w + x + lg == 16_005_922_816
+
+
+def test_host_cpu_model_is_named():
+    name = bench.host_cpu_model()
+    assert isinstance(name, str) and name and "\n" not in name
