@@ -814,11 +814,30 @@ def cpu_baseline(target_s, check=None):
     t_one = time.perf_counter() - t_one
     t_step1 = t_step * t_one / t_all
     wbytes = sum(g.weight_bytes for g in mats) + head["n"] * synthetic.q4k_bytes_per_row(head["k"])
+    # the other configurations: the oracle's median of 3 runs each (generation
+    # outside the timed calls)
+    per_config = {}
+    t_configs = 0.0
+    for name, cfg, m, x in (("tiny", synthetic.TINY, 4, None), ("square_m16", synthetic.SQUARE, 16, None),
+                            ("fc_m16", synthetic.FC, 16, synthetic.fc_activations(16, synthetic.FC["seed"])),
+                            ("lm_head_m16", head, 16, None)):
+        w = synthetic.q4k_matrix(cfg["n"], cfg["k"], cfg["seed"])
+        x = synthetic.activations(m, cfg["k"], cfg["seed"]) if x is None else x
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.gemv_rows(w, cfg["k"], x, threads=threads)
+            times.append(time.perf_counter() - t0)
+        t = float(np.median(times))
+        t_configs += sum(times)
+        per_config[name] = {"ms": round(t * 1e3, 3), "rows_per_s": round(m / t, 2),
+                            "weight_gb_s": round(w.nbytes / t / 1e9, 3)}
     return {"value": round(16.0 / t_step, 4), "unit": "verify rows/s", "cores": threads, "kind": "oracle",
             "cpu_model": host_cpu_model(), "weight_gb_s": round(wbytes / t_step / 1e9, 3),
-            "step_s_extrapolated": round(t_step, 3), "sample_s": round(spent + t_all + t_one, 2),
+            "step_s_extrapolated": round(t_step, 3), "sample_s": round(spent + t_all + t_one + t_configs, 2),
             "sample": f"LM head in full + {len(layer_times)} of {synthetic.LAYERS} stack layers in full "
                       f"(M=16, same bytes as the GPU); step = {synthetic.LAYERS} x mean layer time + head",
+            "configs": per_config,
             "single_core": {"value": round(16.0 / t_step1, 5), "weight_gb_s": round(wbytes / t_step1 / 1e9, 4),
                             "step_s_extrapolated": round(t_step1, 2),
                             "sample": f"one {g0.n} x {g0.k} matrix at 1 thread ({t_one:.2f} s) and at {threads} "

@@ -23,6 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kq_oracle.c")
 _LIB = os.path.join(_HERE, "libkq_oracle.so")
 _lib = None
+_threads = 0  # OpenMP threads when the library was first loaded
 
 REL_TOL = 1e-4  # declared logit tolerance: |G - L| <= REL_TOL * sum_k |w_k x_k|
 
@@ -45,7 +46,7 @@ def build(force: bool = True) -> str:
 
 
 def _load():
-    global _lib
+    global _lib, _threads
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
@@ -86,6 +87,7 @@ def _load():
     lib.kqo_term_mass_q4k.restype = ctypes.c_int
     lib.kqo_num_threads.argtypes = []
     lib.kqo_num_threads.restype = ctypes.c_int
+    _threads = int(lib.kqo_num_threads())
     _lib = lib
     return lib
 
@@ -95,7 +97,11 @@ def _p(a: np.ndarray):
 
 
 def num_threads() -> int:
-    return int(_load().kqo_num_threads())
+    """Threads a call with threads=0 uses: the OpenMP default when the
+    library was first loaded (a call with an explicit count changes the
+    OpenMP setting for later calls; this count does not follow it)."""
+    _load()
+    return _threads
 
 
 def half_to_double(bits: int) -> float:
@@ -161,7 +167,7 @@ def gemv_rows(w: np.ndarray, k: int, x: np.ndarray, rows: Optional[Sequence[int]
     A = np.zeros((m, nout), dtype=np.float64)
     rc = _load().kqo_gemv_rows_fmt(code, _p(w), n, k, _p(x), m,
                                    _p(r_arr) if r_arr is not None else None, nout,
-                                   _p(L), _p(A), int(threads))
+                                   _p(L), _p(A), int(threads) if threads > 0 else num_threads())
     if rc == -3:
         raise ValueError("non-finite activation")
     if rc == -2:
