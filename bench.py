@@ -756,6 +756,14 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     log(f"bench: copy probe {nbytes} bytes x 3")
 
 
+def device_info(torch) -> dict:
+    """The GPU and software the numbers were measured on."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": torch.cuda.get_device_name(0), "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count, "memory_gib": round(pr.total_memory / 2 ** 30, 1),
+            "hip": torch.version.hip, "torch": torch.__version__}
+
+
 def host_cpu_model() -> str:
     """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
     try:
@@ -991,6 +999,7 @@ def main():
         "configs": cfgs,
         "rows_layout": rows_fig,
         "cpu_baseline": cpu,
+        "device": device_info(torch),
         "parity": parity,
     }
     print(json.dumps(rec), flush=True)
