@@ -295,6 +295,25 @@ def graph_time(torch, fn, calls, reps=5):
     return e0.elapsed_time(e1) * 1e3 / (reps * calls)
 
 
+def positive_control(stack, torch):
+    """The all-accept instrument check, reported apart from the results: the
+    LM-head verify at M = 16 with the draft set to the target's own argmax of
+    rows 0..14 must accept all 15 and emit row 15's argmax."""
+    kq, h = stack.kq, stack.head
+    sth = stack.staged[h.k]
+    kq.stage_rows(stack.x[h.k][:16], staged=sth)
+    am, _, _ = kq.verify_staged(stack.w_head, h.n, h.k, sth, 16, stack.draft[:15], stack.head_scratch,
+                                layout=stack.layout)
+    own = [int(v) for v in am.cpu().numpy()]
+    am2, acc2, _ = kq.verify_staged(stack.w_head, h.n, h.k, sth, 16, own[:15], stack.head_scratch,
+                                    layout=stack.layout)
+    got = [int(v) for v in acc2.cpu().numpy()]
+    ok = got == [15, own[15]] and [int(v) for v in am2.cpu().numpy()] == own
+    if not ok:
+        raise RuntimeError(f"positive control: accept {got}, expected [15, {own[15]}]")
+    return {"draft": "the target's own argmax of rows 0-14", "accepted": got[0], "next_token": got[1], "ok": ok}
+
+
 def draft_block_timing(stack, torch, calls=50):
     """The draft block's proposals (argmax of rows 1..15 of a 16-row block
     against the LM head, no accept), timed on the resident LM-head weights
@@ -945,8 +964,10 @@ def main():
                 + ", ".join(f"{k} {v['avg_launch_us']} us ({v['frac']})" for k, v in kr.items() if isinstance(v, dict)))
         else:
             log(f"bench: M={m} step {wall * 1e3:.3f} ms (events {ev * 1e3:.3f} ms), {gbs:.1f} GB/s")
-    draft = ceiling = cfgs = rows_fig = None
+    draft = ceiling = cfgs = rows_fig = control = None
     if not args.no_extras:
+        control = positive_control(stack, torch)
+        log("bench: positive control " + json.dumps(control))
         draft = draft_block_timing(stack, torch)
         ceiling = read_ceiling(stack, torch)
         rows_fig = rows_layout_timing(stack, torch, args.steps)
@@ -995,6 +1016,7 @@ def main():
         "m16_over_m1": round(res[16]["ms_per_step"] / res[1]["ms_per_step"], 4) if len(res) == 2 else None,
         "roofline": top.get("roofline"),
         "read_ceiling": ceiling,
+        "positive_control": control,
         "draft_block_argmax": draft,
         "configs": cfgs,
         "rows_layout": rows_fig,
