@@ -775,6 +775,20 @@ def copy_probe(torch, dev, nbytes=1 << 30):
     log(f"bench: copy probe {nbytes} bytes x 3")
 
 
+def launch_geometry_record(stack) -> dict:
+    """The geometry the timed launches actually used: the chain's persistent
+    workgroups, and the LM-head verify's waves, tiles per wave, workgroups
+    and units (one row group by one 256-column block)."""
+    kq, h = stack.kq, stack.head
+    waves, tpw, wgs, units = kq.launch_geometry(h.n, h.k)
+    rec = {"lm_head_verify": {"waves": waves, "tiles_per_wave": tpw, "rows_per_group": 16 * waves * tpw,
+                              "workgroups": wgs, "units": units}}
+    if stack.launch == "chain":
+        rec["stack_chain"] = {"workgroups": stack.chain(16).workgroups, "rows_per_group": 128,
+                              "phases": len(stack.groups)}
+    return rec
+
+
 def device_info(torch) -> dict:
     """The GPU and software the numbers were measured on."""
     pr = torch.cuda.get_device_properties(0)
@@ -1022,6 +1036,7 @@ def main():
         "rows_layout": rows_fig,
         "cpu_baseline": cpu,
         "device": device_info(torch),
+        "geometry": launch_geometry_record(stack),
         "parity": parity,
     }
     print(json.dumps(rec), flush=True)
