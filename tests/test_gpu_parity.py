@@ -436,3 +436,57 @@ def test_device_drafts_and_draft_block_to_verify_on_device(kq):
     a = am_b.cpu().numpy()
     assert tuple(acc_b.cpu().numpy()) == (15, int(a[15]))
     assert np.array_equal(a[1:16], props.cpu().numpy()) and int(a[0]) == int(head.cpu().numpy()[0])
+
+
+def test_degenerate_inputs(kq):
+    """The method's degenerate ends, Q4_K on both layouts and through the
+    verify:
+    * blocks at the ends of every field: fp16 d and dmin subnormal (down to
+      2^-24), tiny normal, or the largest finite value 65504; 6-bit scales
+      and mins 0 and 63; nibbles 0 and 15;
+    * all-zero activation rows among ordinary ones: every logit of such a
+      row is exactly zero, so its argmax is index 0 (all indices tie, the
+      lowest wins) and the row is flagged;
+    * an all-zero weight matrix: every logit zero, every argmax 0."""
+    from tests.q4k_pack import pack_block
+    g = np.random.default_rng(9)
+    n, k = 200, 1024
+    d_choices = [0x0001, 0x0003, 0x03FF, 0x0400, 0x1000, 0x2A00, 0x7BFF]  # 2^-24 ... 65504
+    rows = []
+    for r in range(n):
+        blocks = []
+        for b in range(k // 256):
+            d, dm = int(g.choice(d_choices)), int(g.choice(d_choices))
+            sc = g.choice([0, 63, 1, 62], 8)
+            mn = g.choice([0, 63, 1], 8)
+            q = g.choice([0, 15, 1, 14], 256)
+            blocks.append(pack_block(d, dm, sc, mn, q))
+        rows.append(b"".join(blocks))
+    w = np.frombuffer(b"".join(rows), dtype=np.uint8).reshape(n, -1).copy()
+    x = synthetic.activations(16, k, 91)
+    x[3] = 0.0
+    x[9] = 0.0
+    L, A = oracle.gemv_rows(w, k, x)
+    assert not np.any(L[3]) and not np.any(L[9])
+    w_d = to_dev(w)
+    G = gpu_logits(kq, w_d, n, k, x)
+    r = check_logits(G, L, A, what="degenerate fields")
+    log(f"degenerate fields: max |d|/tol = {r:.3g}")
+    assert not np.any(G[3]) and not np.any(G[9]), "an all-zero activation row gave a non-zero logit"
+    wt = kq.tile_weights(w_d, n, k)
+    sc_ = kq.new_scratch(n, k, DEV)
+    T = kq.gemv_staged(wt, n, k, kq.stage_rows(to_dev(x)), 16, sc_, layout=kq.LAYOUT_TILED16)
+    torch.cuda.synchronize()
+    assert np.array_equal(T.cpu().numpy(), G)
+    o_am, o_nc = oracle.argmax_flags(L, A)
+    d = synthetic.inject_mismatches(o_am[:15], n, seed=92)
+    g_am, g_acc, _ = gpu_verify(kq, w_d, n, k, x, d)
+    check_argmax(g_am, L, A, what="degenerate fields")
+    check_accept(g_acc[0], g_acc[1], d, g_am, o_am, o_nc, what="degenerate fields")
+    assert int(g_am[3]) == 0 and int(g_am[9]) == 0 and o_nc[3] == n - 1
+
+    z = np.zeros_like(w)
+    G0 = gpu_logits(kq, to_dev(z), n, k, x)
+    assert not np.any(G0), "an all-zero matrix gave a non-zero logit"
+    z_am, z_acc, _ = gpu_verify(kq, to_dev(z), n, k, x, [0] * 15)
+    assert not np.any(z_am) and (int(z_acc[0]), int(z_acc[1])) == (15, 0)
