@@ -120,21 +120,21 @@ const char *kq_status_string(kq_status s);
 
 /* Bytes of device workspace kq_gemv_rows / kq_verify_argmax_accept need for
  * an n x k matrix and m rows (0 for invalid shapes). The workspace holds the
- * staged activations, split-K partial sums and the control words. */
+ * staged activations, split-K partial sums and the control words; it grows
+ * with the number of 16-row slices of m (at m = 64 it is the staged bytes,
+ * rounded up to 256, plus kq_scratch_bytes(n, k)). */
 size_t kq_workspace_bytes(int64_t n, int64_t k, int m);
 
 /* Bytes of a staged activation block for k columns (any m <= 16). */
 size_t kq_staged_bytes(int64_t k);
 
 /* Bytes of a staged activation block for m <= 64 rows of k columns (0 for
- * invalid arguments): (k/256) * s * 16,960 with s = 1, 2 or 4 sixteen-row
- * slices for m <= 16, <= 32, <= 64. Calls of 17 to 32 rows (the token-tree
- * verify, kq_verify_tree_staged, or a longer linear verify) run every
- * weight tile against both slices in the same pass, so the weights are
- * still read once per call. Calls of 33 to 64 rows make two passes (rows
- * 0-31 at two slices, then the rest at one or two): a single pass at four
- * slices is bound by the activation reads from LDS and was 5-15 % slower on
- * MI355X at the LM head's size. */
+ * invalid arguments): (k/256) * s * 16,960 with s = ceil(m/16) sixteen-row
+ * slices (1 to 4). Q4_K calls of 17 to 64 rows (the token-tree verify,
+ * kq_verify_tree_staged, or a longer linear verify) run every weight tile
+ * against all s slices in the same pass, so the weights are still read
+ * once per call. Q5_K and Q6_K calls of 33 to 64 rows make two passes
+ * (rows 0-31 at two slices, then the rest at one or two). */
 size_t kq_staged_bytes_rows(int64_t k, int m);
 
 /* Bytes of device scratch the *_staged calls need for an n x k matrix (in
@@ -142,7 +142,9 @@ size_t kq_staged_bytes_rows(int64_t k, int m);
  * alone: every single-matrix call on n x k may share it (any format,
  * layout and m, ordered on one stream). A call on another shape, or a
  * grouped call, needs its own scratch, or this one zeroed again with
- * kq_workspace_init first. */
+ * kq_workspace_init first. The size covers calls of up to 64 rows; a call
+ * refuses (KQ_ERR_WORKSPACE) only a scratch smaller than its own m needs
+ * (its split-K partial sums grow with the 16-row slices of m). */
 size_t kq_scratch_bytes(int64_t n, int64_t k);
 
 /* Zero the control words of a workspace or scratch buffer of `bytes` bytes

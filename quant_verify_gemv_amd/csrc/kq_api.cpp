@@ -59,6 +59,10 @@ static Shape pick_shape(int64_t n, int count, int fmt, int ms) {
   // slices) so that it still fits a CU's LDS, with three weight register
   // sets and two tiles per wave (each activation read from LDS feeds 32
   // weight rows: 20 % faster than one tile on the LM head).
+  // Three or four slices (33 to 64 Q4_K rows, one pass): the ring holds
+  // two blocks of 3 or 4 slices (101,760 or 135,680 bytes), two weight
+  // register sets, two tiles per wave.
+  if (ms >= 3) return Shape{8, 2, 1, 1, 2};
   if (ms > 1) return Shape{8, 2, 1, 2, 3};
   // Q5_K and Q6_K (two more registers per tile and register set): two
   // tiles per wave from 131,072 rows (7-9 % faster than 12 one-tile waves on
@@ -95,21 +99,23 @@ Geometry geometry(int64_t n, int64_t k, int count, int fmt, int ms) {
 
 // One layout for every call on `count` matrices of n x k, whatever the
 // weight format and the launch's slice count: the arrival counters cover the
-// most row groups, the keys the most workgroups and the partials the largest
-// size of any of these geometries. The offsets then never depend on the
-// call, so a scratch shared by calls of different row counts or formats (or
-// by the two passes of one call) never has one launch's argmax keys or
-// partials where another expects its zeroed counters.
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count) {
+// most row groups and the keys the most workgroups of any of these
+// geometries, and the partials come last. The offsets then never depend on
+// the call, so a scratch shared by calls of different row counts or formats
+// (or by the two passes of one call) never has one launch's argmax keys or
+// partials where another expects its zeroed counters. The partials cover
+// the largest size of the launches of calls of up to max_ms slices (16
+// max_ms rows); a call of fewer rows needs only that much.
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int max_ms) {
   size_t groups = 0, wgs = 0, part = 0;
   for (int f = kFmtQ4; f <= kFmtQ6; ++f) {
     if (!shape_ok(n, k, f)) continue;
-    for (int ms = 1; ms <= 2; ++ms) {
+    for (int ms = 1; ms <= 4; ++ms) {
       const Geometry g = geometry(n, k, count, f, ms);
       const size_t pb = sizeof(float) * (size_t)g.n_wg * 2 * kMaxRows * ms * (size_t)g.rows;
       groups = (size_t)g.n_groups > groups ? (size_t)g.n_groups : groups;
       wgs = (size_t)g.n_wg > wgs ? (size_t)g.n_wg : wgs;
-      part = pb > part ? pb : part;
+      if (ms <= max_ms) part = pb > part ? pb : part;
     }
   }
   ScratchLayout s;
@@ -155,7 +161,9 @@ size_t kq_staged_bytes_rows(int64_t k, int m) {
 
 // Scratch for `count` matrices: the one layout of every format and slice
 // count.
-static size_t scratch_any_fmt(int64_t n, int64_t k, int count) { return scratch_layout(n, k, count).total; }
+static size_t scratch_any_fmt(int64_t n, int64_t k, int count) {
+  return scratch_layout(n, k, count, row_slices(kMaxTreeRows)).total;
+}
 
 size_t kq_scratch_bytes(int64_t n, int64_t k) {
   if (!shape_ok(n, k)) return 0;
@@ -169,7 +177,7 @@ size_t kq_group_scratch_bytes(int64_t n, int64_t k, int count) {
 
 size_t kq_workspace_bytes(int64_t n, int64_t k, int m) {
   if (!shape_ok(n, k) || !staged_ok(k, m)) return 0;
-  return align256(kq_staged_bytes_rows(k, m)) + kq_scratch_bytes(n, k);
+  return align256(kq_staged_bytes_rows(k, m)) + scratch_layout(n, k, 1, row_slices(m)).total;
 }
 
 kq_status kq_launch_geometry(int64_t n, int64_t k, int *waves, int *tiles_per_wave,
@@ -280,9 +288,9 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   // staged slices, and the slices of the launch (of each of the two
   // launches of a call of 33 to 64 rows)
   const int ms = row_slices(m);
-  const bool two_pass = ms == 4;
+  const bool two_pass = ms >= 3 && fmt != kFmtQ4;
   const int ms_a = two_pass ? 2 : ms, ms_b = two_pass ? row_slices(m - 32) : ms;
-  const ScratchLayout sl = scratch_layout(n, k, count);
+  const ScratchLayout sl = scratch_layout(n, k, count, ms);
   if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
   memset(&a, 0, sizeof(a));
@@ -332,13 +340,13 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
     b.row0 = row0;
     b.x_off = (unsigned)((row0 / 16) * kStageBytes);
   };
-  // 33 to 64 rows: two weight passes, rows 0-31 at two slices and the rest
-  // at one or two, rather than one pass at four slices. With four slices
-  // every weight byte costs 16 bytes of LDS activation reads per wave and
-  // the pass is bound by them: on MI355X two passes took 15 % (40 nodes),
-  // 13 % (48) and 5 % (64) less time on the 131,072-row LM head. The first
-  // pass writes the argmaxes of rows 0-31 (no decision); the second reads
-  // them back for the accept decision over all m rows.
+  // 33 to 64 rows: Q4_K runs one pass at three or four slices on two-tile
+  // waves (each activation read from LDS feeds 32 weight rows); on MI355X it
+  // took 6 % (40, 48 nodes) and 13 % (64) less time than two passes on the
+  // 131,072-row LM head. Q5_K and Q6_K records need more registers per
+  // tile, so they run two passes, rows 0-31 at two slices and the rest at
+  // one or two: the first pass writes the argmaxes of rows 0-31 (no
+  // decision); the second reads them back for the decision over all m rows.
   GemvLaunch first;
   if (two_pass) {
     first = a;

@@ -12,9 +12,10 @@ constexpr int64_t kQK = 256;          // weights per Q4_K super-block
 constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // activation rows per MFMA slice (block size of the draft)
 constexpr int kMaxTreeRows = 64;      // activation rows per call: up to 4 slices (token-tree verify)
-// 16-row slices staged for m activation rows: 1, 2 or 4 (a launch runs one
-// or two of them; 33 to 64 rows take two launches)
-constexpr int row_slices(int m) { return m <= 16 ? 1 : m <= 32 ? 2 : 4; }
+// 16-row slices staged for m activation rows: one per 16 rows or part of
+// them (1 to 4); a Q4_K launch runs all of them in one pass over the
+// weights, Q5_K and Q6_K calls of more than 32 rows run two passes
+constexpr int row_slices(int m) { return (m + 15) / 16; }
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
 // Rows per row group of a chain launch (kq_chain_kernel's compute waves times
 // 16-row tiles)
@@ -93,7 +94,7 @@ struct Geometry {
   int tpw;        // 16-row tiles per wave (1 or 2)
   int bi;         // units between workgroup barriers (1, 2 or 4; LDS ring of 2 bi blocks)
   int depth;      // weight register sets (prefetch depth + 1: 4 or 8)
-  int ms;         // 16-row activation slices of the launch (1 or 2)
+  int ms;         // 16-row activation slices of the launch (1 to 4)
   int rows;       // rows per row group = 16 * waves * tpw
   int n_wg_per;   // row groups per matrix
   int n_groups;   // row groups in total = count * n_wg_per
@@ -163,7 +164,7 @@ struct GemvLaunch {
 
 Geometry geometry(int64_t n, int64_t k, int count, int fmt = kFmtQ4, int ms = 1);
 // the one scratch layout of every call on `count` matrices of n x k
-ScratchLayout scratch_layout(int64_t n, int64_t k, int count);
+ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int max_ms);
 
 // Kernel launches (return a hipError_t as int).
 // kq_stage_kernel also zeroes the control words of `ctrl` (a scratch area

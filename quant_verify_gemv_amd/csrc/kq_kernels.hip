@@ -378,8 +378,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   static_assert(!ROWS || FMT == kFmtQ4, "only Q4_K has a row-layout path");
   // MS 16-row activation slices: every unpacked weight operand feeds the
   // MFMAs of all MS slices, so the weights are read once for 16 MS rows
-  // (33 to 64 rows: two launches, rows 0-31 and the rest)
-  static_assert(MS == 1 || MS == 2, "one or two slices per launch");
+  static_assert(MS >= 1 && MS <= 4, "one to four slices per launch");
   constexpr int kRS = 16 * MS;  // activation rows per call at most
   constexpr unsigned kTB = 16u * (unsigned)fmt_block_bytes(FMT);  // tiled record bytes
   // D weight register sets: the weights of unit i + D - 1 are loaded while
@@ -390,7 +389,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // workgroups stage twice the activation chunks per thread and keep one
   // set in flight. The unit loop is unrolled kU = lcm(D, BI, kXL + 1) times
   // so that every register set index and every interval position is static.
-  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : 1;
+  // (three or four slices: the activations of unit i + 1 are loaded at the
+  // start of step i and stored at its end, kXL = 0, which keeps the
+  // two-tile waves within their 256 registers)
+  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : MS >= 3 ? 0 : 1;
   constexpr int kU = lcm_int(lcm_int(D, BI), kXL + 1);
   constexpr int kNth = 64 * W;
   constexpr int kRows = 16 * T * W;
@@ -987,10 +989,16 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
           const bool ok = m < M && row < nrows;
           if (ok && logits) put(&logits[(int64_t)m * N + n], v[j][r]);
           if (a.verify) {
-            // max over the wave's 64 / kCR rows: the lanes with the same c % kCR
             unsigned long long best = ok ? argmax_key(v[j][r], (unsigned)n) : 0ull;
-            best = lanes_max(best, 64, kCR);
-            if (lane < kCR && m < M) atomicMax(&s_keys[m], best);
+            if constexpr ((kCR & (kCR - 1)) == 0) {
+              // max over the wave's 64 / kCR rows: the lanes with the same c % kCR
+              best = lanes_max(best, 64, kCR);
+              if (lane < kCR && m < M) atomicMax(&s_keys[m], best);
+            } else {
+              // three slices (12 chunks a row): lanes of one activation row
+              // are not an xor group, so every lane goes to LDS on its own
+              if (ok) atomicMax(&s_keys[m], best);
+            }
           }
         }
       }
@@ -2184,6 +2192,8 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(kFmtQ4, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ5, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ6, 8, 2, 2, 3, 2)
+    KQ_CASE(kFmtQ4, 8, 2, 1, 2, 3)
+    KQ_CASE(kFmtQ4, 8, 2, 1, 2, 4)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;
   }

@@ -108,7 +108,13 @@ static void products() {
                                   nullptr) == KQ_OK);
     }
   EXPECT(kq_gemv_staged(w, 4, n, k, staged, 4, logits, scratch, scb, nullptr) == KQ_ERR_SHAPE);
-  EXPECT(kq_gemv_staged(w, KQ_LAYOUT_ROWS, n, k, staged, 4, logits, scratch, scb - 256, nullptr) ==
+  EXPECT(kq_gemv_staged(w, KQ_LAYOUT_ROWS, n, k, staged, 64, logits, scratch, scb - 256, nullptr) ==
+         KQ_ERR_WORKSPACE);
+  // a call of at most 16 rows needs only the one-slice part of the scratch
+  const size_t sc1 = wsb - (kq_staged_bytes_rows(k, 16) + 255) / 256 * 256;
+  EXPECT(sc1 < scb);
+  EXPECT(kq_gemv_staged(w, KQ_LAYOUT_ROWS, n, k, staged, 4, logits, scratch, sc1, nullptr) == KQ_OK);
+  EXPECT(kq_gemv_staged(w, KQ_LAYOUT_ROWS, n, k, staged, 4, logits, scratch, sc1 - 256, nullptr) ==
          KQ_ERR_WORKSPACE);
   for (int vl = 0; vl <= 16; ++vl) {
     const bool ok = vl == 3 || vl == 7 || vl == 15;
@@ -154,7 +160,7 @@ static void products() {
                                               gb ? gb : scb, nullptr);
     EXPECT(st == (c >= 1 && c <= KQ_MAX_GROUP ? KQ_OK : KQ_ERR_SHAPE));
   }
-  EXPECT(kq::g_stub.gemv > g0 + 400);
+  EXPECT(kq::g_stub.gemv > g0 + 300);
 
   // softmax rows, gather, stream probe, workspace init
   const size_t smb = kq_softmax_workspace_bytes(16, 131072);

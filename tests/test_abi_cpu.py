@@ -54,10 +54,13 @@ def test_sizes_and_geometry():
     assert kq.workspace_bytes(0, 1024, 1) == 0
     assert kq.staged_bytes(1024) == 4 * 16960
     assert kq.staged_bytes(6656) == 26 * 16960
-    # more than 16 rows: 2 or 4 sixteen-row slices per block
-    assert [kq.staged_bytes(1024, m) for m in (1, 16, 17, 32, 33, 64)] == [4 * 16960 * s for s in (1, 1, 2, 2, 4, 4)]
+    # more than 16 rows: one sixteen-row slice per 16 rows or part of them
+    assert [kq.staged_bytes(1024, m) for m in (1, 16, 17, 32, 33, 48, 49, 64)] == \
+        [4 * 16960 * s for s in (1, 1, 2, 2, 3, 3, 4, 4)]
     assert kq.staged_bytes(1024, 65) == 0 and kq.staged_bytes(1024, 0) == 0
-    assert kq.workspace_bytes(512, 1024, 64) - kq.workspace_bytes(512, 1024, 16) == 3 * 4 * 16960
+    # the workspace grows with the slices of m: staged bytes and split-K partials
+    ws = [kq.workspace_bytes(512, 1024, m) for m in (16, 32, 48, 64)]
+    assert all(b - a >= 4 * 16960 for a, b in zip(ws, ws[1:]))
     for n, k in [(512, 1024), (6656, 6656), (6656, 33280), (131072, 6656), (17920, 6656), (6656, 17920), (1, 256),
                  (35840, 6656)]:
         assert kq.workspace_bytes(n, k, 1) == kq.workspace_bytes(n, k, 16) > 0
@@ -66,7 +69,8 @@ def test_sizes_and_geometry():
         assert waves in (4, 8, 12) and tpw in (1, 2)
         assert units == -(-n // (16 * waves * tpw)) * (k // 256)
         assert 1 <= nwg <= min(units, 768)
-        assert kq.scratch_bytes(n, k) <= kq.workspace_bytes(n, k, 16)
+        a256 = -(-kq.staged_bytes(k, 64) // 256) * 256
+        assert kq.workspace_bytes(n, k, 64) == a256 + kq.scratch_bytes(n, k)
     with pytest.raises(kq.KQError):
         kq.launch_geometry(16, 100)
 

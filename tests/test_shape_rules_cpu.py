@@ -2,7 +2,7 @@
 random shapes drawn around every limit: k a positive multiple of 256 up to
 2^28; 1 <= n < 2^31; 1 <= m <= 64; the weight matrix (rows rounded up to
 16) and the staged activations each below 4 GiB; staged blocks of 16,960
-bytes per 16-row slice (1, 2 or 4 slices for m <= 16, 32, 64); tiled copies
+bytes per 16-row slice (ceil(m/16) slices: 1 to 4); tiled copies
 of ceil(n/16) * (k/256) * 16 * block bytes; launch units of one row group by
 one 256-column block. CPU only: the queries make no device call."""
 import numpy as np
@@ -16,7 +16,7 @@ BLOCK = {"q4k": 144, "q5k": 176, "q6k": 210}
 
 
 def slices(m):
-    return 1 if m <= 16 else 2 if m <= 32 else 4
+    return -(-m // 16)
 
 
 def k_ok(k):
