@@ -342,7 +342,7 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   };
   // 33 to 64 rows: Q4_K runs one pass at three or four slices on two-tile
   // waves (each activation read from LDS feeds 32 weight rows); on MI355X it
-  // took 6 % (40, 48 nodes) and 13 % (64) less time than two passes on the
+  // took 18 % (40, 48 nodes) and 12 % (64) less time than two passes on the
   // 131,072-row LM head. Q5_K and Q6_K records need more registers per
   // tile, so they run two passes, rows 0-31 at two slices and the rest at
   // one or two: the first pass writes the argmaxes of rows 0-31 (no
