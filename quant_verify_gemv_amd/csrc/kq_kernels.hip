@@ -389,10 +389,14 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
   // workgroups stage twice the activation chunks per thread and keep one
   // set in flight. The unit loop is unrolled kU = lcm(D, BI, kXL + 1) times
   // so that every register set index and every interval position is static.
-  // (three or four slices: the activations of unit i + 1 are loaded at the
-  // start of step i and stored at its end, kXL = 0, which keeps the
-  // two-tile waves within their 256 registers)
-  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : MS >= 3 ? 0 : 1;
+  // Three or four slices: the activations of unit i + 1 are copied into LDS
+  // by direct-to-LDS buffer loads issued in step i (kDma, no register
+  // staging, so the two-tile waves stay within their 256 registers); the
+  // workgroup barrier that ends step i waits for them. The ring's two
+  // halves are indexed statically, so the compiler sees that a copy into
+  // one half never aliases the reads of the other.
+  constexpr bool kDma = MS >= 3;
+  constexpr int kXL = (W >= 8 && T == 1 && MS == 1) ? 3 : kDma ? 0 : 1;
   constexpr int kU = lcm_int(lcm_int(D, BI), kXL + 1);
   constexpr int kNth = 64 * W;
   constexpr int kRows = 16 * T * W;
@@ -593,6 +597,25 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       for (int j = 0; j < kXj; ++j)
         if (j < kXj - 1 || tid + kNth * j < kXc) *(u32x4 *)(&s_x[buf][(tid + kNth * j) * 16]) = x.a[j];
     };
+    // buffer_load_dwordx4 ... lds: every lane's 16 bytes go straight to LDS at
+    // the wave's base + 16 x lane, so instruction j of wave w copies chunks
+    // kNth j + 64 w .. + 63 of the record (one contiguous KiB); lanes past
+    // the record's end issue nothing. `buf` must be a compile-time constant.
+    auto dma_x = [&](const int buf) {
+      const unsigned src = (unsigned)bx * x_rec + x_off;
+#pragma unroll
+      for (int j = 0; j < kXj; ++j) {
+        const int cb = kNth * j + 64 * wave_u;
+        if (cb < kXc && cb + lane < kXc)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              x_rsrc, (__attribute__((address_space(3))) void *)(&s_x[buf][cb * 16]), 16,
+              (unsigned)(cb + lane) * 16u, src, 0, 0);
+      }
+      if (ux < u_last) {
+        ++ux;
+        if (++bx == KB) bx = 0;
+      }
+    };
 
     auto write_rows = [&](int g, const f32x4(&v)[T][MS]) {
       int mat;
@@ -642,7 +665,12 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     // of units 0..BI-1 (to buffers 0..BI-1 before the first barrier), the
     // weights of units 1..D-2, then the activations of units BI..BI+kXL-1,
     // which stay in registers (set u % (kXL + 1)).
-    {
+    if constexpr (kDma) {
+      static_assert(BI == 1 && kXL == 0 && D == 2, "direct-to-LDS ring: one unit per barrier, two register sets");
+      load_w(wr[0]);
+      dma_x(0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): unit 0's activations are in LDS
+    } else {
       XRegs xp[BI];
       load_w(wr[0]);
 #pragma unroll
@@ -686,10 +714,16 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
         __builtin_amdgcn_s_setprio(1);
       else
         __builtin_amdgcn_s_setprio(0);
-      load_x(xl);
-      load_w(pf);
+      static_assert(!kDma || kU % kNB == 0, "ring half of a step fixed by its place in the unrolled loop");
+      if constexpr (kDma) {
+        load_w(pf);
+        dma_x((pos + BI) % kNB);
+      } else {
+        load_x(xl);
+        load_w(pf);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      const uint8_t *xb = s_x[i % kNB];
+      const uint8_t *xb = s_x[kDma ? pos % kNB : i % kNB];
       if (i < nu) {
         if constexpr (FMT == kFmtQ6) {
           // Q6_K: w = d sc (q - 32), sc a signed 8-bit scale per 16 columns.
@@ -895,7 +929,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
         bc = 0;
         ++gc;
       }
-      store_x((int)((i + BI) % kNB), xs);
+      if constexpr (kDma) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): unit i + 1's activations are in LDS
+      } else {
+        store_x((int)((i + BI) % kNB), xs);
+      }
       if (pos % BI == BI - 1) __syncthreads();
     };
 
