@@ -130,11 +130,10 @@ size_t kq_staged_bytes(int64_t k);
 
 /* Bytes of a staged activation block for m <= 64 rows of k columns (0 for
  * invalid arguments): (k/256) * s * 16,960 with s = ceil(m/16) sixteen-row
- * slices (1 to 4). Q4_K calls of 17 to 64 rows (the token-tree verify,
+ * slices (1 to 4). Calls of 17 to 64 rows (the token-tree verify,
  * kq_verify_tree_staged, or a longer linear verify) run every weight tile
- * against all s slices in the same pass, so the weights are still read
- * once per call. Q5_K and Q6_K calls of 33 to 64 rows make two passes
- * (rows 0-31 at two slices, then the rest at one or two). */
+ * against all s slices in the same pass, in every format, so the weights
+ * are still read once per call. */
 size_t kq_staged_bytes_rows(int64_t k, int m);
 
 /* Bytes of device scratch the *_staged calls need for an n x k matrix (in

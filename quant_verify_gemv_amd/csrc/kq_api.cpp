@@ -54,14 +54,13 @@ static Shape pick_shape(int64_t n, int count, int fmt, int ms) {
   return {KQ_GEOM_WAVES, KQ_GEOM_TPW, KQ_GEOM_PER_CU, KQ_GEOM_BI, KQ_GEOM_DEPTH};
 #endif
   const int64_t rows = n * count;
-  // Two activation slices (17 to 32 rows, or one pass of a larger call):
-  // the LDS ring shrinks to 4 blocks (every block now holds 2 staged
-  // slices) so that it still fits a CU's LDS, with three weight register
-  // sets and two tiles per wave (each activation read from LDS feeds 32
-  // weight rows: 20 % faster than one tile on the LM head).
-  // Three or four slices (33 to 64 Q4_K rows, one pass): the ring holds
-  // two blocks of 3 or 4 slices (101,760 or 135,680 bytes), two weight
-  // register sets, two tiles per wave.
+  // Two activation slices (17 to 32 rows): the LDS ring shrinks to 4
+  // blocks (every block now holds 2 staged slices) so that it still fits a
+  // CU's LDS, with three weight register sets and two tiles per wave (each
+  // activation read from LDS feeds 32 weight rows: 20 % faster than one
+  // tile on the LM head). Three or four slices (33 to 64 rows): the ring
+  // holds two blocks of 3 or 4 slices (101,760 or 135,680 bytes), two
+  // weight register sets, two tiles per wave; every format.
   if (ms >= 3) return Shape{8, 2, 1, 1, 2};
   if (ms > 1) return Shape{8, 2, 1, 2, 3};
   // Q5_K and Q6_K (two more registers per tile and register set): two
@@ -102,8 +101,8 @@ Geometry geometry(int64_t n, int64_t k, int count, int fmt, int ms) {
 // most row groups and the keys the most workgroups of any of these
 // geometries, and the partials come last. The offsets then never depend on
 // the call, so a scratch shared by calls of different row counts or formats
-// (or by the two passes of one call) never has one launch's argmax keys or
-// partials where another expects its zeroed counters. The partials cover
+// never has one launch's argmax keys or partials where another expects its
+// zeroed counters. The partials cover
 // the largest size of the launches of calls of up to max_ms slices (16
 // max_ms rows); a call of fewer rows needs only that much.
 ScratchLayout scratch_layout(int64_t n, int64_t k, int count, int max_ms) {
@@ -285,11 +284,8 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
     if (!al(w[i], 16)) return KQ_ERR_ALIGN;
   if (!al(staged, 256) || !al(scratch, 256)) return KQ_ERR_ALIGN;
   if (x_to_stage && !al(x_to_stage, 16)) return KQ_ERR_ALIGN;
-  // staged slices, and the slices of the launch (of each of the two
-  // launches of a call of 33 to 64 rows)
+  // staged slices: the launch runs all of them in one pass over the weights
   const int ms = row_slices(m);
-  const bool two_pass = ms >= 3 && fmt != kFmtQ4;
-  const int ms_a = two_pass ? 2 : ms, ms_b = two_pass ? row_slices(m - 32) : ms;
   const ScratchLayout sl = scratch_layout(n, k, count, ms);
   if (scratch_bytes < sl.total) return KQ_ERR_WORKSPACE;
   GemvLaunch a;
@@ -324,63 +320,37 @@ static kq_status run(const void *const *w, int layout, int count, int64_t n, int
   a.k_draft = verify && accept_out && !tree_parent ? m - 1 : 0;
   a.verify = verify ? 1 : 0;
   a.x_rec = (unsigned)(ms * kStageBytes);
-  // The rows [row0, row0 + rows) of the call, at `pms` slices from staged
-  // slice row0 / 16 on.
   uint8_t *sc = (uint8_t *)scratch;
-  auto part = [&](GemvLaunch &b, int row0, int rows, int pms) {
-    b.g = geometry(n, k, count, fmt, pms);
-    float *lg[kMaxGroup] = {};
-    for (int i = 0; i < count; ++i) lg[i] = logits && logits[i] ? logits[i] + (int64_t)row0 * n : nullptr;
-    fill_phase(b.ph, b.g, w, lg, count, n, k, staged);
-    b.done = (unsigned *)sc;
-    b.group_cnt = (unsigned *)(sc + sl.cnt_off);
-    b.wg_keys = (unsigned long long *)(sc + sl.keys_off);
-    b.partials = (float *)(sc + sl.part_off);
-    b.m = rows;
-    b.row0 = row0;
-    b.x_off = (unsigned)((row0 / 16) * kStageBytes);
-  };
-  // 33 to 64 rows: Q4_K runs one pass at three or four slices on two-tile
-  // waves (each activation read from LDS feeds 32 weight rows); on MI355X it
-  // took 18 % (40, 48 nodes) and 12 % (64) less time than two passes on the
-  // 131,072-row LM head. Q5_K and Q6_K records need more registers per
-  // tile, so they run two passes, rows 0-31 at two slices and the rest at
-  // one or two: the first pass writes the argmaxes of rows 0-31 (no
-  // decision); the second reads them back for the decision over all m rows.
-  GemvLaunch first;
-  if (two_pass) {
-    first = a;
-    part(first, 0, 32, ms_a);
-    first.accept_out = nullptr;
-    first.tree = 0;
-    first.path_out = nullptr;
-    first.k_draft = 0;
-    part(a, 32, m - 32, ms_b);
-    a.am_prev = argmax;
-    a.argmax_out = argmax ? argmax + 32 : nullptr;
-    a.head_out = nullptr;
-  } else {
-    part(a, 0, m, ms);
-    // Plain Q4_K products of the 128-row geometry (at most 16 rows) run on
-    // the chain kernel's specialised waves as a one-phase launch (its own
-    // last-arrival reduction, so no co-residency is needed): same units and
-    // summation orders, so the results are bitwise those of kq_gemv_kernel;
-    // measured 2-3 % faster on the 33,280 -> 6,656 fc and about 5 % on
-    // 6,656 x 6,656 (MI355X, interleaved graphs of back-to-back calls).
-    if (!verify && fmt == kFmtQ4 && ms == 1 && a.g.waves * a.g.tpw * 16 == kChainRows) {
-      a.chain_single = 1;
-      a.bar = (unsigned *)(sc + kBarOff);
-      a.err = (unsigned *)(sc + kErrOff);
-      a.epoch = (unsigned *)(sc + kEpochOff);
-    }
+  a.g = geometry(n, k, count, fmt, ms);
+  fill_phase(a.ph, a.g, w, logits, count, n, k, staged);
+  a.done = (unsigned *)sc;
+  a.group_cnt = (unsigned *)(sc + sl.cnt_off);
+  a.wg_keys = (unsigned long long *)(sc + sl.keys_off);
+  a.partials = (float *)(sc + sl.part_off);
+  a.m = m;
+  // 17 to 64 rows: one pass over the weights at two to four slices, on
+  // two-tile waves (each activation read from LDS feeds 32 weight rows). At
+  // 33 to 64 rows it took 18-25 % less time than two passes (rows 0-31,
+  // then the rest) on the 131,072-row LM head (40 to 64 tree nodes; Q4_K,
+  // Q5_K and Q6_K, MI355X, interleaved).
+  //
+  // Plain Q4_K products of the 128-row geometry (at most 16 rows) run on
+  // the chain kernel's specialised waves as a one-phase launch (its own
+  // last-arrival reduction, so no co-residency is needed): same units and
+  // summation orders, so the results are bitwise those of kq_gemv_kernel;
+  // measured 2-3 % faster on the 33,280 -> 6,656 fc and about 5 % on
+  // 6,656 x 6,656 (MI355X, interleaved graphs of back-to-back calls).
+  if (!verify && fmt == kFmtQ4 && ms == 1 && a.g.waves * a.g.tpw * 16 == kChainRows) {
+    a.chain_single = 1;
+    a.bar = (unsigned *)(sc + kBarOff);
+    a.err = (unsigned *)(sc + kErrOff);
+    a.epoch = (unsigned *)(sc + kEpochOff);
   }
   if (dry) return KQ_OK;  // every check passed; nothing enqueued
   if (x_to_stage) {
-    const int64_t groups = two_pass && first.g.n_groups > a.g.n_groups ? first.g.n_groups : a.g.n_groups;
-    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, groups, stream))
+    if (launch_stage(x_to_stage, m, k, (uint8_t *)staged, (unsigned *)scratch, a.g.n_groups, stream))
       return KQ_ERR_LAUNCH;
   }
-  if (two_pass && launch_gemv(first, stream)) return KQ_ERR_LAUNCH;
   if (launch_gemv(a, stream)) return KQ_ERR_LAUNCH;
   return KQ_OK;
 }

@@ -13,8 +13,7 @@ constexpr int64_t kBlockBytes = 144;  // bytes per super-block
 constexpr int kMaxRows = 16;          // activation rows per MFMA slice (block size of the draft)
 constexpr int kMaxTreeRows = 64;      // activation rows per call: up to 4 slices (token-tree verify)
 // 16-row slices staged for m activation rows: one per 16 rows or part of
-// them (1 to 4); a Q4_K launch runs all of them in one pass over the
-// weights, Q5_K and Q6_K calls of more than 32 rows run two passes
+// them (1 to 4); a launch runs all of them in one pass over the weights
 constexpr int row_slices(int m) { return (m + 15) / 16; }
 constexpr int kMaxGroup = 8;          // matrices per grouped launch
 // Rows per row group of a chain launch (kq_chain_kernel's compute waves times
@@ -146,15 +145,9 @@ struct GemvLaunch {
   int tree;                      // 1: tree accept over m nodes
   int32_t *path_out;             // tree, may be null: the accepted path's nodes
   int verify;
-  // Staged activations of a single launch: block b's first slice of this
-  // launch at b * x_rec + x_off (x_rec = the staged slices per block times
-  // kStageBytes). A launch that takes slices past the first (the second pass
-  // of a two-pass tree) covers rows row0 .. row0 + m - 1 of the call; the
-  // argmaxes of rows 0 .. row0 - 1 are read from am_prev (device memory,
-  // written by the earlier pass) for the accept decision.
-  unsigned x_rec, x_off;
-  int row0;
-  const int32_t *am_prev;
+  // Staged activations of a single launch: block b's record at b * x_rec
+  // (x_rec = the staged slices per block times kStageBytes).
+  unsigned x_rec;
   // single launches (no chain table): 1 runs the launch's one phase on
   // kq_chain_kernel (plain Q4_K products of the 128-row geometry, m <= 16),
   // with kq_gemv_kernel's last-arrival reduction of split row groups

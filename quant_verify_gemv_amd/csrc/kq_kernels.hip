@@ -581,9 +581,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     int bx = u0 % KB;
     const __amdgpu_buffer_rsrc_t x_rsrc = dev_rsrc(KQ_PH(ph, staged));
     const unsigned x_rec = a.x_rec;
-    const unsigned x_off = a.x_off;
     auto load_x = [&](XRegs &x) {
-      const unsigned src = (unsigned)bx * x_rec + x_off;
+      const unsigned src = (unsigned)bx * x_rec;
 #pragma unroll
       for (int j = 0; j < kXj; ++j)
         x.a[j] = buf_ld16(x_rsrc, (unsigned)(j < kXj - 1 ? tid + kNth * j : xlast) * 16u, src);
@@ -602,7 +601,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
     // kNth j + 64 w .. + 63 of the record (one contiguous KiB); lanes past
     // the record's end issue nothing. `buf` must be a compile-time constant.
     auto dma_x = [&](const int buf) {
-      const unsigned src = (unsigned)bx * x_rec + x_off;
+      const unsigned src = (unsigned)bx * x_rec;
 #pragma unroll
       for (int j = 0; j < kXj; ++j) {
         const int cb = kNth * j + 64 * wave_u;
@@ -1125,14 +1124,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? (T == 1 ? 3 : 2) : 1) void kq_gemv
       }
     }
     __syncthreads();
-    // rows of this launch at row0 + tid; an earlier pass's rows from am_prev
-    const int R0 = a.row0, MT = R0 + M;
+    const int MT = M;
     if (tid < M) {
       const int am = (int)(0xFFFFFFFFu - (unsigned)(s_keys[tid] & 0xFFFFFFFFull));
-      s_am[R0 + tid] = am;
+      s_am[tid] = am;
       if (tid >= a.argmax_from) a.argmax_out[tid - a.argmax_from] = am;
-    } else if (tid - M < R0) {
-      s_am[tid - M] = a.am_prev[tid - M];
     }
     __syncthreads();
     if (a.accept_out && a.tree) {
@@ -2189,7 +2185,7 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     const dim3 block(64 * (kCwW + kCwP));
     if (a.chain_single) {
       // one phase, m <= 16, plain products of Q4_K weights
-      if (a.verify || a.g.ms != 1 || a.x_rec != (unsigned)kStageBytes || a.x_off != 0u ||
+      if (a.verify || a.g.ms != 1 || a.x_rec != (unsigned)kStageBytes ||
           layout_fmt(a.layout) != kFmtQ4)
         return (int)hipErrorInvalidConfiguration;
       if (a.layout == KQ_LAYOUT_ROWS)
@@ -2232,6 +2228,10 @@ int launch_gemv(const GemvLaunch &a, void *stream) {
     KQ_CASE(kFmtQ6, 8, 2, 2, 3, 2)
     KQ_CASE(kFmtQ4, 8, 2, 1, 2, 3)
     KQ_CASE(kFmtQ4, 8, 2, 1, 2, 4)
+    KQ_CASE(kFmtQ5, 8, 2, 1, 2, 3)
+    KQ_CASE(kFmtQ5, 8, 2, 1, 2, 4)
+    KQ_CASE(kFmtQ6, 8, 2, 1, 2, 3)
+    KQ_CASE(kFmtQ6, 8, 2, 1, 2, 4)
 #undef KQ_CASE
     default: return (int)hipErrorInvalidConfiguration;
   }

@@ -4,7 +4,7 @@ Row counts are drawn log-uniform from 1 to 150,000, depths from one block up
 to a bounded matrix size, activation rows from 1 to 64 and the format from
 Q4_K, Q5_K and Q6_K. That mixes launches with fewer units than workgroups,
 row groups split over one to many workgroups, ragged last tiles, every row
-geometry and the one- and two-pass paths for more than 16 rows, in
+geometry and one to four activation slices per pass, in
 combinations no hand-picked shape list covers. Each case checks every logit
 of the staged product, the row-major calls bitwise against the tiled one,
 the verify's argmax (with flags) and accept, and for more than 16 rows a
