@@ -217,16 +217,26 @@ def alloc_workspace(nbytes: int, device):
 
 
 class Workspace:
-    """Device workspace cache keyed by device (grows as needed)."""
+    """Default device workspaces, one per device and stream (grows as
+    needed). Calls on different streams get different buffers, so calls that
+    leave `workspace` out may overlap on two streams; calls on one stream are
+    ordered and share its buffer. Each buffer is recorded as used by its
+    stream, so the allocator does not hand a replaced buffer's memory to
+    other work before that stream's pending calls are done, and the stream
+    waits for the new buffer's zero fill."""
 
     def __init__(self):
         self._bufs = {}
 
-    def get(self, nbytes: int, device):
-        key = str(device)
+    def get(self, nbytes: int, device, stream=None):
+        torch = _torch()
+        s = torch.cuda.current_stream(device) if stream is None else stream
+        key = (str(device), int(s.cuda_stream))
         b = self._bufs.get(key)
         if b is None or b.numel() < nbytes:
-            b = alloc_workspace(nbytes, device)
+            b = alloc_workspace(nbytes, device)  # zero-filled on the current stream
+            s.wait_stream(torch.cuda.current_stream(device))
+            b.record_stream(s)
             self._bufs[key] = b
         return b
 
@@ -244,7 +254,7 @@ def gemv_rows(w, n: int, k: int, x, logits=None, workspace=None, stream=None):
     if logits is None:
         logits = torch.empty((m, n), dtype=torch.float32, device=x.device)
     need = workspace_bytes(n, k, m)
-    ws = workspace if workspace is not None else _WS.get(need, x.device)
+    ws = workspace if workspace is not None else _WS.get(need, x.device, stream)
     _check(load().kq_gemv_rows(_dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(x, "x", torch.float32), m,
                                _dev_ptr(logits, "logits", torch.float32), _dev_ptr(ws, "workspace"),
                                ws.numel(), _stream_handle(stream)), "kq_gemv_rows")
@@ -267,7 +277,7 @@ def verify(w, n: int, k: int, x, draft: Sequence[int], want_logits: bool = False
     else:
         am, acc, lg = out
     need = workspace_bytes(n, k, m)
-    ws = workspace if workspace is not None else _WS.get(need, x.device)
+    ws = workspace if workspace is not None else _WS.get(need, x.device, stream)
     _check(load().kq_verify_argmax_accept(
         _dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(x, "x", torch.float32), m, dr,
         _dev_ptr(am, "argmax", torch.int32), _dev_ptr(acc, "accept", torch.int32),
@@ -308,7 +318,7 @@ def draft_block_argmax(w, n: int, k: int, x, verify_length: int, want_head: bool
     else:
         props, head = out
     need = workspace_bytes(n, k, verify_length + 1)
-    ws = workspace if workspace is not None else _WS.get(need, x.device)
+    ws = workspace if workspace is not None else _WS.get(need, x.device, stream)
     _check(load().kq_draft_block_argmax(
         _dev_ptr(w, "w", torch.uint8), n, k, _dev_ptr(x, "x", torch.float32), verify_length,
         _dev_ptr(props, "proposals", torch.int32), _dev_ptr(head, "head", torch.int32) if head is not None else None,
@@ -544,7 +554,7 @@ def softmax_rows(logits, temperature: float = 1.0, soft_cap: float = 0.0, probs=
     if probs is None:
         probs = torch.empty_like(logits)
     need = softmax_workspace_bytes(m, n)
-    ws = workspace if workspace is not None else _WS.get(max(need, 256), logits.device)
+    ws = workspace if workspace is not None else _WS.get(max(need, 256), logits.device, stream)
     _check(load().kq_softmax_rows(_dev_ptr(logits, "logits", torch.float32), m, n, float(temperature),
                                   float(soft_cap), _dev_ptr(probs, "probs", torch.float32), _dev_ptr(ws, "workspace"),
                                   ws.numel(), _stream_handle(stream)), "kq_softmax_rows")

@@ -94,6 +94,46 @@ def test_two_streams_with_separate_workspaces(kq):
     log("streams: 8 concurrent rounds on two streams equal the calls made alone")
 
 
+def test_two_streams_with_default_workspaces(kq):
+    """Calls that leave the workspace out on two streams at once: the
+    binding keeps one default workspace per device and stream, so the two
+    streams' calls never share a buffer. Eight rounds of kq_gemv_rows on
+    stream 1 and kq_verify_argmax_accept on stream 2, enqueued alternately
+    with no ordering between the streams, each equal bit for bit to the
+    same call made alone on its own workspace."""
+    nA = kA = synthetic.HIDDEN
+    nB, kB, mB = 32768, synthetic.HIDDEN, 8
+    wA = torch.from_numpy(synthetic.q4k_matrix(nA, kA, 311)).to(DEV)
+    wB = torch.from_numpy(synthetic.q4k_matrix(nB, kB, 312)).to(DEV)
+    xA = torch.from_numpy(synthetic.activations(16, kA, 313)).to(DEV)
+    xB = torch.from_numpy(synthetic.activations(mB, kB, 314)).to(DEV)
+    draft = list(range(200, 200 + mB - 1))
+    refA = kq.gemv_rows(wA, nA, kA, xA, workspace=kq.lib.alloc_workspace(kq.workspace_bytes(nA, kA, 16), DEV))
+    amB, accB, lgB = kq.verify(wB, nB, kB, xB, draft, want_logits=True,
+                               workspace=kq.lib.alloc_workspace(kq.workspace_bytes(nB, kB, mB), DEV))
+    torch.cuda.synchronize()
+    refA, amB, accB, lgB = refA.clone(), amB.clone(), accB.clone(), lgB.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(8):
+        oA = torch.full((16, nA), float("nan"), device=DEV)
+        oam = torch.full((mB,), -1, dtype=torch.int32, device=DEV)
+        oacc = torch.full((2,), -1, dtype=torch.int32, device=DEV)
+        olg = torch.full((mB, nB), float("nan"), device=DEV)
+        torch.cuda.synchronize()  # the fills are done before either stream starts
+        kq.gemv_rows(wA, nA, kA, xA, logits=oA, stream=s1)
+        kq.verify(wB, nB, kB, xB, draft, want_logits=True, stream=s2, out=(oam, oacc, olg))
+        outs.append((oA, oam, oacc, olg))
+    torch.cuda.synchronize()
+    for rep, (oA, oam, oacc, olg) in enumerate(outs):
+        assert torch.equal(oA, refA), f"round {rep}: stream-1 logits differ from the call alone"
+        assert torch.equal(oam, amB) and torch.equal(oacc, accB), f"round {rep}: stream-2 argmax / accept differ"
+        assert torch.equal(olg, lgB), f"round {rep}: stream-2 verify logits differ"
+    log("streams: default workspaces, 8 concurrent rounds on two streams equal the calls made alone")
+
+
 def test_four_host_threads_each_with_its_own_stream(kq):
     """Host reentrancy: four Python threads enter the library at once (ctypes
     releases the interpreter lock during each call), each enqueueing twelve
