@@ -183,6 +183,33 @@ def test_tree_verify_lm_head(kq):
     del rows
 
 
+@pytest.mark.parametrize("fmt,m", [("q5k", 48), ("q5k", 64), ("q6k", 40)])
+def test_tree_verify_lm_head_q5k_q6k_one_pass(kq, fmt, m):
+    """Q5_K and Q6_K LM heads (6,656 -> 131,072) at three and four slices in
+    one pass: every logit of every node row within tolerance, the argmax with
+    flags, and the walk equal to the oracle's walk on the GPU's argmax."""
+    h = synthetic.LM_HEAD
+    n, k = h["n"], h["k"]
+    x = synthetic.activations(m, k, 4343 + m)
+    w = synthetic.kquant_matrix(fmt, n, k, h["seed"] + 7)
+    log(f"tree {fmt}: oracle over {m} rows of the LM head")
+    L, A = oracle.gemv_rows(w, k, x, fmt=fmt)
+    o_am, _ = oracle.argmax_flags(L, A)
+    wt = kq.tile_weights(to_dev(w), n, k, fmt=fmt)
+    sc = kq.new_scratch(n, k, DEV)
+    st = kq.stage_rows(to_dev(x))
+    parent, token = make_tree(np.random.default_rng(50 + m), m, o_am, n)
+    am, acc, path, lg = kq.verify_tree_staged(wt, n, k, st, parent, token, sc, want_logits=True,
+                                              layout=kq.FORMATS[fmt][0])
+    torch.cuda.synchronize()
+    r = check_logits(lg.cpu().numpy(), L, A, what=f"tree {fmt} logits m={m}")
+    am, acc, path = am.cpu().numpy(), acc.cpu().numpy(), path.cpu().numpy()
+    check_argmax(am, L, A, what=f"tree {fmt} m={m}")
+    g_acc, g_nxt, g_path = oracle.tree_accept(parent, token, am)
+    assert (int(acc[0]), int(acc[1])) == (g_acc, g_nxt) and list(path[:g_acc]) == g_path
+    log(f"tree {fmt}: m={m} logits max |d|/tol = {r:.3g}, accepted {g_acc}")
+
+
 @pytest.mark.parametrize("m", [40, 64])
 def test_more_than_32_rows_host_staged_and_device_drafts(kq, m):
     """More than 32 rows (one pass at 3 or 4 slices) through the entry
