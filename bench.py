@@ -433,10 +433,10 @@ def kquant_timings(stack, torch, time_calls):
     """The Q5_K and Q6_K paths on the benchmark's shapes: the square
     6,656 x 6,656 product at M = 1 and 16 over 16 rotating copies of each
     format, and the LM-head verify (6,656 -> 131,072, M = 16, k = 15) with
-    Q6_K weights (the output layer's usual k-quant). Weight bytes per call
-    are the format's own (176 or 210 per 256 weights). Then the token-tree
-    verify of 24, 32, 48 and 64 nodes on the resident Q4_K LM head (rows/s
-    counts the tree's nodes)."""
+    Q6_K weights (the output layer's usual k-quant) and a 64-node token tree
+    on it. Weight bytes per call are the format's own (176 or 210 per 256
+    weights). Then the token-tree verify of 24, 32, 48 and 64 nodes on the
+    resident Q4_K LM head (rows/s counts the tree's nodes)."""
     kq = stack.kq
     dev = stack.dev
     out = {}
@@ -474,6 +474,20 @@ def kquant_timings(stack, torch, time_calls):
                                                  out=(stack.am, stack.acc, None), layout=kq.LAYOUT_Q6K_TILED16))
     out["lm_head_verify_m16_q6k"] = rate(h.n * (h.k // 256) * 210, 16, us,
                                          h.n * (h.k // 256) * 210 + 4 * 16 * h.k + 4 * 18)
+    # a 64-node token tree on the same Q6_K head, all nodes in one pass
+    g6 = np.random.default_rng(78)
+    x6 = torch.from_numpy(synthetic.activations(64, h.k, 4242)).to(dev)
+    parent6 = [-1] + [int(g6.integers(max(0, j - 6), j)) for j in range(1, 64)]
+    token6 = [0] + [int(t) for t in g6.integers(0, h.n, 63)]
+    st6 = kq.stage_rows(x6)
+    am6 = torch.empty(64, dtype=torch.int32, device=dev)
+    acc6 = torch.empty(2, dtype=torch.int32, device=dev)
+    path6 = torch.empty(64, dtype=torch.int32, device=dev)
+    us = time_calls(lambda i: kq.verify_tree_staged(w6, h.n, h.k, st6, parent6, token6, stack.head_scratch,
+                                                      out=(am6, acc6, path6, None), layout=kq.LAYOUT_Q6K_TILED16))
+    t6 = rate(h.n * (h.k // 256) * 210, 64, us, h.n * (h.k // 256) * 210 + 4 * 64 * h.k + 4 * (2 * 64 + 2))
+    t6["m64_over_lm_head_m16_q6k"] = round(us / out["lm_head_verify_m16_q6k"]["us_per_call"], 4)
+    out["tree_verify_lm_head_q6k_m64"] = t6
     del w6
     # token-tree verify on the resident Q4_K head: a tree of m nodes (parent
     # within the previous 6 nodes, seeded tokens), all nodes in one pass
