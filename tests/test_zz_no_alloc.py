@@ -3,7 +3,8 @@
 ABI twice in a row, the LM-head shape and then a smaller one, each compared
 bit for bit with kq_verify_argmax_accept on a workspace of its own (same
 kernels, same geometry): logits, argmax and the accept decision; the smaller
-call's logits also against the oracle."""
+call's logits also against the oracle; calls of two slices and one slice in
+turn; and the call captured in a HIP graph."""
 import ctypes
 
 import numpy as np
@@ -69,6 +70,25 @@ def test_noalloc_verify_matches_workspace_call_twice(kq):
         if n <= 4096:
             L, A = oracle.gemv_rows(w, k, x)
             check_logits(lg_a, L, A, what=f"noalloc n={n} k={k} m={m}")
+
+
+def test_noalloc_verify_more_rows_then_fewer(kq):
+    """Calls of different slice counts on the one device array: a 24-row
+    call (two slices) puts its staged rows, and so its control words and
+    partials, at other offsets than the 8-row call after it. Each equals the
+    workspace call bit for bit, and its logits the oracle."""
+    n, k = 2000, 2304
+    w = synthetic.q4k_matrix(n, k, 95)
+    wd = torch.from_numpy(w).to(DEV)
+    for m in (24, 8, 24):
+        log(f"noalloc: n={n} k={k} m={m}")
+        x = synthetic.activations(m, k, 96 + m)
+        draft = [int(t) for t in np.random.default_rng(97 + m).integers(0, n, m - 1)]
+        (am_a, acc_a, lg_a), (am_b, acc_b, lg_b) = verify_both(kq, wd, n, k, torch.from_numpy(x).to(DEV), draft)
+        assert np.array_equal(am_a, am_b) and np.array_equal(acc_a, acc_b), f"m={m}: argmax or accept"
+        assert np.array_equal(lg_a.view(np.uint32), lg_b.view(np.uint32)), f"m={m}: logits"
+        L, A = oracle.gemv_rows(w, k, x)
+        check_logits(lg_a, L, A, what=f"noalloc m={m}")
 
 
 def test_noalloc_verify_replays_from_a_graph(kq):
