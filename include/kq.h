@@ -324,8 +324,8 @@ kq_status kq_verify_staged_dev(const void *w, int layout, int64_t n, int64_t k, 
 /* Token-tree verify (ch. 33 "Speculation: the local win and the
  * distributed verdict", section 33.7: the hardware-aware token tree spends
  * the batch arithmetic a weight stream leaves idle on near-miss branches,
- * at 24, 32, 48 or 64 nodes). One pass over the weights (two above 32 nodes)
- * scores all m nodes (m <= 64; activation row i is node i's position),
+ * at 24, 32, 48 or 64 nodes). One pass over the weights scores all m nodes
+ * (m <= 64; activation row i is node i's position),
  * takes every row's argmax (ties -> lowest index) and walks the tree: from
  * the root (node 0), move to a child whose token equals the current node's
  * argmax (the lowest index when siblings repeat a token) until none does.
